@@ -1,0 +1,69 @@
+"""Byte accounting for the compressed cache and for one decode call.
+
+Host-side arithmetic used to report achieved bandwidth; no device work.
+
+Layout facts (the library's documented storage, see include/mkv.h):
+  * packed record of one 16-token block: K values, V values, K indices (u8),
+    V indices (u8), each [16][r]  ->  16 * r * 2 * (s + 1) bytes;
+  * per-block keys (min and max of every channel): 2 * d * s bytes;
+  * dense block of 16 tokens: 16 * 2 * d * s bytes.
+"""
+from __future__ import annotations
+
+BLOCK = 16
+
+
+def dense_kv_bytes(tokens: int, d: int, s: int) -> int:
+    """K and V of `tokens` tokens of one head: Eq. 2 of the reading notes per layer and head."""
+    return 2 * tokens * d * s
+
+
+def packed_record_bytes(r: int, s: int) -> int:
+    return BLOCK * r * 2 * (s + 1)
+
+
+def meta_block_bytes(d: int, s: int) -> int:
+    return 2 * d * s
+
+
+def quest_key_overhead(block: int = BLOCK) -> float:
+    """Per-block min+max keys relative to the block's dense K+V (paper section 6.3)."""
+    return meta_block_bytes(128, 2) / dense_kv_bytes(block, 128, 2)
+
+
+def notes_compressed_bytes(tokens: int, r: int, alpha: float, s: int, idx_bytes: int) -> dict:
+    """The reading notes' own accounting (Eq. 20-22): all-token K at r channels,
+    exact K/V of the selected tokens, and one index per kept element."""
+    k_all = tokens * r * s
+    sel = int(round(alpha * tokens)) * r * s * 2
+    idx = tokens * r * idx_bytes
+    return dict(k_all=k_all, selected=sel, indices=idx, total=k_all + sel + idx)
+
+
+def theoretical_speedup(alpha: float, beta: float) -> float:
+    """T*d / (s_selected * r) = 1 / (alpha * beta) (reading notes, Eq. 15)."""
+    return 1.0 / (alpha * beta)
+
+
+def decode_call_bytes(d: int, s: int, hkv: int, batch: int, hq: int, seg_summary) -> dict:
+    """Algorithmic bytes one decode call must read.
+
+    seg_summary: list over requests of lists over segments of dicts with
+      kind ('dense'|'packed'), filled tokens, r, n_blocks, union (the number of
+      distinct blocks selected by the query heads of a KV head, summed over KV
+      heads of the request).
+    Counts: every block's keys (all KV heads), each union record once, every
+    dense token, R_k and R_v per unit, plus the queries read and outputs written.
+    """
+    meta = records = dense = 0
+    for req in seg_summary:
+        for sg in req:
+            if sg["kind"] == "packed":
+                meta += sg["n_blocks"] * hkv * meta_block_bytes(d, s)
+                records += sg["union"] * packed_record_bytes(sg["r"], s)
+            else:
+                dense += dense_kv_bytes(sg["filled"], d, s) * hkv
+    rot = batch * hkv * 2 * d * d * 4
+    qo = 2 * batch * hq * d * 4
+    return dict(meta=meta, records=records, dense=dense, rot=rot, qo=qo,
+                total=meta + records + dense + rot + qo)

@@ -1,0 +1,210 @@
+/* mkv.h -- C ABI of the MosaicKV decode hot path for AMD Instinct MI355X (gfx950).
+ *
+ * MosaicKV ("MosaicKV: Serving Long-Context LLM with Dynamic Two-D KV Cache
+ * Compression", arXiv 2607.00760) compresses a KV cache in two dimensions:
+ * every key/value vector is rotated by its head's SVD-derived orthogonal
+ * matrix and keeps only its own r largest elements, stored as packed
+ * (channel index, value) pairs; at decode time each query head scores blocks
+ * of 16 tokens from per-block min/max keys, keeps the top-k blocks and runs
+ * attention directly on the packed vectors, rotating the result back.
+ *
+ * Sources cited below:
+ *   [N] "MosaicKV 阅读笔记" (reading notes, zhongzhuzhou.org): SVD background
+ *       (Eq. 3-5), rotation (Eq. 6-8), per-vector selection (Eq. 9,
+ *       Algorithm 1), block score / compressed attention / inverse rotation
+ *       (Eq. 12-14), packed sparse attention section, Quest paragraph.
+ *   [S] paperlayer.ai summary of the paper: sections 4.2, 4.3, 5.1-5.4, 6.3.
+ *
+ * Conventions for every call:
+ *   - Arguments are validated on the host before anything is enqueued. On an
+ *     error nothing is enqueued, no state changes, and a status is returned.
+ *   - Device work is enqueued on the caller's HIP stream (`stream` is a
+ *     hipStream_t; NULL is the null stream); calls return after the enqueue.
+ *     Faults of enqueued work surface at the caller's next synchronisation.
+ *   - The library allocates no device memory and keeps no state between calls
+ *     apart from the optional kernel-timing facility below. The caller owns
+ *     every buffer. Calls on distinct caches are thread-safe; one cache must be
+ *     used from one stream at a time.
+ *   - Inputs must be finite (NaN/Inf behaviour is unspecified).
+ *   - The GPU path supports head_dim == 128, storage MKV_F32 or MKV_BF16, and
+ *     1 to 4 query heads per KV head.
+ */
+#ifndef MKV_H
+#define MKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MKV_BLOCK_TOKENS 16        /* tokens per block ([S] 6.3: Quest block size 16) */
+#define MKV_HEAD_DIM 128           /* the only head dimension of the GPU path */
+#define MKV_MAX_GROUP 4            /* query heads per KV head */
+#define MKV_MAX_SEGMENTS 8         /* segments per request */
+#define MKV_MAX_PACKED_BLOCKS 65536 /* blocks of one packed segment (1,048,576 tokens) */
+
+typedef enum {
+    MKV_OK = 0,
+    MKV_ERR_ARG = 1,         /* invalid argument or descriptor */
+    MKV_ERR_UNSUPPORTED = 2, /* valid but not supported here (head_dim, dtype, group size) */
+    MKV_ERR_CAPACITY = 3,    /* an append would pass a request's total capacity */
+    MKV_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+    MKV_ERR_NOCONVERGE = 5,  /* eigensolver did not converge */
+    MKV_ERR_HIP = 6          /* a HIP launch or event call failed */
+} mkv_status;
+
+typedef enum { MKV_F32 = 0, MKV_BF16 = 1 } mkv_dtype;
+typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1 } mkv_seg_kind;
+
+/* One segment of one request ([S] 4.1, 4.3: the cache is split into segments,
+ * each with its own channel retention and block retention).
+ *
+ * kind      MKV_SEG_DENSE: tokens are rotated and stored at full width and are
+ *           always attended (attention-sink and recent-window segments).
+ *           MKV_SEG_PACKED: tokens keep their own r largest rotated elements
+ *           ([N] Eq. 9) and blocks are chosen per query head by top-k.
+ * r         kept elements per vector, 1..head_dim (packed only).
+ * keep_ppm  block keep ratio in parts per million, 1..1000000 (packed only);
+ *           k = ceil(keep_ppm * n_blocks / 1e6) in integers, clamped to [1, n].
+ * k_abs     if > 0, keep min(k_abs, n_blocks) blocks instead.
+ * t_begin   position of the segment's first token; segments of a request are
+ *           contiguous and ordered: t_begin[0] = 0, t_begin[j+1] = t_begin[j] + t_cap[j].
+ * t_cap     capacity in tokens (> 0).
+ * data      device buffer of mkv_segment_bytes() bytes (layout below).
+ * meta      device buffer of the meta bytes reported by mkv_segment_bytes()
+ *           (packed only; NULL for dense).
+ * Across the requests of one cache, segment j must have the same kind, r,
+ * keep_ppm and k_abs; t_begin and t_cap may differ per request.
+ *
+ * Device layouts (s = bytes per stored element, nb = ceil(t_cap / 16),
+ * block l holds positions t_begin + 16 l .. t_begin + 16 l + 15, slot = position - block start):
+ *   dense data : [n_kv_heads][nb][2][16][d] stored rotated K' (index 0) and V'.
+ *   packed data: [n_kv_heads][nb][record], record of 16 * r * 2 * (s + 1) bytes =
+ *                K values [16][r] | V values [16][r] | K indices [16][r] u8 |
+ *                V indices [16][r] u8; each vector's kept channels in ascending
+ *                channel order. Slots of a block past its last token are zero.
+ *   packed meta: [n_kv_heads][ceil(nb / 64)][2 d s / 16][64][16 bytes]: for the
+ *                block l, lane l % 64 of tile l / 64 holds, per 16-byte group,
+ *                the (min, max) pairs of 16 / (2 s) consecutive channels
+ *                (bf16: channels 4g..4g+3, f32: 2g..2g+1), min first. min/max are
+ *                taken over the block's tokens of the stored sparse keys (0 at
+ *                dropped channels) in IEEE totalOrder (-0 < +0).
+ */
+typedef struct mkv_segment {
+    int32_t kind;
+    int32_t r;
+    int32_t keep_ppm;
+    int32_t k_abs;
+    int64_t t_begin;
+    int64_t t_cap;
+    void *data;
+    void *meta;
+} mkv_segment;
+
+/* A compressed cache for one attention layer of a batch of requests.
+ *   segs  host array [batch][n_segments], owned by the caller.
+ *   len   host array [batch]: tokens stored per request. Host-authoritative:
+ *         mkv_compress_append advances it after enqueueing, so no device-to-host
+ *         synchronisation is ever needed.
+ *   rot   device [batch][n_kv_heads][2][d][d] float32: R_k (index 0) and R_v,
+ *         row c = c-th right singular vector ([N] Eq. 4, 6-8), e.g. from
+ *         mkv_rotation_from_prefill. Query head h uses KV head h / (n_q_heads / n_kv_heads).
+ */
+typedef struct mkv_cache {
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+    int32_t n_segments;
+    mkv_segment *segs;
+    int64_t *len;
+    const float *rot;
+} mkv_cache;
+
+/* Human-readable name of a status code (static string). */
+const char *mkv_status_str(mkv_status s);
+
+/* Rotation of one head from its prefill vectors ([N] Eq. 4, 6-8; [S] 2.3).
+ * x_host [T][d] on the host, in `dtype` (f32 values, or bf16 bit patterns as
+ * uint16). Computes G = X^T X in float64 (no centering), its eigenvectors by
+ * Householder tridiagonalisation and implicit QL, orders them by descending
+ * eigenvalue and makes the largest-magnitude entry of each row positive (ties
+ * to the lower index). R_out [d][d] host float32 (row c = c-th vector),
+ * sigma_out [d] host float64 (nullable) = sqrt(max(eigenvalue, 0)).
+ * Synchronous host computation (OpenMP); d in 1..256, T >= 0.
+ * Errors: MKV_ERR_ARG, MKV_ERR_NOCONVERGE. */
+mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtype, int64_t T, int32_t d,
+                                     float *R_out, double *sigma_out);
+
+/* Bytes of the device buffers of one segment: returns the data bytes and
+ * writes the meta bytes (0 for dense) to meta_bytes_out (nullable).
+ * Returns 0 for invalid arguments. */
+size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads,
+                         int64_t t_cap, size_t *meta_bytes_out);
+
+/* Compress and append new tokens ([N] Eq. 7-9, Algorithm 1; [S] 4.2, 5.2, 5.4:
+ * new vectors are rotated by the head's R, keep their top-r elements and are
+ * packed on arrival; prefill uses the same call with many tokens).
+ * k_new, v_new: device [batch][n_kv_heads][n_max][d] in the cache dtype; request b
+ * appends rows 0 .. n_new[b]-1 at positions len[b] ... (n_new host [batch], each
+ * 0..n_max). Each vector is rotated in float64 with exact products (summed in
+ * ascending input channel), ranked by the unrounded magnitudes (ties to the
+ * lower channel) and rounded once, to nearest even, to the storage type.
+ * Packed segments also update the min/max keys of the blocks they touch.
+ * Advances c->len on success.
+ * Errors: MKV_ERR_ARG, MKV_ERR_UNSUPPORTED, MKV_ERR_CAPACITY, MKV_ERR_HIP. */
+mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new,
+                               const int32_t *n_new, int32_t n_max, void *stream);
+
+/* Recompute the per-block min/max keys of packed segment `seg` of every request
+ * from its stored records ([N] Quest paragraph; [S] 5.2). The result equals the
+ * keys kept up to date by mkv_compress_append, bit for bit.
+ * Errors: MKV_ERR_ARG, MKV_ERR_UNSUPPORTED, MKV_ERR_HIP. */
+mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream);
+
+/* Workspace bytes mkv_decode_attn needs for this cache (sized from capacities,
+ * so it does not change as the cache fills). */
+size_t mkv_decode_workspace_bytes(const mkv_cache *c);
+
+/* Columns of sel_out needed at the current lengths: max over requests of the
+ * sum over packed segments of k. */
+int64_t mkv_decode_sel_cols(const mkv_cache *c);
+
+/* Decode attention straight from the compressed cache ([N] Eq. 12-14; [S] 4.2,
+ * 5.3). For every request b and query head h, with q' = R_k q:
+ *   score of block l = (1/sqrt d) sum_c max(q'_c mx_c, q'_c mn_c) over the
+ *     block's min/max keys, for every block of every packed segment;
+ *   per packed segment, the k blocks of highest score (ties to the lower block);
+ *   o = softmax(q' K^T / sqrt d) V^ over every stored dense token and every
+ *     token of a selected block, with K^, V^ the packed sparse vectors;
+ *   out = o R_v (the inverse rotation).
+ * q [batch][n_q_heads][d] device float32; out [batch][n_q_heads][d] device float32.
+ * sel_out (nullable) device int32 [batch][n_q_heads][sel_cols]: per packed
+ *   segment in order, its k selected block indices (relative to the segment)
+ *   ascending, then -1 up to sel_cols (>= mkv_decode_sel_cols()).
+ * workspace: device buffer of at least mkv_decode_workspace_bytes() bytes.
+ * Scores accumulate in float32, the softmax and the sums in float32. A head
+ * with no stored token outputs zeros.
+ * Errors: MKV_ERR_ARG, MKV_ERR_UNSUPPORTED, MKV_ERR_WORKSPACE, MKV_ERR_HIP. */
+mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32_t *sel_out,
+                           int64_t sel_cols, void *workspace, size_t ws_bytes, void *stream);
+
+/* Optional kernel timing (a diagnostic, not thread-safe): while enabled, every
+ * kernel the library launches is bracketed by HIP events on its stream.
+ * mkv_timing_read synchronises those events and returns, per stage, the summed
+ * milliseconds and the number of launches since the last read, then clears
+ * them. Stages: 0 compress, 1 block_meta, 2 q_rotate, 3 score, 4 select,
+ * 5 attend, 6 merge. */
+#define MKV_N_STAGES 7
+mkv_status mkv_timing_enable(int32_t on);
+mkv_status mkv_timing_read(double *ms_out, int64_t *count_out, int32_t n_stages);
+const char *mkv_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MKV_H */

@@ -1,0 +1,139 @@
+"""ctypes binding of libmkv.so (include/mkv.h). Argument marshalling only.
+
+Every function has the name of the C entry point it calls. Errors raise
+MkvError carrying the C status. The shared library must exist (built by
+build.py / __graft_entry__.build()); if it cannot be loaded this module raises
+at import time -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmkv.so")
+
+MKV_OK, MKV_ERR_ARG, MKV_ERR_UNSUPPORTED, MKV_ERR_CAPACITY, MKV_ERR_WORKSPACE, MKV_ERR_NOCONVERGE, \
+    MKV_ERR_HIP = range(7)
+MKV_F32, MKV_BF16 = 0, 1
+MKV_SEG_DENSE, MKV_SEG_PACKED = 0, 1
+MKV_BLOCK_TOKENS = 16
+MKV_HEAD_DIM = 128
+MKV_MAX_GROUP = 4
+MKV_MAX_SEGMENTS = 8
+MKV_MAX_PACKED_BLOCKS = 65536
+MKV_N_STAGES = 7
+
+EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
+           "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",
+           "mkv_timing_enable", "mkv_timing_read", "mkv_stage_name"]
+
+
+class mkv_segment(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("keep_ppm", ctypes.c_int32),
+                ("k_abs", ctypes.c_int32), ("t_begin", ctypes.c_int64), ("t_cap", ctypes.c_int64),
+                ("data", ctypes.c_void_p), ("meta", ctypes.c_void_p)]
+
+
+class mkv_cache(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("segs", ctypes.POINTER(mkv_segment)), ("len", ctypes.POINTER(ctypes.c_int64)),
+                ("rot", ctypes.c_void_p)]
+
+
+class MkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, mkv_status_str(status), status))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmkv.so not built at %s (run __graft_entry__.build())" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.mkv_status_str.restype = ctypes.c_char_p
+    L.mkv_status_str.argtypes = [ctypes.c_int]
+    L.mkv_rotation_from_prefill.restype = ctypes.c_int
+    L.mkv_rotation_from_prefill.argtypes = [P, I32, I64, I32, P, P]
+    L.mkv_segment_bytes.restype = SZ
+    L.mkv_segment_bytes.argtypes = [I32, I32, I32, I32, I32, I64, ctypes.POINTER(SZ)]
+    L.mkv_compress_append.restype = ctypes.c_int
+    L.mkv_compress_append.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P]
+    L.mkv_block_meta.restype = ctypes.c_int
+    L.mkv_block_meta.argtypes = [ctypes.POINTER(mkv_cache), I32, P]
+    L.mkv_decode_workspace_bytes.restype = SZ
+    L.mkv_decode_workspace_bytes.argtypes = [ctypes.POINTER(mkv_cache)]
+    L.mkv_decode_sel_cols.restype = I64
+    L.mkv_decode_sel_cols.argtypes = [ctypes.POINTER(mkv_cache)]
+    L.mkv_decode_attn.restype = ctypes.c_int
+    L.mkv_decode_attn.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I64, P, SZ, P]
+    L.mkv_timing_enable.restype = ctypes.c_int
+    L.mkv_timing_enable.argtypes = [I32]
+    L.mkv_timing_read.restype = ctypes.c_int
+    L.mkv_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), I32]
+    L.mkv_stage_name.restype = ctypes.c_char_p
+    L.mkv_stage_name.argtypes = [I32]
+    return L
+
+
+LIB = _load()
+
+
+def _check(st: int, where: str):
+    if st != MKV_OK:
+        raise MkvError(st, where)
+
+
+def mkv_status_str(st: int) -> str:
+    return LIB.mkv_status_str(st).decode()
+
+
+def mkv_rotation_from_prefill(x_ptr: int, dtype: int, T: int, d: int, R_out_ptr: int, sigma_out_ptr):
+    _check(LIB.mkv_rotation_from_prefill(x_ptr, dtype, T, d, R_out_ptr, sigma_out_ptr),
+           "mkv_rotation_from_prefill")
+
+
+def mkv_segment_bytes(dtype: int, kind: int, r: int, d: int, n_kv_heads: int, t_cap: int):
+    meta = ctypes.c_size_t(0)
+    data = LIB.mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap, ctypes.byref(meta))
+    return int(data), int(meta.value)
+
+
+def mkv_compress_append(cache: mkv_cache, k_ptr: int, v_ptr: int, n_new_ptr: int, n_max: int, stream: int):
+    _check(LIB.mkv_compress_append(ctypes.byref(cache), k_ptr, v_ptr, n_new_ptr, n_max, stream),
+           "mkv_compress_append")
+
+
+def mkv_block_meta(cache: mkv_cache, seg: int, stream: int):
+    _check(LIB.mkv_block_meta(ctypes.byref(cache), seg, stream), "mkv_block_meta")
+
+
+def mkv_decode_workspace_bytes(cache: mkv_cache) -> int:
+    return int(LIB.mkv_decode_workspace_bytes(ctypes.byref(cache)))
+
+
+def mkv_decode_sel_cols(cache: mkv_cache) -> int:
+    return int(LIB.mkv_decode_sel_cols(ctypes.byref(cache)))
+
+
+def mkv_decode_attn(cache: mkv_cache, q_ptr: int, out_ptr: int, sel_ptr, sel_cols: int, ws_ptr: int,
+                    ws_bytes: int, stream: int):
+    _check(LIB.mkv_decode_attn(ctypes.byref(cache), q_ptr, out_ptr, sel_ptr, sel_cols, ws_ptr, ws_bytes,
+                               stream), "mkv_decode_attn")
+
+
+def mkv_timing_enable(on: bool):
+    _check(LIB.mkv_timing_enable(1 if on else 0), "mkv_timing_enable")
+
+
+def mkv_timing_read():
+    ms = (ctypes.c_double * MKV_N_STAGES)()
+    cnt = (ctypes.c_int64 * MKV_N_STAGES)()
+    _check(LIB.mkv_timing_read(ms, cnt, MKV_N_STAGES), "mkv_timing_read")
+    return {LIB.mkv_stage_name(i).decode(): (ms[i], int(cnt[i])) for i in range(MKV_N_STAGES)}
+
+
+def mkv_stage_name(i: int) -> str:
+    return LIB.mkv_stage_name(i).decode()

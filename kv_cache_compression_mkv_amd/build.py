@@ -1,0 +1,61 @@
+"""Build libmkv.so (HIP kernels for gfx950 + host C++ library) in-tree."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libmkv.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+
+HIP_SOURCES = ["compress.hip", "decode.hip"]
+HOST_SOURCES = ["mkv_host.cpp", "rotation.cpp"]
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             # no packed-fp32 instructions anywhere in the device code
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fopenmp", "-D__HIP_PLATFORM_AMD__",
+              "-I" + os.path.join(ROCM, "include")]
+
+
+def _run(cmd):
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = False, save_temps: bool = False) -> str:
+    bdir = os.path.join(ROOT, "_build", "mkv")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if save_temps:
+            cmd += ["-save-temps=obj"]
+        if verbose:
+            print(" ".join(cmd))
+        _run(cmd)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(bdir, src + ".o")
+        cmd = ["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        _run(cmd)
+        objs.append(obj)
+    tmp = OUT + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + \
+        ["-lgomp", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd))
+    _run(cmd)
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    import sys
+    print(build(verbose=True, save_temps="--save-temps" in sys.argv))

@@ -1,0 +1,254 @@
+// Compression of new K/V vectors into dense or packed segments, and the bulk
+// recomputation of per-block min/max keys.
+//
+// Per vector ("MosaicKV 阅读笔记" reading notes, Eq. 7-9 and Algorithm 1;
+// paper summary sections 4.2 and 5.2):
+//   x'_c = sum_j R[c][j] x_j          float64, exact products, j ascending
+//   keep the r channels of largest |x'_c| (ties to the lower channel)
+//   store (channel, round(x'_c)) pairs in ascending channel order
+// Packed segments also keep per-block min/max keys of the stored sparse key
+// vectors up to date (the Quest-style block keys of the reading notes' Quest
+// paragraph and the paper's section 5.2).
+//
+// One workgroup of two waves handles one block of one (request, segment, KV
+// head): wave 0 the keys, wave 1 the values. Lane l owns channels l and l+64,
+// so the top-r selection is a wave-wide radix search with ballots and the
+// packing order falls out of a ballot prefix count.
+#include "device_util.hpp"
+#include "mkv_internal.h"
+
+namespace mkv {
+
+namespace {
+
+// Compute x' = R x for the wave's token staged in xs (float, exact copy of
+// the stored input). Lane owns channels c0 = lane and c1 = lane + 64.
+__device__ __forceinline__ void rotate_f64(const float *__restrict__ R, const float *xs, int lane,
+                                           double &acc0, double &acc1) {
+    const float4 *r0 = reinterpret_cast<const float4 *>(R + (size_t)lane * D);
+    const float4 *r1 = reinterpret_cast<const float4 *>(R + (size_t)(lane + 64) * D);
+    const float4 *x4 = reinterpret_cast<const float4 *>(xs);
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll 4
+    for (int j = 0; j < D / 4; ++j) {
+        const float4 u = r0[j], v = r1[j], x = x4[j];
+        a0 = fma((double)u.x, (double)x.x, a0);
+        a0 = fma((double)u.y, (double)x.y, a0);
+        a0 = fma((double)u.z, (double)x.z, a0);
+        a0 = fma((double)u.w, (double)x.w, a0);
+        a1 = fma((double)v.x, (double)x.x, a1);
+        a1 = fma((double)v.y, (double)x.y, a1);
+        a1 = fma((double)v.z, (double)x.z, a1);
+        a1 = fma((double)v.w, (double)x.w, a1);
+    }
+    acc0 = a0;
+    acc1 = a1;
+}
+
+// Keep the r channels of largest magnitude (ties to the lower channel).
+// Keys are the magnitude bit patterns (63 bits; order = magnitude order).
+// The r-th largest key is found bit by bit with ballot counts.
+__device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane, bool &keep0,
+                                          bool &keep1) {
+    const uint64_t k0 = (uint64_t)__double_as_longlong(v0) & 0x7FFFFFFFFFFFFFFFull;
+    const uint64_t k1 = (uint64_t)__double_as_longlong(v1) & 0x7FFFFFFFFFFFFFFFull;
+    uint64_t thr = 0;
+    for (int bit = 62; bit >= 0; --bit) {
+        const uint64_t cand = thr | (1ull << bit);
+        const int cnt = popc64(ballot(k0 >= cand)) + popc64(ballot(k1 >= cand));
+        if (cnt >= r) thr = cand;
+    }
+    const bool gt0 = k0 > thr, gt1 = k1 > thr;
+    const int need = r - popc64(ballot(gt0)) - popc64(ballot(gt1));
+    const uint64_t e0 = ballot(k0 == thr), e1 = ballot(k1 == thr);
+    const uint64_t below = lanes_below(lane);
+    const int rank0 = popc64(e0 & below);
+    const int rank1 = popc64(e0) + popc64(e1 & below);
+    keep0 = gt0 || ((k0 == thr) && rank0 < need);
+    keep1 = gt1 || ((k1 == thr) && rank1 < need);
+}
+
+template <typename ST>
+__global__ __launch_bounds__(128) void k_compress(const CompressArgs A) {
+    using bits_t = typename ST::bits_t;
+    const CompressEntry &E = A.ent[blockIdx.z];
+    if ((int)blockIdx.x >= E.nblk) return;
+    const int blk = E.blk0 + (int)blockIdx.x;
+    const int g = (int)blockIdx.y;
+    const int wave = (int)(threadIdx.x >> 6);  // 0: K, 1: V
+    const int lane = lane_id();
+    const int p0 = blk * BT;
+    const int sa = max(E.a, p0) - p0;
+    const int se = min(E.e, p0 + BT) - p0;
+    const size_t unit = (size_t)E.b * A.n_kv + g;
+    const float *R = A.rot + (unit * 2 + wave) * D * D;
+    const bits_t *xin = reinterpret_cast<const bits_t *>(wave ? A.v_new : A.k_new) + unit * A.n_max * D;
+    __shared__ __align__(16) float xs[2][D];
+
+    const bool packed = E.kind == MKV_SEG_PACKED;
+    const int r = E.r;
+    char *blkbase;
+    if (packed) {
+        const size_t rec = (size_t)BT * r * 2 * (ST::bytes + 1);
+        blkbase = static_cast<char *>(E.data) + ((size_t)g * E.nbcap + blk) * rec;
+    } else {
+        blkbase = static_cast<char *>(E.data) + ((size_t)g * E.nbcap + blk) * 2 * BT * D * ST::bytes;
+    }
+    bits_t *vals = packed ? reinterpret_cast<bits_t *>(blkbase + (size_t)wave * BT * r * ST::bytes)
+                          : reinterpret_cast<bits_t *>(blkbase + (size_t)wave * BT * D * ST::bytes);
+    uint8_t *idxs = packed ? reinterpret_cast<uint8_t *>(blkbase + (size_t)2 * BT * r * ST::bytes +
+                                                         (size_t)wave * BT * r)
+                           : nullptr;
+
+    // per-block keys (keys wave, packed segments): running totalOrder min/max
+    const bool do_meta = packed && wave == 0;
+    const int G16 = 2 * D * ST::bytes / 16;  // 16-byte groups per block
+    const int cpg = 16 / (2 * ST::bytes);    // channels per group
+    char *meta_tile = nullptr;
+    uint32_t mn0 = 0xFFFFFFFFu, mx0 = 0u, mn1 = 0xFFFFFFFFu, mx1 = 0u;
+    if (do_meta) {
+        const int ntile = (E.nbcap + META_TILE - 1) / META_TILE;
+        meta_tile = static_cast<char *>(E.meta) + ((size_t)g * ntile + blk / META_TILE) * G16 * META_TILE * 16;
+        if (sa > 0) {  // block already holds tokens: start from its keys
+            const int bl = blk % META_TILE;
+            for (int h = 0; h < 2; ++h) {
+                const int c = lane + 64 * h;
+                const bits_t *pr = reinterpret_cast<const bits_t *>(
+                    meta_tile + ((size_t)(c / cpg) * META_TILE + bl) * 16 + (c % cpg) * 2 * ST::bytes);
+                const uint32_t kmn = order_key<ST>(pr[0]), kmx = order_key<ST>(pr[1]);
+                if (h == 0) { mn0 = kmn; mx0 = kmx; } else { mn1 = kmn; mx1 = kmx; }
+            }
+        }
+    }
+
+    for (int slot = sa; slot < se; ++slot) {
+        const int row = E.row0 + (p0 + slot - E.a);
+        const bits_t *xr = xin + (size_t)row * D;
+        xs[wave][lane] = bits_to_float<ST>(xr[lane]);
+        xs[wave][lane + 64] = bits_to_float<ST>(xr[lane + 64]);
+        wave_lds_sync();
+        double v0, v1;
+        rotate_f64(R, xs[wave], lane, v0, v1);
+        wave_lds_sync();
+        const bits_t s0 = round_store<ST>(v0), s1 = round_store<ST>(v1);
+        if (packed) {
+            bool keep0, keep1;
+            topr_keep(v0, v1, r, lane, keep0, keep1);
+            const uint64_t m0 = ballot(keep0), m1 = ballot(keep1);
+            const uint64_t below = lanes_below(lane);
+            bits_t *vrow = vals + (size_t)slot * r;
+            uint8_t *irow = idxs + (size_t)slot * r;
+            if (keep0) {
+                const int pos = popc64(m0 & below);
+                vrow[pos] = s0;
+                irow[pos] = (uint8_t)lane;
+            }
+            if (keep1) {
+                const int pos = popc64(m0) + popc64(m1 & below);
+                vrow[pos] = s1;
+                irow[pos] = (uint8_t)(lane + 64);
+            }
+            if (do_meta) {
+                const uint32_t q0 = order_key<ST>(keep0 ? s0 : (bits_t)0);
+                const uint32_t q1 = order_key<ST>(keep1 ? s1 : (bits_t)0);
+                mn0 = min(mn0, q0); mx0 = max(mx0, q0);
+                mn1 = min(mn1, q1); mx1 = max(mx1, q1);
+            }
+        } else {
+            bits_t *vrow = vals + (size_t)slot * D;
+            vrow[lane] = s0;
+            vrow[lane + 64] = s1;
+        }
+    }
+
+    // a block started by this call: clear the slots after its last token
+    if (sa == 0 && se < BT) {
+        if (packed) {
+            for (int i = se * r + lane; i < BT * r; i += 64) {
+                vals[i] = (bits_t)0;
+                idxs[i] = 0;
+            }
+        } else {
+            for (int i = se * D + lane; i < BT * D; i += 64) vals[i] = (bits_t)0;
+        }
+    }
+
+    if (do_meta && se > sa) {
+        const int bl = blk % META_TILE;
+        for (int h = 0; h < 2; ++h) {
+            const int c = lane + 64 * h;
+            bits_t *pr = reinterpret_cast<bits_t *>(meta_tile + ((size_t)(c / cpg) * META_TILE + bl) * 16 +
+                                                    (c % cpg) * 2 * ST::bytes);
+            pr[0] = key_to_bits<ST>(h == 0 ? mn0 : mn1);
+            pr[1] = key_to_bits<ST>(h == 0 ? mx0 : mx1);
+        }
+    }
+}
+
+// Bulk recomputation of the per-block keys of one packed segment from the
+// stored records. One wave per block: the kept values of each valid token are
+// scattered into a zeroed dense row in LDS and folded into totalOrder min/max.
+template <typename ST>
+__global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
+    using bits_t = typename ST::bits_t;
+    const MetaEntry &E = A.ent[blockIdx.z];
+    const int blk = (int)blockIdx.x;
+    if (blk >= E.nb) return;
+    const int g = (int)blockIdx.y;
+    const int lane = lane_id();
+    const int r = E.r;
+    const size_t rec = (size_t)BT * r * 2 * (ST::bytes + 1);
+    const char *base = static_cast<const char *>(E.data) + ((size_t)g * E.nbcap + blk) * rec;
+    const bits_t *kv = reinterpret_cast<const bits_t *>(base);
+    const uint8_t *ki = reinterpret_cast<const uint8_t *>(base + (size_t)2 * BT * r * ST::bytes);
+    const int nvalid = min(BT, E.filled - blk * BT);
+    __shared__ bits_t row[D];
+    uint32_t mn0 = 0xFFFFFFFFu, mx0 = 0u, mn1 = 0xFFFFFFFFu, mx1 = 0u;
+    for (int t = 0; t < nvalid; ++t) {
+        row[lane] = 0;
+        row[lane + 64] = 0;
+        wave_lds_sync();
+        for (int m = lane; m < r; m += 64) row[ki[t * r + m] & (D - 1)] = kv[t * r + m];
+        wave_lds_sync();
+        const uint32_t q0 = order_key<ST>(row[lane]), q1 = order_key<ST>(row[lane + 64]);
+        mn0 = min(mn0, q0); mx0 = max(mx0, q0);
+        mn1 = min(mn1, q1); mx1 = max(mx1, q1);
+        wave_lds_sync();
+    }
+    const int G16 = 2 * D * ST::bytes / 16;
+    const int cpg = 16 / (2 * ST::bytes);
+    const int ntile = (E.nbcap + META_TILE - 1) / META_TILE;
+    char *tile = static_cast<char *>(E.meta) + ((size_t)g * ntile + blk / META_TILE) * G16 * META_TILE * 16;
+    const int bl = blk % META_TILE;
+    for (int h = 0; h < 2; ++h) {
+        const int c = lane + 64 * h;
+        bits_t *pr = reinterpret_cast<bits_t *>(tile + ((size_t)(c / cpg) * META_TILE + bl) * 16 +
+                                                (c % cpg) * 2 * ST::bytes);
+        pr[0] = key_to_bits<ST>(h == 0 ? mn0 : mn1);
+        pr[1] = key_to_bits<ST>(h == 0 ? mx0 : mx1);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s) {
+    if (a.n_ent <= 0 || max_blk <= 0) return hipSuccess;
+    const dim3 grid((unsigned)max_blk, (unsigned)a.n_kv, (unsigned)a.n_ent);
+    if (dtype == MKV_BF16)
+        hipLaunchKernelGGL(k_compress<Bf16>, grid, dim3(128), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_compress<F32>, grid, dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_meta(const MetaArgs &a, int dtype, int max_nb, hipStream_t s) {
+    if (a.n_ent <= 0 || max_nb <= 0) return hipSuccess;
+    const dim3 grid((unsigned)max_nb, (unsigned)a.n_kv, (unsigned)a.n_ent);
+    if (dtype == MKV_BF16)
+        hipLaunchKernelGGL(k_block_meta<Bf16>, grid, dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_block_meta<F32>, grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace mkv

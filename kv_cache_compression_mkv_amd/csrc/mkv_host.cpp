@@ -1,0 +1,438 @@
+// C ABI of the MosaicKV decode path: argument validation, launch planning and
+// the optional kernel timing. All device work is in compress.hip / decode.hip.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "mkv_internal.h"
+
+using namespace mkv;
+
+namespace {
+
+// ---------------------------------------------------------------- timing --
+struct PendingPair {
+    hipEvent_t a, b;
+};
+struct Timing {
+    bool on = false;
+    std::vector<PendingPair> pending[MKV_N_STAGES];
+    std::vector<hipEvent_t> pool;
+    std::mutex mu;
+};
+Timing &timing() {
+    static Timing t;
+    return t;
+}
+
+hipEvent_t take_event(Timing &t) {
+    if (!t.pool.empty()) {
+        hipEvent_t e = t.pool.back();
+        t.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+mkv_status timed(int stage, hipStream_t s, F &&launch) {
+    Timing &t = timing();
+    hipEvent_t a = nullptr, b = nullptr;
+    if (t.on) {
+        std::lock_guard<std::mutex> g(t.mu);
+        a = take_event(t);
+        b = take_event(t);
+        if (!a || !b) return MKV_ERR_HIP;
+        if (hipEventRecord(a, s) != hipSuccess) return MKV_ERR_HIP;
+    }
+    if (launch() != hipSuccess) return MKV_ERR_HIP;
+    if (t.on) {
+        std::lock_guard<std::mutex> g(t.mu);
+        if (hipEventRecord(b, s) != hipSuccess) return MKV_ERR_HIP;
+        t.pending[stage].push_back({a, b});
+    }
+    return MKV_OK;
+}
+
+// ------------------------------------------------------------ validation --
+int64_t keep_blocks(int64_t n, int32_t keep_ppm, int32_t k_abs) {
+    if (n <= 0) return 0;
+    int64_t k = k_abs > 0 ? std::min<int64_t>(k_abs, n) : ((int64_t)keep_ppm * n + 999999) / 1000000;
+    return std::max<int64_t>(1, std::min(k, n));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int elem_bytes(int32_t dtype) { return dtype == MKV_BF16 ? 2 : 4; }
+
+const mkv_segment &segof(const mkv_cache *c, int b, int j) { return c->segs[(size_t)b * c->n_segments + j]; }
+
+int64_t seg_filled(const mkv_cache *c, int b, int j) {
+    const mkv_segment &s = segof(c, b, j);
+    return std::max<int64_t>(0, std::min<int64_t>(c->len[b] - s.t_begin, s.t_cap));
+}
+
+mkv_status check_cache(const mkv_cache *c) {
+    if (!c || !c->segs || !c->len || !c->rot) return MKV_ERR_ARG;
+    if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
+        return MKV_ERR_ARG;
+    if (c->n_segments < 1 || c->n_segments > MKV_MAX_SEGMENTS) return MKV_ERR_ARG;
+    if (c->dtype != MKV_F32 && c->dtype != MKV_BF16) return MKV_ERR_UNSUPPORTED;
+    if (c->head_dim != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4) return MKV_ERR_UNSUPPORTED;
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t t = 0;
+        for (int j = 0; j < c->n_segments; ++j) {
+            const mkv_segment &s = segof(c, b, j);
+            const mkv_segment &s0 = segof(c, 0, j);
+            if (s.kind != MKV_SEG_DENSE && s.kind != MKV_SEG_PACKED) return MKV_ERR_ARG;
+            if (s.t_begin != t || s.t_cap < 1 || !s.data) return MKV_ERR_ARG;
+            if (s.kind != s0.kind || s.r != s0.r || s.keep_ppm != s0.keep_ppm || s.k_abs != s0.k_abs)
+                return MKV_ERR_ARG;
+            if (s.kind == MKV_SEG_PACKED) {
+                if (s.r < 1 || s.r > c->head_dim || !s.meta || s.k_abs < 0) return MKV_ERR_ARG;
+                if (s.k_abs == 0 && (s.keep_ppm < 1 || s.keep_ppm > 1000000)) return MKV_ERR_ARG;
+                if (ceil_div(s.t_cap, BT) > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
+            }
+            if ((reinterpret_cast<uintptr_t>(s.data) & 15) || (reinterpret_cast<uintptr_t>(s.meta) & 15))
+                return MKV_ERR_ARG;
+            t += s.t_cap;
+        }
+        if (t > INT32_MAX) return MKV_ERR_UNSUPPORTED;
+        if (c->len[b] < 0 || c->len[b] > t) return MKV_ERR_ARG;
+    }
+    return MKV_OK;
+}
+
+// ---------------------------------------------------------- workspace map --
+struct WsMap {
+    size_t qa, qs, scores, mask, sel, part, total;
+    int64_t sc_off[MKV_MAX_SEGMENTS], mk_off[MKV_MAX_SEGMENTS], sl_off[MKV_MAX_SEGMENTS];
+    int32_t nbcap[MKV_MAX_SEGMENTS], kcap[MKV_MAX_SEGMENTS], pseg[MKV_MAX_SEGMENTS];
+    int npk;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsMap ws_map(const mkv_cache *c) {
+    WsMap m{};
+    const size_t B = c->batch, Hq = c->n_q_heads, Hkv = c->n_kv_heads;
+    const int G = (int)(Hq / Hkv);
+    int64_t sc = 0, mk = 0, sl = 0;
+    m.npk = 0;
+    for (int j = 0; j < c->n_segments; ++j) {
+        if (segof(c, 0, j).kind != MKV_SEG_PACKED) continue;
+        int64_t nbc = 0;
+        for (int b = 0; b < c->batch; ++b) nbc = std::max<int64_t>(nbc, ceil_div(segof(c, b, j).t_cap, BT));
+        const mkv_segment &s = segof(c, 0, j);
+        const int p = m.npk++;
+        m.pseg[p] = j;
+        m.nbcap[p] = (int32_t)nbc;
+        m.kcap[p] = (int32_t)keep_blocks(nbc, s.keep_ppm, s.k_abs);
+        m.sc_off[p] = sc;
+        m.mk_off[p] = mk;
+        m.sl_off[p] = sl;
+        sc += (int64_t)(B * Hq) * nbc;
+        mk += (int64_t)(B * Hkv) * nbc;
+        sl += (int64_t)(B * Hq) * m.kcap[p];
+    }
+    size_t off = 0;
+    m.qa = off;
+    off = align256(off + B * Hq * D * 4);
+    m.qs = off;
+    off = align256(off + B * Hkv * D * 2 * G * 4);
+    m.scores = off;
+    off = align256(off + (size_t)sc * 4);
+    m.mask = off;
+    off = align256(off + (size_t)mk * 4);
+    m.sel = off;
+    off = align256(off + (size_t)sl * 4);
+    m.part = off;
+    off = align256(off + B * Hq * MAX_SPLITS * PART * 4);
+    m.total = off;
+    return m;
+}
+
+int64_t sel_cols_now(const mkv_cache *c) {
+    int64_t best = 0;
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t s = 0;
+        for (int j = 0; j < c->n_segments; ++j) {
+            const mkv_segment &sg = segof(c, b, j);
+            if (sg.kind != MKV_SEG_PACKED) continue;
+            s += keep_blocks(ceil_div(seg_filled(c, b, j), BT), sg.keep_ppm, sg.k_abs);
+        }
+        best = std::max(best, s);
+    }
+    return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mkv_status_str(mkv_status s) {
+    switch (s) {
+    case MKV_OK: return "ok";
+    case MKV_ERR_ARG: return "invalid argument";
+    case MKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MKV_ERR_CAPACITY: return "append exceeds segment capacity";
+    case MKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case MKV_ERR_NOCONVERGE: return "eigensolver did not converge";
+    case MKV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads, int64_t t_cap,
+                         size_t *meta_bytes_out) {
+    if (meta_bytes_out) *meta_bytes_out = 0;
+    if ((dtype != MKV_F32 && dtype != MKV_BF16) || d < 1 || n_kv_heads < 1 || t_cap < 1) return 0;
+    const size_t s = elem_bytes(dtype);
+    const size_t nb = (size_t)ceil_div(t_cap, BT);
+    if (kind == MKV_SEG_DENSE) return (size_t)n_kv_heads * nb * 2 * BT * d * s;
+    if (kind != MKV_SEG_PACKED || r < 1 || r > d) return 0;
+    if (meta_bytes_out) {
+        const size_t ntile = ceil_div((int64_t)nb, META_TILE);
+        *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * d * s;
+    }
+    return (size_t)n_kv_heads * nb * BT * r * 2 * (s + 1);
+}
+
+mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
+                               int32_t n_max, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    if (!n_new || n_max < 0) return MKV_ERR_ARG;
+    bool any = false;
+    for (int b = 0; b < c->batch; ++b) {
+        if (n_new[b] < 0 || n_new[b] > n_max) return MKV_ERR_ARG;
+        int64_t cap = 0;
+        for (int j = 0; j < c->n_segments; ++j) cap += segof(c, b, j).t_cap;
+        if (c->len[b] + n_new[b] > cap) return MKV_ERR_CAPACITY;
+        any = any || n_new[b] > 0;
+    }
+    if (!any) return MKV_OK;
+    if (!k_new || !v_new) return MKV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    std::vector<CompressEntry> ents;
+    for (int b = 0; b < c->batch; ++b) {
+        const int64_t p0 = c->len[b], p1 = c->len[b] + n_new[b];
+        for (int j = 0; j < c->n_segments; ++j) {
+            const mkv_segment &sg = segof(c, b, j);
+            const int64_t a = std::max(p0, sg.t_begin) - sg.t_begin;
+            const int64_t e = std::min(p1, sg.t_begin + sg.t_cap) - sg.t_begin;
+            if (e <= a) continue;
+            CompressEntry E{};
+            E.data = sg.data;
+            E.meta = sg.meta;
+            E.a = (int32_t)a;
+            E.e = (int32_t)e;
+            E.row0 = (int32_t)(sg.t_begin + a - p0);
+            E.b = b;
+            E.r = sg.r;
+            E.kind = sg.kind;
+            E.blk0 = (int32_t)(a / BT);
+            E.nblk = (int32_t)((e - 1) / BT - a / BT + 1);
+            E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
+            ents.push_back(E);
+        }
+    }
+    for (size_t i0 = 0; i0 < ents.size(); i0 += TABLE) {
+        CompressArgs A;
+        memset(&A, 0, sizeof(A));
+        const size_t n = std::min<size_t>(TABLE, ents.size() - i0);
+        int max_blk = 0;
+        for (size_t i = 0; i < n; ++i) {
+            A.ent[i] = ents[i0 + i];
+            max_blk = std::max(max_blk, A.ent[i].nblk);
+        }
+        A.k_new = k_new;
+        A.v_new = v_new;
+        A.rot = c->rot;
+        A.n_ent = (int32_t)n;
+        A.n_kv = c->n_kv_heads;
+        A.n_max = n_max;
+        st = timed(0, s, [&] { return launch_compress(A, c->dtype, max_blk, s); });
+        if (st != MKV_OK) return st;
+    }
+    for (int b = 0; b < c->batch; ++b) c->len[b] += n_new[b];
+    return MKV_OK;
+}
+
+mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    if (seg < 0 || seg >= c->n_segments || segof(c, 0, seg).kind != MKV_SEG_PACKED) return MKV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int b0 = 0; b0 < c->batch; b0 += TABLE) {
+        MetaArgs A;
+        memset(&A, 0, sizeof(A));
+        const int n = std::min(TABLE, c->batch - b0);
+        int max_nb = 0;
+        for (int i = 0; i < n; ++i) {
+            const mkv_segment &sg = segof(c, b0 + i, seg);
+            MetaEntry &E = A.ent[i];
+            E.data = sg.data;
+            E.meta = sg.meta;
+            E.filled = (int32_t)seg_filled(c, b0 + i, seg);
+            E.nb = (int32_t)ceil_div(E.filled, BT);
+            E.r = sg.r;
+            E.b = b0 + i;
+            E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
+            max_nb = std::max(max_nb, E.nb);
+        }
+        A.n_ent = n;
+        A.n_kv = c->n_kv_heads;
+        st = timed(1, s, [&] { return launch_block_meta(A, c->dtype, max_nb, s); });
+        if (st != MKV_OK) return st;
+    }
+    return MKV_OK;
+}
+
+size_t mkv_decode_workspace_bytes(const mkv_cache *c) {
+    if (check_cache(c) != MKV_OK) return 0;
+    return ws_map(c).total;
+}
+
+int64_t mkv_decode_sel_cols(const mkv_cache *c) {
+    if (check_cache(c) != MKV_OK) return -1;
+    return sel_cols_now(c);
+}
+
+mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
+                           void *workspace, size_t ws_bytes, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    if (!q || !out) return MKV_ERR_ARG;
+    if (sel_out && sel_cols < sel_cols_now(c)) return MKV_ERR_ARG;
+    const WsMap m = ws_map(c);
+    if (!workspace || ws_bytes < m.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return MKV_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int G = c->n_q_heads / c->n_kv_heads;
+    const int sb = elem_bytes(c->dtype);
+    char *ws = static_cast<char *>(workspace);
+    const int per_launch = std::max(1, TABLE / c->n_segments);
+
+    for (int b0 = 0; b0 < c->batch; b0 += per_launch) {
+        DecodeArgs A;
+        memset(&A, 0, sizeof(A));
+        const int n_req = std::min(per_launch, c->batch - b0);
+        A.rot = c->rot;
+        A.q = q;
+        A.out = out;
+        A.sel_out = sel_out;
+        A.sel_cols = sel_cols;
+        A.qa = reinterpret_cast<float *>(ws + m.qa);
+        A.qs = reinterpret_cast<float *>(ws + m.qs);
+        A.scores = reinterpret_cast<float *>(ws + m.scores);
+        A.mask = reinterpret_cast<uint32_t *>(ws + m.mask);
+        A.sel = reinterpret_cast<int32_t *>(ws + m.sel);
+        A.part = reinterpret_cast<float *>(ws + m.part);
+        for (int p = 0; p < m.npk; ++p) {
+            A.sc_off[p] = m.sc_off[p];
+            A.mk_off[p] = m.mk_off[p];
+            A.sl_off[p] = m.sl_off[p];
+            A.nbcap[p] = m.nbcap[p];
+            A.kcap[p] = m.kcap[p];
+            A.pseg[p] = m.pseg[p];
+        }
+        A.b0 = b0;
+        A.n_req = n_req;
+        A.nseg = c->n_segments;
+        A.npk = m.npk;
+        A.hq = c->n_q_heads;
+        A.hkv = c->n_kv_heads;
+        int max_tiles = 0, max_nb = 0;
+        int64_t Wmax = 0;
+        for (int i = 0; i < n_req; ++i) {
+            int64_t W = 0;
+            for (int j = 0; j < c->n_segments; ++j) {
+                const mkv_segment &sg = segof(c, b0 + i, j);
+                DSeg &D_ = A.seg[i * c->n_segments + j];
+                D_.data = sg.data;
+                D_.meta = sg.meta;
+                D_.kind = sg.kind;
+                D_.r = sg.r;
+                D_.filled = (int32_t)seg_filled(c, b0 + i, j);
+                D_.nb = (int32_t)ceil_div(D_.filled, BT);
+                D_.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
+                if (sg.kind == MKV_SEG_PACKED) {
+                    D_.k = (int32_t)keep_blocks(D_.nb, sg.keep_ppm, sg.k_abs);
+                    max_tiles = std::max(max_tiles, (int)ceil_div(D_.nb, META_TILE));
+                    max_nb = std::max(max_nb, D_.nb);
+                    const int64_t rec = (int64_t)BT * sg.r * 2 * (sb + 1);
+                    W += (int64_t)G * D_.k * ((G > 1 ? rec * 4 / 5 : rec) + 256);
+                } else {
+                    W += (int64_t)D_.nb * (2 * BT * D * sb + 256);
+                }
+            }
+            Wmax = std::max(Wmax, W);
+        }
+        // splits: about 64 KB of cache reads each, at most MAX_SPLITS per unit
+        A.S = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS, ceil_div(Wmax, 64 * 1024)));
+        A.sel_kpt = max_nb <= 1024 ? 1 : max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
+
+        st = timed(2, s, [&] { return launch_qrot(A, G, s); });
+        if (st != MKV_OK) return st;
+        if (m.npk > 0) {
+            st = timed(3, s, [&] { return launch_score(A, c->dtype, G, max_tiles, s); });
+            if (st != MKV_OK) return st;
+            st = timed(4, s, [&] { return launch_select(A, G, A.sel_kpt, s); });
+            if (st != MKV_OK) return st;
+        }
+        st = timed(5, s, [&] { return launch_attend(A, c->dtype, G, s); });
+        if (st != MKV_OK) return st;
+        st = timed(6, s, [&] { return launch_merge(A, G, s); });
+        if (st != MKV_OK) return st;
+    }
+    return MKV_OK;
+}
+
+mkv_status mkv_timing_enable(int32_t on) {
+    Timing &t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.on = on != 0;
+    return MKV_OK;
+}
+
+mkv_status mkv_timing_read(double *ms_out, int64_t *count_out, int32_t n_stages) {
+    if (!ms_out || !count_out || n_stages < 0) return MKV_ERR_ARG;
+    Timing &t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    mkv_status st = MKV_OK;
+    for (int i = 0; i < MKV_N_STAGES; ++i) {
+        double ms = 0.0;
+        for (PendingPair &p : t.pending[i]) {
+            float e = 0.f;
+            if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&e, p.a, p.b) != hipSuccess)
+                st = MKV_ERR_HIP;
+            ms += e;
+            t.pool.push_back(p.a);
+            t.pool.push_back(p.b);
+        }
+        if (i < n_stages) {
+            ms_out[i] = ms;
+            count_out[i] = (int64_t)t.pending[i].size();
+        }
+        t.pending[i].clear();
+    }
+    return st;
+}
+
+const char *mkv_stage_name(int32_t stage) {
+    static const char *names[MKV_N_STAGES] = {"compress", "block_meta", "q_rotate", "score",
+                                              "select",   "attend",     "merge"};
+    return (stage >= 0 && stage < MKV_N_STAGES) ? names[stage] : "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal launch descriptors shared by the host library and the HIP kernels.
+//
+// Every kernel receives its whole per-launch table by value (kernel arguments
+// stay below 4 KB), so no host-to-device copy precedes a launch and the calls
+// never synchronise. Requests beyond one table are handled by further launches.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/mkv.h"
+
+namespace mkv {
+
+constexpr int D = MKV_HEAD_DIM;
+constexpr int BT = MKV_BLOCK_TOKENS;
+constexpr int TABLE = 64;       // (request, segment) entries per launch
+constexpr int META_TILE = 64;   // blocks per meta tile
+constexpr int MAX_SPLITS = 256; // attention splits per (request, KV head)
+constexpr int PART = D + 2;     // floats per split partial: m, l, acc[D]
+
+// ---- compression ----------------------------------------------------------
+struct CompressEntry {
+    void *data;      // segment data
+    void *meta;      // packed meta or nullptr
+    int32_t a, e;    // new tokens occupy local positions [a, e) of the segment
+    int32_t row0;    // input row of local position a
+    int32_t b;       // request
+    int32_t r;       // kept elements (packed)
+    int32_t kind;    // MKV_SEG_*
+    int32_t blk0;    // first block touched
+    int32_t nblk;    // blocks touched
+    int32_t nbcap;   // block capacity of the segment
+    int32_t pad;
+};  // 56 bytes
+
+struct CompressArgs {
+    CompressEntry ent[TABLE];
+    const void *k_new;
+    const void *v_new;
+    const float *rot;
+    int32_t n_ent, n_kv, n_max, pad;
+};
+
+struct MetaEntry {
+    const void *data;
+    void *meta;
+    int32_t filled, nb, r, b, nbcap, pad;
+};  // 40 bytes
+
+struct MetaArgs {
+    MetaEntry ent[TABLE];
+    int32_t n_ent, n_kv;
+};
+
+// ---- decode ----------------------------------------------------------------
+struct DSeg {
+    const void *data;
+    const void *meta;
+    int32_t kind, r;
+    int32_t filled;  // tokens stored
+    int32_t nb;      // blocks stored
+    int32_t k;       // blocks kept (packed)
+    int32_t nbcap;   // block capacity (layout stride)
+};  // 40 bytes
+
+struct DecodeArgs {
+    DSeg seg[TABLE];  // [n_req][nseg]
+    const float *rot;
+    const float *q;
+    float *out;
+    int32_t *sel_out;
+    float *qa;        // [B][Hq][D] q' * log2(e) / sqrt(D)
+    float *qs;        // [B][Hkv][D][2G] (max(q',0), min(q',0)) / sqrt(D)
+    float *scores;    // per packed j: [B][Hq][nbcap_j]
+    uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j]
+    int32_t *sel;     // per packed j: [B][Hq][kcap_j]
+    float *part;      // [B][Hq][S][PART]
+    int64_t sel_cols;
+    int64_t sc_off[MKV_MAX_SEGMENTS];
+    int64_t mk_off[MKV_MAX_SEGMENTS];
+    int64_t sl_off[MKV_MAX_SEGMENTS];
+    int32_t nbcap[MKV_MAX_SEGMENTS];  // per packed j (max over requests)
+    int32_t kcap[MKV_MAX_SEGMENTS];
+    int32_t pseg[MKV_MAX_SEGMENTS];   // segment index of packed j
+    int32_t b0, n_req, nseg, npk, hq, hkv, S, sel_kpt;
+};
+
+// ---- launchers (defined in the .hip files) --------------------------------
+hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s);
+hipError_t launch_block_meta(const MetaArgs &a, int dtype, int max_nb, hipStream_t s);
+hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s);
+hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hipStream_t s);
+hipError_t launch_select(const DecodeArgs &a, int G, int kpt, hipStream_t s);
+hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s);
+
+}  // namespace mkv

@@ -1,0 +1,55 @@
+"""Host-side (numpy) readers of the documented device layouts (include/mkv.h).
+
+Used to inspect what the library stored; no arithmetic of the method here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BT = 16
+TILE = 64
+
+
+def _vals(raw: np.ndarray, dtype: str):
+    if dtype == "bf16":
+        bits = raw.view(np.uint16)
+        return bits, (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bits = raw.view(np.uint32)
+    return bits, bits.view(np.float32).astype(np.float64)
+
+
+def unpack_packed(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str):
+    """-> dict of K/V values (float64), value bits and indices, each [hkv][nbcap][16][r]."""
+    s = 2 if dtype == "bf16" else 4
+    rec = BT * r * 2 * (s + 1)
+    a = np.ascontiguousarray(data, np.uint8).reshape(hkv, nbcap, rec)
+    kb, kv = _vals(np.ascontiguousarray(a[:, :, :BT * r * s]).reshape(-1), dtype)
+    vb, vv = _vals(np.ascontiguousarray(a[:, :, BT * r * s:2 * BT * r * s]).reshape(-1), dtype)
+    ki = a[:, :, 2 * BT * r * s:2 * BT * r * s + BT * r].reshape(hkv, nbcap, BT, r)
+    vi = a[:, :, 2 * BT * r * s + BT * r:].reshape(hkv, nbcap, BT, r)
+    shp = (hkv, nbcap, BT, r)
+    return dict(kval=kv.reshape(shp), vval=vv.reshape(shp), kbits=kb.reshape(shp), vbits=vb.reshape(shp),
+                kidx=ki, vidx=vi)
+
+
+def unpack_dense(data: np.ndarray, hkv: int, nbcap: int, dtype: str, d: int = 128):
+    """-> (values float64, bits), each [hkv][nbcap][2][16][d]."""
+    bits, vals = _vals(np.ascontiguousarray(data, np.uint8).reshape(-1), dtype)
+    shp = (hkv, nbcap, 2, BT, d)
+    return vals.reshape(shp), bits.reshape(shp)
+
+
+def unpack_meta(meta: np.ndarray, hkv: int, nbcap: int, dtype: str, d: int = 128):
+    """-> (values float64 [hkv][nbcap][2][d] (min, max), bits same shape)."""
+    s = 2 if dtype == "bf16" else 4
+    ng = 2 * d * s // 16
+    cpg = d // ng
+    ntile = -(-nbcap // TILE)
+    raw = np.ascontiguousarray(meta, np.uint8).reshape(hkv, ntile, ng, TILE, 16)
+    bits, vals = _vals(np.ascontiguousarray(raw).reshape(-1), dtype)
+    # [hkv][ntile][ng][TILE][cpg][2] -> [hkv][ntile*TILE][2][ng*cpg]
+    shp = (hkv, ntile, ng, TILE, cpg, 2)
+    def re(x):
+        x = x.reshape(shp).transpose(0, 1, 3, 5, 2, 4).reshape(hkv, ntile * TILE, 2, ng * cpg)
+        return x[:, :nbcap]
+    return re(vals), re(bits)

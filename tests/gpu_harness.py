@@ -1,0 +1,193 @@
+"""Shared helpers of the GPU parity tests: build a cache from the seeded
+workloads through the C ABI, run the oracle on chosen (request, KV head)
+units, and compare the two sides."""
+from __future__ import annotations
+
+import ctypes
+import sys
+import time
+
+import numpy as np
+
+import mkv_synth as synth
+from oracle import oracle as orc
+
+DT_CODE = {"f32": 0, "bf16": 1}
+
+
+def log(msg):
+    print("[%s] %s" % (time.strftime("%H:%M:%S"), msg), flush=True)
+    sys.stdout.flush()
+
+
+def raw_to_f64(bits_or_vals, dtype):
+    if dtype == "bf16":
+        return synth.bf16_bits_to_f32(bits_or_vals).astype(np.float64)
+    return np.asarray(bits_or_vals, np.float32).astype(np.float64)
+
+
+def gen_raw(w, t_ends, t_begins=None):
+    """Raw stored K/V for every (b, g): arrays [B][Hkv][Tmax][d] of uint16 bits (bf16)
+    or float32 (f32), rows [t_begin_b, t_end_b) of each request's stream."""
+    B, hkv, d, dt = w["batch"], w["n_kv_heads"], w["d"], w["dtype"]
+    t_begins = t_begins if t_begins is not None else [0] * B
+    n = [int(e) - int(s) for s, e in zip(t_begins, t_ends)]
+    nmax = max(max(n), 1)
+    npdt = np.uint16 if dt == "bf16" else np.float32
+    K = np.zeros((B, hkv, nmax, d), npdt)
+    V = np.zeros((B, hkv, nmax, d), npdt)
+    for b in range(B):
+        for g in range(hkv):
+            for kind, arr in ((0, K), (1, V)):
+                out = np.empty((n[b], d), npdt)
+                synth.gen_kv_into(w["cfg"], b, g, kind, int(t_begins[b]), int(t_ends[b]), dt, out, d)
+                arr[b, g, :n[b]] = out
+    return K, V, n
+
+
+def rotations(L, w, K, V, n):
+    """Library rotations from each unit's prefill rows: [B][Hkv][2][d][d] float32."""
+    B, hkv, d = w["batch"], w["n_kv_heads"], w["d"]
+    R = np.zeros((B, hkv, 2, d, d), np.float32)
+    code = DT_CODE[w["dtype"]]
+    for b in range(B):
+        for g in range(hkv):
+            for kind, arr in ((0, K), (1, V)):
+                x = np.ascontiguousarray(arr[b, g, :n[b]])
+                out = np.empty((d, d), np.float32)
+                L.mkv_rotation_from_prefill(x.ctypes.data, code, n[b], d, out.ctypes.data, None)
+                R[b, g, kind] = out
+    return R
+
+
+def to_device(torch, arr, device="cuda"):
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(device)
+    return torch.from_numpy(arr).to(device)
+
+
+def build(torch, w, lengths=None, R=None, raw=None):
+    """Cache filled with every request's first `lengths[b]` tokens in one append."""
+    from kv_cache_compression_mkv_amd import _lib as L
+    from kv_cache_compression_mkv_amd.cache import Cache
+    lengths = list(w["lengths"] if lengths is None else lengths)
+    if raw is None:
+        raw = gen_raw(w, lengths)
+    K, V, n = raw
+    if R is None:
+        R = rotations(L, w, K, V, n)
+    c = Cache(w["batch"], w["n_q_heads"], w["n_kv_heads"], w["dtype"], w["segs"])
+    c.set_rotation(R)
+    c.append(to_device(torch, K), to_device(torch, V), n)
+    torch.cuda.synchronize()
+    return c, (K, V, n), R
+
+
+def oracle_unit(w, raw, R, b, g, length, segs=None):
+    K, V, _ = raw
+    dt = w["dtype"]
+    segs = w["segs"][b] if segs is None else segs
+    Kr = raw_to_f64(K[b, g, :length], dt)
+    Vr = raw_to_f64(V[b, g, :length], dt)
+    Rk = R[b, g, 0].astype(np.float64)
+    Rv = R[b, g, 1].astype(np.float64)
+    return orc.compress_unit(Kr, Vr, Rk, Rv, segs, length, dt), Rk, Rv
+
+
+def bits_of(values_f64, dtype):
+    f = np.asarray(values_f64, np.float64).astype(np.float32)
+    if dtype == "bf16":
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+    return f.view(np.uint32)
+
+
+def compare_compress(cache, w, comp, b, g, length):
+    """Bit-exact comparison of one unit's stored cache with the oracle's."""
+    from kv_cache_compression_mkv_amd import layout
+    dt, hkv = w["dtype"], w["n_kv_heads"]
+    pj = 0
+    for j, s in enumerate(w["segs"][b]):
+        nbcap = -(-s["t_cap"] // 16)
+        filled = min(max(length - s["t_begin"], 0), s["t_cap"])
+        data = cache.data[b][j].cpu().numpy()
+        if s["kind"] == synth.DENSE:
+            vals, bits = layout.unpack_dense(data, hkv, nbcap, dt)
+            for t in range(filled):
+                blk, slot = divmod(t, 16)
+                tt = s["t_begin"] + t
+                for kind, hat in ((0, comp["Khat"]), (1, comp["Vhat"])):
+                    exp = bits_of(hat[tt], dt)
+                    got = bits[g, blk, kind, slot]
+                    assert np.array_equal(got, exp), "dense b=%d g=%d seg=%d t=%d kind=%d" % (b, g, j, tt, kind)
+            nb = -(-filled // 16)
+            if filled % 16:
+                assert np.all(bits[g, nb - 1, :, filled % 16:] == 0)
+            continue
+        r = s["r"]
+        P = layout.unpack_packed(data, hkv, nbcap, r, dt)
+        for t in range(filled):
+            blk, slot = divmod(t, 16)
+            tt = s["t_begin"] + t
+            for hat, idx, gbits, gidx, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
+                                                (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
+                ei = idx[tt][:r]
+                gi = gidx[g, blk, slot]
+                assert np.array_equal(gi.astype(np.int64), ei.astype(np.int64)), \
+                    "%s idx b=%d g=%d seg=%d t=%d: %s vs %s" % (name, b, g, j, tt, gi, ei)
+                assert np.array_equal(gbits[g, blk, slot], bits_of(hat[tt, ei], dt)), \
+                    "%s val b=%d g=%d seg=%d t=%d" % (name, b, g, j, tt)
+        nb = -(-filled // 16)
+        if filled % 16:
+            assert np.all(P["kbits"][g, nb - 1, filled % 16:] == 0)
+            assert np.all(P["vidx"][g, nb - 1, filled % 16:] == 0)
+        mvals, mbits = layout.unpack_meta(cache.meta[b][j].cpu().numpy(), hkv, nbcap, dt)
+        om = comp["meta"][pj]
+        assert om.shape[0] == nb
+        if nb:
+            assert np.array_equal(mbits[g, :nb], bits_of(om, dt)), "meta b=%d g=%d seg=%d" % (b, g, j)
+        pj += 1
+
+
+def split_sel(sel_row, seg_k):
+    """sel_out row [Hq-slice][cols] -> list over packed segments of [G][k]."""
+    out, o = [], 0
+    for k in seg_k:
+        out.append(sel_row[:, o:o + k])
+        o += k
+    return out
+
+
+def check_decode_unit(w, comp, Rk, Rv, q_unit, out_gpu, sel_gpu_unit, tol, length, b, g):
+    """Compare one unit's decode: selection (with the near-tie exemption) and
+    outputs against the oracle forced to the GPU's selection."""
+    segs = w["segs"][b]
+    nk = orc.seg_blocks(segs, length)
+    seg_k = [k for _, k in nk]
+    gsel = split_sel(sel_gpu_unit, seg_k)
+    own = orc.decode_unit(comp, q_unit, Rk, Rv)
+    forced = orc.decode_unit(comp, q_unit, Rk, Rv, forced_sel=gsel)
+    G = q_unit.shape[0]
+    n_exempt = 0
+    for pj, (gs, os_, sc) in enumerate(zip(gsel, own["sel"], own["scores"])):
+        for h in range(G):
+            a, e = set(gs[h].tolist()), set(os_[h].tolist())
+            assert len(a) == len(gs[h]) and all(0 <= x < sc.shape[1] for x in a), "invalid GPU selection"
+            assert list(gs[h]) == sorted(gs[h]), "GPU selection not ascending"
+            if a != e:
+                tau = own["tau"][h, pj]
+                smax = np.abs(sc[h]).max()
+                for blk in a ^ e:
+                    s = sc[h, blk]
+                    lim = 1e-4 * max(abs(s), abs(tau), 1e-6 * smax)
+                    assert abs(s - tau) <= lim, \
+                        "b=%d g=%d h=%d seg=%d block %d score %.9g vs threshold %.9g" % (b, g, h, pj, blk, s, tau)
+                    n_exempt += 1
+    for h in range(G):
+        ref = forced["out"][h]
+        nr = np.linalg.norm(ref)
+        err = np.linalg.norm(out_gpu[h] - ref)
+        if nr == 0:
+            assert err == 0, "b=%d g=%d h=%d expected zeros" % (b, g, h)
+        else:
+            assert err / nr <= tol, "b=%d g=%d h=%d rel L2 %.3g > %.3g" % (b, g, h, err / nr, tol)
+    return n_exempt

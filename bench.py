@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MosaicKV hot path on one MI355X.
+
+One step = mkv_compress_append of one new token per request (rotate in
+float64, top-r, pack, block-key update) followed by mkv_decode_attn (query
+rotation, block scoring, top-k, sparse attention, merge, inverse rotation).
+
+Default workload (128K context): GQA layer with 32 query / 8 KV heads, d=128,
+batch 4, T=131072 tokens per request, bf16 storage, segments: 64 dense sink,
+[64, 63520) packed r=26 keep 5%, [63520, 126976) packed r=38 keep 10%, 4096
+dense recent, then a packed update segment (r=38, keep 10%) that receives the
+new decode tokens. Inputs are seeded synthetic data (mkv_synth) resident in
+HBM before the timed region.
+
+Prints one JSON line (see README of the repository root for fields).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mkv_synth as synth  # noqa: E402
+
+METRIC = "decode-attn effective KV tokens/s/GPU + achieved HBM GB/s vs 8 TB/s peak"
+PEAK_GBPS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def log(msg):
+    print("[bench %s] %s" % (time.strftime("%H:%M:%S"), msg), file=sys.stderr, flush=True)
+
+
+def workload(cfg: int, scale: int, extra: int):
+    w = synth.workload(cfg, scale=scale)
+    if cfg != 5:
+        w = synth.with_update_segment(w, cap=extra)
+    return w
+
+
+def gen_rows(w, t_end):
+    """Raw stored K/V [B][Hkv][t_end][d] (bf16 bit patterns or float32)."""
+    B, hkv, d, dt = w["batch"], w["n_kv_heads"], w["d"], w["dtype"]
+    npdt = np.uint16 if dt == "bf16" else np.float32
+    K = np.empty((B, hkv, t_end, d), npdt)
+    V = np.empty((B, hkv, t_end, d), npdt)
+    for b in range(B):
+        for g in range(hkv):
+            synth.gen_kv_into(w["cfg"], b, g, 0, 0, t_end, dt, K[b, g], d)
+            synth.gen_kv_into(w["cfg"], b, g, 1, 0, t_end, dt, V[b, g], d)
+    return K, V
+
+
+def rotations(L, w, K, V, T):
+    B, hkv, d = w["batch"], w["n_kv_heads"], w["d"]
+    code = L.MKV_BF16 if w["dtype"] == "bf16" else L.MKV_F32
+    R = np.empty((B, hkv, 2, d, d), np.float32)
+    for b in range(B):
+        for g in range(hkv):
+            for kind, arr in ((0, K), (1, V)):
+                x = np.ascontiguousarray(arr[b, g, :T[b]])
+                L.mkv_rotation_from_prefill(x.ctypes.data, code, int(T[b]), d, R[b, g, kind].ctypes.data, None)
+    return R
+
+
+def dev(torch, a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def union_summary(w, lengths, sel):
+    """Per request and segment: filled tokens, blocks and the number of distinct
+    blocks the query heads of each KV head selected (summed over KV heads)."""
+    from kv_cache_compression_mkv_amd.bytes_model import keep_blocks
+    G = w["n_q_heads"] // w["n_kv_heads"]
+    out = []
+    for b in range(w["batch"]):
+        L = int(lengths[b])
+        rows, col = [], 0
+        for s in w["segs"][b]:
+            filled = min(max(L - s["t_begin"], 0), s["t_cap"])
+            if s["kind"] == synth.DENSE:
+                rows.append(dict(kind="dense", filled=filled))
+                continue
+            nb = -(-filled // 16)
+            k = keep_blocks(nb, s["keep_ppm"], s["k_abs"])
+            uni = 0
+            for g in range(w["n_kv_heads"]):
+                blocks = sel[b, g * G:(g + 1) * G, col:col + k]
+                uni += len(np.unique(blocks))
+            col += k
+            rows.append(dict(kind="packed", filled=filled, r=s["r"], n_blocks=nb, union=uni))
+        out.append(rows)
+    return out
+
+
+def counter_traffic(kernel_key: str):
+    """HBM bytes per dispatch from the committed counter summary, or None when it
+    is missing or was taken on other kernel sources."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    src = os.path.join(ROOT, "kv_cache_compression_mkv_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(src)):
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(f.read())
+    if c.get("source_sha256") != h.hexdigest():
+        return None
+    k = c.get("kernels", {}).get(kernel_key)
+    if not k:
+        return None
+    return (k["fetch_kib"] + k["write_kib"]) * 1024.0 * c.get("copy_factor", 1.0)
+
+
+def cpu_baseline(w, K, V, R, T0, steps, n_units, nthreads):
+    """The oracle as it stands, on a bounded sample: n_units (request, KV head)
+    units each run `steps` decode steps (append one token, then decode); the
+    per-unit step time is scaled to all units of the workload."""
+    from oracle import oracle as orc
+    G = w["n_q_heads"] // w["n_kv_heads"]
+    dt = w["dtype"]
+    to64 = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if dt == "bf16" else \
+        (lambda a: a.astype(np.float64))
+    units = [(u // w["n_kv_heads"], u % w["n_kv_heads"]) for u in range(n_units)]
+    total, n = 0.0, 0
+    for b, g in units:
+        Kr = to64(K[b, g, :T0[b] + steps])
+        Vr = to64(V[b, g, :T0[b] + steps])
+        Rk, Rv = R[b, g, 0].astype(np.float64), R[b, g, 1].astype(np.float64)
+        st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]), dt, nthreads=nthreads)
+        for s in range(steps):
+            q = synth.gen_q(w["cfg"], 5000 + s, w["batch"], w["n_q_heads"], dt)[b, g * G:(g + 1) * G]
+            t0 = time.perf_counter()
+            st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]) + s + 1, dt, nthreads=nthreads,
+                                   state=st)
+            orc.decode_unit(st, q.astype(np.float64), Rk, Rv, nthreads=nthreads)
+            total += time.perf_counter() - t0
+            n += 1
+    per_unit_step = total / n
+    full_step = per_unit_step * w["batch"] * w["n_kv_heads"]
+    return dict(value=float(np.sum(T0) / full_step), unit="tokens/s", cores=nthreads, kind="oracle",
+                sample="%d (request, KV head) units x %d steps of append-1-token + decode at T=%d; "
+                       "per-unit step %.2f ms scaled to %d units" % (n_units, steps, int(T0[0]),
+                                                                  per_unit_step * 1e3,
+                                                                  w["batch"] * w["n_kv_heads"]),
+                seconds=float(total))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1-5 (default 3: 128K context)")
+    ap.add_argument("--scale", type=int, default=1, help="divide token counts (1 = full size)")
+    ap.add_argument("--cpu-units", type=int, default=4, help="oracle sample size (0 disables)")
+    ap.add_argument("--cpu-steps", type=int, default=10)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)."
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    K_steps, W_steps = args.steps, args.warmup
+    cap_extra = W_steps + 2 * K_steps + 64
+    w = workload(args.config, args.scale, cap_extra)
+    T0 = np.asarray(w["lengths"], np.int64)
+    B, hq, hkv, d, dt = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["d"], w["dtype"]
+    G = hq // hkv
+    n_step_total = W_steps + 2 * K_steps + 1
+    log("workload cfg=%d scale=%d B=%d T=%s dtype=%s" % (args.config, args.scale, B, list(T0), dt))
+
+    t = time.time()
+    K, V = gen_rows(w, int(T0.max()) + n_step_total)
+    log("generated inputs in %.1f s" % (time.time() - t))
+
+    import torch  # noqa: E402
+    from kv_cache_compression_mkv_amd import _lib as L
+    from kv_cache_compression_mkv_amd import bytes_model as bm
+    from kv_cache_compression_mkv_amd.cache import Cache
+
+    t = time.time()
+    R = rotations(L, w, K, V, T0)
+    log("host rotations in %.1f s" % (time.time() - t))
+
+    c = Cache(B, hq, hkv, dt, w["segs"])
+    c.set_rotation(R)
+    kpre = dev(torch, K[:, :, :int(T0.max())])
+    vpre = dev(torch, V[:, :, :int(T0.max())])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    c.append(kpre, vpre, [int(x) for x in T0])
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    del kpre, vpre
+    log("prefill compress of %d tokens in %.2f ms" % (int(T0.sum()), prefill_ms))
+
+    # per-step inputs, resident in HBM before timing
+    newk = [dev(torch, np.stack([K[b, :, T0[b] + s:T0[b] + s + 1] for b in range(B)])) for s in range(n_step_total)]
+    newv = [dev(torch, np.stack([V[b, :, T0[b] + s:T0[b] + s + 1] for b in range(B)])) for s in range(n_step_total)]
+    qs = [torch.from_numpy(synth.gen_q(args.config, s, B, hq, dt)).cuda() for s in range(n_step_total)]
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+    c.workspace()
+    ones = [1] * B
+    step = 0
+
+    def run_step():
+        nonlocal step
+        c.append(newk[step], newv[step], ones)
+        c.decode(qs[step], out=out)
+        step += 1
+
+    for _ in range(W_steps):
+        run_step()
+    torch.cuda.synchronize()
+    len_start = np.asarray(c.lengths)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K_steps):
+        run_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / K_steps
+    mean_len = float(np.sum(len_start)) + B * (K_steps + 1) / 2.0
+    value = mean_len / (ms_per_step / 1e3)
+    log("timed %d steps: %.3f ms/step wall, %.3f ms/step GPU events" % (K_steps, ms_per_step, gpu_ms / K_steps))
+
+    # per-kernel durations, live: HIP events around every launch of the same steps
+    L.mkv_timing_enable(True)
+    for _ in range(K_steps):
+        run_step()
+    torch.cuda.synchronize()
+    stages = L.mkv_timing_read()
+    L.mkv_timing_enable(False)
+    stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items()}
+    log("per-launch ms: " + ", ".join("%s %.4f" % (k, v) for k, v in stage_ms.items() if v))
+
+    # algorithmic bytes of one decode call at the current lengths, from its own selections
+    _, sel = c.decode(qs[step], out=out, want_sel=True)
+    torch.cuda.synchronize()
+    lens_now = np.asarray(c.lengths)
+    summ = union_summary(w, lens_now, sel.cpu().numpy())
+    sb = 2 if dt == "bf16" else 4
+    call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
+    attend_bytes = call["records"] + call["dense"]
+    score_bytes = call["meta"]
+    append_bytes = B * hkv * 2 * (d * d * 4 + d * sb)
+    step_bytes = call["total"] + append_bytes
+    cand = {"attend": attend_bytes, "score": score_bytes}
+    dom = max(cand, key=lambda k: stage_ms.get(k, 0.0))
+    dom_ms = stage_ms[dom]
+    achieved = cand[dom] / (dom_ms * 1e-3) / 1e9
+    traffic = counter_traffic(dom)
+    dense_equiv = bm.dense_kv_bytes(int(np.sum(lens_now)), d, sb) * hkv
+
+    cpu = None
+    if args.cpu_units > 0:
+        nthreads = synth.host_threads()
+        log("oracle CPU baseline on %d units x %d steps, %d threads" % (args.cpu_units, args.cpu_steps, nthreads))
+        cpu = cpu_baseline(w, K, V, R, T0, args.cpu_steps, args.cpu_units, nthreads)
+        log("oracle: %.3g tokens/s over %.1f s" % (cpu["value"], cpu["seconds"]))
+        cpu.pop("seconds")
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("plain copy of %d bytes done (counter calibration)" % n)
+
+    seg_desc = "; ".join("%s[%d,%d)%s" % ("D" if s["kind"] == 0 else "P", s["t_begin"], s["t_begin"] + s["t_cap"],
+                                          "" if s["kind"] == 0 else " r=%d keep=%s" % (
+                                              s["r"], ("%d blocks" % s["k_abs"]) if s["k_abs"] else
+                                              ("%g%%" % (s["keep_ppm"] / 1e4))))
+                         for s in w["segs"][0])
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W_steps,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "config%d: GQA %d/%d heads d=%d, batch %d, T=%d/request at start, %s storage; "
+                        "step = append 1 token/request + decode attention" % (args.config, hq, hkv, d, B,
+                                                                              int(T0[0]), dt),
+            "global_batch": B,
+            "seq_len": int(T0.max()),
+            "segments": seg_desc,
+            "storage": dt,
+            "parallelism": "single GPU",
+        },
+        "achieved_step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_alg_bytes": int(step_bytes),
+        "decode_alg_bytes": {k: int(v) for k, v in call.items()},
+        "dense_equiv_bytes": int(dense_equiv),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items() if v},
+        "gpu_event_ms_per_step": round(gpu_ms / K_steps, 4),
+        "prefill_compress_ms": round(prefill_ms, 3),
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": int(cand[dom]),
+            "avg_launch_ms": round(dom_ms, 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,6 +40,15 @@ def notes_compressed_bytes(tokens: int, r: int, alpha: float, s: int, idx_bytes:
     return dict(k_all=k_all, selected=sel, indices=idx, total=k_all + sel + idx)
 
 
+def keep_blocks(n: int, keep_ppm: int, k_abs: int) -> int:
+    """Blocks a packed segment keeps (the rule of include/mkv.h): k_abs if set,
+    else ceil(keep_ppm * n / 1e6) in integers; clamped to [1, n]; 0 if n = 0."""
+    if n <= 0:
+        return 0
+    k = min(k_abs, n) if k_abs > 0 else (keep_ppm * n + 999999) // 1000000
+    return max(1, min(k, n))
+
+
 def theoretical_speedup(alpha: float, beta: float) -> float:
     """T*d / (s_selected * r) = 1 / (alpha * beta) (reading notes, Eq. 15)."""
     return 1.0 / (alpha * beta)

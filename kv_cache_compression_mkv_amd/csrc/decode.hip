@@ -314,7 +314,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const DecodeArgs A) {
     int pos = pos0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        if (keepv[i]) {
+        if (keepv[i] && pos < k) {
             const int idx = base + i;
             sl[pos] = idx;
             if (so) so[coloff + pos] = idx;
@@ -552,6 +552,7 @@ __global__ __launch_bounds__(256) void k_attend(const DecodeArgs A) {
             for (int64_t it = i0; it < i1; ++it) {
                 const int rank = (int)(it / G), hl = (int)(it % G);
                 const int blk = sel[(size_t)hl * A.kcap[myj] + rank];
+                if ((unsigned)blk >= (unsigned)S.nb) continue;  // never taken for a valid selection
                 const int hm = (int)mk[blk];
                 if (hm & ((1 << hl) - 1)) continue;  // a lower head already covers this block
                 const int nv = min(BT, S.filled - blk * BT);

@@ -258,22 +258,24 @@ static int64_t seg_filled(int64_t len, int64_t tb, int64_t cap) {
 /* Number of blocks of `block` tokens that a segment holding `filled` tokens has. */
 static int64_t n_blocks_of(int64_t filled, int block) { return (filled + block - 1) / block; }
 
-/* Compress every token of a unit and build the per-block keys.
+/* Compress tokens [t_from, len) of a unit and rebuild the per-block keys of
+ * every block holding one of them (tokens before t_from are already stored).
  *   Kraw, Vraw [len][d]: stored raw inputs (as exact doubles)
  *   Rk, Rv [d][d]
  *   Khat, Vhat [len][d]: stored values, 0 at dropped channels
  *   Kidx, Vidx [len][d]: kept channels ascending, then -1 (dense tokens: 0..d-1)
- *   meta: concatenation over packed segments of [n_blocks][2][d] (mn, mx)
+ *   meta: packed segments one after the other, each [ceil(t_cap/block)][2][d] (mn, mx)
  * Returns 0, or 1 when a token falls outside every segment. */
-int orc_compress_unit(int d, int64_t len, int dtype, int block,
+int orc_compress_unit(int d, int64_t len, int64_t t_from, int dtype, int block,
                       const double *Kraw, const double *Vraw, const double *Rk, const double *Rv,
                       int nseg, const int32_t *kind, const int64_t *t_begin, const int64_t *t_cap,
                       const int32_t *r, double *Khat, double *Vhat, int16_t *Kidx, int16_t *Vidx,
                       double *meta, int nthreads) {
-    for (int64_t t = 0; t < len; ++t)
+    if (t_from < 0) t_from = 0;
+    for (int64_t t = t_from; t < len; ++t)
         if (find_segment(nseg, t_begin, t_cap, t) < 0) return 1;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
-    for (int64_t t = 0; t < len; ++t) {
+    for (int64_t t = t_from; t < len; ++t) {
         const int j = find_segment(nseg, t_begin, t_cap, t);
         for (int which = 0; which < 2; ++which) {
             const double *x = (which == 0 ? Kraw : Vraw) + t * d;
@@ -307,7 +309,8 @@ int orc_compress_unit(int d, int64_t len, int dtype, int block,
         if (kind[j] != ORC_PACKED) continue;
         const int64_t filled = seg_filled(len, t_begin[j], t_cap[j]);
         const int64_t nb = n_blocks_of(filled, block);
-        for (int64_t l = 0; l < nb; ++l) {
+        const int64_t from = t_from > t_begin[j] ? (t_from - t_begin[j]) / block : 0;
+        for (int64_t l = from; l < nb; ++l) {
             double *mn = meta + (off + l) * 2 * d, *mx = mn + d;
             const int64_t t0 = t_begin[j] + l * block;
             int64_t t1 = t0 + block;
@@ -323,7 +326,7 @@ int orc_compress_unit(int d, int64_t len, int dtype, int block,
                 mx[c] = hi;
             }
         }
-        off += nb;
+        off += n_blocks_of(t_cap[j], block);
     }
     return 0;
 }
@@ -402,14 +405,14 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
             free(tmp); free(chosen);
             continue;
         }
-        int64_t noff = 0, koff = 0;
+        int64_t noff = 0, koff = 0, moff = 0;
         int pj = 0;
         for (int j = 0; j < nseg; ++j) {
             if (kind[j] != ORC_PACKED) continue;
             const int64_t nb = n_blocks_of(seg_filled(len, t_begin[j], t_cap[j]), block);
             const int64_t k = orc_block_keep(nb, keep_ppm[j], k_abs[j]);
             for (int64_t l = 0; l < nb; ++l) {
-                const double *mn = meta + (noff + l) * 2 * d, *mx = mn + d;
+                const double *mn = meta + (moff + l) * 2 * d, *mx = mn + d;
                 double s = 0.0;
                 for (int c = 0; c < d; ++c) {
                     const double a = qr[c] * mx[c], b = qr[c] * mn[c];
@@ -433,6 +436,7 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
             }
             noff += nb;
             koff += k;
+            moff += n_blocks_of(t_cap[j], block);
             pj++;
         }
         /* token set in position order: every filled dense token and every

@@ -53,7 +53,7 @@ def _lib():
         L.orc_block_keep.restype = I64
         L.orc_block_keep.argtypes = [I64, I32, I32]
         L.orc_compress_unit.restype = ctypes.c_int
-        L.orc_compress_unit.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.c_int, P, P, P, P,
+        L.orc_compress_unit.argtypes = [ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                         ctypes.c_int, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         L.orc_decode_unit.restype = ctypes.c_int
         L.orc_decode_unit.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P,
@@ -140,31 +140,45 @@ def seg_blocks(segs, length: int, block: int = BLOCK):
 
 
 def compress_unit(Kraw, Vraw, Rk, Rv, segs, length: int, dtype: str, block: int = BLOCK,
-                  nthreads: int | None = None):
+                  nthreads: int | None = None, state=None):
     """Compress one (request, KV head) unit. Returns a dict with Khat, Vhat, Kidx, Vidx
-    ([len][d]) and meta: list (one per packed segment) of [n_blocks][2][d]."""
-    Kraw = _c(Kraw, np.float64)[:length]
-    Vraw = _c(Vraw, np.float64)[:length]
+    ([len][d]) and meta: list (one per packed segment) of [n_blocks][2][d].
+
+    state: a dict returned by an earlier call on the same unit; then only the
+    tokens from its length on are compressed, into the same arrays (their row
+    capacity is the row count of the raw inputs given the first time)."""
+    if Kraw.shape[0] < length or Vraw.shape[0] < length:
+        raise ValueError("compress_unit: %d input rows for length %d" % (min(Kraw.shape[0], Vraw.shape[0]), length))
     d = Kraw.shape[1]
     Rk, Rv = _c(Rk, np.float64), _c(Rv, np.float64)
     kind, tb, cap, r, keep, kabs = _seg_arrays(segs)
-    nbs = [nb for nb, _ in seg_blocks(segs, length, block)]
-    Khat = np.empty((length, d)); Vhat = np.empty((length, d))
-    Kidx = np.empty((length, d), np.int16); Vidx = np.empty((length, d), np.int16)
-    meta = np.empty((max(sum(nbs), 1), 2, d))
-    rc = _lib().orc_compress_unit(d, length, DTYPES[dtype], block, Kraw.ctypes.data, Vraw.ctypes.data,
+    nbcaps = [-(-s["t_cap"] // block) for s in segs if s["kind"] == PACKED]
+    if state is None:
+        rows = max(Kraw.shape[0], length, 1)
+        st = dict(Khat=np.zeros((rows, d)), Vhat=np.zeros((rows, d)), Kidx=np.full((rows, d), -1, np.int16),
+                  Vidx=np.full((rows, d), -1, np.int16), meta_flat=np.zeros((max(sum(nbcaps), 1), 2, d)),
+                  length=0, segs=segs, dtype=dtype, block=block)
+    else:
+        st = state
+        if st["Khat"].shape[0] < length:
+            raise ValueError("compress_unit: state holds %d rows, need %d" % (st["Khat"].shape[0], length))
+    t_from = st["length"]
+    Kin = _c(Kraw[:length], np.float64)
+    Vin = _c(Vraw[:length], np.float64)
+    rc = _lib().orc_compress_unit(d, length, t_from, DTYPES[dtype], block, Kin.ctypes.data, Vin.ctypes.data,
                                   Rk.ctypes.data, Rv.ctypes.data, len(segs), kind.ctypes.data,
-                                  tb.ctypes.data, cap.ctypes.data, r.ctypes.data, Khat.ctypes.data,
-                                  Vhat.ctypes.data, Kidx.ctypes.data, Vidx.ctypes.data, meta.ctypes.data,
-                                  nthreads or threads())
+                                  tb.ctypes.data, cap.ctypes.data, r.ctypes.data, st["Khat"].ctypes.data,
+                                  st["Vhat"].ctypes.data, st["Kidx"].ctypes.data, st["Vidx"].ctypes.data,
+                                  st["meta_flat"].ctypes.data, nthreads or threads())
     if rc != 0:
         raise RuntimeError("oracle compress failed (%d)" % rc)
+    st["length"] = length
     metas, o = [], 0
-    for nb in nbs:
-        metas.append(meta[o:o + nb])
-        o += nb
-    return dict(Khat=Khat, Vhat=Vhat, Kidx=Kidx, Vidx=Vidx, meta=metas, meta_flat=meta,
-                length=length, segs=segs, dtype=dtype, block=block)
+    for (nb, _), nbc in zip(seg_blocks(segs, length, block), nbcaps):
+        metas.append(st["meta_flat"][o:o + nb])
+        o += nbc
+    st["meta"] = metas
+    return st
 
 
 def decode_unit(comp, q, Rk, Rv, forced_sel=None, nthreads: int | None = None):

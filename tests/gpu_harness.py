@@ -73,7 +73,8 @@ def build(torch, w, lengths=None, R=None, raw=None):
     lengths = list(w["lengths"] if lengths is None else lengths)
     if raw is None:
         raw = gen_raw(w, lengths)
-    K, V, n = raw
+    K, V, _ = raw
+    n = lengths
     if R is None:
         R = rotations(L, w, K, V, n)
     c = Cache(w["batch"], w["n_q_heads"], w["n_kv_heads"], w["dtype"], w["segs"])

@@ -263,11 +263,9 @@ def main():
     summ = union_summary(w, lens_now, sel.cpu().numpy())
     sb = 2 if dt == "bf16" else 4
     call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
-    attend_bytes = call["records"] + call["dense"]
-    score_bytes = call["meta"]
     append_bytes = B * hkv * 2 * (d * d * 4 + d * sb)
     step_bytes = call["total"] + append_bytes
-    cand = {"attend": attend_bytes, "score": score_bytes}
+    cand = {"attend_packed": call["records"], "attend_dense": call["dense"], "score": call["meta"]}
     dom = max(cand, key=lambda k: stage_ms.get(k, 0.0))
     dom_ms = stage_ms[dom]
     achieved = cand[dom] / (dom_ms * 1e-3) / 1e9

@@ -130,7 +130,8 @@ const char *mkv_status_str(mkv_status s);
 /* Rotation of one head from its prefill vectors ([N] Eq. 4, 6-8; [S] 2.3).
  * x_host [T][d] on the host, in `dtype` (f32 values, or bf16 bit patterns as
  * uint16). Computes G = X^T X in float64 (no centering), its eigenvectors by
- * Householder tridiagonalisation and implicit QL, orders them by descending
+ * Householder tridiagonalisation and the implicit symmetric QR iteration
+ * (Wilkinson shifts), orders them by descending
  * eigenvalue and makes the largest-magnitude entry of each row positive (ties
  * to the lower index). R_out [d][d] host float32 (row c = c-th vector),
  * sigma_out [d] host float64 (nullable) = sqrt(max(eigenvalue, 0)).
@@ -197,8 +198,8 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
  * mkv_timing_read synchronises those events and returns, per stage, the summed
  * milliseconds and the number of launches since the last read, then clears
  * them. Stages: 0 compress, 1 block_meta, 2 q_rotate, 3 score, 4 select,
- * 5 attend, 6 merge. */
-#define MKV_N_STAGES 7
+ * 5 attend_dense, 6 attend_packed, 7 merge (split merge + inverse rotation). */
+#define MKV_N_STAGES 8
 mkv_status mkv_timing_enable(int32_t on);
 mkv_status mkv_timing_read(double *ms_out, int64_t *count_out, int32_t n_stages);
 const char *mkv_stage_name(int32_t stage);

@@ -22,7 +22,7 @@ MKV_HEAD_DIM = 128
 MKV_MAX_GROUP = 4
 MKV_MAX_SEGMENTS = 8
 MKV_MAX_PACKED_BLOCKS = 65536
-MKV_N_STAGES = 7
+MKV_N_STAGES = 8
 
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
            "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",

@@ -2,13 +2,14 @@
 //
 // Steps ("MosaicKV 阅读笔记" reading notes Eq. 12-14; paper summary sections
 // 4.2 and 5.3, and the reading notes' Quest paragraph for the block keys):
-//   q_rotate : q' = R_k q for the G query heads of a KV head
-//   score    : s_l = (1/sqrt d) sum_c max(q'_c mx_c, q'_c mn_c) per block
-//   select   : per query head and packed segment, the k best blocks
-//              (ties to the lower block), plus a per-block head mask
-//   attend   : split-KV attention over dense blocks and the union of the
-//              group's selected packed blocks, online softmax in base 2
-//   merge    : log-sum-exp merge of the splits, then out = o R_v
+//   q_rotate      : q' = R_k q for the G query heads of a KV head
+//   score         : s_l = (1/sqrt d) sum_c max(q'_c mx_c, q'_c mn_c) per block
+//   select        : per query head and packed segment, the k best blocks
+//                   (ties to the lower block), plus a per-block head mask
+//   attend_dense  : split-KV attention over the dense (sink / recent) blocks
+//   attend_packed : split-KV attention over the union of the group's selected
+//                   packed blocks
+//   merge         : log-sum-exp merge of every split, then out = o R_v
 //
 // All of it is bandwidth-bound gather work: every kernel runs on the vector
 // ALU (no MFMA); meta and record reads are 16-byte coalesced loads.
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
     float acc[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.f;
-#pragma unroll 2
+#pragma unroll 8
     for (int grp = 0; grp < NG; ++grp) {
         const uint4 w = mt[grp * META_TILE + lane];
         float mn[CPG], mx[CPG];
@@ -123,89 +124,80 @@ __global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
 }
 
 // ----------------------------------------------------------------------------
-// block-wide helpers for 1024-thread workgroups
+// select: one workgroup of up to 16 waves per (request, query head, packed
+// segment). Lane l of wave w holds the keys of blocks (w*KPT + i)*64 + l, so
+// block order is (wave, i, lane) order. Counting is done with ballots and
+// scalar popcounts; the k-th largest key is found two bits at a time below
+// the bits every key shares. Blocks above it are kept, equal ones by
+// ascending block index; ballot prefix counts give each kept block its place
+// in the ascending output.
 // ----------------------------------------------------------------------------
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_MAX_WAVES = 16;
 
 struct SelShared {
-    int red[2][SEL_WAVES][3];
-    uint32_t ured[2][SEL_WAVES][2];
-    int scan[SEL_WAVES];
+    int v[2][SEL_MAX_WAVES][3];
 };
 
-__device__ __forceinline__ void block_sum3(SelShared &sh, int &phase, int &a, int &b, int &c) {
-    a = wave_sum_i(a);
-    b = wave_sum_i(b);
-    c = wave_sum_i(c);
+// sum three wave-uniform values over the workgroup's waves
+__device__ __forceinline__ void xwave_sum3(SelShared &sh, int &ph, int nw, int &a, int &b, int &c) {
+    if (nw == 1) return;
     const int w = (int)(threadIdx.x >> 6);
     if (lane_id() == 0) {
-        sh.red[phase][w][0] = a;
-        sh.red[phase][w][1] = b;
-        sh.red[phase][w][2] = c;
+        sh.v[ph][w][0] = a;
+        sh.v[ph][w][1] = b;
+        sh.v[ph][w][2] = c;
     }
     __syncthreads();
     a = b = c = 0;
-#pragma unroll
-    for (int i = 0; i < SEL_WAVES; ++i) {
-        a += sh.red[phase][i][0];
-        b += sh.red[phase][i][1];
-        c += sh.red[phase][i][2];
+    for (int i = 0; i < nw; ++i) {
+        a += sh.v[ph][i][0];
+        b += sh.v[ph][i][1];
+        c += sh.v[ph][i][2];
     }
-    phase ^= 1;
+    ph ^= 1;
 }
 
-__device__ __forceinline__ void block_minmax(SelShared &sh, int &phase, uint32_t &mn, uint32_t &mx) {
+// exclusive prefix over waves of a wave-uniform value
+__device__ __forceinline__ int xwave_excl(SelShared &sh, int &ph, int nw, int v) {
+    if (nw == 1) return 0;
+    const int w = (int)(threadIdx.x >> 6);
+    if (lane_id() == 0) sh.v[ph][w][0] = v;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += sh.v[ph][i][0];
+    ph ^= 1;
+    return before;
+}
+
+__device__ __forceinline__ void xwave_minmax(SelShared &sh, int &ph, int nw, uint32_t &mn, uint32_t &mx) {
     mn = wave_min_u(mn);
     mx = wave_max_u(mx);
+    if (nw == 1) return;
     const int w = (int)(threadIdx.x >> 6);
     if (lane_id() == 0) {
-        sh.ured[phase][w][0] = mn;
-        sh.ured[phase][w][1] = mx;
+        sh.v[ph][w][0] = (int)mn;
+        sh.v[ph][w][1] = (int)mx;
     }
     __syncthreads();
     mn = 0xFFFFFFFFu;
     mx = 0u;
-#pragma unroll
-    for (int i = 0; i < SEL_WAVES; ++i) {
-        mn = min(mn, sh.ured[phase][i][0]);
-        mx = max(mx, sh.ured[phase][i][1]);
+    for (int i = 0; i < nw; ++i) {
+        mn = min(mn, (uint32_t)sh.v[ph][i][0]);
+        mx = max(mx, (uint32_t)sh.v[ph][i][1]);
     }
-    phase ^= 1;
+    ph ^= 1;
 }
 
-// exclusive prefix sum over the workgroup (thread order)
-__device__ __forceinline__ int block_excl_scan(SelShared &sh, int v, int &total) {
-    const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
-    int incl = v;
+template <int KPT>
+__device__ __forceinline__ int count_ge(const uint32_t (&key)[KPT], uint32_t cand) {
+    int n = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
-    __syncthreads();  // sh.scan free
-    if (lane == 63) sh.scan[w] = incl;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-#pragma unroll
-    for (int i = 0; i < SEL_WAVES; ++i) {
-        const int s = sh.scan[i];
-        if (i < w) before += s;
-        total += s;
-    }
-    return before + incl - v;
+    for (int i = 0; i < KPT; ++i) n += popc64(ballot(key[i] >= cand));
+    return n;
 }
 
-// ----------------------------------------------------------------------------
-// select: one 1024-thread workgroup per (request, query head, packed segment).
-// Thread t holds the scores of blocks [t*KPT, t*KPT+KPT) as order-preserving
-// keys. The k-th largest key is found two bits at a time (counting keys at or
-// above three candidates), starting below the bits all keys share. Blocks
-// above the threshold are kept, equal ones by ascending block index.
-// ----------------------------------------------------------------------------
 template <int G, int KPT>
-__global__ __launch_bounds__(SEL_THREADS) void k_select(const DecodeArgs A) {
+__global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
     const int z = (int)blockIdx.z;
     const int bl = z / A.npk, j = z % A.npk;
     const int b = A.b0 + bl, g = (int)blockIdx.y, hi = (int)blockIdx.x;
@@ -213,33 +205,33 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const DecodeArgs A) {
     const DSeg &S = seg_of(A, bl, A.pseg[j]);
     const int n = S.nb, k = S.k;
     const int nbc = A.nbcap[j];
+    const int nw = (int)(blockDim.x >> 6), w = (int)(threadIdx.x >> 6), lane = lane_id();
     __shared__ SelShared sh;
-    int phase = 0;
-    const int t = (int)threadIdx.x;
+    int ph = 0;
 
     // sel_out column offset of this packed segment for this request
     int coloff = 0;
     for (int jj = 0; jj < j; ++jj) coloff += seg_of(A, bl, A.pseg[jj]).k;
     int32_t *so = A.sel_out ? A.sel_out + ((size_t)b * A.hq + h) * A.sel_cols : nullptr;
     if (so && j == A.npk - 1) {
-        for (int64_t c = coloff + k + t; c < A.sel_cols; c += SEL_THREADS) so[c] = -1;
+        for (int64_t c = coloff + k + (int)threadIdx.x; c < A.sel_cols; c += blockDim.x) so[c] = -1;
     }
     if (n <= 0 || k <= 0) return;
 
+    // keys; 0 marks a missing block (every finite score has a key above 0x007FFFFF)
     const float *sc = A.scores + A.sc_off[j] + ((size_t)b * A.hq + h) * nbc;
     uint32_t key[KPT];
-    const int base = t * KPT;
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const int idx = base + i;
-        key[i] = idx < n ? score_key(sc[idx]) : 0u;
-        if (idx < n) {
+        const int blk = (w * KPT + i) * 64 + lane;
+        key[i] = blk < n ? score_key(sc[blk]) : 0u;
+        if (blk < n) {
             kmn = min(kmn, key[i]);
             kmx = max(kmx, key[i]);
         }
     }
-    block_minmax(sh, phase, kmn, kmx);
+    xwave_minmax(sh, ph, nw, kmn, kmx);
     uint32_t thr;
     if (k >= n) {
         thr = kmn;
@@ -247,132 +239,95 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const DecodeArgs A) {
         const uint32_t diff = kmn ^ kmx;
         int bit = diff ? 31 - __clz(diff) : -1;
         thr = diff ? (kmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u))) : kmx;
-        while (bit >= 0) {
+        while (bit >= 0) {  // invariant: at least k keys are >= thr
             if (bit >= 1) {
                 const uint32_t c1 = thr | (1u << (bit - 1)), c2 = thr | (2u << (bit - 1)),
                                c3 = thr | (3u << (bit - 1));
-                int n1 = 0, n2 = 0, n3 = 0;
-#pragma unroll
-                for (int i = 0; i < KPT; ++i) {
-                    const bool v = base + i < n;
-                    n1 += (v && key[i] >= c1);
-                    n2 += (v && key[i] >= c2);
-                    n3 += (v && key[i] >= c3);
-                }
-                block_sum3(sh, phase, n1, n2, n3);
+                int n1 = count_ge<KPT>(key, c1), n2 = count_ge<KPT>(key, c2), n3 = count_ge<KPT>(key, c3);
+                xwave_sum3(sh, ph, nw, n1, n2, n3);
                 if (n3 >= k) thr = c3;
                 else if (n2 >= k) thr = c2;
                 else if (n1 >= k) thr = c1;
                 bit -= 2;
             } else {
-                const uint32_t c1 = thr | 1u;
-                int n1 = 0, n2 = 0, n3 = 0;
-#pragma unroll
-                for (int i = 0; i < KPT; ++i) n1 += (base + i < n && key[i] >= c1);
-                block_sum3(sh, phase, n1, n2, n3);
-                if (n1 >= k) thr = c1;
+                int n1 = count_ge<KPT>(key, thr | 1u), n2 = 0, n3 = 0;
+                xwave_sum3(sh, ph, nw, n1, n2, n3);
+                if (n1 >= k) thr |= 1u;
                 bit -= 1;
             }
         }
     }
-    // keys above the threshold, and how many equal ones are needed
-    int ngt = 0, neq = 0, dummy = 0;
+    // thr > 0 is the k-th largest key: keep every larger key and the first
+    // (k - #larger) equal keys in block order
+    int ngt = 0, neq = 0, unused = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const bool v = base + i < n;
-        ngt += (v && key[i] > thr);
-        neq += (v && key[i] == thr);
+        ngt += popc64(ballot(key[i] > thr));
+        neq += popc64(ballot(key[i] == thr));
     }
-    int my_eq = neq;
-    block_sum3(sh, phase, ngt, neq, dummy);
+    xwave_sum3(sh, ph, nw, ngt, neq, unused);
     const int need = k - ngt;
-    int eq_before = 0;
-    if (neq > need) {
-        int tot;
-        eq_before = block_excl_scan(sh, my_eq, tot);
-    }
-    int cnt = 0;
-    uint32_t selbits = 0;  // bit i: block base+i kept (KPT <= 32 per word below)
-    bool keepv[KPT];
-    int eqr = eq_before;
+    const uint64_t below = lanes_below(lane);
+    uint64_t selm = 0;
+    if (neq <= need) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const bool v = base + i < n;
-        bool kp = v && key[i] > thr;
-        if (v && key[i] == thr) {
-            kp = (neq <= need) || (eqr < need);
-            ++eqr;
+        for (int i = 0; i < KPT; ++i)
+            if (key[i] >= thr) selm |= 1ull << i;
+    } else {
+        int eqw = 0;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) eqw += popc64(ballot(key[i] == thr));
+        int run = xwave_excl(sh, ph, nw, eqw);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const uint64_t em = ballot(key[i] == thr);
+            const int rank = run + popc64(em & below);
+            if (key[i] > thr || (key[i] == thr && rank < need)) selm |= 1ull << i;
+            run += popc64(em);
         }
-        keepv[i] = kp;
-        cnt += kp;
     }
-    (void)selbits;
-    int tot;
-    const int pos0 = block_excl_scan(sh, cnt, tot);
+    int cw = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) cw += popc64(ballot((selm >> i) & 1));
+    int base = xwave_excl(sh, ph, nw, cw);
     int32_t *sl = A.sel + A.sl_off[j] + ((size_t)b * A.hq + h) * A.kcap[j];
     uint32_t *mk = A.mask + A.mk_off[j] + ((size_t)b * A.hkv + g) * nbc;
-    int pos = pos0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        if (keepv[i] && pos < k) {
-            const int idx = base + i;
-            sl[pos] = idx;
-            if (so) so[coloff + pos] = idx;
-            atomicOr(mk + idx, 1u << hi);
-            ++pos;
+        const bool sel = (selm >> i) & 1;
+        const uint64_t m = ballot(sel);
+        if (sel) {
+            const int pos = base + popc64(m & below);
+            if (pos < k) {
+                const int blk = (w * KPT + i) * 64 + lane;
+                sl[pos] = blk;
+                if (so) so[coloff + pos] = blk;
+                atomicOr(mk + blk, 1u << hi);
+            }
         }
+        base += popc64(m);
     }
 }
 
 // ----------------------------------------------------------------------------
-// attend: four waves per workgroup, each wave an independent split of one
-// (request, KV head) unit. The unit's work list is, segment by segment,
-// dense blocks (all heads) and packed items (rank, head) in rank-major order;
-// an item whose block a lower head of the group also selected is skipped, so
-// each union block is read once and serves every head that chose it. Splits
-// are equal shares of the list weighted by bytes.
+// shared pieces of the attention kernels
 // ----------------------------------------------------------------------------
-template <typename ST>
-struct Loader;
-template <>
-struct Loader<Bf16> {
-    // 8 consecutive stored values starting at element e0 (16-byte aligned)
-    __device__ __forceinline__ static void load8(const void *base, int e0, float v[8]) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + (size_t)e0 * 2);
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-    }
-};
-template <>
-struct Loader<F32> {
-    __device__ __forceinline__ static void load8(const void *base, int e0, float v[8]) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const char *>(base) + (size_t)e0 * 4);
-        const float4 a = p[0], c = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
-    }
-};
-
-__device__ __forceinline__ void load_idx8(const uint8_t *base, int e0, int ix[8]) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(base + e0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ix[i] = (int)((w.x >> (8 * i)) & (D - 1));
-        ix[4 + i] = (int)((w.y >> (8 * i)) & (D - 1));
-    }
-}
-
 template <int G>
 struct WaveState {
-    float m[G];   // running max (log2 units), uniform across the wave
-    float l;      // lane-private partial sum for lane (t, h)
+    float m;  // running max (log2 units) of the lane's head h = lane % G
+    float l;  // lane-private partial sum for lane (t, h)
+    __device__ __forceinline__ void init() {
+        m = -INFINITY;
+        l = 0.f;
+    }
+    // running max of head i (lane i holds head i at token 0)
+    __device__ __forceinline__ float head_max(int i) const { return __shfl(m, i, 64); }
 };
 
-// Online-softmax step over the 16 logits of one block held in zb[t*G + h].
-// Lanes t*G+h (< 16G) own one logit each. Returns per-head rescale factors
-// (uniform) and leaves p in zb.
+// Online-softmax step over the 16 logits of one block held in zb[t*G + h]
+// (lane t*G+h owns one). The running max only moves when a block exceeds it
+// by more than 2^8, so rescales are rare. Leaves p in zb and returns the
+// per-head rescale factors (uniform).
 template <int G>
 __device__ __forceinline__ void softmax_block(float *zb, int nv, int hm, WaveState<G> &st, float alpha[G]) {
     const int lane = lane_id();
@@ -383,11 +338,7 @@ __device__ __forceinline__ void softmax_block(float *zb, int nv, int hm, WaveSta
     float bm = z;
 #pragma unroll
     for (int o = G; o < 16 * G; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
-    // m for this lane's head
-    float mh = st.m[0];
-#pragma unroll
-    for (int i = 1; i < G; ++i)
-        if (h == i) mh = st.m[i];
+    const float mh = st.m;
     float mnew = mh, a = 1.f;
     if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
         a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
@@ -396,256 +347,190 @@ __device__ __forceinline__ void softmax_block(float *zb, int nv, int hm, WaveSta
     const float p = valid ? exp2f(z - mnew) : 0.f;
     if (own) {
         st.l = st.l * a + p;
+        st.m = mnew;
         zb[lane] = p;
     }
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        alpha[i] = __shfl(a, i, 64);
-        st.m[i] = __shfl(mnew, i, 64);
+    for (int i = 0; i < G; ++i) alpha[i] = __shfl(a, i, 64);
+}
+
+// 8 consecutive stored values (bf16: one 16-byte load; f32: two)
+template <typename ST>
+struct Vals8;
+template <>
+struct Vals8<Bf16> {
+    uint4 w;
+    __device__ __forceinline__ void load(const char *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void get(float v[8]) const {
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    }
+    __device__ __forceinline__ void raw(uint16_t v[8]) const {
+        v[0] = (uint16_t)w.x; v[1] = (uint16_t)(w.x >> 16);
+        v[2] = (uint16_t)w.y; v[3] = (uint16_t)(w.y >> 16);
+        v[4] = (uint16_t)w.z; v[5] = (uint16_t)(w.z >> 16);
+        v[6] = (uint16_t)w.w; v[7] = (uint16_t)(w.w >> 16);
+    }
+};
+template <>
+struct Vals8<F32> {
+    uint4 a, b;
+    __device__ __forceinline__ void load(const char *p) {
+        a = reinterpret_cast<const uint4 *>(p)[0];
+        b = reinterpret_cast<const uint4 *>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void get(float v[8]) const {
+        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+        v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+        v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    }
+    __device__ __forceinline__ void raw(uint32_t v[8]) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+__device__ __forceinline__ void idx8(uint2 w, int ix[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ix[i] = (int)((w.x >> (8 * i)) & (D - 1));
+        ix[4 + i] = (int)((w.y >> (8 * i)) & (D - 1));
     }
 }
 
+// split s of N equal parts of [0, n)
+__device__ __forceinline__ void split_range(int64_t n, int s, int S, int64_t &i0, int64_t &i1) {
+    i0 = n * s / S;
+    i1 = n * (s + 1) / S;
+}
+
+// ----------------------------------------------------------------------------
+// attend_dense: four waves per workgroup, each wave one split of the unit's
+// dense blocks. Lane (tg, ch) = (lane / 16, lane % 16) covers tokens tg, tg+4,
+// tg+8, tg+12 on channels 8ch..8ch+7; the K and V loads of a block are issued
+// together. Logits reduce over the 16 lanes of a token group; the V sums stay
+// in registers until the end.
+// ----------------------------------------------------------------------------
 template <typename ST, int G>
-__global__ __launch_bounds__(256) void k_attend(const DecodeArgs A) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_attend_dense(const DecodeArgs A) {
     const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
     const int b = A.b0 + bl;
     const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
     const int s = (int)blockIdx.x * 4 + wave;
-    const int S_ = A.S;
-
     __shared__ __align__(16) float qsh[G][D];
-    __shared__ __align__(16) float accs[4][G][D];
     __shared__ __align__(16) float zbs[4][16 * G];
     for (int i = (int)threadIdx.x; i < G * D; i += 256)
         qsh[i / D][i % D] = A.qa[((size_t)b * A.hq + g * G) * D + i];
     __syncthreads();
-    if (s >= S_) return;
-
-    float *acc = &accs[wave][0][0];
+    if (s >= A.S_d) return;
     float *zb = zbs[wave];
-    for (int i = lane; i < G * D; i += 64) acc[i] = 0.f;
-
-    WaveState<G> st;
-#pragma unroll
-    for (int i = 0; i < G; ++i) st.m[i] = -INFINITY;
-    st.l = 0.f;
-
-    // dense-path registers: lane = (token group tg, channel chunk ch)
     const int tg = lane >> 4, ch = lane & 15;
-    float qd[G][8], vacc[G][8];
+    float vacc[G][8];
 #pragma unroll
     for (int i = 0; i < G; ++i)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            qd[i][c] = qsh[i][ch * 8 + c];
-            vacc[i][c] = 0.f;
-        }
+        for (int c = 0; c < 8; ++c) vacc[i][c] = 0.f;
+    WaveState<G> st;
+    st.init();
 
-    // ---- work partition ----
-    const int sb = ST::bytes;
-    int64_t W = 0;
+    constexpr int sb = ST::bytes;
+    int64_t nblocks = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &S = seg_of(A, bl, si);
-        if (S.kind == MKV_SEG_DENSE)
-            W += (int64_t)S.nb * (2 * BT * D * sb + 256);
-        else
-            W += (int64_t)G * S.k * ((G > 1 ? (BT * S.r * 2 * (sb + 1) * 4) / 5 : BT * S.r * 2 * (sb + 1)) + 256);
+        if (S.kind == MKV_SEG_DENSE) nblocks += S.nb;
     }
-    const int64_t lo = W * s / S_, hi = W * (s + 1) / S_;
-    wave_lds_sync();
-
-    int64_t Wb = 0;
-    int pj = 0;
+    int64_t i0, i1;
+    split_range(nblocks, s, A.S_d, i0, i1);
+    int64_t before = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &S = seg_of(A, bl, si);
-        const bool dense = S.kind == MKV_SEG_DENSE;
-        const int64_t w = dense ? (int64_t)(2 * BT * D * sb + 256)
-                                : (int64_t)((G > 1 ? (BT * S.r * 2 * (sb + 1) * 4) / 5 : BT * S.r * 2 * (sb + 1)) + 256);
-        const int64_t items = dense ? (int64_t)S.nb : (int64_t)G * S.k;
-        int64_t i0 = lo - Wb, i1 = hi - Wb;
-        i0 = i0 <= 0 ? 0 : (i0 + w - 1) / w;
-        i1 = i1 <= 0 ? 0 : (i1 + w - 1) / w;
-        if (i0 > items) i0 = items;
-        if (i1 > items) i1 = items;
-        Wb += items * w;
-        const int myj = pj;
-        if (!dense) ++pj;
-        if (i0 >= i1) continue;
-
-        if (dense) {
-            const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * 2 * BT * D * sb;
-            for (int64_t it = i0; it < i1; ++it) {
-                const int blk = (int)it;
-                const int nv = min(BT, S.filled - blk * BT);
-                const char *kb = seg_base + (size_t)blk * 2 * BT * D * sb;
-                const char *vb = kb + (size_t)BT * D * sb;
-                // logits: lane (tg, ch) covers tokens tg, tg+4, tg+8, tg+12 on channels 8ch..8ch+7
-                float part[4][G];
+        if (S.kind != MKV_SEG_DENSE) continue;
+        const int64_t a0 = max(i0 - before, (int64_t)0), a1 = min(i1 - before, (int64_t)S.nb);
+        before += S.nb;
+        if (a0 >= a1) continue;
+        const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * 2 * BT * D * sb;
+        for (int64_t blk = a0; blk < a1; ++blk) {
+            const int nv = min(BT, S.filled - (int)blk * BT);
+            const char *kb = seg_base + (size_t)blk * 2 * BT * D * sb;
+            const char *vb = kb + (size_t)BT * D * sb;
+            Vals8<ST> kr[4], vr[4];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int tt = 4 * ii + tg;
-                    float kv[8];
-                    Loader<ST>::load8(kb, tt * D + ch * 8, kv);
+            for (int ii = 0; ii < 4; ++ii) {
+                kr[ii].load(kb + (size_t)((4 * ii + tg) * D + ch * 8) * sb);
+                vr[ii].load(vb + (size_t)((4 * ii + tg) * D + ch * 8) * sb);
+            }
+            float part[4][G];
 #pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        float a = 0.f;
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) a = fmaf(qd[i][c], kv[c], a);
-                        part[ii][i] = a;
-                    }
-                }
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        float v = part[ii][i];
-                        v += __shfl_xor(v, 1, 64);
-                        v += __shfl_xor(v, 2, 64);
-                        v += __shfl_xor(v, 4, 64);
-                        v += __shfl_xor(v, 8, 64);
-                        part[ii][i] = v;
-                    }
-                if (ch < G) {
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        float v = part[ii][0];
-#pragma unroll
-                        for (int i = 1; i < G; ++i)
-                            if (ch == i) v = part[ii][i];
-                        zb[(4 * ii + tg) * G + ch] = v;
-                    }
-                }
-                wave_lds_sync();
-                float alpha[G];
-                softmax_block<G>(zb, nv, (1 << G) - 1, st, alpha);
+            for (int ii = 0; ii < 4; ++ii) {
+                float kv[8];
+                kr[ii].get(kv);
 #pragma unroll
                 for (int i = 0; i < G; ++i) {
-                    if (alpha[i] != 1.f) {
-                        for (int c = lane; c < D; c += 64) acc[i * D + c] *= alpha[i];
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) vacc[i][c] *= alpha[i];
-                    }
+                    const float4 qa = *reinterpret_cast<const float4 *>(&qsh[i][ch * 8]);
+                    const float4 qb = *reinterpret_cast<const float4 *>(&qsh[i][ch * 8 + 4]);
+                    float a = qa.x * kv[0];
+                    a = fmaf(qa.y, kv[1], a);
+                    a = fmaf(qa.z, kv[2], a);
+                    a = fmaf(qa.w, kv[3], a);
+                    a = fmaf(qb.x, kv[4], a);
+                    a = fmaf(qb.y, kv[5], a);
+                    a = fmaf(qb.z, kv[6], a);
+                    a = fmaf(qb.w, kv[7], a);
+                    part[ii][i] = a;
                 }
-                wave_lds_sync();
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int tt = 4 * ii + tg;
-                    float vv[8];
-                    Loader<ST>::load8(vb, tt * D + ch * 8, vv);
-#pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        const float p = zb[tt * G + i];
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) vacc[i][c] = fmaf(p, vv[c], vacc[i][c]);
-                    }
-                }
-                wave_lds_sync();
             }
-        } else {
-            const int r = S.r;
-            const size_t rec = (size_t)BT * r * 2 * (sb + 1);
-            const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * rec;
-            const int32_t *sel = A.sel + A.sl_off[myj] + ((size_t)b * A.hq + g * G) * A.kcap[myj];
-            const uint32_t *mk = A.mask + A.mk_off[myj] + ((size_t)b * A.hkv + g) * A.nbcap[myj];
-            const int nch = 2 * r;               // chunks of 8 elements per half-record
-            const uint32_t mr = ((1u << 20) + (uint32_t)r - 1) / (uint32_t)r;  // e / r = (e * mr) >> 20
-            for (int64_t it = i0; it < i1; ++it) {
-                const int rank = (int)(it / G), hl = (int)(it % G);
-                const int blk = sel[(size_t)hl * A.kcap[myj] + rank];
-                if ((unsigned)blk >= (unsigned)S.nb) continue;  // never taken for a valid selection
-                const int hm = (int)mk[blk];
-                if (hm & ((1 << hl) - 1)) continue;  // a lower head already covers this block
-                const int nv = min(BT, S.filled - blk * BT);
-                const char *base = seg_base + (size_t)blk * rec;
-                const void *kval = base;
-                const void *vval = base + (size_t)BT * r * sb;
-                const uint8_t *kidx = reinterpret_cast<const uint8_t *>(base + (size_t)2 * BT * r * sb);
-                const uint8_t *vidx = kidx + BT * r;
-                if (lane < 16 * G) zb[lane] = 0.f;
-                wave_lds_sync();
-                // ---- K: gather-dot into zb[t][h]
-                for (int c = lane; c < nch; c += 64) {
-                    const int e0 = c * 8;
-                    float kv[8];
-                    int ix[8];
-                    Loader<ST>::load8(kval, e0, kv);
-                    load_idx8(kidx, e0, ix);
-                    const int t0 = (int)(((uint32_t)e0 * mr) >> 20);
-                    if (r >= 8) {
-                        const int tb = (t0 + 1) * r;
 #pragma unroll
-                        for (int i = 0; i < G; ++i) {
-                            if (!((hm >> i) & 1)) continue;
-                            float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float pr = qsh[i][ix[e]] * kv[e];
-                                if (e0 + e >= tb) s1 += pr; else s0 += pr;
-                            }
-                            atomicAdd(&zb[t0 * G + i], s0);
-                            if (t0 + 1 < BT) atomicAdd(&zb[(t0 + 1) * G + i], s1);
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < G; ++i) {
-                            if (!((hm >> i) & 1)) continue;
-                            int tt = t0, tb = (t0 + 1) * r;
-                            float s0 = 0.f;
-                            for (int e = 0; e < 8; ++e) {
-                                if (e0 + e >= tb) {
-                                    atomicAdd(&zb[tt * G + i], s0);
-                                    s0 = 0.f;
-                                    ++tt;
-                                    tb += r;
-                                }
-                                s0 += qsh[i][ix[e]] * kv[e];
-                            }
-                            atomicAdd(&zb[tt * G + i], s0);
-                        }
-                    }
-                }
-                wave_lds_sync();
-                float alpha[G];
-                softmax_block<G>(zb, nv, hm, st, alpha);
+            for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
                 for (int i = 0; i < G; ++i) {
-                    if (alpha[i] != 1.f) {
-                        for (int c = lane; c < D; c += 64) acc[i * D + c] *= alpha[i];
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) vacc[i][c] *= alpha[i];
-                    }
+                    float v = part[ii][i];
+                    v += __shfl_xor(v, 1, 64);
+                    v += __shfl_xor(v, 2, 64);
+                    v += __shfl_xor(v, 4, 64);
+                    v += __shfl_xor(v, 8, 64);
+                    part[ii][i] = v;
                 }
-                wave_lds_sync();
-                // ---- V: scatter-add p * v into acc[h][channel]
-                for (int c = lane; c < nch; c += 64) {
-                    const int e0 = c * 8;
-                    float vv[8];
-                    int ix[8];
-                    Loader<ST>::load8(vval, e0, vv);
-                    load_idx8(vidx, e0, ix);
-                    const int t0 = (int)(((uint32_t)e0 * mr) >> 20);
+            if (ch < G) {
 #pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        if (!((hm >> i) & 1)) continue;
-                        int tt = t0, tb = (t0 + 1) * r;
-                        float p = zb[tt * G + i];
+                for (int ii = 0; ii < 4; ++ii) {
+                    float v = part[ii][0];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            while (e0 + e >= tb) {
-                                ++tt;
-                                tb += r;
-                                p = zb[min(tt, BT - 1) * G + i];
-                            }
-                            atomicAdd(&acc[i * D + ix[e]], p * vv[e]);
-                        }
-                    }
+                    for (int i = 1; i < G; ++i)
+                        if (ch == i) v = part[ii][i];
+                    zb[(4 * ii + tg) * G + ch] = v;
                 }
-                wave_lds_sync();
             }
+            wave_lds_sync();
+            float alpha[G];
+            softmax_block<G>(zb, nv, (1 << G) - 1, st, alpha);
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                if (alpha[i] != 1.f) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) vacc[i][c] *= alpha[i];
+                }
+            wave_lds_sync();
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int tt = 4 * ii + tg;
+                float vv[8];
+                vr[ii].get(vv);
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const float p = zb[tt * G + i];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) vacc[i][c] = fmaf(p, vv[c], vacc[i][c]);
+                }
+            }
+            wave_lds_sync();
         }
     }
-
-    // fold the dense-path register accumulators into acc
+    // partials: m, l and acc[h][c]; acc sums over the four token groups
 #pragma unroll
     for (int i = 0; i < G; ++i)
 #pragma unroll
@@ -655,98 +540,416 @@ __global__ __launch_bounds__(256) void k_attend(const DecodeArgs A) {
             v += __shfl_xor(v, 32, 64);
             vacc[i][c] = v;
         }
-    wave_lds_sync();
-    if (tg == 0) {
-#pragma unroll
-        for (int i = 0; i < G; ++i)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[i * D + ch * 8 + c] += vacc[i][c];
-    }
-    wave_lds_sync();
-    // l per head: sum the lanes (t, h) over t
     float lsum = lane < 16 * G ? st.l : 0.f;
 #pragma unroll
     for (int o = G; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const float li = __shfl(lsum, i, 64);
+        const float mi = st.head_max(i);
         float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + s) * PART;
         if (lane == 0) {
-            pp[0] = st.m[i];
+            pp[0] = mi;
             pp[1] = li;
         }
-        pp[2 + lane] = acc[i * D + lane];
-        pp[2 + 64 + lane] = acc[i * D + 64 + lane];
+        if (tg == 0) {
+            float2 *d2 = reinterpret_cast<float2 *>(pp + 2 + ch * 8);  // partials are 8-byte aligned
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) d2[c / 2] = make_float2(vacc[i][c], vacc[i][c + 1]);
+        }
     }
 }
 
 // ----------------------------------------------------------------------------
-// merge: one workgroup per (request, KV head): combine the splits of each
-// head (fixed order), normalise, then out_j = sum_c R_v[c][j] o_c.
+// attend_packed: four waves per workgroup, each wave one split of the unit's
+// packed items. Item (rank, head) of a packed segment is the rank-th block
+// that head selected; an item whose block a lower head of the group also
+// selected is dropped, so every union block is read once and serves each head
+// that chose it. Items are resolved 64 at a time into a compact list, and the
+// records of the list stream through a two-deep register pipeline (the next
+// record's K and V loads are in flight while the current one is computed).
+//
+// Per record: lane c (of 2r chunks of 8 elements) gathers q'[h][idx] from LDS
+// for the 8 K elements and adds into the token logits (at most two tokens per
+// chunk when r >= 8); after the softmax the 8 V elements scatter p * v into
+// the wave's accumulator acc[h][channel] with LDS float atomics.
+// ----------------------------------------------------------------------------
+template <typename ST, int NR>
+struct RecBuf {
+    Vals8<ST> kv[NR], vv[NR];
+    uint2 ki[NR], vi[NR];
+};
+
+// global loads one record puts in flight (per lane)
+template <typename ST, int NR>
+constexpr int rec_loads() { return NR * (2 * (ST::bytes == 2 ? 1 : 2) + 2); }
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] (15 = no wait) | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <typename ST, int NR>
+__device__ __forceinline__ void load_rec(const char *base, int r, int lane, RecBuf<ST, NR> &B) {
+    constexpr uint32_t sb = ST::bytes;
+    const uint32_t nch = 2 * r;
+    const uint32_t voff = (uint32_t)BT * r * sb;
+    const uint32_t kioff = 2u * BT * r * sb;
+    const uint32_t vioff = kioff + (uint32_t)BT * r;
+    // every lane loads (lanes past the last chunk re-read it), so the loads
+    // need no predication and stay in flight behind the current record
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const uint32_t c = min((uint32_t)(lane + 64 * rd), nch - 1);
+        B.kv[rd].load(base + c * 8 * sb);
+        B.vv[rd].load(base + voff + c * 8 * sb);
+        B.ki[rd] = *reinterpret_cast<const uint2 *>(base + kioff + c * 8);
+        B.vi[rd] = *reinterpret_cast<const uint2 *>(base + vioff + c * 8);
+    }
+}
+
+// Per-wave LDS scratch of the packed path.
+template <typename ST, int G, int NR>
+struct PackedLds {
+    float zb[16 * G];                 // logits, then probabilities, lane t*G+h
+    float zp[G][64 * NR][2];          // per chunk: partial logits of its first and second token
+    typename ST::bits_t vt[BT][D];    // one record's stored V vectors, dense; zero between records
+};
+
+template <typename ST, int G, int NR, bool NEXT_IN_FLIGHT>
+__device__ __forceinline__ void proc_rec(const RecBuf<ST, NR> &B, int r, uint32_t mr, int hm, int nv,
+                                         const float (*qsh)[D], PackedLds<ST, G, NR> &L, float (&acc)[G][2],
+                                         WaveState<G> &st) {
+    const int lane = lane_id();
+    const int nch = 2 * r;
+    // this record's loads are complete once only the next record's remain
+    vm_wait<NEXT_IN_FLIGHT ? rec_loads<ST, NR>() : 0>();
+
+    // ---- K: q'[h][idx] * value summed per chunk (8 elements, at most two tokens when r >= 8;
+    //      for r < 8 one partial per element)
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const int c = lane + 64 * rd;
+        float kv[8];
+        int ix[8];
+        B.kv[rd].get(kv);
+        idx8(B.ki[rd], ix);
+        const int e0 = c * 8;
+        const int t0 = (int)(((uint32_t)e0 * mr) >> 20);
+        const int tb = (t0 + 1) * r;
+#pragma unroll 1
+        for (int i = 0; i < G; ++i) {
+            if (!((hm >> i) & 1)) continue;
+            if (r >= 8) {
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pr = qsh[i][ix[e]] * kv[e];
+                    if (e0 + e >= tb) s1 += pr;
+                    else s0 += pr;
+                }
+                if (c < nch) *reinterpret_cast<float2 *>(L.zp[i][c]) = make_float2(s0, s1);
+            } else if (c < nch) {
+                // r < 8: 16 r <= 112 products, stored one per element
+                float *pe = &L.zp[i][0][0];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pe[e0 + e] = qsh[i][ix[e]] * kv[e];
+            }
+        }
+    }
+    wave_lds_sync();
+    // ---- token logits: lane t*G+h sums the chunks (or elements) of token t
+    if (lane < 16 * G) {
+        const int t = lane / G, h = lane % G;
+        float z = 0.f;
+        if ((hm >> h) & 1) {
+            if (r >= 8) {
+                const int cf = (t * r) >> 3, cl = ((t + 1) * r - 1) >> 3;
+                for (int c = cf; c <= cl; ++c) {
+                    const int tc = (int)(((uint32_t)(c * 8) * mr) >> 20);
+                    z += L.zp[h][c][tc == t ? 0 : 1];
+                }
+            } else {
+                const float *pe = &L.zp[h][0][0];
+                for (int e = t * r; e < (t + 1) * r; ++e) z += pe[e];
+            }
+        }
+        L.zb[lane] = z;
+    }
+    wave_lds_sync();
+    float alpha[G];
+    softmax_block<G>(L.zb, nv, hm, st, alpha);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        acc[i][0] *= alpha[i];
+        acc[i][1] *= alpha[i];
+    }
+    // ---- V: scatter the record's values into the dense tile
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const int c = lane + 64 * rd;
+        if (c < nch) {
+            typename ST::bits_t vv[8];
+            int ix[8];
+            B.vv[rd].raw(vv);
+            idx8(B.vi[rd], ix);
+            const int e0 = c * 8;
+            int tt = (int)(((uint32_t)e0 * mr) >> 20), tb = (tt + 1) * r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (e0 + e >= tb) {  // at most one token boundary per element step
+                    ++tt;
+                    tb += r;
+                }
+                L.vt[tt][ix[e]] = vv[e];
+            }
+        }
+    }
+    wave_lds_sync();
+    // ---- lane l accumulates channels l and l + 64 over the valid tokens
+    for (int t = 0; t < nv; ++t) {
+        const float a = bits_to_float<ST>(L.vt[t][lane]), b = bits_to_float<ST>(L.vt[t][lane + 64]);
+        float p[G];
+        if constexpr (G == 4) {
+            const float4 p4 = *reinterpret_cast<const float4 *>(&L.zb[t * 4]);
+            p[0] = p4.x; p[1] = p4.y; p[2] = p4.z; p[3] = p4.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < G; ++i) p[i] = L.zb[t * G + i];
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            acc[i][0] = fmaf(p[i], a, acc[i][0]);
+            acc[i][1] = fmaf(p[i], b, acc[i][1]);
+        }
+    }
+    wave_lds_sync();
+    // ---- clear what the scatter wrote
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const int c = lane + 64 * rd;
+        if (c < nch) {
+            int ix[8];
+            idx8(B.vi[rd], ix);
+            const int e0 = c * 8;
+            int tt = (int)(((uint32_t)e0 * mr) >> 20), tb = (tt + 1) * r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (e0 + e >= tb) {
+                    ++tt;
+                    tb += r;
+                }
+                L.vt[tt][ix[e]] = 0;
+            }
+        }
+    }
+    wave_lds_sync();
+}
+
+// list entries are wave-uniform: read them into scalar registers, so each
+// record load is a scalar base plus a loop-invariant per-lane offset
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <typename ST, int G, int NR>
+__device__ __forceinline__ void run_list(const int2 *list, int n, const char *seg_base, size_t rec, int r,
+                                         int filled, const float (*qsh)[D], PackedLds<ST, G, NR> &L,
+                                         float (&acc)[G][2], WaveState<G> &st) {
+    const int lane = lane_id();
+    const uint32_t mr = ((1u << 20) + (uint32_t)r - 1) / (uint32_t)r;  // e / r = (e * mr) >> 20 for e < 16r
+    RecBuf<ST, NR> B0, B1;
+    if (n > 0) load_rec<ST, NR>(seg_base + (size_t)uniform_int(list[0].x) * rec, r, lane, B0);
+    for (int i = 0; i < n; i += 2) {
+        const int b0 = uniform_int(list[i].x), h0 = uniform_int(list[i].y);
+        if (i + 1 < n) {
+            load_rec<ST, NR>(seg_base + (size_t)uniform_int(list[i + 1].x) * rec, r, lane, B1);
+            proc_rec<ST, G, NR, true>(B0, r, mr, h0, min(BT, filled - b0 * BT), qsh, L, acc, st);
+        } else {
+            proc_rec<ST, G, NR, false>(B0, r, mr, h0, min(BT, filled - b0 * BT), qsh, L, acc, st);
+            break;
+        }
+        const int b1 = uniform_int(list[i + 1].x), h1 = uniform_int(list[i + 1].y);
+        if (i + 2 < n) {
+            load_rec<ST, NR>(seg_base + (size_t)uniform_int(list[i + 2].x) * rec, r, lane, B0);
+            proc_rec<ST, G, NR, true>(B1, r, mr, h1, min(BT, filled - b1 * BT), qsh, L, acc, st);
+        } else {
+            proc_rec<ST, G, NR, false>(B1, r, mr, h1, min(BT, filled - b1 * BT), qsh, L, acc, st);
+        }
+    }
+}
+
+__device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
+    const int64_t rec = (int64_t)BT * r * 2 * (sb + 1);
+    return (G > 1 ? rec * 4 / 5 : rec) + 256;
+}
+
+template <typename ST, int G, int NR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_attend_packed(const DecodeArgs A) {
+    const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
+    const int b = A.b0 + bl;
+    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
+    const int s = (int)blockIdx.x * 4 + wave;
+    constexpr int sb = ST::bytes;
+
+    __shared__ __align__(16) float qsh[G][D];
+    __shared__ __align__(16) PackedLds<ST, G, NR> lds[4];
+    __shared__ int2 lists[4][64];
+    for (int i = (int)threadIdx.x; i < G * D; i += 256)
+        qsh[i / D][i % D] = A.qa[((size_t)b * A.hq + g * G) * D + i];
+    __syncthreads();
+    if (s >= A.S_p) return;
+    {
+        PackedLds<ST, G, NR> &L = lds[wave];
+        int2 *list = lists[wave];
+        for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
+        float acc[G][2];
+#pragma unroll
+        for (int i = 0; i < G; ++i) acc[i][0] = acc[i][1] = 0.f;
+        WaveState<G> st;
+        st.init();
+
+        int64_t W = 0;
+        for (int si = 0; si < A.nseg; ++si) {
+            const DSeg &S = seg_of(A, bl, si);
+            if (S.kind == MKV_SEG_PACKED) W += (int64_t)G * S.k * packed_weight(S.r, sb, G);
+        }
+        const int64_t lo = W * s / A.S_p, hi = W * (s + 1) / A.S_p;
+        int64_t Wb = 0;
+        int pj = 0;
+        for (int si = 0; si < A.nseg; ++si) {
+            const DSeg &S = seg_of(A, bl, si);
+            if (S.kind != MKV_SEG_PACKED) continue;
+            const int myj = pj++;
+            const int64_t w = packed_weight(S.r, sb, G);
+            const int64_t items = (int64_t)G * S.k;
+            int64_t i0 = lo - Wb, i1 = hi - Wb;
+            i0 = i0 <= 0 ? 0 : (i0 + w - 1) / w;
+            i1 = i1 <= 0 ? 0 : (i1 + w - 1) / w;
+            i0 = min(i0, items);
+            i1 = min(i1, items);
+            Wb += items * w;
+            if (i0 >= i1) continue;
+            const int r = S.r;
+            const size_t rec = (size_t)BT * r * 2 * (sb + 1);
+            const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * rec;
+            const int kc = A.kcap[myj];
+            const int32_t *sel = A.sel + A.sl_off[myj] + ((size_t)b * A.hq + g * G) * kc;
+            const uint32_t *mk = A.mask + A.mk_off[myj] + ((size_t)b * A.hkv + g) * A.nbcap[myj];
+            for (int64_t base = i0; base < i1; base += 64) {
+                // resolve up to 64 items into (block, head mask) pairs
+                const int64_t it = base + lane;
+                bool keep = false;
+                int blk = 0, hm = 0;
+                if (it < i1) {
+                    const int rank = (int)(it / G), hl = (int)(it % G);
+                    blk = sel[(size_t)hl * kc + rank];
+                    if ((unsigned)blk < (unsigned)S.nb) {
+                        hm = (int)mk[blk];
+                        keep = !(hm & ((1 << hl) - 1));
+                    }
+                }
+                const uint64_t km = ballot(keep);
+                if (keep) list[popc64(km & lanes_below(lane))] = make_int2(blk, hm);
+                const int n = popc64(km);
+                wave_lds_sync();
+                run_list<ST, G, NR>(list, n, seg_base, rec, r, S.filled, qsh, L, acc, st);
+                wave_lds_sync();
+            }
+        }
+        // write this split's partials (after the dense splits)
+        float lsum = lane < 16 * G ? st.l : 0.f;
+#pragma unroll
+        for (int o = G; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const float li = __shfl(lsum, i, 64);
+            const float mi = st.head_max(i);
+            float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + A.S_d + s) * PART;
+            if (lane == 0) {
+                pp[0] = mi;
+                pp[1] = li;
+            }
+            pp[2 + lane] = acc[i][0];
+            pp[2 + 64 + lane] = acc[i][1];
+        }
+    }
+
+}
+
+// ----------------------------------------------------------------------------
+// merge: one workgroup per (request, query head): log-sum-exp merge of the
+// head's dense and packed splits in split order, then out_j = sum_c R_v[c][j] o_c.
 // ----------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
-    const int bl = (int)blockIdx.y, g = (int)blockIdx.x;
-    const int b = A.b0 + bl;
-    const int t = (int)threadIdx.x;
-    const int S_ = A.S;
-    __shared__ float wsc[G][MAX_SPLITS];
-    __shared__ float Ls[G];
-    __shared__ __align__(16) float osh[G][D];
-    for (int i = 0; i < G; ++i) {
-        const float *pp = A.part + ((size_t)b * A.hq + g * G + i) * MAX_SPLITS * PART;
-        if (t < 64) {
-            float M = -INFINITY;
-            for (int s = t; s < S_; s += 64) M = fmaxf(M, pp[(size_t)s * PART]);
+    const int bl = (int)blockIdx.y, h = (int)blockIdx.x;
+    const int b = A.b0 + bl, g = h / G;
+    const int t = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x >> 6);
+    const int Stot = A.S_d + A.S_p;
+    const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_SPLITS * PART;
+    __shared__ float wsc[MAX_SPLITS];
+    __shared__ float part_o[2][D];
+    __shared__ __align__(16) float osh[D];
+    __shared__ float Lsh;
+    if (wave == 0) {
+        float M = -INFINITY;
+        for (int x = lane; x < Stot; x += 64) M = fmaxf(M, pp[(size_t)x * PART]);
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-            float L = 0.f;
-            for (int s = t; s < S_; s += 64) {
-                const float m = pp[(size_t)s * PART];
-                const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-                wsc[i][s] = w;
-                L += w * pp[(size_t)s * PART + 1];
-            }
-            L = wave_sum(L);
-            if (t == 0) Ls[i] = L;
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        float L = 0.f;
+        for (int x = lane; x < Stot; x += 64) {
+            const float m = pp[(size_t)x * PART];
+            const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+            wsc[x] = w;
+            L += w * pp[(size_t)x * PART + 1];
         }
+        L = wave_sum(L);
+        if (lane == 0) Lsh = L;
     }
     __syncthreads();
-    for (int x = t; x < G * D; x += 256) {
-        const int i = x / D, c = x % D;
-        const float *pp = A.part + ((size_t)b * A.hq + g * G + i) * MAX_SPLITS * PART;
+    {
+        const int c = t & (D - 1), half = t >> 7;  // two halves of the splits
         float o = 0.f;
-        for (int s = 0; s < S_; ++s) o = fmaf(wsc[i][s], pp[(size_t)s * PART + 2 + c], o);
-        const float L = Ls[i];
-        osh[i][c] = L > 0.f ? o / L : 0.f;
+        int y = half;
+#pragma unroll 4
+        for (; y < Stot; y += 2) o = fmaf(wsc[y], pp[(size_t)y * PART + 2 + c], o);
+        part_o[half][c] = o;
+    }
+    __syncthreads();
+    if (t < D) {
+        const float L = Lsh;
+        osh[t] = L > 0.f ? (part_o[0][t] + part_o[1][t]) / L : 0.f;
     }
     __syncthreads();
     if (t < D) {
         const float *Rv = A.rot + (((size_t)b * A.hkv + g) * 2 + 1) * D * D;
-        float acc[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) acc[i] = 0.f;
-        for (int c = 0; c < D; ++c) {
-            const float r = Rv[(size_t)c * D + t];
-#pragma unroll
-            for (int i = 0; i < G; ++i) acc[i] = fmaf(r, osh[i][c], acc[i]);
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < D; c += 2) {
+            o0 = fmaf(Rv[(size_t)c * D + t], osh[c], o0);
+            o1 = fmaf(Rv[(size_t)(c + 1) * D + t], osh[c + 1], o1);
         }
-#pragma unroll
-        for (int i = 0; i < G; ++i) A.out[((size_t)b * A.hq + g * G + i) * D + t] = acc[i];
+        A.out[((size_t)b * A.hq + h) * D + t] = o0 + o1;
     }
 }
 
-template <int G>
-hipError_t select_launch(const DecodeArgs &a, int kpt, hipStream_t s) {
+template <int G, int KPT>
+hipError_t select_launch_kpt(const DecodeArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)G, (unsigned)a.hkv, (unsigned)(a.n_req * a.npk));
-    switch (kpt) {
-    case 1: hipLaunchKernelGGL((k_select<G, 1>), grid, dim3(SEL_THREADS), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_select<G, 4>), grid, dim3(SEL_THREADS), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_select<G, 16>), grid, dim3(SEL_THREADS), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_select<G, 64>), grid, dim3(SEL_THREADS), 0, s, a); break;
+    hipLaunchKernelGGL((k_select<G, KPT>), grid, dim3(64 * a.sel_waves), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t select_launch(const DecodeArgs &a, hipStream_t s) {
+    switch (a.sel_kpt) {
+    case 4: return select_launch_kpt<G, 4>(a, s);
+    case 16: return select_launch_kpt<G, 16>(a, s);
+    case 64: return select_launch_kpt<G, 64>(a, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -775,16 +978,27 @@ hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hi
     return hipGetLastError();
 }
 
-hipError_t launch_select(const DecodeArgs &a, int G, int kpt, hipStream_t s) {
+hipError_t launch_select(const DecodeArgs &a, int G, hipStream_t s) {
     if (a.npk == 0) return hipSuccess;
-    if (G == 1) return select_launch<1>(a, kpt, s);
-    if (G == 2) return select_launch<2>(a, kpt, s);
-    return select_launch<4>(a, kpt, s);
+    if (G == 1) return select_launch<1>(a, s);
+    if (G == 2) return select_launch<2>(a, s);
+    return select_launch<4>(a, s);
 }
 
-hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, hipStream_t s) {
-    const dim3 grid((unsigned)((a.S + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
-#define MKV_ATT(ST, GG) hipLaunchKernelGGL((k_attend<ST, GG>), grid, dim3(256), 0, s, a)
+hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s) {
+    const dim3 grid((unsigned)a.hq, (unsigned)a.n_req);
+    switch (G) {
+    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_dense(const DecodeArgs &a, int dtype, int G, hipStream_t s) {
+    const dim3 grid((unsigned)((a.S_d + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
+#define MKV_ATT(ST, GG) hipLaunchKernelGGL((k_attend_dense<ST, GG>), grid, dim3(256), 0, s, a)
     if (dtype == MKV_BF16) {
         if (G == 1) MKV_ATT(Bf16, 1); else if (G == 2) MKV_ATT(Bf16, 2); else MKV_ATT(Bf16, 4);
     } else {
@@ -794,13 +1008,24 @@ hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s) {
-    const dim3 grid((unsigned)a.hkv, (unsigned)a.n_req);
-    switch (G) {
-    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+template <typename ST, int G>
+void packed_launch(const DecodeArgs &a, int nr, dim3 grid, hipStream_t s) {
+    if (nr <= 1) hipLaunchKernelGGL((k_attend_packed<ST, G, 1>), grid, dim3(256), 0, s, a);
+    else if (nr == 2) hipLaunchKernelGGL((k_attend_packed<ST, G, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attend_packed<ST, G, 4>), grid, dim3(256), 0, s, a);
+}
+
+// nr: 64-lane rounds of 8-element chunks of the widest packed record, ceil(2 r_max / 64)
+hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int nr, hipStream_t s) {
+    const dim3 grid((unsigned)((a.S_p + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
+    if (dtype == MKV_BF16) {
+        if (G == 1) packed_launch<Bf16, 1>(a, nr, grid, s);
+        else if (G == 2) packed_launch<Bf16, 2>(a, nr, grid, s);
+        else packed_launch<Bf16, 4>(a, nr, grid, s);
+    } else {
+        if (G == 1) packed_launch<F32, 1>(a, nr, grid, s);
+        else if (G == 2) packed_launch<F32, 2>(a, nr, grid, s);
+        else packed_launch<F32, 4>(a, nr, grid, s);
     }
     return hipGetLastError();
 }

@@ -352,10 +352,10 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
         A.npk = m.npk;
         A.hq = c->n_q_heads;
         A.hkv = c->n_kv_heads;
-        int max_tiles = 0, max_nb = 0;
-        int64_t Wmax = 0;
+        int max_tiles = 0, max_nb = 0, max_r = 1;
+        int64_t Wmax = 0, Dmax = 0;
         for (int i = 0; i < n_req; ++i) {
-            int64_t W = 0;
+            int64_t W = 0, Dn = 0;
             for (int j = 0; j < c->n_segments; ++j) {
                 const mkv_segment &sg = segof(c, b0 + i, j);
                 DSeg &D_ = A.seg[i * c->n_segments + j];
@@ -370,29 +370,38 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
                     D_.k = (int32_t)keep_blocks(D_.nb, sg.keep_ppm, sg.k_abs);
                     max_tiles = std::max(max_tiles, (int)ceil_div(D_.nb, META_TILE));
                     max_nb = std::max(max_nb, D_.nb);
+                    max_r = std::max(max_r, (int)sg.r);
                     const int64_t rec = (int64_t)BT * sg.r * 2 * (sb + 1);
                     W += (int64_t)G * D_.k * ((G > 1 ? rec * 4 / 5 : rec) + 256);
                 } else {
-                    W += (int64_t)D_.nb * (2 * BT * D * sb + 256);
+                    Dn += (int64_t)D_.nb * 2 * BT * D * sb;
                 }
             }
             Wmax = std::max(Wmax, W);
+            Dmax = std::max(Dmax, Dn);
         }
-        // splits: about 64 KB of cache reads each, at most MAX_SPLITS per unit
-        A.S = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS, ceil_div(Wmax, 64 * 1024)));
-        A.sel_kpt = max_nb <= 1024 ? 1 : max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
+        // splits of about 64 KB of cache reads each
+        A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 64 * 1024)));
+        A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 64 * 1024)));
+        // select: up to 16 waves, 4 / 16 / 64 keys per lane
+        const int kpt = max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
+        A.sel_kpt = kpt;
+        A.sel_waves = (int32_t)std::max<int64_t>(1, ceil_div(max_nb, 64 * kpt));
 
         st = timed(2, s, [&] { return launch_qrot(A, G, s); });
         if (st != MKV_OK) return st;
         if (m.npk > 0) {
             st = timed(3, s, [&] { return launch_score(A, c->dtype, G, max_tiles, s); });
             if (st != MKV_OK) return st;
-            st = timed(4, s, [&] { return launch_select(A, G, A.sel_kpt, s); });
+            st = timed(4, s, [&] { return launch_select(A, G, s); });
             if (st != MKV_OK) return st;
         }
-        st = timed(5, s, [&] { return launch_attend(A, c->dtype, G, s); });
+        st = timed(5, s, [&] { return launch_attend_dense(A, c->dtype, G, s); });
         if (st != MKV_OK) return st;
-        st = timed(6, s, [&] { return launch_merge(A, G, s); });
+        const int nr = 2 * max_r <= 64 ? 1 : 2 * max_r <= 128 ? 2 : 4;
+        st = timed(6, s, [&] { return launch_attend_packed(A, c->dtype, G, nr, s); });
+        if (st != MKV_OK) return st;
+        st = timed(7, s, [&] { return launch_merge(A, G, s); });
         if (st != MKV_OK) return st;
     }
     return MKV_OK;
@@ -430,8 +439,8 @@ mkv_status mkv_timing_read(double *ms_out, int64_t *count_out, int32_t n_stages)
 }
 
 const char *mkv_stage_name(int32_t stage) {
-    static const char *names[MKV_N_STAGES] = {"compress", "block_meta", "q_rotate", "score",
-                                              "select",   "attend",     "merge"};
+    static const char *names[MKV_N_STAGES] = {"compress", "block_meta",   "q_rotate",      "score",
+                                              "select",   "attend_dense", "attend_packed", "merge"};
     return (stage >= 0 && stage < MKV_N_STAGES) ? names[stage] : "unknown";
 }
 

@@ -75,7 +75,7 @@ struct DecodeArgs {
     float *scores;    // per packed j: [B][Hq][nbcap_j]
     uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j]
     int32_t *sel;     // per packed j: [B][Hq][kcap_j]
-    float *part;      // [B][Hq][S][PART]
+    float *part;      // [B][Hq][MAX_SPLITS][PART]: dense splits, then packed splits
     int64_t sel_cols;
     int64_t sc_off[MKV_MAX_SEGMENTS];
     int64_t mk_off[MKV_MAX_SEGMENTS];
@@ -83,7 +83,11 @@ struct DecodeArgs {
     int32_t nbcap[MKV_MAX_SEGMENTS];  // per packed j (max over requests)
     int32_t kcap[MKV_MAX_SEGMENTS];
     int32_t pseg[MKV_MAX_SEGMENTS];   // segment index of packed j
-    int32_t b0, n_req, nseg, npk, hq, hkv, S, sel_kpt;
+    int32_t b0, n_req, nseg, npk, hq, hkv;
+    int32_t S_d;       // dense splits per unit (>= 1)
+    int32_t S_p;       // packed splits per unit (>= 1), S_d + S_p <= MAX_SPLITS
+    int32_t sel_kpt;   // keys per lane in select
+    int32_t sel_waves; // waves per select workgroup
 };
 
 // ---- launchers (defined in the .hip files) --------------------------------
@@ -91,8 +95,9 @@ hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStr
 hipError_t launch_block_meta(const MetaArgs &a, int dtype, int max_nb, hipStream_t s);
 hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s);
 hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hipStream_t s);
-hipError_t launch_select(const DecodeArgs &a, int G, int kpt, hipStream_t s);
-hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, hipStream_t s);
+hipError_t launch_select(const DecodeArgs &a, int G, hipStream_t s);
+hipError_t launch_attend_dense(const DecodeArgs &a, int dtype, int G, hipStream_t s);
+hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int nr, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s);
 
 }  // namespace mkv

@@ -138,53 +138,92 @@ struct SelShared {
     int v[2][SEL_MAX_WAVES][3];
 };
 
+// DPP row (16-lane) reductions on integers; every lane of the row gets the result
+#define MKV_RORI(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), ctrl, 0xf, 0xf, false)
+__device__ __forceinline__ int row_sum16_i(int v) {
+    v += MKV_RORI(v, 0x121);
+    v += MKV_RORI(v, 0x122);
+    v += MKV_RORI(v, 0x124);
+    v += MKV_RORI(v, 0x128);
+    return v;
+}
+__device__ __forceinline__ uint32_t row_min16_u(uint32_t v) {
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x121));
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x122));
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x124));
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x128));
+    return v;
+}
+__device__ __forceinline__ uint32_t row_max16_u(uint32_t v) {
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x121));
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x122));
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x124));
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x128));
+    return v;
+}
+#undef MKV_RORI
+__device__ __forceinline__ int lane_int(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// wave-uniform min / max of a per-lane value
+__device__ __forceinline__ void wave_minmax_u(uint32_t &mn, uint32_t &mx) {
+    const uint32_t a = row_min16_u(mn), b = row_max16_u(mx);
+    mn = min(min((uint32_t)lane_int((int)a, 0), (uint32_t)lane_int((int)a, 16)),
+             min((uint32_t)lane_int((int)a, 32), (uint32_t)lane_int((int)a, 48)));
+    mx = max(max((uint32_t)lane_int((int)b, 0), (uint32_t)lane_int((int)b, 16)),
+             max((uint32_t)lane_int((int)b, 32), (uint32_t)lane_int((int)b, 48)));
+}
+
+// Cross-wave helpers (nw <= 16 waves): after the barrier, lane i of every
+// wave reads wave i's entry and a DPP row reduction combines them.
 // sum three wave-uniform values over the workgroup's waves
 __device__ __forceinline__ void xwave_sum3(SelShared &sh, int &ph, int nw, int &a, int &b, int &c) {
     if (nw == 1) return;
-    const int w = (int)(threadIdx.x >> 6);
-    if (lane_id() == 0) {
+    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+    if (lane == 0) {
         sh.v[ph][w][0] = a;
         sh.v[ph][w][1] = b;
         sh.v[ph][w][2] = c;
     }
     __syncthreads();
-    a = b = c = 0;
-    for (int i = 0; i < nw; ++i) {
-        a += sh.v[ph][i][0];
-        b += sh.v[ph][i][1];
-        c += sh.v[ph][i][2];
+    int x = 0, y = 0, z = 0;
+    if (lane < nw) {
+        x = sh.v[ph][lane][0];
+        y = sh.v[ph][lane][1];
+        z = sh.v[ph][lane][2];
     }
+    a = lane_int(row_sum16_i(x), 0);
+    b = lane_int(row_sum16_i(y), 0);
+    c = lane_int(row_sum16_i(z), 0);
     ph ^= 1;
 }
 
 // exclusive prefix over waves of a wave-uniform value
 __device__ __forceinline__ int xwave_excl(SelShared &sh, int &ph, int nw, int v) {
     if (nw == 1) return 0;
-    const int w = (int)(threadIdx.x >> 6);
-    if (lane_id() == 0) sh.v[ph][w][0] = v;
+    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+    if (lane == 0) sh.v[ph][w][0] = v;
     __syncthreads();
-    int before = 0;
-    for (int i = 0; i < w; ++i) before += sh.v[ph][i][0];
+    const int x = lane < w ? sh.v[ph][lane][0] : 0;
     ph ^= 1;
-    return before;
+    return lane_int(row_sum16_i(x), 0);
 }
 
 __device__ __forceinline__ void xwave_minmax(SelShared &sh, int &ph, int nw, uint32_t &mn, uint32_t &mx) {
-    mn = wave_min_u(mn);
-    mx = wave_max_u(mx);
+    wave_minmax_u(mn, mx);
     if (nw == 1) return;
-    const int w = (int)(threadIdx.x >> 6);
-    if (lane_id() == 0) {
+    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+    if (lane == 0) {
         sh.v[ph][w][0] = (int)mn;
         sh.v[ph][w][1] = (int)mx;
     }
     __syncthreads();
-    mn = 0xFFFFFFFFu;
-    mx = 0u;
-    for (int i = 0; i < nw; ++i) {
-        mn = min(mn, (uint32_t)sh.v[ph][i][0]);
-        mx = max(mx, (uint32_t)sh.v[ph][i][1]);
+    uint32_t a = 0xFFFFFFFFu, b = 0u;
+    if (lane < nw) {
+        a = (uint32_t)sh.v[ph][lane][0];
+        b = (uint32_t)sh.v[ph][lane][1];
     }
+    mn = (uint32_t)lane_int((int)row_min16_u(a), 0);
+    mx = (uint32_t)lane_int((int)row_max16_u(b), 0);
     ph ^= 1;
 }
 
@@ -312,46 +351,64 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
 // ----------------------------------------------------------------------------
 // shared pieces of the attention kernels
 // ----------------------------------------------------------------------------
+// Reductions over the 16 lanes of a DPP row (every lane gets the result).
+#define MKV_ROR(v, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false))
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, MKV_ROR(v, 0x121));
+    v = fmaxf(v, MKV_ROR(v, 0x122));
+    v = fmaxf(v, MKV_ROR(v, 0x124));
+    v = fmaxf(v, MKV_ROR(v, 0x128));
+    return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += MKV_ROR(v, 0x121);
+    v += MKV_ROR(v, 0x122);
+    v += MKV_ROR(v, 0x124);
+    v += MKV_ROR(v, 0x128);
+    return v;
+}
+#undef MKV_ROR
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Online-softmax state. Softmax lanes are head-major: lane h*16 + t holds
+// token t of query head h, so each head is one DPP row.
 template <int G>
 struct WaveState {
-    float m;  // running max (log2 units) of the lane's head h = lane % G
-    float l;  // lane-private partial sum for lane (t, h)
+    float m;  // running max (log2 units) of the lane's head, uniform within the row
+    float l;  // lane-private partial sum of p
     __device__ __forceinline__ void init() {
         m = -INFINITY;
         l = 0.f;
     }
-    // running max of head i (lane i holds head i at token 0)
-    __device__ __forceinline__ float head_max(int i) const { return __shfl(m, i, 64); }
+    __device__ __forceinline__ float head_max(int i) const { return lane_value(m, 16 * i); }
+    __device__ __forceinline__ float head_sum(int i) const { return lane_value(row_sum16(l), 16 * i); }
 };
 
-// Online-softmax step over the 16 logits of one block held in zb[t*G + h]
-// (lane t*G+h owns one). The running max only moves when a block exceeds it
-// by more than 2^8, so rescales are rare. Leaves p in zb and returns the
-// per-head rescale factors (uniform).
+// One online-softmax step over a block of 16 tokens. z is the logit of lane
+// (h, t) = (lane / 16, lane % 16), valid marks real (token, head) pairs. The
+// running max only moves when a block exceeds it by more than 2^8, so
+// rescales are rare. Writes p to zb[t * G + h]; alpha[i] is head i's rescale.
 template <int G>
-__device__ __forceinline__ void softmax_block(float *zb, int nv, int hm, WaveState<G> &st, float alpha[G]) {
+__device__ __forceinline__ void softmax16(float z, bool valid, float *zb, WaveState<G> &st, float alpha[G]) {
     const int lane = lane_id();
-    const int t = lane / G, h = lane % G;
-    const bool own = lane < 16 * G;
-    const bool valid = own && t < nv && ((hm >> h) & 1);
-    const float z = valid ? zb[lane] : -INFINITY;
-    float bm = z;
-#pragma unroll
-    for (int o = G; o < 16 * G; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+    const float zz = valid ? z : -INFINITY;
+    const float bm = row_max16(zz);
     const float mh = st.m;
     float mnew = mh, a = 1.f;
     if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
         a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
         mnew = bm;
     }
-    const float p = valid ? exp2f(z - mnew) : 0.f;
-    if (own) {
+    const float p = valid ? exp2f(zz - mnew) : 0.f;
+    if (lane < 16 * G) {
         st.l = st.l * a + p;
         st.m = mnew;
-        zb[lane] = p;
+        zb[(lane & 15) * G + (lane >> 4)] = p;
     }
 #pragma unroll
-    for (int i = 0; i < G; ++i) alpha[i] = __shfl(a, i, 64);
+    for (int i = 0; i < G; ++i) alpha[i] = lane_value(a, 16 * i);
 }
 
 // 8 consecutive stored values (bf16: one 16-byte load; f32: two)
@@ -484,17 +541,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
                     part[ii][i] = a;
                 }
             }
+            // a token group is one DPP row of 16 lanes
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-                for (int i = 0; i < G; ++i) {
-                    float v = part[ii][i];
-                    v += __shfl_xor(v, 1, 64);
-                    v += __shfl_xor(v, 2, 64);
-                    v += __shfl_xor(v, 4, 64);
-                    v += __shfl_xor(v, 8, 64);
-                    part[ii][i] = v;
-                }
+                for (int i = 0; i < G; ++i) part[ii][i] = row_sum16(part[ii][i]);
             if (ch < G) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
@@ -507,7 +558,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             }
             wave_lds_sync();
             float alpha[G];
-            softmax_block<G>(zb, nv, (1 << G) - 1, st, alpha);
+            {
+                const int h = lane >> 4, t = lane & 15;
+                const bool valid = h < G && t < nv;
+                softmax16<G>(valid ? zb[t * G + h] : 0.f, valid, zb, st, alpha);
+            }
 #pragma unroll
             for (int i = 0; i < G; ++i)
                 if (alpha[i] != 1.f) {
@@ -540,12 +595,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             v += __shfl_xor(v, 32, 64);
             vacc[i][c] = v;
         }
-    float lsum = lane < 16 * G ? st.l : 0.f;
-#pragma unroll
-    for (int o = G; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        const float li = __shfl(lsum, i, 64);
+        const float li = st.head_sum(i);
         const float mi = st.head_max(i);
         float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + s) * PART;
         if (lane == 0) {
@@ -614,10 +666,49 @@ __device__ __forceinline__ void load_rec(const char *base, int r, int lane, RecB
 // Per-wave LDS scratch of the packed path.
 template <typename ST, int G, int NR>
 struct PackedLds {
-    float zb[16 * G];                 // logits, then probabilities, lane t*G+h
+    float zb[16 * G];                 // probabilities p[t][h] at t * G + h
     float zp[G][64 * NR][2];          // per chunk: partial logits of its first and second token
-    typename ST::bits_t vt[BT][D];    // one record's stored V vectors, dense; zero between records
+    typename ST::bits_t vt[BT][64][2]; // one record's stored V vectors, dense (channel c at [c % 64][c / 64]);
+                                       // zero between records
 };
+
+// acc[h][*] += sum_t p[t][h] * v[t][lane, lane + 64] from the dense tile, for
+// head I only (I >= 0) or for every head (I = -1).
+template <typename ST, int G, int NR, int I>
+__device__ __forceinline__ void accum_v(const PackedLds<ST, G, NR> &L, float (&acc)[G][2], int lane) {
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        float a, b;
+        if constexpr (ST::bytes == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(&L.vt[t][lane][0]);
+            a = bf16_lo(w);
+            b = bf16_hi(w);
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2 *>(&L.vt[t][lane][0]);
+            a = __uint_as_float(w.x);
+            b = __uint_as_float(w.y);
+        }
+        if constexpr (I >= 0) {
+            const float p = L.zb[t * G + I];
+            acc[I][0] = fmaf(p, a, acc[I][0]);
+            acc[I][1] = fmaf(p, b, acc[I][1]);
+        } else {
+            float p[G];
+            if constexpr (G == 4) {
+                const float4 p4 = *reinterpret_cast<const float4 *>(&L.zb[t * 4]);
+                p[0] = p4.x; p[1] = p4.y; p[2] = p4.z; p[3] = p4.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < G; ++i) p[i] = L.zb[t * G + i];
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                acc[i][0] = fmaf(p[i], a, acc[i][0]);
+                acc[i][1] = fmaf(p[i], b, acc[i][1]);
+            }
+        }
+    }
+}
 
 template <typename ST, int G, int NR, bool NEXT_IN_FLIGHT>
 __device__ __forceinline__ void proc_rec(const RecBuf<ST, NR> &B, int r, uint32_t mr, int hm, int nv,
@@ -661,27 +752,31 @@ __device__ __forceinline__ void proc_rec(const RecBuf<ST, NR> &B, int r, uint32_
         }
     }
     wave_lds_sync();
-    // ---- token logits: lane t*G+h sums the chunks (or elements) of token t
-    if (lane < 16 * G) {
-        const int t = lane / G, h = lane % G;
+    // ---- token logits: lane (h, t) = (lane / 16, lane % 16) sums the chunks (or elements) of token t
+    float alpha[G];
+    {
+        const int h = lane >> 4, t = lane & 15;
+        const bool valid = h < G && t < nv && ((hm >> h) & 1);
         float z = 0.f;
-        if ((hm >> h) & 1) {
+        if (valid) {
             if (r >= 8) {
+                // token t spans chunks cf..cl: at most 4 * NR + 1 of them, since r <= 32 * NR
                 const int cf = (t * r) >> 3, cl = ((t + 1) * r - 1) >> 3;
-                for (int c = cf; c <= cl; ++c) {
-                    const int tc = (int)(((uint32_t)(c * 8) * mr) >> 20);
-                    z += L.zp[h][c][tc == t ? 0 : 1];
+#pragma unroll
+                for (int k = 0; k <= 4 * NR; ++k) {
+                    const int c = cf + k;
+                    if (c <= cl) {
+                        const int tc = (int)(((uint32_t)(c * 8) * mr) >> 20);
+                        z += L.zp[h][c][tc == t ? 0 : 1];
+                    }
                 }
             } else {
                 const float *pe = &L.zp[h][0][0];
                 for (int e = t * r; e < (t + 1) * r; ++e) z += pe[e];
             }
         }
-        L.zb[lane] = z;
+        softmax16<G>(z, valid, L.zb, st, alpha);
     }
-    wave_lds_sync();
-    float alpha[G];
-    softmax_block<G>(L.zb, nv, hm, st, alpha);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         acc[i][0] *= alpha[i];
@@ -704,49 +799,30 @@ __device__ __forceinline__ void proc_rec(const RecBuf<ST, NR> &B, int r, uint32_
                     ++tt;
                     tb += r;
                 }
-                L.vt[tt][ix[e]] = vv[e];
+                L.vt[tt][ix[e] & 63][ix[e] >> 6] = vv[e];
             }
         }
     }
     wave_lds_sync();
-    // ---- lane l accumulates channels l and l + 64 over the valid tokens
-    for (int t = 0; t < nv; ++t) {
-        const float a = bits_to_float<ST>(L.vt[t][lane]), b = bits_to_float<ST>(L.vt[t][lane + 64]);
-        float p[G];
-        if constexpr (G == 4) {
-            const float4 p4 = *reinterpret_cast<const float4 *>(&L.zb[t * 4]);
-            p[0] = p4.x; p[1] = p4.y; p[2] = p4.z; p[3] = p4.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < G; ++i) p[i] = L.zb[t * G + i];
-        }
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            acc[i][0] = fmaf(p[i], a, acc[i][0]);
-            acc[i][1] = fmaf(p[i], b, acc[i][1]);
-        }
+    // ---- lane l accumulates channels l and l + 64 over the 16 slots (rows of
+    //      missing tokens are zero and their p is 0); most union blocks serve
+    //      a single head, which gets its own path
+    if (__popc(hm) == 1) {
+        const int i = __ffs(hm) - 1;
+        if (i == 0) accum_v<ST, G, NR, 0>(L, acc, lane);
+        if constexpr (G > 1) if (i == 1) accum_v<ST, G, NR, 1>(L, acc, lane);
+        if constexpr (G > 2) if (i == 2) accum_v<ST, G, NR, 2>(L, acc, lane);
+        if constexpr (G > 3) if (i == 3) accum_v<ST, G, NR, 3>(L, acc, lane);
+    } else {
+        accum_v<ST, G, NR, -1>(L, acc, lane);
     }
-    wave_lds_sync();
-    // ---- clear what the scatter wrote
+    // ---- clear the tile with full-width stores (LDS operations of a wave run in order)
+    {
+        constexpr int n16 = (int)sizeof(L.vt) / 16;  // 16-byte pieces: 256 (bf16) or 512 (f32)
+        uint4 *v4 = reinterpret_cast<uint4 *>(&L.vt[0][0][0]);
 #pragma unroll
-    for (int rd = 0; rd < NR; ++rd) {
-        const int c = lane + 64 * rd;
-        if (c < nch) {
-            int ix[8];
-            idx8(B.vi[rd], ix);
-            const int e0 = c * 8;
-            int tt = (int)(((uint32_t)e0 * mr) >> 20), tb = (tt + 1) * r;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (e0 + e >= tb) {
-                    ++tt;
-                    tb += r;
-                }
-                L.vt[tt][ix[e]] = 0;
-            }
-        }
+        for (int i = 0; i < n16 / 64; ++i) v4[lane + 64 * i] = make_uint4(0, 0, 0, 0);
     }
-    wave_lds_sync();
 }
 
 // list entries are wave-uniform: read them into scalar registers, so each
@@ -803,7 +879,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     {
         PackedLds<ST, G, NR> &L = lds[wave];
         int2 *list = lists[wave];
-        for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
+        for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0][0])[i] = 0;
         float acc[G][2];
 #pragma unroll
         for (int i = 0; i < G; ++i) acc[i][0] = acc[i][1] = 0.f;
@@ -859,12 +935,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             }
         }
         // write this split's partials (after the dense splits)
-        float lsum = lane < 16 * G ? st.l : 0.f;
-#pragma unroll
-        for (int o = G; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const float li = __shfl(lsum, i, 64);
+            const float li = st.head_sum(i);
             const float mi = st.head_max(i);
             float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + A.S_d + s) * PART;
             if (lane == 0) {
@@ -890,7 +963,7 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     const int Stot = A.S_d + A.S_p;
     const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_SPLITS * PART;
     __shared__ float wsc[MAX_SPLITS];
-    __shared__ float part_o[2][D];
+    __shared__ __align__(16) float part_o[8][D];
     __shared__ __align__(16) float osh[D];
     __shared__ float Lsh;
     if (wave == 0) {
@@ -910,17 +983,29 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     }
     __syncthreads();
     {
-        const int c = t & (D - 1), half = t >> 7;  // two halves of the splits
-        float o = 0.f;
-        int y = half;
+        // thread (group, quad): channels 4*quad..4*quad+3 over splits group, group+8, ...
+        const int quad = t & 31, grp = t >> 5;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-        for (; y < Stot; y += 2) o = fmaf(wsc[y], pp[(size_t)y * PART + 2 + c], o);
-        part_o[half][c] = o;
+        for (int y = grp; y < Stot; y += 8) {
+            const float w = wsc[y];
+            const float *src = pp + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
+            const float2 x0 = *reinterpret_cast<const float2 *>(src);
+            const float2 x1 = *reinterpret_cast<const float2 *>(src + 2);
+            o.x = fmaf(w, x0.x, o.x);
+            o.y = fmaf(w, x0.y, o.y);
+            o.z = fmaf(w, x1.x, o.z);
+            o.w = fmaf(w, x1.y, o.w);
+        }
+        *reinterpret_cast<float4 *>(&part_o[grp][quad * 4]) = o;
     }
     __syncthreads();
     if (t < D) {
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o += part_o[k][t];
         const float L = Lsh;
-        osh[t] = L > 0.f ? (part_o[0][t] + part_o[1][t]) / L : 0.f;
+        osh[t] = L > 0.f ? o / L : 0.f;
     }
     __syncthreads();
     if (t < D) {

@@ -29,6 +29,15 @@
  *   - top-k per query head and per packed segment, ties to the lower block;
  *   - dense segments are always attended.
  *
+ * Parity unpinned: no value printed on the pages fixes these conventions, so
+ * only the agreement of this oracle with the GPU path checks them -- block
+ * keys taken from the stored sparse keys, the ascending stored order of kept
+ * channels, the integer ceil of the keep ratio, top-k per packed segment with
+ * dense segments always attended, per-query-head selection read once per KV
+ * group, rotated dense storage, partial tail blocks, the serving layout with
+ * one packed segment after the sink, totalOrder on signed zeros, block keys
+ * of decode-time appends, and the input generator.
+ *
  * All floating point is IEEE binary64; built with -ffp-contract=off.
  */
 #include <math.h>

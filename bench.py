@@ -177,7 +177,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct layer caches visited round-robin (keeps every call cache-cold)")
     ap.add_argument("--copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
+                    help="also run a streaming scale kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)."
@@ -297,12 +297,14 @@ def main():
         cpu.pop("seconds")
 
     if args.copy_mib > 0:
+        # a plain streaming kernel of known traffic: reads n bytes, writes n bytes
         n = args.copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
         torch.cuda.synchronize()
-        log("plain copy of %d bytes done (counter calibration)" % n)
+        torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        log("calibration kernel: read %d bytes, wrote %d bytes" % (n, n))
 
     seg_desc = "; ".join("%s[%d,%d)%s" % ("D" if s["kind"] == 0 else "P", s["t_begin"], s["t_begin"] + s["t_cap"],
                                           "" if s["kind"] == 0 else " r=%d keep=%s" % (

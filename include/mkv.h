@@ -44,6 +44,7 @@ extern "C" {
 #define MKV_MAX_GROUP 4            /* query heads per KV head */
 #define MKV_MAX_SEGMENTS 8         /* segments per request */
 #define MKV_MAX_PACKED_BLOCKS 65536 /* blocks of one packed segment (1,048,576 tokens) */
+#define MKV_PACKED_TAIL_BYTES 256   /* bytes after the last record of a packed data buffer */
 
 typedef enum {
     MKV_OK = 0,
@@ -85,6 +86,9 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1 } mkv_seg_kind;
  *                K values [16][r] | V values [16][r] | K indices [16][r] u8 |
  *                V indices [16][r] u8; each vector's kept channels in ascending
  *                channel order. Slots of a block past its last token are zero.
+ *                MKV_PACKED_TAIL_BYTES follow the last record: decode reads
+ *                whole dwords around each record's fields and may touch them
+ *                (their contents are never used, nothing writes them).
  *   packed meta: [n_kv_heads][ceil(nb / 64)][2 d s / 16][64][16 bytes]: for the
  *                block l, lane l % 64 of tile l / 64 holds, per 16-byte group,
  *                the (min, max) pairs of 16 / (2 s) consecutive channels

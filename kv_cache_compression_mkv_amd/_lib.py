@@ -22,6 +22,7 @@ MKV_HEAD_DIM = 128
 MKV_MAX_GROUP = 4
 MKV_MAX_SEGMENTS = 8
 MKV_MAX_PACKED_BLOCKS = 65536
+MKV_PACKED_TAIL_BYTES = 256
 MKV_N_STAGES = 8
 
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",

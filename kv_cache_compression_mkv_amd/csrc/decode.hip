@@ -452,14 +452,6 @@ struct Vals8<F32> {
     }
 };
 
-__device__ __forceinline__ void idx8(uint2 w, int ix[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ix[i] = (int)((w.x >> (8 * i)) & (D - 1));
-        ix[4 + i] = (int)((w.y >> (8 * i)) & (D - 1));
-    }
-}
-
 // split s of N equal parts of [0, n)
 __device__ __forceinline__ void split_range(int64_t n, int s, int S, int64_t &i0, int64_t &i1) {
     i0 = n * s / S;
@@ -617,25 +609,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 // packed items. Item (rank, head) of a packed segment is the rank-th block
 // that head selected; an item whose block a lower head of the group also
 // selected is dropped, so every union block is read once and serves each head
-// that chose it. Items are resolved 64 at a time into a compact list, and the
-// records of the list stream through a two-deep register pipeline (the next
-// record's K and V loads are in flight while the current one is computed).
+// that chose it. Items are resolved 64 at a time into a compact list whose
+// records stream through a three-deep register pipeline (two records' loads
+// stay in flight while one is computed).
 //
-// Per record: lane c (of 2r chunks of 8 elements) gathers q'[h][idx] from LDS
-// for the 8 K elements and adds into the token logits (at most two tokens per
-// chunk when r >= 8); after the softmax the 8 V elements scatter p * v into
-// the wave's accumulator acc[h][channel] with LDS float atomics.
+// Lane (t, p) = (lane / 4, lane % 4) owns part p of token t: elements
+// [p Q, min((p + 1) Q, r)) of the token's r, Q = ceil(r / 4), QM >= Q being the
+// compile-time bound. It loads dword-aligned windows of the four regions of
+// the record that cover its elements, so no lane's work crosses a token:
+//   K       z_h(t) = sum of q'_h[idx] * val over the token's four parts (q' is
+//           gathered from LDS; the parts add with DPP quad permutes);
+//   softmax per head, running max over the wave that only moves when a block
+//           exceeds it by 2^8 (so rescales are rare), p = exp2(z - m),
+//           lane-private running sums;
+//   V       the stored values scatter into the wave's dense tile [16][128]
+//           (a token's kept channels are distinct, so no two lanes of one
+//           token collide; window bytes past a lane's part go to the lane's
+//           slot of a dummy row); lane l then accumulates channels 2l, 2l + 1
+//           over the 16 rows
+//           and clears the tile.
 // ----------------------------------------------------------------------------
-template <typename ST, int NR>
-struct RecBuf {
-    Vals8<ST> kv[NR], vv[NR];
-    uint2 ki[NR], vi[NR];
-};
-
-// global loads one record puts in flight (per lane)
-template <typename ST, int NR>
-constexpr int rec_loads() { return NR * (2 * (ST::bytes == 2 ? 1 : 2) + 2); }
-
 // wait until at most N vector-memory loads of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -644,215 +637,251 @@ __device__ __forceinline__ void vm_wait() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <typename ST, int NR>
-__device__ __forceinline__ void load_rec(const char *base, int r, int lane, RecBuf<ST, NR> &B) {
-    constexpr uint32_t sb = ST::bytes;
-    const uint32_t nch = 2 * r;
-    const uint32_t voff = (uint32_t)BT * r * sb;
-    const uint32_t kioff = 2u * BT * r * sb;
-    const uint32_t vioff = kioff + (uint32_t)BT * r;
-    // every lane loads (lanes past the last chunk re-read it), so the loads
-    // need no predication and stay in flight behind the current record
+struct alignas(4) W4 { uint32_t x, y, z, w; };
+struct alignas(4) W3 { uint32_t x, y, z; };
+struct alignas(4) W2 { uint32_t x, y; };
+
+// N consecutive dwords from a 4-byte aligned address, in 16-byte pieces
+template <int N>
+__device__ __forceinline__ void load_words(const char *p, uint32_t (&w)[N]) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
 #pragma unroll
-    for (int rd = 0; rd < NR; ++rd) {
-        const uint32_t c = min((uint32_t)(lane + 64 * rd), nch - 1);
-        B.kv[rd].load(base + c * 8 * sb);
-        B.vv[rd].load(base + voff + c * 8 * sb);
-        B.ki[rd] = *reinterpret_cast<const uint2 *>(base + kioff + c * 8);
-        B.vi[rd] = *reinterpret_cast<const uint2 *>(base + vioff + c * 8);
+    for (int i = 0; i < N / 4; ++i) {
+        const W4 v = *reinterpret_cast<const W4 *>(q + 4 * i);
+        w[4 * i] = v.x;
+        w[4 * i + 1] = v.y;
+        w[4 * i + 2] = v.z;
+        w[4 * i + 3] = v.w;
+    }
+    constexpr int b = N - N % 4;
+    if constexpr (N % 4 == 3) {
+        const W3 v = *reinterpret_cast<const W3 *>(q + b);
+        w[b] = v.x;
+        w[b + 1] = v.y;
+        w[b + 2] = v.z;
+    } else if constexpr (N % 4 == 2) {
+        const W2 v = *reinterpret_cast<const W2 *>(q + b);
+        w[b] = v.x;
+        w[b + 1] = v.y;
+    } else if constexpr (N % 4 == 1) {
+        w[b] = q[b];
     }
 }
+template <int N>
+constexpr int load_instrs() { return N / 4 + (N % 4 ? 1 : 0); }
 
-// Per-wave LDS scratch of the packed path.
-template <typename ST, int G, int NR>
-struct PackedLds {
-    float zb[16 * G];                 // probabilities p[t][h] at t * G + h
-    float zp[G][64 * NR][2];          // per chunk: partial logits of its first and second token
-    typename ST::bits_t vt[BT][64][2]; // one record's stored V vectors, dense (channel c at [c % 64][c / 64]);
-                                       // zero between records
+// One record's windows for one lane.
+template <typename ST, int QM>
+struct PkWin {
+    // values: a bf16 window may start 2 bytes before the lane's first element
+    static constexpr int NV = ST::bytes == 2 ? (2 * QM + 5) / 4 : QM;
+    // indices: the window may start up to 3 bytes early
+    static constexpr int NI = (QM + 6) / 4;
+    static constexpr int LOADS = 2 * load_instrs<NV>() + 2 * load_instrs<NI>();
+    uint32_t kv[NV], vv[NV], ki[NI], vi[NI];
 };
 
-// acc[h][*] += sum_t p[t][h] * v[t][lane, lane + 64] from the dense tile, for
-// head I only (I >= 0) or for every head (I = -1).
-template <typename ST, int G, int NR, int I>
-__device__ __forceinline__ void accum_v(const PackedLds<ST, G, NR> &L, float (&acc)[G][2], int lane) {
+// Per-lane constants of one packed segment.
+template <typename ST, int QM>
+struct PkGeom {
+    uint32_t o_kv, o_vv, o_ki, o_vi;  // window offsets in the record
+    uint32_t sv, si;                  // byte shifts of the value / index windows
+    int cnt;                          // elements of this lane's part
+    int row;                          // t * 128: this token's tile row
+    __device__ __forceinline__ void init(int r) {
+        const int lane = lane_id();
+        const int t = lane >> 2, p = lane & 3;
+        const int Q = (r + 3) >> 2;
+        const uint32_t e0 = (uint32_t)(t * r + p * Q);
+        cnt = max(0, min(Q, r - p * Q));
+        const uint32_t reg = (uint32_t)BT * r * ST::bytes;  // one value region
+        const uint32_t vb = e0 * ST::bytes;
+        sv = vb & 3u;
+        si = e0 & 3u;
+        o_kv = vb & ~3u;
+        o_vv = reg + o_kv;
+        o_ki = 2 * reg + (e0 & ~3u);
+        o_vi = o_ki + (uint32_t)BT * r;
+        row = t * D;
+    }
+};
+
+template <typename ST, int QM>
+__device__ __forceinline__ void load_win(const char *rec, const PkGeom<ST, QM> &gm, PkWin<ST, QM> &W) {
+    load_words(rec + gm.o_kv, W.kv);
+    load_words(rec + gm.o_vv, W.vv);
+    load_words(rec + gm.o_ki, W.ki);
+    load_words(rec + gm.o_vi, W.vi);
+}
+
+// Per-wave LDS of the packed path: the dense V tile; row 16 absorbs masked writes.
+template <typename ST, int G>
+struct PkLds {
+    typename ST::bits_t vt[BT + 1][D];
+};
+
+template <int G>
+struct PkState {
+    float acc[G][2];  // channels 2 lane, 2 lane + 1
+    float l[G];       // lane-private sums of p (each token counted by its 4 lanes)
+    float m[G];       // running max per head (wave-uniform)
+};
+
+#define MKV_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false))
+__device__ __forceinline__ float quad_sum(float v) {
+    v += MKV_DPP(v, 0xB1);  // quad_perm [1, 0, 3, 2]
+    v += MKV_DPP(v, 0x4E);  // quad_perm [2, 3, 0, 1]
+    return v;
+}
+// max over the wave of a value replicated within each quad
+__device__ __forceinline__ float wave_max_quads(float v) {
+    v = fmaxf(v, MKV_DPP(v, 0x124));  // row_ror 4
+    v = fmaxf(v, MKV_DPP(v, 0x128));  // row_ror 8
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+#undef MKV_DPP
+__device__ __forceinline__ float wave_sum_all(float v) {
+    v = row_sum16(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// acc[I][*] += sum_t p_t * tile[t][2 lane, 2 lane + 1]; p_t sits in lane 4 t
+// of p and is read into a scalar register
+template <typename ST, int G, int I>
+__device__ __forceinline__ void pk_accum(const PkLds<ST, G> &L, PkState<G> &S, float p, int lane) {
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
         float a, b;
         if constexpr (ST::bytes == 2) {
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(&L.vt[t][lane][0]);
+            const uint32_t w = reinterpret_cast<const uint32_t *>(&L.vt[t][0])[lane];
             a = bf16_lo(w);
             b = bf16_hi(w);
         } else {
-            const uint2 w = *reinterpret_cast<const uint2 *>(&L.vt[t][lane][0]);
+            const uint2 w = reinterpret_cast<const uint2 *>(&L.vt[t][0])[lane];
             a = __uint_as_float(w.x);
             b = __uint_as_float(w.y);
         }
-        if constexpr (I >= 0) {
-            const float p = L.zb[t * G + I];
-            acc[I][0] = fmaf(p, a, acc[I][0]);
-            acc[I][1] = fmaf(p, b, acc[I][1]);
-        } else {
-            float p[G];
-            if constexpr (G == 4) {
-                const float4 p4 = *reinterpret_cast<const float4 *>(&L.zb[t * 4]);
-                p[0] = p4.x; p[1] = p4.y; p[2] = p4.z; p[3] = p4.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < G; ++i) p[i] = L.zb[t * G + i];
-            }
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                acc[i][0] = fmaf(p[i], a, acc[i][0]);
-                acc[i][1] = fmaf(p[i], b, acc[i][1]);
-            }
-        }
+        const float pt = lane_value(p, 4 * t);
+        S.acc[I][0] = fmaf(pt, a, S.acc[I][0]);
+        S.acc[I][1] = fmaf(pt, b, S.acc[I][1]);
     }
 }
 
-template <typename ST, int G, int NR, bool NEXT_IN_FLIGHT>
-__device__ __forceinline__ void proc_rec(const RecBuf<ST, NR> &B, int r, uint32_t mr, int hm, int nv,
-                                         const float (*qsh)[D], PackedLds<ST, G, NR> &L, float (&acc)[G][2],
-                                         WaveState<G> &st) {
-    const int lane = lane_id();
-    const int nch = 2 * r;
-    // this record's loads are complete once only the next record's remain
-    vm_wait<NEXT_IN_FLIGHT ? rec_loads<ST, NR>() : 0>();
+// the I-th value of a lane's window (masked to 0 past its part for K)
+template <typename ST, int NV>
+__device__ __forceinline__ uint32_t win_word(const uint32_t (&w)[NV], int k, uint32_t sv) {
+    if constexpr (ST::bytes == 2) return __builtin_amdgcn_alignbyte(w[k + 1], w[k], sv);
+    else return w[k];
+}
 
-    // ---- K: q'[h][idx] * value summed per chunk (8 elements, at most two tokens when r >= 8;
-    //      for r < 8 one partial per element)
+template <typename ST, int G, int QM, int WAITN>
+__device__ __forceinline__ void pk_proc(const PkWin<ST, QM> &W, const PkGeom<ST, QM> &gm, int hm, int nv,
+                                        const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S) {
+    const int lane = lane_id();
+    vm_wait<WAITN>();
+    // indices: element j = byte j of the aligned index words
+    constexpr int NIW = (QM + 3) / 4;
+    uint32_t ki[NIW], vi[NIW];
 #pragma unroll
-    for (int rd = 0; rd < NR; ++rd) {
-        const int c = lane + 64 * rd;
-        float kv[8];
-        int ix[8];
-        B.kv[rd].get(kv);
-        idx8(B.ki[rd], ix);
-        const int e0 = c * 8;
-        const int t0 = (int)(((uint32_t)e0 * mr) >> 20);
-        const int tb = (t0 + 1) * r;
-#pragma unroll 1
-        for (int i = 0; i < G; ++i) {
-            if (!((hm >> i) & 1)) continue;
-            if (r >= 8) {
-                float s0 = 0.f, s1 = 0.f;
+    for (int k = 0; k < NIW; ++k) {
+        ki[k] = __builtin_amdgcn_alignbyte(W.ki[k + 1], W.ki[k], gm.si);
+        vi[k] = __builtin_amdgcn_alignbyte(W.vi[k + 1], W.vi[k], gm.si);
+    }
+    // ---- V scatter first: its LDS writes drain while K is computed
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pr = qsh[i][ix[e]] * kv[e];
-                    if (e0 + e >= tb) s1 += pr;
-                    else s0 += pr;
-                }
-                if (c < nch) *reinterpret_cast<float2 *>(L.zp[i][c]) = make_float2(s0, s1);
-            } else if (c < nch) {
-                // r < 8: 16 r <= 112 products, stored one per element
-                float *pe = &L.zp[i][0][0];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pe[e0 + e] = qsh[i][ix[e]] * kv[e];
-            }
+    for (int j = 0; j < QM; ++j) {
+        // past the lane's part the index byte belongs to other data: such
+        // writes go to the lane's own slot of the dummy row
+        const int c = (int)((vi[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+        const int at = j < gm.cnt ? gm.row + c : BT * D + lane;
+        if constexpr (ST::bytes == 2) {
+            const uint32_t w = win_word<ST>(W.vv, j >> 1, gm.sv);
+            (&L.vt[0][0])[at] = (uint16_t)((j & 1) ? (w >> 16) : w);
+        } else {
+            (&L.vt[0][0])[at] = W.vv[j];
         }
     }
-    wave_lds_sync();
-    // ---- token logits: lane (h, t) = (lane / 16, lane % 16) sums the chunks (or elements) of token t
-    float alpha[G];
-    {
-        const int h = lane >> 4, t = lane & 15;
-        const bool valid = h < G && t < nv && ((hm >> h) & 1);
-        float z = 0.f;
-        if (valid) {
-            if (r >= 8) {
-                // token t spans chunks cf..cl: at most 4 * NR + 1 of them, since r <= 32 * NR
-                const int cf = (t * r) >> 3, cl = ((t + 1) * r - 1) >> 3;
+    // ---- K: this lane's partial logit per head
+    float kval[QM];
+    if constexpr (ST::bytes == 2) {
 #pragma unroll
-                for (int k = 0; k <= 4 * NR; ++k) {
-                    const int c = cf + k;
-                    if (c <= cl) {
-                        const int tc = (int)(((uint32_t)(c * 8) * mr) >> 20);
-                        z += L.zp[h][c][tc == t ? 0 : 1];
-                    }
-                }
-            } else {
-                const float *pe = &L.zp[h][0][0];
-                for (int e = t * r; e < (t + 1) * r; ++e) z += pe[e];
-            }
+        for (int k = 0; k < QM / 2; ++k) {
+            const uint32_t w = win_word<ST>(W.kv, k, gm.sv);
+            kval[2 * k] = 2 * k < gm.cnt ? bf16_lo(w) : 0.f;
+            kval[2 * k + 1] = 2 * k + 1 < gm.cnt ? bf16_hi(w) : 0.f;
         }
-        softmax16<G>(z, valid, L.zb, st, alpha);
-    }
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        acc[i][0] *= alpha[i];
-        acc[i][1] *= alpha[i];
-    }
-    // ---- V: scatter the record's values into the dense tile
-#pragma unroll
-    for (int rd = 0; rd < NR; ++rd) {
-        const int c = lane + 64 * rd;
-        if (c < nch) {
-            typename ST::bits_t vv[8];
-            int ix[8];
-            B.vv[rd].raw(vv);
-            idx8(B.vi[rd], ix);
-            const int e0 = c * 8;
-            int tt = (int)(((uint32_t)e0 * mr) >> 20), tb = (tt + 1) * r;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (e0 + e >= tb) {  // at most one token boundary per element step
-                    ++tt;
-                    tb += r;
-                }
-                L.vt[tt][ix[e] & 63][ix[e] >> 6] = vv[e];
-            }
-        }
-    }
-    wave_lds_sync();
-    // ---- lane l accumulates channels l and l + 64 over the 16 slots (rows of
-    //      missing tokens are zero and their p is 0); most union blocks serve
-    //      a single head, which gets its own path
-    if (__popc(hm) == 1) {
-        const int i = __ffs(hm) - 1;
-        if (i == 0) accum_v<ST, G, NR, 0>(L, acc, lane);
-        if constexpr (G > 1) if (i == 1) accum_v<ST, G, NR, 1>(L, acc, lane);
-        if constexpr (G > 2) if (i == 2) accum_v<ST, G, NR, 2>(L, acc, lane);
-        if constexpr (G > 3) if (i == 3) accum_v<ST, G, NR, 3>(L, acc, lane);
     } else {
-        accum_v<ST, G, NR, -1>(L, acc, lane);
+#pragma unroll
+        for (int j = 0; j < QM; ++j) kval[j] = j < gm.cnt ? __uint_as_float(W.kv[j]) : 0.f;
     }
-    // ---- clear the tile with full-width stores (LDS operations of a wave run in order)
+    const bool valid = (lane >> 2) < nv;
+    float pv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        pv[h] = 0.f;
+        if (!((hm >> h) & 1)) continue;
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < QM; ++j) {
+            const int c = (int)((ki[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+            z = fmaf(qsh[h][c], kval[j], z);
+        }
+        z = valid ? quad_sum(z) : -INFINITY;
+        const float bm = wave_max_quads(z);
+        const float mh = S.m[h];
+        if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
+            const float a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
+            S.m[h] = bm;
+            S.acc[h][0] *= a;
+            S.acc[h][1] *= a;
+            S.l[h] *= a;
+        }
+        const float p = valid ? exp2f(z - S.m[h]) : 0.f;
+        S.l[h] += p;
+        pv[h] = p;
+    }
+    wave_lds_sync();
+    // ---- V accumulate over the 16 rows, then clear them
+    if (hm & 1) pk_accum<ST, G, 0>(L, S, pv[0], lane);
+    if constexpr (G > 1) if (hm & 2) pk_accum<ST, G, 1>(L, S, pv[1], lane);
+    if constexpr (G > 2) if (hm & 4) pk_accum<ST, G, 2>(L, S, pv[2], lane);
+    if constexpr (G > 3) if (hm & 8) pk_accum<ST, G, 3>(L, S, pv[3], lane);
     {
-        constexpr int n16 = (int)sizeof(L.vt) / 16;  // 16-byte pieces: 256 (bf16) or 512 (f32)
-        uint4 *v4 = reinterpret_cast<uint4 *>(&L.vt[0][0][0]);
+        constexpr int n16 = BT * D * ST::bytes / 16;  // 16-byte pieces of rows 0..15
+        uint4 *v4 = reinterpret_cast<uint4 *>(&L.vt[0][0]);
 #pragma unroll
         for (int i = 0; i < n16 / 64; ++i) v4[lane + 64 * i] = make_uint4(0, 0, 0, 0);
     }
 }
 
 // list entries are wave-uniform: read them into scalar registers, so each
-// record load is a scalar base plus a loop-invariant per-lane offset
+// record load is a scalar base plus loop-invariant per-lane offsets
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <typename ST, int G, int NR>
-__device__ __forceinline__ void run_list(const int2 *list, int n, const char *seg_base, size_t rec, int r,
-                                         int filled, const float (*qsh)[D], PackedLds<ST, G, NR> &L,
-                                         float (&acc)[G][2], WaveState<G> &st) {
-    const int lane = lane_id();
-    const uint32_t mr = ((1u << 20) + (uint32_t)r - 1) / (uint32_t)r;  // e / r = (e * mr) >> 20 for e < 16r
-    RecBuf<ST, NR> B0, B1;
-    if (n > 0) load_rec<ST, NR>(seg_base + (size_t)uniform_int(list[0].x) * rec, r, lane, B0);
-    for (int i = 0; i < n; i += 2) {
-        const int b0 = uniform_int(list[i].x), h0 = uniform_int(list[i].y);
-        if (i + 1 < n) {
-            load_rec<ST, NR>(seg_base + (size_t)uniform_int(list[i + 1].x) * rec, r, lane, B1);
-            proc_rec<ST, G, NR, true>(B0, r, mr, h0, min(BT, filled - b0 * BT), qsh, L, acc, st);
-        } else {
-            proc_rec<ST, G, NR, false>(B0, r, mr, h0, min(BT, filled - b0 * BT), qsh, L, acc, st);
-            break;
-        }
-        const int b1 = uniform_int(list[i + 1].x), h1 = uniform_int(list[i + 1].y);
-        if (i + 2 < n) {
-            load_rec<ST, NR>(seg_base + (size_t)uniform_int(list[i + 2].x) * rec, r, lane, B0);
-            proc_rec<ST, G, NR, true>(B1, r, mr, h1, min(BT, filled - b1 * BT), qsh, L, acc, st);
-        } else {
-            proc_rec<ST, G, NR, false>(B1, r, mr, h1, min(BT, filled - b1 * BT), qsh, L, acc, st);
-        }
+template <typename ST, int G, int QM>
+__device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_base, size_t rec, int r,
+                                       int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S) {
+    PkGeom<ST, QM> gm;
+    gm.init(r);
+    constexpr int WN = 2 * PkWin<ST, QM>::LOADS;
+    PkWin<ST, QM> B0, B1, B2;
+    // loads past the end of the list repeat its last record, so every step
+    // has exactly two records in flight behind the one it computes
+    auto at = [&](int i) {
+        return seg_base + (size_t)uniform_int(list[min(i, n - 1)].x) * rec;
+    };
+    auto nv_of = [&](int i) { return min(BT, filled - uniform_int(list[i].x) * BT); };
+    load_win(at(0), gm, B0);
+    load_win(at(1), gm, B1);
+    for (int i = 0; i < n; i += 3) {
+        load_win(at(i + 2), gm, B2);
+        pk_proc<ST, G, QM, WN>(B0, gm, uniform_int(list[i].y), nv_of(i), qsh, L, S);
+        if (i + 1 >= n) break;
+        load_win(at(i + 3), gm, B0);
+        pk_proc<ST, G, QM, WN>(B1, gm, uniform_int(list[i + 1].y), nv_of(i + 1), qsh, L, S);
+        if (i + 2 >= n) break;
+        load_win(at(i + 4), gm, B1);
+        pk_proc<ST, G, QM, WN>(B2, gm, uniform_int(list[i + 2].y), nv_of(i + 2), qsh, L, S);
     }
 }
 
@@ -861,7 +890,8 @@ __device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
 }
 
-template <typename ST, int G, int NR>
+// QA < QB: segments with ceil(r / 4) <= QA run the QA code, the others QB
+template <typename ST, int G, int QA, int QB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_attend_packed(const DecodeArgs A) {
     const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
     const int b = A.b0 + bl;
@@ -869,88 +899,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const int s = (int)blockIdx.x * 4 + wave;
     constexpr int sb = ST::bytes;
 
-    __shared__ __align__(16) float qsh[G][D];
-    __shared__ __align__(16) PackedLds<ST, G, NR> lds[4];
+    // q' * log2(e) / sqrt(d) per head; channels 128..255 are zero so that any
+    // index byte of a window gathers a finite value
+    __shared__ __align__(16) float qsh[G][2 * D];
+    __shared__ __align__(16) PkLds<ST, G> lds[4];
     __shared__ int2 lists[4][64];
-    for (int i = (int)threadIdx.x; i < G * D; i += 256)
-        qsh[i / D][i % D] = A.qa[((size_t)b * A.hq + g * G) * D + i];
+    for (int i = (int)threadIdx.x; i < G * 2 * D; i += 256) {
+        const int h = i / (2 * D), c = i % (2 * D);
+        qsh[h][c] = c < D ? A.qa[((size_t)b * A.hq + g * G + h) * D + c] : 0.f;
+    }
     __syncthreads();
     if (s >= A.S_p) return;
-    {
-        PackedLds<ST, G, NR> &L = lds[wave];
-        int2 *list = lists[wave];
-        for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0][0])[i] = 0;
-        float acc[G][2];
+    PkLds<ST, G> &L = lds[wave];
+    int2 *list = lists[wave];
+    for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
+    PkState<G> S;
 #pragma unroll
-        for (int i = 0; i < G; ++i) acc[i][0] = acc[i][1] = 0.f;
-        WaveState<G> st;
-        st.init();
-
-        int64_t W = 0;
-        for (int si = 0; si < A.nseg; ++si) {
-            const DSeg &S = seg_of(A, bl, si);
-            if (S.kind == MKV_SEG_PACKED) W += (int64_t)G * S.k * packed_weight(S.r, sb, G);
-        }
-        const int64_t lo = W * s / A.S_p, hi = W * (s + 1) / A.S_p;
-        int64_t Wb = 0;
-        int pj = 0;
-        for (int si = 0; si < A.nseg; ++si) {
-            const DSeg &S = seg_of(A, bl, si);
-            if (S.kind != MKV_SEG_PACKED) continue;
-            const int myj = pj++;
-            const int64_t w = packed_weight(S.r, sb, G);
-            const int64_t items = (int64_t)G * S.k;
-            int64_t i0 = lo - Wb, i1 = hi - Wb;
-            i0 = i0 <= 0 ? 0 : (i0 + w - 1) / w;
-            i1 = i1 <= 0 ? 0 : (i1 + w - 1) / w;
-            i0 = min(i0, items);
-            i1 = min(i1, items);
-            Wb += items * w;
-            if (i0 >= i1) continue;
-            const int r = S.r;
-            const size_t rec = (size_t)BT * r * 2 * (sb + 1);
-            const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * rec;
-            const int kc = A.kcap[myj];
-            const int32_t *sel = A.sel + A.sl_off[myj] + ((size_t)b * A.hq + g * G) * kc;
-            const uint32_t *mk = A.mask + A.mk_off[myj] + ((size_t)b * A.hkv + g) * A.nbcap[myj];
-            for (int64_t base = i0; base < i1; base += 64) {
-                // resolve up to 64 items into (block, head mask) pairs
-                const int64_t it = base + lane;
-                bool keep = false;
-                int blk = 0, hm = 0;
-                if (it < i1) {
-                    const int rank = (int)(it / G), hl = (int)(it % G);
-                    blk = sel[(size_t)hl * kc + rank];
-                    if ((unsigned)blk < (unsigned)S.nb) {
-                        hm = (int)mk[blk];
-                        keep = !(hm & ((1 << hl) - 1));
-                    }
-                }
-                const uint64_t km = ballot(keep);
-                if (keep) list[popc64(km & lanes_below(lane))] = make_int2(blk, hm);
-                const int n = popc64(km);
-                wave_lds_sync();
-                run_list<ST, G, NR>(list, n, seg_base, rec, r, S.filled, qsh, L, acc, st);
-                wave_lds_sync();
-            }
-        }
-        // write this split's partials (after the dense splits)
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const float li = st.head_sum(i);
-            const float mi = st.head_max(i);
-            float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + A.S_d + s) * PART;
-            if (lane == 0) {
-                pp[0] = mi;
-                pp[1] = li;
-            }
-            pp[2 + lane] = acc[i][0];
-            pp[2 + 64 + lane] = acc[i][1];
-        }
+    for (int i = 0; i < G; ++i) {
+        S.acc[i][0] = S.acc[i][1] = 0.f;
+        S.l[i] = 0.f;
+        S.m[i] = -INFINITY;
     }
 
+    int64_t W = 0;
+    for (int si = 0; si < A.nseg; ++si) {
+        const DSeg &Sg = seg_of(A, bl, si);
+        if (Sg.kind == MKV_SEG_PACKED) W += (int64_t)G * Sg.k * packed_weight(Sg.r, sb, G);
+    }
+    const int64_t lo = W * s / A.S_p, hi = W * (s + 1) / A.S_p;
+    int64_t Wb = 0;
+    int pj = 0;
+    for (int si = 0; si < A.nseg; ++si) {
+        const DSeg &Sg = seg_of(A, bl, si);
+        if (Sg.kind != MKV_SEG_PACKED) continue;
+        const int myj = pj++;
+        const int64_t w = packed_weight(Sg.r, sb, G);
+        const int64_t items = (int64_t)G * Sg.k;
+        int64_t i0 = lo - Wb, i1 = hi - Wb;
+        i0 = i0 <= 0 ? 0 : (i0 + w - 1) / w;
+        i1 = i1 <= 0 ? 0 : (i1 + w - 1) / w;
+        i0 = min(i0, items);
+        i1 = min(i1, items);
+        Wb += items * w;
+        if (i0 >= i1) continue;
+        const int r = Sg.r;
+        const size_t rec = (size_t)BT * r * 2 * (sb + 1);
+        const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
+        const int kc = A.kcap[myj];
+        const int32_t *sel = A.sel + A.sl_off[myj] + ((size_t)b * A.hq + g * G) * kc;
+        const uint32_t *mk = A.mask + A.mk_off[myj] + ((size_t)b * A.hkv + g) * A.nbcap[myj];
+        for (int64_t base = i0; base < i1; base += 64) {
+            // resolve up to 64 items into (block, head mask) pairs
+            const int64_t it = base + lane;
+            bool keep = false;
+            int blk = 0, hm = 0;
+            if (it < i1) {
+                const int rank = (int)(it / G), hl = (int)(it % G);
+                blk = sel[(size_t)hl * kc + rank];
+                if ((unsigned)blk < (unsigned)Sg.nb) {
+                    hm = (int)mk[blk];
+                    keep = !(hm & ((1 << hl) - 1));
+                }
+            }
+            const uint64_t km = ballot(keep);
+            if (keep) list[popc64(km & lanes_below(lane))] = make_int2(blk, hm);
+            const int n = popc64(km);
+            wave_lds_sync();
+            if (n > 0) {
+                if (((r + 3) >> 2) <= QA)
+                    pk_run<ST, G, QA>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+                else
+                    pk_run<ST, G, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+            }
+            wave_lds_sync();
+        }
+    }
+    // write this split's partials (after the dense splits)
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const float li = wave_sum_all(S.l[i]) * 0.25f;
+        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + A.S_d + s) * PART;
+        if (lane == 0) {
+            pp[0] = S.m[i];
+            pp[1] = li;
+        }
+        reinterpret_cast<float2 *>(pp + 2)[lane] = make_float2(S.acc[i][0], S.acc[i][1]);
+    }
 }
-
 // ----------------------------------------------------------------------------
 // merge: one workgroup per (request, query head): log-sum-exp merge of the
 // head's dense and packed splits in split order, then out_j = sum_c R_v[c][j] o_c.
@@ -1094,23 +1129,27 @@ hipError_t launch_attend_dense(const DecodeArgs &a, int dtype, int G, hipStream_
 }
 
 template <typename ST, int G>
-void packed_launch(const DecodeArgs &a, int nr, dim3 grid, hipStream_t s) {
-    if (nr <= 1) hipLaunchKernelGGL((k_attend_packed<ST, G, 1>), grid, dim3(256), 0, s, a);
-    else if (nr == 2) hipLaunchKernelGGL((k_attend_packed<ST, G, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attend_packed<ST, G, 4>), grid, dim3(256), 0, s, a);
+void packed_launch(const DecodeArgs &a, int qmax, dim3 grid, hipStream_t s) {
+#define MKV_PK(QA, QB) hipLaunchKernelGGL((k_attend_packed<ST, G, QA, QB>), grid, dim3(256), 0, s, a)
+    if (qmax <= 4) MKV_PK(4, 4);
+    else if (qmax <= 8) MKV_PK(4, 8);
+    else if (qmax <= 10) MKV_PK(8, 10);
+    else if (qmax <= 16) MKV_PK(10, 16);
+    else MKV_PK(16, 32);
+#undef MKV_PK
 }
 
-// nr: 64-lane rounds of 8-element chunks of the widest packed record, ceil(2 r_max / 64)
-hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int nr, hipStream_t s) {
+// qmax = ceil(r_max / 4): elements per lane of the widest packed segment
+hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s) {
     const dim3 grid((unsigned)((a.S_p + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
     if (dtype == MKV_BF16) {
-        if (G == 1) packed_launch<Bf16, 1>(a, nr, grid, s);
-        else if (G == 2) packed_launch<Bf16, 2>(a, nr, grid, s);
-        else packed_launch<Bf16, 4>(a, nr, grid, s);
+        if (G == 1) packed_launch<Bf16, 1>(a, qmax, grid, s);
+        else if (G == 2) packed_launch<Bf16, 2>(a, qmax, grid, s);
+        else packed_launch<Bf16, 4>(a, qmax, grid, s);
     } else {
-        if (G == 1) packed_launch<F32, 1>(a, nr, grid, s);
-        else if (G == 2) packed_launch<F32, 2>(a, nr, grid, s);
-        else packed_launch<F32, 4>(a, nr, grid, s);
+        if (G == 1) packed_launch<F32, 1>(a, qmax, grid, s);
+        else if (G == 2) packed_launch<F32, 2>(a, qmax, grid, s);
+        else packed_launch<F32, 4>(a, qmax, grid, s);
     }
     return hipGetLastError();
 }

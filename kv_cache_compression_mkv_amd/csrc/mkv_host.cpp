@@ -203,7 +203,7 @@ size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int3
         const size_t ntile = ceil_div((int64_t)nb, META_TILE);
         *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * d * s;
     }
-    return (size_t)n_kv_heads * nb * BT * r * 2 * (s + 1);
+    return (size_t)n_kv_heads * nb * BT * r * 2 * (s + 1) + MKV_PACKED_TAIL_BYTES;
 }
 
 mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
@@ -398,8 +398,8 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
         }
         st = timed(5, s, [&] { return launch_attend_dense(A, c->dtype, G, s); });
         if (st != MKV_OK) return st;
-        const int nr = 2 * max_r <= 64 ? 1 : 2 * max_r <= 128 ? 2 : 4;
-        st = timed(6, s, [&] { return launch_attend_packed(A, c->dtype, G, nr, s); });
+        const int qmax = (max_r + 3) / 4;
+        st = timed(6, s, [&] { return launch_attend_packed(A, c->dtype, G, qmax, s); });
         if (st != MKV_OK) return st;
         st = timed(7, s, [&] { return launch_merge(A, G, s); });
         if (st != MKV_OK) return st;

@@ -97,7 +97,7 @@ hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s);
 hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hipStream_t s);
 hipError_t launch_select(const DecodeArgs &a, int G, hipStream_t s);
 hipError_t launch_attend_dense(const DecodeArgs &a, int dtype, int G, hipStream_t s);
-hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int nr, hipStream_t s);
+hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s);
 
 }  // namespace mkv

@@ -22,7 +22,7 @@ def unpack_packed(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str):
     """-> dict of K/V values (float64), value bits and indices, each [hkv][nbcap][16][r]."""
     s = 2 if dtype == "bf16" else 4
     rec = BT * r * 2 * (s + 1)
-    a = np.ascontiguousarray(data, np.uint8).reshape(hkv, nbcap, rec)
+    a = np.ascontiguousarray(data, np.uint8)[:hkv * nbcap * rec].reshape(hkv, nbcap, rec)
     kb, kv = _vals(np.ascontiguousarray(a[:, :, :BT * r * s]).reshape(-1), dtype)
     vb, vv = _vals(np.ascontiguousarray(a[:, :, BT * r * s:2 * BT * r * s]).reshape(-1), dtype)
     ki = a[:, :, 2 * BT * r * s:2 * BT * r * s + BT * r].reshape(hkv, nbcap, BT, r)

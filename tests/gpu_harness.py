@@ -102,50 +102,68 @@ def bits_of(values_f64, dtype):
     return f.view(np.uint32)
 
 
+def _head_bytes(t, g, per_head):
+    return t[g * per_head:(g + 1) * per_head].cpu().numpy()
+
+
+def _first_bad(ok_rows, t0):
+    bad = np.nonzero(~ok_rows)[0]
+    return int(bad[0]) + t0 if bad.size else None
+
+
 def compare_compress(cache, w, comp, b, g, length):
-    """Bit-exact comparison of one unit's stored cache with the oracle's."""
+    """Bit-exact comparison of one unit's stored cache with the oracle's: dense
+    rows, packed indices and values, zero padding of the tail block, block keys."""
     from kv_cache_compression_mkv_amd import layout
-    dt, hkv = w["dtype"], w["n_kv_heads"]
+    dt = w["dtype"]
+    sb = 2 if dt == "bf16" else 4
+    d = w.get("d", 128)
     pj = 0
     for j, s in enumerate(w["segs"][b]):
         nbcap = -(-s["t_cap"] // 16)
         filled = min(max(length - s["t_begin"], 0), s["t_cap"])
-        data = cache.data[b][j].cpu().numpy()
+        nb = -(-filled // 16)
+        tb = s["t_begin"]
         if s["kind"] == synth.DENSE:
-            vals, bits = layout.unpack_dense(data, hkv, nbcap, dt)
-            for t in range(filled):
-                blk, slot = divmod(t, 16)
-                tt = s["t_begin"] + t
-                for kind, hat in ((0, comp["Khat"]), (1, comp["Vhat"])):
-                    exp = bits_of(hat[tt], dt)
-                    got = bits[g, blk, kind, slot]
-                    assert np.array_equal(got, exp), "dense b=%d g=%d seg=%d t=%d kind=%d" % (b, g, j, tt, kind)
-            nb = -(-filled // 16)
+            data = _head_bytes(cache.data[b][j], g, nbcap * 2 * 16 * d * sb)
+            _, bits = layout.unpack_dense(data, 1, nbcap, dt, d)
+            for kind, hat in ((0, comp["Khat"]), (1, comp["Vhat"])):
+                got = bits[0, :, kind].reshape(nbcap * 16, d)[:filled]
+                exp = bits_of(hat[tb:tb + filled], dt)
+                bad = _first_bad(np.all(got == exp, axis=1), tb)
+                assert bad is None, "dense b=%d g=%d seg=%d t=%d kind=%d" % (b, g, j, bad, kind)
             if filled % 16:
-                assert np.all(bits[g, nb - 1, :, filled % 16:] == 0)
+                assert np.all(bits[0, nb - 1, :, filled % 16:] == 0)
             continue
         r = s["r"]
-        P = layout.unpack_packed(data, hkv, nbcap, r, dt)
-        for t in range(filled):
-            blk, slot = divmod(t, 16)
-            tt = s["t_begin"] + t
-            for hat, idx, gbits, gidx, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
-                                                (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
-                ei = idx[tt][:r]
-                gi = gidx[g, blk, slot]
-                assert np.array_equal(gi.astype(np.int64), ei.astype(np.int64)), \
-                    "%s idx b=%d g=%d seg=%d t=%d: %s vs %s" % (name, b, g, j, tt, gi, ei)
-                assert np.array_equal(gbits[g, blk, slot], bits_of(hat[tt, ei], dt)), \
-                    "%s val b=%d g=%d seg=%d t=%d" % (name, b, g, j, tt)
-        nb = -(-filled // 16)
+        rec = 16 * r * 2 * (sb + 1)
+        P = layout.unpack_packed(_head_bytes(cache.data[b][j], g, nbcap * rec), 1, nbcap, r, dt)
+        for hat, idx, gbits, gidx, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
+                                            (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
+            ei = idx[tb:tb + filled, :r].astype(np.int64)
+            gi = gidx[0].reshape(nbcap * 16, r)[:filled].astype(np.int64)
+            bad = _first_bad(np.all(gi == ei, axis=1), tb)
+            assert bad is None, "%s idx b=%d g=%d seg=%d t=%d: %s vs %s" % (
+                name, b, g, j, bad, gi[bad - tb], ei[bad - tb])
+            ev = bits_of(np.take_along_axis(hat[tb:tb + filled], ei, axis=1), dt)
+            gv = gbits[0].reshape(nbcap * 16, r)[:filled]
+            bad = _first_bad(np.all(gv == ev, axis=1), tb)
+            assert bad is None, "%s val b=%d g=%d seg=%d t=%d" % (name, b, g, j, bad)
         if filled % 16:
-            assert np.all(P["kbits"][g, nb - 1, filled % 16:] == 0)
-            assert np.all(P["vidx"][g, nb - 1, filled % 16:] == 0)
-        mvals, mbits = layout.unpack_meta(cache.meta[b][j].cpu().numpy(), hkv, nbcap, dt)
+            assert np.all(P["kbits"][0, nb - 1, filled % 16:] == 0)
+            assert np.all(P["vbits"][0, nb - 1, filled % 16:] == 0)
+            assert np.all(P["kidx"][0, nb - 1, filled % 16:] == 0)
+            assert np.all(P["vidx"][0, nb - 1, filled % 16:] == 0)
+        ng = 2 * d * sb // 16
+        ntile = -(-nbcap // 64)
+        mraw = _head_bytes(cache.meta[b][j], g, ntile * ng * 64 * 16)
+        _, mbits = layout.unpack_meta(mraw, 1, nbcap, dt, d)
         om = comp["meta"][pj]
         assert om.shape[0] == nb
         if nb:
-            assert np.array_equal(mbits[g, :nb], bits_of(om, dt)), "meta b=%d g=%d seg=%d" % (b, g, j)
+            ok = np.all(mbits[0, :nb] == bits_of(om, dt), axis=(1, 2))
+            bad = _first_bad(ok, 0)
+            assert bad is None, "meta b=%d g=%d seg=%d block=%d" % (b, g, j, bad)
         pj += 1
 
 

@@ -39,12 +39,12 @@ def test_status_strings(L):
 def test_segment_bytes(L):
     # packed r=38 bf16: 3648-byte records; meta 512 B per block in 64-block tiles
     data, meta = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_PACKED, 38, 128, 8, 63456)
-    assert data == 8 * 3966 * 3648
+    assert data == 8 * 3966 * 3648 + L.MKV_PACKED_TAIL_BYTES
     assert meta == 8 * 62 * 64 * 512
     data, meta = L.mkv_segment_bytes(L.MKV_F32, L.MKV_SEG_PACKED, 32, 128, 1, 4016)
-    assert data == 251 * 5120 and meta == 4 * 64 * 1024
+    assert data == 251 * 5120 + L.MKV_PACKED_TAIL_BYTES and meta == 4 * 64 * 1024
     data, meta = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_PACKED, 26, 128, 1, 16)
-    assert data == 2496
+    assert data == 2496 + L.MKV_PACKED_TAIL_BYTES
     data, meta = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_DENSE, 0, 128, 8, 100)
     assert data == 8 * 7 * 2 * 16 * 128 * 2 and meta == 0
     assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_PACKED, 0, 128, 8, 100)[0] == 0

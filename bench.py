@@ -281,7 +281,8 @@ def main():
     call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
     append_bytes = B * hkv * 2 * (d * d * 4 + d * sb)
     step_bytes = call["total"] + append_bytes
-    cand = {"attend_packed": call["records"], "attend_dense": call["dense"], "score": call["meta"]}
+    cand = {"attend": call["records"] + call["dense"], "score": call["meta"], "select": 0,
+            "merge": 0, "q_rotate": 0}
     dom = max(cand, key=lambda k: stage_ms.get(k, 0.0))
     dom_ms = stage_ms[dom]
     achieved = cand[dom] / (dom_ms * 1e-3) / 1e9

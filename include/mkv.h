@@ -202,8 +202,9 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
  * mkv_timing_read synchronises those events and returns, per stage, the summed
  * milliseconds and the number of launches since the last read, then clears
  * them. Stages: 0 compress, 1 block_meta, 2 q_rotate, 3 score, 4 select,
- * 5 attend_dense, 6 attend_packed, 7 merge (split merge + inverse rotation). */
-#define MKV_N_STAGES 8
+ * 5 attend (dense blocks and selected packed blocks), 6 merge (split merge +
+ * inverse rotation). */
+#define MKV_N_STAGES 7
 mkv_status mkv_timing_enable(int32_t on);
 mkv_status mkv_timing_read(double *ms_out, int64_t *count_out, int32_t n_stages);
 const char *mkv_stage_name(int32_t stage);

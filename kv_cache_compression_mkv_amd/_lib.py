@@ -23,7 +23,7 @@ MKV_MAX_GROUP = 4
 MKV_MAX_SEGMENTS = 8
 MKV_MAX_PACKED_BLOCKS = 65536
 MKV_PACKED_TAIL_BYTES = 256
-MKV_N_STAGES = 8
+MKV_N_STAGES = 7
 
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
            "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",

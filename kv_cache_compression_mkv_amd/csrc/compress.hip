@@ -45,6 +45,22 @@ __device__ __forceinline__ void rotate_f64(const float *__restrict__ R, const fl
     acc1 = a1;
 }
 
+// The same product sum with R staged in LDS (rows padded to D + 1 floats, so
+// the 64 lanes reading 64 rows at one column hit distinct banks). Identical
+// operation order, hence identical bits.
+__device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const float *xs, int lane,
+                                               double &acc0, double &acc1) {
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < D; ++j) {
+        const double x = (double)xs[j];
+        a0 = fma((double)Rs[lane][j], x, a0);
+        a1 = fma((double)Rs[lane + 64][j], x, a1);
+    }
+    acc0 = a0;
+    acc1 = a1;
+}
+
 // Keep the r channels of largest magnitude (ties to the lower channel).
 // Keys are the magnitude bit patterns (63 bits; order = magnitude order).
 // The r-th largest key is found bit by bit with ballot counts.
@@ -68,8 +84,12 @@ __device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane,
     keep1 = gt1 || ((k1 == thr) && rank1 < need);
 }
 
-template <typename ST>
-__global__ __launch_bounds__(128) void k_compress(const CompressArgs A) {
+// STAGE (appends of a few tokens): 512 threads first copy R_k and R_v into
+// LDS with one round of coalesced 16-byte loads, then waves 0 and 1 compute
+// from LDS; without it (bulk appends) each lane reads its R rows, which the
+// 16 tokens of the block reuse through the caches.
+template <typename ST, bool STAGE>
+__global__ __launch_bounds__(STAGE ? 512 : 128) void k_compress(const CompressArgs A) {
     using bits_t = typename ST::bits_t;
     const CompressEntry &E = A.ent[blockIdx.z];
     if ((int)blockIdx.x >= E.nblk) return;
@@ -82,6 +102,26 @@ __global__ __launch_bounds__(128) void k_compress(const CompressArgs A) {
     const int se = min(E.e, p0 + BT) - p0;
     const size_t unit = (size_t)E.b * A.n_kv + g;
     const float *R = A.rot + (unit * 2 + wave) * D * D;
+    const float (*Rs)[D + 1] = nullptr;
+    if constexpr (STAGE) {
+        __shared__ float Rst[2][D][D + 1];
+        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + unit * 2 * D * D);
+        float4 v[2 * D * D / 4 / 512];
+#pragma unroll
+        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) v[k] = Rg[threadIdx.x + 512 * k];
+#pragma unroll
+        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) {
+            const int i = (int)threadIdx.x + 512 * k;
+            const int m = i / (D * D / 4), c = (i / (D / 4)) % D, j = (i % (D / 4)) * 4;
+            Rst[m][c][j] = v[k].x;
+            Rst[m][c][j + 1] = v[k].y;
+            Rst[m][c][j + 2] = v[k].z;
+            Rst[m][c][j + 3] = v[k].w;
+        }
+        __syncthreads();
+        if (wave >= 2) return;
+        Rs = Rst[wave];
+    }
     const bits_t *xin = reinterpret_cast<const bits_t *>(wave ? A.v_new : A.k_new) + unit * A.n_max * D;
     __shared__ __align__(16) float xs[2][D];
 
@@ -128,7 +168,8 @@ __global__ __launch_bounds__(128) void k_compress(const CompressArgs A) {
         xs[wave][lane + 64] = bits_to_float<ST>(xr[lane + 64]);
         wave_lds_sync();
         double v0, v1;
-        rotate_f64(R, xs[wave], lane, v0, v1);
+        if constexpr (STAGE) rotate_f64_lds(Rs, xs[wave], lane, v0, v1);
+        else rotate_f64(R, xs[wave], lane, v0, v1);
         wave_lds_sync();
         const bits_t s0 = round_store<ST>(v0), s1 = round_store<ST>(v1);
         if (packed) {
@@ -234,10 +275,15 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
 hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s) {
     if (a.n_ent <= 0 || max_blk <= 0) return hipSuccess;
     const dim3 grid((unsigned)max_blk, (unsigned)a.n_kv, (unsigned)a.n_ent);
-    if (dtype == MKV_BF16)
-        hipLaunchKernelGGL(k_compress<Bf16>, grid, dim3(128), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_compress<F32>, grid, dim3(128), 0, s, a);
+    // a block of work per (entry, KV head) at most twice: stage R in LDS
+    const bool stage = max_blk <= 2;
+    if (dtype == MKV_BF16) {
+        if (stage) hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k_compress<Bf16, false>), grid, dim3(128), 0, s, a);
+    } else {
+        if (stage) hipLaunchKernelGGL((k_compress<F32, true>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k_compress<F32, false>), grid, dim3(128), 0, s, a);
+    }
     return hipGetLastError();
 }
 

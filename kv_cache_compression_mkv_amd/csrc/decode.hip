@@ -6,9 +6,8 @@
 //   score         : s_l = (1/sqrt d) sum_c max(q'_c mx_c, q'_c mn_c) per block
 //   select        : per query head and packed segment, the k best blocks
 //                   (ties to the lower block), plus a per-block head mask
-//   attend_dense  : split-KV attention over the dense (sink / recent) blocks
-//   attend_packed : split-KV attention over the union of the group's selected
-//                   packed blocks
+//   attend        : split-KV attention over the dense (sink / recent) blocks
+//                   and the union of the group's selected packed blocks
 //   merge         : log-sum-exp merge of every split, then out = o R_v
 //
 // All of it is bandwidth-bound gather work: every kernel runs on the vector
@@ -30,38 +29,51 @@ __device__ __forceinline__ const DSeg &seg_of(const DecodeArgs &A, int bl, int s
 }
 
 // ----------------------------------------------------------------------------
-// q_rotate: one workgroup per (request, KV head); thread c computes q'_c.
+// q_rotate: four workgroups per (request, KV head), 32 channels each. The 8
+// lanes of channel c sum 16 columns each of R_k[c] . q (one round of 16-byte
+// loads per lane) and add up with DPP (quad swaps, then the half-row mirror).
 // ----------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(128) void k_qrot(const DecodeArgs A) {
-    const int bl = (int)blockIdx.y, g = (int)blockIdx.x;
+__global__ __launch_bounds__(256) void k_qrot(const DecodeArgs A) {
+    const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
     const int b = A.b0 + bl;
-    const int c = (int)threadIdx.x;
+    const int tid = (int)threadIdx.x;
+    const int k = tid & 7;
+    const int c = (int)blockIdx.x * 32 + (tid >> 3);
     __shared__ __align__(16) float qsh[G][D];
-    for (int i = 0; i < G; ++i) qsh[i][c] = A.q[((size_t)b * A.hq + g * G + i) * D + c];
-    __syncthreads();
     const float4 *Rr = reinterpret_cast<const float4 *>(A.rot + (((size_t)b * A.hkv + g) * 2) * D * D +
-                                                        (size_t)c * D);
+                                                        (size_t)c * D + 16 * k);
+    float4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = Rr[u];
+    for (int i = tid; i < G * D; i += 256) qsh[i / D][i % D] = A.q[((size_t)b * A.hq + g * G) * D + i];
+    __syncthreads();
     float acc[G];
 #pragma unroll
-    for (int i = 0; i < G; ++i) acc[i] = 0.f;
-    for (int j = 0; j < D / 4; ++j) {
-        const float4 r = Rr[j];
+    for (int i = 0; i < G; ++i) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(&qsh[i][16 * k]);
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 x = x4[u];
+            a = fmaf(r[u].x, x.x, a);
+            a = fmaf(r[u].y, x.y, a);
+            a = fmaf(r[u].z, x.z, a);
+            a = fmaf(r[u].w, x.w, a);
+        }
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xf, 0xf, false));
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xf, 0xf, false));
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xf, 0xf, false));
+        acc[i] = a;
+    }
+    if (k == 0) {
+        float *qs = A.qs + (((size_t)b * A.hkv + g) * D + c) * 2 * G;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const float4 x = reinterpret_cast<const float4 *>(qsh[i])[j];
-            acc[i] = fmaf(r.x, x.x, acc[i]);
-            acc[i] = fmaf(r.y, x.y, acc[i]);
-            acc[i] = fmaf(r.z, x.z, acc[i]);
-            acc[i] = fmaf(r.w, x.w, acc[i]);
+            A.qa[((size_t)b * A.hq + g * G + i) * D + c] = acc[i] * (kRsqrtD * kLog2e);
+            qs[i] = fmaxf(acc[i], 0.f) * kRsqrtD;
+            qs[G + i] = fminf(acc[i], 0.f) * kRsqrtD;
         }
-    }
-    float *qs = A.qs + (((size_t)b * A.hkv + g) * D + c) * 2 * G;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        A.qa[((size_t)b * A.hq + g * G + i) * D + c] = acc[i] * (kRsqrtD * kLog2e);
-        qs[i] = fmaxf(acc[i], 0.f) * kRsqrtD;
-        qs[G + i] = fminf(acc[i], 0.f) * kRsqrtD;
     }
 }
 
@@ -372,262 +384,39 @@ __device__ __forceinline__ float lane_value(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Online-softmax state. Softmax lanes are head-major: lane h*16 + t holds
-// token t of query head h, so each head is one DPP row.
-template <int G>
-struct WaveState {
-    float m;  // running max (log2 units) of the lane's head, uniform within the row
-    float l;  // lane-private partial sum of p
-    __device__ __forceinline__ void init() {
-        m = -INFINITY;
-        l = 0.f;
-    }
-    __device__ __forceinline__ float head_max(int i) const { return lane_value(m, 16 * i); }
-    __device__ __forceinline__ float head_sum(int i) const { return lane_value(row_sum16(l), 16 * i); }
-};
-
-// One online-softmax step over a block of 16 tokens. z is the logit of lane
-// (h, t) = (lane / 16, lane % 16), valid marks real (token, head) pairs. The
-// running max only moves when a block exceeds it by more than 2^8, so
-// rescales are rare. Writes p to zb[t * G + h]; alpha[i] is head i's rescale.
-template <int G>
-__device__ __forceinline__ void softmax16(float z, bool valid, float *zb, WaveState<G> &st, float alpha[G]) {
-    const int lane = lane_id();
-    const float zz = valid ? z : -INFINITY;
-    const float bm = row_max16(zz);
-    const float mh = st.m;
-    float mnew = mh, a = 1.f;
-    if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
-        a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
-        mnew = bm;
-    }
-    const float p = valid ? exp2f(zz - mnew) : 0.f;
-    if (lane < 16 * G) {
-        st.l = st.l * a + p;
-        st.m = mnew;
-        zb[(lane & 15) * G + (lane >> 4)] = p;
-    }
-#pragma unroll
-    for (int i = 0; i < G; ++i) alpha[i] = lane_value(a, 16 * i);
-}
-
-// 8 consecutive stored values (bf16: one 16-byte load; f32: two)
-template <typename ST>
-struct Vals8;
-template <>
-struct Vals8<Bf16> {
-    uint4 w;
-    __device__ __forceinline__ void load(const char *p) { w = *reinterpret_cast<const uint4 *>(p); }
-    __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
-    __device__ __forceinline__ void get(float v[8]) const {
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-    }
-    __device__ __forceinline__ void raw(uint16_t v[8]) const {
-        v[0] = (uint16_t)w.x; v[1] = (uint16_t)(w.x >> 16);
-        v[2] = (uint16_t)w.y; v[3] = (uint16_t)(w.y >> 16);
-        v[4] = (uint16_t)w.z; v[5] = (uint16_t)(w.z >> 16);
-        v[6] = (uint16_t)w.w; v[7] = (uint16_t)(w.w >> 16);
-    }
-};
-template <>
-struct Vals8<F32> {
-    uint4 a, b;
-    __device__ __forceinline__ void load(const char *p) {
-        a = reinterpret_cast<const uint4 *>(p)[0];
-        b = reinterpret_cast<const uint4 *>(p)[1];
-    }
-    __device__ __forceinline__ void zero() { a = b = make_uint4(0, 0, 0, 0); }
-    __device__ __forceinline__ void get(float v[8]) const {
-        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-        v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-        v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
-    }
-    __device__ __forceinline__ void raw(uint32_t v[8]) const {
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-};
-
-// split s of N equal parts of [0, n)
-__device__ __forceinline__ void split_range(int64_t n, int s, int S, int64_t &i0, int64_t &i1) {
-    i0 = n * s / S;
-    i1 = n * (s + 1) / S;
-}
-
 // ----------------------------------------------------------------------------
-// attend_dense: four waves per workgroup, each wave one split of the unit's
-// dense blocks. Lane (tg, ch) = (lane / 16, lane % 16) covers tokens tg, tg+4,
-// tg+8, tg+12 on channels 8ch..8ch+7; the K and V loads of a block are issued
-// together. Logits reduce over the 16 lanes of a token group; the V sums stay
-// in registers until the end.
-// ----------------------------------------------------------------------------
-template <typename ST, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_attend_dense(const DecodeArgs A) {
-    const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
-    const int b = A.b0 + bl;
-    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
-    const int s = (int)blockIdx.x * 4 + wave;
-    __shared__ __align__(16) float qsh[G][D];
-    __shared__ __align__(16) float zbs[4][16 * G];
-    for (int i = (int)threadIdx.x; i < G * D; i += 256)
-        qsh[i / D][i % D] = A.qa[((size_t)b * A.hq + g * G) * D + i];
-    __syncthreads();
-    if (s >= A.S_d) return;
-    float *zb = zbs[wave];
-    const int tg = lane >> 4, ch = lane & 15;
-    float vacc[G][8];
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) vacc[i][c] = 0.f;
-    WaveState<G> st;
-    st.init();
-
-    constexpr int sb = ST::bytes;
-    int64_t nblocks = 0;
-    for (int si = 0; si < A.nseg; ++si) {
-        const DSeg &S = seg_of(A, bl, si);
-        if (S.kind == MKV_SEG_DENSE) nblocks += S.nb;
-    }
-    int64_t i0, i1;
-    split_range(nblocks, s, A.S_d, i0, i1);
-    int64_t before = 0;
-    for (int si = 0; si < A.nseg; ++si) {
-        const DSeg &S = seg_of(A, bl, si);
-        if (S.kind != MKV_SEG_DENSE) continue;
-        const int64_t a0 = max(i0 - before, (int64_t)0), a1 = min(i1 - before, (int64_t)S.nb);
-        before += S.nb;
-        if (a0 >= a1) continue;
-        const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * 2 * BT * D * sb;
-        for (int64_t blk = a0; blk < a1; ++blk) {
-            const int nv = min(BT, S.filled - (int)blk * BT);
-            const char *kb = seg_base + (size_t)blk * 2 * BT * D * sb;
-            const char *vb = kb + (size_t)BT * D * sb;
-            Vals8<ST> kr[4], vr[4];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                kr[ii].load(kb + (size_t)((4 * ii + tg) * D + ch * 8) * sb);
-                vr[ii].load(vb + (size_t)((4 * ii + tg) * D + ch * 8) * sb);
-            }
-            float part[4][G];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                float kv[8];
-                kr[ii].get(kv);
-#pragma unroll
-                for (int i = 0; i < G; ++i) {
-                    const float4 qa = *reinterpret_cast<const float4 *>(&qsh[i][ch * 8]);
-                    const float4 qb = *reinterpret_cast<const float4 *>(&qsh[i][ch * 8 + 4]);
-                    float a = qa.x * kv[0];
-                    a = fmaf(qa.y, kv[1], a);
-                    a = fmaf(qa.z, kv[2], a);
-                    a = fmaf(qa.w, kv[3], a);
-                    a = fmaf(qb.x, kv[4], a);
-                    a = fmaf(qb.y, kv[5], a);
-                    a = fmaf(qb.z, kv[6], a);
-                    a = fmaf(qb.w, kv[7], a);
-                    part[ii][i] = a;
-                }
-            }
-            // a token group is one DPP row of 16 lanes
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-                for (int i = 0; i < G; ++i) part[ii][i] = row_sum16(part[ii][i]);
-            if (ch < G) {
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    float v = part[ii][0];
-#pragma unroll
-                    for (int i = 1; i < G; ++i)
-                        if (ch == i) v = part[ii][i];
-                    zb[(4 * ii + tg) * G + ch] = v;
-                }
-            }
-            wave_lds_sync();
-            float alpha[G];
-            {
-                const int h = lane >> 4, t = lane & 15;
-                const bool valid = h < G && t < nv;
-                softmax16<G>(valid ? zb[t * G + h] : 0.f, valid, zb, st, alpha);
-            }
-#pragma unroll
-            for (int i = 0; i < G; ++i)
-                if (alpha[i] != 1.f) {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) vacc[i][c] *= alpha[i];
-                }
-            wave_lds_sync();
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int tt = 4 * ii + tg;
-                float vv[8];
-                vr[ii].get(vv);
-#pragma unroll
-                for (int i = 0; i < G; ++i) {
-                    const float p = zb[tt * G + i];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) vacc[i][c] = fmaf(p, vv[c], vacc[i][c]);
-                }
-            }
-            wave_lds_sync();
-        }
-    }
-    // partials: m, l and acc[h][c]; acc sums over the four token groups
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float v = vacc[i][c];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            vacc[i][c] = v;
-        }
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const float li = st.head_sum(i);
-        const float mi = st.head_max(i);
-        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + s) * PART;
-        if (lane == 0) {
-            pp[0] = mi;
-            pp[1] = li;
-        }
-        if (tg == 0) {
-            float2 *d2 = reinterpret_cast<float2 *>(pp + 2 + ch * 8);  // partials are 8-byte aligned
-#pragma unroll
-            for (int c = 0; c < 8; c += 2) d2[c / 2] = make_float2(vacc[i][c], vacc[i][c + 1]);
-        }
-    }
-}
-
-// ----------------------------------------------------------------------------
-// attend_packed: four waves per workgroup, each wave one split of the unit's
-// packed items. Item (rank, head) of a packed segment is the rank-th block
+// attend: four waves per workgroup, each wave one split of a (request, KV
+// head) unit's work. The launch holds two kinds of workgroups: the first
+// ceil(S_p / 4) in x take the packed union records, the rest the dense
+// blocks, so both stream at once. Every split carries one online softmax state
+// per query head; merge combines them.
+//
+// Packed items: item (rank, head) of a packed segment is the rank-th block
 // that head selected; an item whose block a lower head of the group also
 // selected is dropped, so every union block is read once and serves each head
-// that chose it. Items are resolved 64 at a time into a compact list whose
-// records stream through a three-deep register pipeline (two records' loads
-// stay in flight while one is computed).
+// that chose it. Items are resolved 64 at a time into a compact list.
 //
-// Lane (t, p) = (lane / 4, lane % 4) owns part p of token t: elements
-// [p Q, min((p + 1) Q, r)) of the token's r, Q = ceil(r / 4), QM >= Q being the
-// compile-time bound. It loads dword-aligned windows of the four regions of
-// the record that cover its elements, so no lane's work crosses a token:
-//   K       z_h(t) = sum of q'_h[idx] * val over the token's four parts (q' is
-//           gathered from LDS; the parts add with DPP quad permutes);
+// Dense blocks and packed records both stream through a two-deep register
+// pipeline (the next one's loads are in flight while one is computed; a
+// deeper pipeline costs more registers than the occupancy it displaces).
+//
+// Lane (t, p) = (lane / 4, lane % 4) owns part p of token t. For a packed
+// record that is elements [p Q, min((p + 1) Q, r)) of the token's r,
+// Q = ceil(r / 4), QM >= Q being the compile-time bound: the lane loads
+// dword-aligned windows of the four regions of the record that cover its
+// elements, so no lane's work crosses a token. For a dense block it is
+// channels 32 p .. 32 p + 31 of token t's key.
+//   K       z_h(t) = sum of q'_h[c] k_t[c] over the token's four parts (q' in
+//           LDS; the parts add with DPP quad permutes);
 //   softmax per head, running max over the wave that only moves when a block
 //           exceeds it by 2^8 (so rescales are rare), p = exp2(z - m),
 //           lane-private running sums;
-//   V       the stored values scatter into the wave's dense tile [16][128]
-//           (a token's kept channels are distinct, so no two lanes of one
-//           token collide; window bytes past a lane's part go to the lane's
-//           slot of a dummy row); lane l then accumulates channels 2l, 2l + 1
-//           over the 16 rows
-//           and clears the tile.
+//   V       lane l accumulates channels 2l, 2l + 1 over the 16 tokens, p_t
+//           read from lane 4 t into a scalar register. Dense rows are read
+//           directly; packed values first scatter into the wave's dense tile
+//           [16][128] (a token's kept channels are distinct, so no two lanes
+//           of one token collide; window bytes past a lane's part go to the
+//           lane's slot of a dummy row), which is cleared after use.
 // ----------------------------------------------------------------------------
 // wait until at most N vector-memory loads of this wave are outstanding
 template <int N>
@@ -745,6 +534,26 @@ __device__ __forceinline__ float wave_sum_all(float v) {
     return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// One online-softmax step of head h over a block of 16 tokens: z is this
+// lane's part of token (lane / 4)'s logit (log2 units). Returns p, replicated
+// over the token's four lanes.
+template <int G>
+__device__ __forceinline__ float softmax_step(float z, bool valid, PkState<G> &S, int h) {
+    z = valid ? quad_sum(z) : -INFINITY;
+    const float bm = wave_max_quads(z);
+    const float mh = S.m[h];
+    if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
+        const float a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
+        S.m[h] = bm;
+        S.acc[h][0] *= a;
+        S.acc[h][1] *= a;
+        S.l[h] *= a;
+    }
+    const float p = valid ? exp2f(z - S.m[h]) : 0.f;
+    S.l[h] += p;
+    return p;
+}
+
 // acc[I][*] += sum_t p_t * tile[t][2 lane, 2 lane + 1]; p_t sits in lane 4 t
 // of p and is read into a scalar register
 template <typename ST, int G, int I>
@@ -826,19 +635,7 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM> &W, const PkGeom<ST,
             const int c = (int)((ki[j >> 2] >> (8 * (j & 3))) & 0xFFu);
             z = fmaf(qsh[h][c], kval[j], z);
         }
-        z = valid ? quad_sum(z) : -INFINITY;
-        const float bm = wave_max_quads(z);
-        const float mh = S.m[h];
-        if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
-            const float a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
-            S.m[h] = bm;
-            S.acc[h][0] *= a;
-            S.acc[h][1] *= a;
-            S.l[h] *= a;
-        }
-        const float p = valid ? exp2f(z - S.m[h]) : 0.f;
-        S.l[h] += p;
-        pv[h] = p;
+        pv[h] = softmax_step<G>(z, valid, S, h);
     }
     wave_lds_sync();
     // ---- V accumulate over the 16 rows, then clear them
@@ -863,25 +660,120 @@ __device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_
                                        int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S) {
     PkGeom<ST, QM> gm;
     gm.init(r);
-    constexpr int WN = 2 * PkWin<ST, QM>::LOADS;
-    PkWin<ST, QM> B0, B1, B2;
-    // loads past the end of the list repeat its last record, so every step
-    // has exactly two records in flight behind the one it computes
+    constexpr int WN = PkWin<ST, QM>::LOADS;
+    PkWin<ST, QM> B0, B1;
+    // a load past the end of the list repeats its last record, so every step
+    // has exactly one record in flight behind the one it computes
     auto at = [&](int i) {
         return seg_base + (size_t)uniform_int(list[min(i, n - 1)].x) * rec;
     };
     auto nv_of = [&](int i) { return min(BT, filled - uniform_int(list[i].x) * BT); };
     load_win(at(0), gm, B0);
-    load_win(at(1), gm, B1);
-    for (int i = 0; i < n; i += 3) {
-        load_win(at(i + 2), gm, B2);
+    for (int i = 0; i < n; i += 2) {
+        load_win(at(i + 1), gm, B1);
         pk_proc<ST, G, QM, WN>(B0, gm, uniform_int(list[i].y), nv_of(i), qsh, L, S);
         if (i + 1 >= n) break;
-        load_win(at(i + 3), gm, B0);
+        load_win(at(i + 2), gm, B0);
         pk_proc<ST, G, QM, WN>(B1, gm, uniform_int(list[i + 1].y), nv_of(i + 1), qsh, L, S);
-        if (i + 2 >= n) break;
-        load_win(at(i + 4), gm, B1);
-        pk_proc<ST, G, QM, WN>(B2, gm, uniform_int(list[i + 2].y), nv_of(i + 2), qsh, L, S);
+    }
+}
+
+// One dense block for one lane: 32 channels of token t's key (lane (t, p)),
+// and channels 2 lane, 2 lane + 1 of all 16 value rows.
+template <typename ST>
+struct DnWin {
+    static constexpr int NK = 32 * ST::bytes / 4;
+    static constexpr int VW = ST::bytes / 2;  // value dwords per row and lane
+    static constexpr int LOADS = load_instrs<NK>() + BT;
+    uint32_t k[NK];
+    uint32_t v[BT][VW];
+};
+
+template <typename ST>
+__device__ __forceinline__ void load_dense(const char *blk, DnWin<ST> &W) {
+    constexpr int sb = ST::bytes;
+    const int lane = lane_id();
+    const int t = lane >> 2, p = lane & 3;
+    load_words(blk + (size_t)(t * D + 32 * p) * sb, W.k);
+    const char *vb = blk + (size_t)BT * D * sb + (size_t)lane * 2 * sb;
+#pragma unroll
+    for (int row = 0; row < BT; ++row) {
+        if constexpr (DnWin<ST>::VW == 1) {
+            W.v[row][0] = *reinterpret_cast<const uint32_t *>(vb + (size_t)row * D * sb);
+        } else {
+            const uint2 x = *reinterpret_cast<const uint2 *>(vb + (size_t)row * D * sb);
+            W.v[row][0] = x.x;
+            W.v[row][1] = x.y;
+        }
+    }
+}
+
+template <typename ST, int G, int WAITN>
+__device__ __forceinline__ void dn_proc(const DnWin<ST> &W, int nv, const float (*qsh)[2 * D], PkState<G> &S) {
+    const int lane = lane_id();
+    const int p = lane & 3;
+    vm_wait<WAITN>();
+    // q' stays in LDS: without this barrier its reads would be hoisted out of
+    // the block loop into 32 G registers
+    asm volatile("" ::: "memory");
+    // K: head by head; the scheduling barrier keeps one head's 32 q' values
+    // live at a time instead of all G heads' (which would not fit)
+    const bool valid = (lane >> 2) < nv;
+    float pv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float4 *q4 = reinterpret_cast<const float4 *>(&qsh[h][32 * p]);
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 q = q4[i];
+            if constexpr (ST::bytes == 2) {
+                z = fmaf(q.x, bf16_lo(W.k[2 * i]), z);
+                z = fmaf(q.y, bf16_hi(W.k[2 * i]), z);
+                z = fmaf(q.z, bf16_lo(W.k[2 * i + 1]), z);
+                z = fmaf(q.w, bf16_hi(W.k[2 * i + 1]), z);
+            } else {
+                z = fmaf(q.x, __uint_as_float(W.k[4 * i]), z);
+                z = fmaf(q.y, __uint_as_float(W.k[4 * i + 1]), z);
+                z = fmaf(q.z, __uint_as_float(W.k[4 * i + 2]), z);
+                z = fmaf(q.w, __uint_as_float(W.k[4 * i + 3]), z);
+            }
+        }
+        pv[h] = softmax_step<G>(z, valid, S, h);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // V: head by head, so that only one head's 16 weights are scalar at a time
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            float a, b;
+            if constexpr (ST::bytes == 2) {
+                a = bf16_lo(W.v[t][0]);
+                b = bf16_hi(W.v[t][0]);
+            } else {
+                a = __uint_as_float(W.v[t][0]);
+                b = __uint_as_float(W.v[t][DnWin<ST>::VW - 1]);
+            }
+            const float pt = lane_value(pv[h], 4 * t);
+            S.acc[h][0] = fmaf(pt, a, S.acc[h][0]);
+            S.acc[h][1] = fmaf(pt, b, S.acc[h][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// dense blocks [a0, a1) of one segment, one at a time: dense splits run beside
+// the longer packed splits of the same launch, which hide their latency, and
+// a second block buffer would not fit in the registers of four waves per SIMD
+template <typename ST, int G>
+__device__ __forceinline__ void dn_run(const char *seg_base, int a0, int a1, int filled, const float (*qsh)[2 * D],
+                                       PkState<G> &S) {
+    constexpr size_t blk_bytes = (size_t)2 * BT * D * ST::bytes;
+    DnWin<ST> B;
+    for (int i = a0; i < a1; ++i) {
+        load_dense(seg_base + (size_t)i * blk_bytes, B);
+        dn_proc<ST, G, 0>(B, min(BT, filled - i * BT), qsh, S);
     }
 }
 
@@ -890,37 +782,66 @@ __device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
 }
 
-// QA < QB: segments with ceil(r / 4) <= QA run the QA code, the others QB
-template <typename ST, int G, int QA, int QB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_attend_packed(const DecodeArgs A) {
-    const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
-    const int b = A.b0 + bl;
-    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
-    const int s = (int)blockIdx.x * 4 + wave;
-    constexpr int sb = ST::bytes;
-
-    // q' * log2(e) / sqrt(d) per head; channels 128..255 are zero so that any
-    // index byte of a window gathers a finite value
-    __shared__ __align__(16) float qsh[G][2 * D];
-    __shared__ __align__(16) PkLds<ST, G> lds[4];
-    __shared__ int2 lists[4][64];
-    for (int i = (int)threadIdx.x; i < G * 2 * D; i += 256) {
-        const int h = i / (2 * D), c = i % (2 * D);
-        qsh[h][c] = c < D ? A.qa[((size_t)b * A.hq + g * G + h) * D + c] : 0.f;
+template <typename ST, int G>
+__device__ __forceinline__ void write_partial(const DecodeArgs &A, int b, int g, int split, const PkState<G> &S) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const float li = wave_sum_all(S.l[i]) * 0.25f;
+        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + split) * PART;
+        if (lane == 0) {
+            pp[0] = S.m[i];
+            pp[1] = li;
+        }
+        reinterpret_cast<float2 *>(pp + 2)[lane] = make_float2(S.acc[i][0], S.acc[i][1]);
     }
-    __syncthreads();
-    if (s >= A.S_p) return;
-    PkLds<ST, G> &L = lds[wave];
-    int2 *list = lists[wave];
-    for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
-    PkState<G> S;
+}
+
+template <int G>
+__device__ __forceinline__ void init_state(PkState<G> &S) {
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         S.acc[i][0] = S.acc[i][1] = 0.f;
         S.l[i] = 0.f;
         S.m[i] = -INFINITY;
     }
+}
 
+// dense split s of S_d: an equal share of the unit's dense blocks
+template <typename ST, int G>
+__device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, int b, int g, int s,
+                                                   const float (*qsh)[2 * D]) {
+    constexpr int sb = ST::bytes;
+    PkState<G> S;
+    init_state<G>(S);
+    int64_t nblocks = 0;
+    for (int si = 0; si < A.nseg; ++si) {
+        const DSeg &Sg = seg_of(A, bl, si);
+        if (Sg.kind == MKV_SEG_DENSE) nblocks += Sg.nb;
+    }
+    const int64_t i0 = nblocks * s / A.S_d, i1 = nblocks * (s + 1) / A.S_d;
+    int64_t before = 0;
+    for (int si = 0; si < A.nseg; ++si) {
+        const DSeg &Sg = seg_of(A, bl, si);
+        if (Sg.kind != MKV_SEG_DENSE) continue;
+        const int64_t a0 = max(i0 - before, (int64_t)0), a1 = min(i1 - before, (int64_t)Sg.nb);
+        before += Sg.nb;
+        if (a0 >= a1) continue;
+        const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * 2 * BT * D * sb;
+        dn_run<ST, G>(seg_base, (int)a0, (int)a1, Sg.filled, qsh, S);
+    }
+    write_partial<ST, G>(A, b, g, s, S);
+}
+
+// packed split s of S_p: an equal share (by bytes) of the unit's union records
+template <typename ST, int G, int QA, int QB>
+__device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl, int b, int g, int s,
+                                                    const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list) {
+    constexpr int sb = ST::bytes;
+    const int lane = lane_id();
+    for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
+    PkState<G> S;
+    init_state<G>(S);
     int64_t W = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &Sg = seg_of(A, bl, si);
@@ -974,63 +895,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             wave_lds_sync();
         }
     }
-    // write this split's partials (after the dense splits)
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const float li = wave_sum_all(S.l[i]) * 0.25f;
-        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + A.S_d + s) * PART;
-        if (lane == 0) {
-            pp[0] = S.m[i];
-            pp[1] = li;
-        }
-        reinterpret_cast<float2 *>(pp + 2)[lane] = make_float2(S.acc[i][0], S.acc[i][1]);
+    write_partial<ST, G>(A, b, g, A.S_d + s, S);
+}
+
+// QA < QB: packed segments with ceil(r / 4) <= QA run the QA code, the others QB
+template <typename ST, int G, int QA, int QB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_attend(const DecodeArgs A) {
+    const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
+    const int b = A.b0 + bl;
+    // wave-uniform: the split bounds and their 64-bit arithmetic stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int px = (A.S_p + 3) / 4;
+    // q' * log2(e) / sqrt(d) per head; channels 128..255 are zero so that any
+    // index byte of a packed window gathers a finite value
+    __shared__ __align__(16) float qsh[G][2 * D];
+    __shared__ __align__(16) PkLds<ST, G> lds[4];
+    __shared__ int2 lists[4][64];
+    for (int i = (int)threadIdx.x; i < G * 2 * D; i += 256) {
+        const int h = i / (2 * D), c = i % (2 * D);
+        qsh[h][c] = c < D ? A.qa[((size_t)b * A.hq + g * G + h) * D + c] : 0.f;
+    }
+    __syncthreads();
+    if ((int)blockIdx.x < px) {
+        const int s = (int)blockIdx.x * 4 + wave;
+        if (s < A.S_p) attend_packed_split<ST, G, QA, QB>(A, bl, b, g, s, qsh, lds[wave], lists[wave]);
+    } else {
+        const int s = ((int)blockIdx.x - px) * 4 + wave;
+        if (s < A.S_d) attend_dense_split<ST, G>(A, bl, b, g, s, qsh);
     }
 }
+
 // ----------------------------------------------------------------------------
 // merge: one workgroup per (request, query head): log-sum-exp merge of the
 // head's dense and packed splits in split order, then out_j = sum_c R_v[c][j] o_c.
+// Thread (cc, j4) = (t / 32, t % 32) loads rows 16 cc .. 16 cc + 15 of R_v at
+// columns 4 j4 .. 4 j4 + 3 first, so those loads overlap the merge.
 // ----------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
+    static_assert(MAX_SPLITS <= 256, "one thread per split");
     const int bl = (int)blockIdx.y, h = (int)blockIdx.x;
     const int b = A.b0 + bl, g = h / G;
     const int t = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x >> 6);
     const int Stot = A.S_d + A.S_p;
     const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_SPLITS * PART;
     __shared__ float wsc[MAX_SPLITS];
+    __shared__ float red[2][4];
     __shared__ __align__(16) float part_o[8][D];
     __shared__ __align__(16) float osh[D];
-    __shared__ float Lsh;
-    if (wave == 0) {
-        float M = -INFINITY;
-        for (int x = lane; x < Stot; x += 64) M = fmaxf(M, pp[(size_t)x * PART]);
+    const int j4 = t & 31, cc = t >> 5;
+    const float4 *Rv4 = reinterpret_cast<const float4 *>(A.rot + (((size_t)b * A.hkv + g) * 2 + 1) * D * D);
+    float4 rv[16];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float L = 0.f;
-        for (int x = lane; x < Stot; x += 64) {
-            const float m = pp[(size_t)x * PART];
-            const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-            wsc[x] = w;
-            L += w * pp[(size_t)x * PART + 1];
-        }
-        L = wave_sum(L);
-        if (lane == 0) Lsh = L;
+    for (int u = 0; u < 16; ++u) rv[u] = Rv4[(size_t)(cc * 16 + u) * (D / 4) + j4];
+
+    // split weights: w_s = exp2(m_s - M), L = sum_s w_s l_s (MAX_SPLITS == 256 threads)
+    float m = -INFINITY, l = 0.f;
+    if (t < Stot) {
+        m = pp[(size_t)t * PART];
+        l = pp[(size_t)t * PART + 1];
+    }
+    {
+        float v = row_max16(m);
+        v = fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+        if (lane == 0) red[0][wave] = v;
     }
     __syncthreads();
+    const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    if (t < MAX_SPLITS) wsc[t] = w;
     {
-        // thread (group, quad): channels 4*quad..4*quad+3 over splits group, group+8, ...
+        const float v = wave_sum(w * l);
+        if (lane == 0) red[1][wave] = v;
+    }
+    __syncthreads();
+    const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    {
+        // thread (grp, quad): channels 4 quad .. 4 quad + 3 over splits grp, grp + 8, ...
         const int quad = t & 31, grp = t >> 5;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
         for (int y = grp; y < Stot; y += 8) {
-            const float w = wsc[y];
+            const float wy = wsc[y];
             const float *src = pp + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
             const float2 x0 = *reinterpret_cast<const float2 *>(src);
             const float2 x1 = *reinterpret_cast<const float2 *>(src + 2);
-            o.x = fmaf(w, x0.x, o.x);
-            o.y = fmaf(w, x0.y, o.y);
-            o.z = fmaf(w, x1.x, o.z);
-            o.w = fmaf(w, x1.y, o.w);
+            o.x = fmaf(wy, x0.x, o.x);
+            o.y = fmaf(wy, x0.y, o.y);
+            o.z = fmaf(wy, x1.x, o.z);
+            o.w = fmaf(wy, x1.y, o.w);
         }
         *reinterpret_cast<float4 *>(&part_o[grp][quad * 4]) = o;
     }
@@ -1039,19 +992,27 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
         float o = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) o += part_o[k][t];
-        const float L = Lsh;
         osh[t] = L > 0.f ? o / L : 0.f;
     }
     __syncthreads();
-    if (t < D) {
-        const float *Rv = A.rot + (((size_t)b * A.hkv + g) * 2 + 1) * D * D;
-        float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < D; c += 2) {
-            o0 = fmaf(Rv[(size_t)c * D + t], osh[c], o0);
-            o1 = fmaf(Rv[(size_t)(c + 1) * D + t], osh[c + 1], o1);
+    {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float oc = osh[cc * 16 + u];
+            acc.x = fmaf(rv[u].x, oc, acc.x);
+            acc.y = fmaf(rv[u].y, oc, acc.y);
+            acc.z = fmaf(rv[u].z, oc, acc.z);
+            acc.w = fmaf(rv[u].w, oc, acc.w);
         }
-        A.out[((size_t)b * A.hq + h) * D + t] = o0 + o1;
+        *reinterpret_cast<float4 *>(&part_o[cc][4 * j4]) = acc;
+    }
+    __syncthreads();
+    if (t < D) {
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o += part_o[k][t];
+        A.out[((size_t)b * A.hq + h) * D + t] = o;
     }
 }
 
@@ -1075,11 +1036,11 @@ hipError_t select_launch(const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s) {
-    const dim3 grid((unsigned)a.hkv, (unsigned)a.n_req);
+    const dim3 grid(D / 32, (unsigned)a.hkv, (unsigned)a.n_req);
     switch (G) {
-    case 1: hipLaunchKernelGGL(k_qrot<1>, grid, dim3(128), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_qrot<2>, grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_qrot<4>, grid, dim3(128), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(k_qrot<1>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_qrot<2>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_qrot<4>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1116,21 +1077,9 @@ hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attend_dense(const DecodeArgs &a, int dtype, int G, hipStream_t s) {
-    const dim3 grid((unsigned)((a.S_d + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
-#define MKV_ATT(ST, GG) hipLaunchKernelGGL((k_attend_dense<ST, GG>), grid, dim3(256), 0, s, a)
-    if (dtype == MKV_BF16) {
-        if (G == 1) MKV_ATT(Bf16, 1); else if (G == 2) MKV_ATT(Bf16, 2); else MKV_ATT(Bf16, 4);
-    } else {
-        if (G == 1) MKV_ATT(F32, 1); else if (G == 2) MKV_ATT(F32, 2); else MKV_ATT(F32, 4);
-    }
-#undef MKV_ATT
-    return hipGetLastError();
-}
-
 template <typename ST, int G>
-void packed_launch(const DecodeArgs &a, int qmax, dim3 grid, hipStream_t s) {
-#define MKV_PK(QA, QB) hipLaunchKernelGGL((k_attend_packed<ST, G, QA, QB>), grid, dim3(256), 0, s, a)
+void attend_launch(const DecodeArgs &a, int qmax, dim3 grid, hipStream_t s) {
+#define MKV_PK(QA, QB) hipLaunchKernelGGL((k_attend<ST, G, QA, QB>), grid, dim3(256), 0, s, a)
     if (qmax <= 4) MKV_PK(4, 4);
     else if (qmax <= 8) MKV_PK(4, 8);
     else if (qmax <= 10) MKV_PK(8, 10);
@@ -1140,16 +1089,16 @@ void packed_launch(const DecodeArgs &a, int qmax, dim3 grid, hipStream_t s) {
 }
 
 // qmax = ceil(r_max / 4): elements per lane of the widest packed segment
-hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s) {
-    const dim3 grid((unsigned)((a.S_p + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
+hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s) {
+    const dim3 grid((unsigned)((a.S_p + 3) / 4 + (a.S_d + 3) / 4), (unsigned)a.hkv, (unsigned)a.n_req);
     if (dtype == MKV_BF16) {
-        if (G == 1) packed_launch<Bf16, 1>(a, qmax, grid, s);
-        else if (G == 2) packed_launch<Bf16, 2>(a, qmax, grid, s);
-        else packed_launch<Bf16, 4>(a, qmax, grid, s);
+        if (G == 1) attend_launch<Bf16, 1>(a, qmax, grid, s);
+        else if (G == 2) attend_launch<Bf16, 2>(a, qmax, grid, s);
+        else attend_launch<Bf16, 4>(a, qmax, grid, s);
     } else {
-        if (G == 1) packed_launch<F32, 1>(a, qmax, grid, s);
-        else if (G == 2) packed_launch<F32, 2>(a, qmax, grid, s);
-        else packed_launch<F32, 4>(a, qmax, grid, s);
+        if (G == 1) attend_launch<F32, 1>(a, qmax, grid, s);
+        else if (G == 2) attend_launch<F32, 2>(a, qmax, grid, s);
+        else attend_launch<F32, 4>(a, qmax, grid, s);
     }
     return hipGetLastError();
 }

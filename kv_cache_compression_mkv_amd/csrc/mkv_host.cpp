@@ -380,8 +380,8 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
             Wmax = std::max(Wmax, W);
             Dmax = std::max(Dmax, Dn);
         }
-        // splits of about 64 KB of cache reads each
-        A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 64 * 1024)));
+        // splits of about 64 KB of packed reads and 128 KB of dense reads each
+        A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
         A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 64 * 1024)));
         // select: up to 16 waves, 4 / 16 / 64 keys per lane
         const int kpt = max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
@@ -396,12 +396,10 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
             st = timed(4, s, [&] { return launch_select(A, G, s); });
             if (st != MKV_OK) return st;
         }
-        st = timed(5, s, [&] { return launch_attend_dense(A, c->dtype, G, s); });
-        if (st != MKV_OK) return st;
         const int qmax = (max_r + 3) / 4;
-        st = timed(6, s, [&] { return launch_attend_packed(A, c->dtype, G, qmax, s); });
+        st = timed(5, s, [&] { return launch_attend(A, c->dtype, G, qmax, s); });
         if (st != MKV_OK) return st;
-        st = timed(7, s, [&] { return launch_merge(A, G, s); });
+        st = timed(6, s, [&] { return launch_merge(A, G, s); });
         if (st != MKV_OK) return st;
     }
     return MKV_OK;
@@ -439,8 +437,8 @@ mkv_status mkv_timing_read(double *ms_out, int64_t *count_out, int32_t n_stages)
 }
 
 const char *mkv_stage_name(int32_t stage) {
-    static const char *names[MKV_N_STAGES] = {"compress", "block_meta",   "q_rotate",      "score",
-                                              "select",   "attend_dense", "attend_packed", "merge"};
+    static const char *names[MKV_N_STAGES] = {"compress", "block_meta", "q_rotate", "score",
+                                              "select",   "attend",     "merge"};
     return (stage >= 0 && stage < MKV_N_STAGES) ? names[stage] : "unknown";
 }
 

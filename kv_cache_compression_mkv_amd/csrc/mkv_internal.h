@@ -84,8 +84,8 @@ struct DecodeArgs {
     int32_t kcap[MKV_MAX_SEGMENTS];
     int32_t pseg[MKV_MAX_SEGMENTS];   // segment index of packed j
     int32_t b0, n_req, nseg, npk, hq, hkv;
-    int32_t S_d;       // dense splits per unit (>= 1)
-    int32_t S_p;       // packed splits per unit (>= 1), S_d + S_p <= MAX_SPLITS
+    int32_t S_d;       // dense attention splits per unit (>= 1)
+    int32_t S_p;       // packed attention splits per unit (>= 1), S_d + S_p <= MAX_SPLITS
     int32_t sel_kpt;   // keys per lane in select
     int32_t sel_waves; // waves per select workgroup
 };
@@ -96,8 +96,7 @@ hipError_t launch_block_meta(const MetaArgs &a, int dtype, int max_nb, hipStream
 hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s);
 hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hipStream_t s);
 hipError_t launch_select(const DecodeArgs &a, int G, hipStream_t s);
-hipError_t launch_attend_dense(const DecodeArgs &a, int dtype, int G, hipStream_t s);
-hipError_t launch_attend_packed(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s);
+hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s);
 
 }  // namespace mkv

@@ -84,13 +84,10 @@ __global__ __launch_bounds__(256) void k_qrot(const DecodeArgs A) {
 // into positive and negative parts: max(q mx, q mn) = q+ mx + q- mn.
 // ----------------------------------------------------------------------------
 template <typename ST, int G>
-__global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
-    const int z = (int)blockIdx.z;
-    const int bl = z / A.npk, j = z % A.npk;
-    const int b = A.b0 + bl, g = (int)blockIdx.y;
+__device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, int g, int tile) {
+    const int b = A.b0 + bl;
     const DSeg &S = seg_of(A, bl, A.pseg[j]);
-    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
-    const int tile = (int)blockIdx.x * 4 + wave;
+    const int lane = lane_id();
     const int ntile = (S.nb + META_TILE - 1) / META_TILE;
     if (tile >= ntile) return;
     const int l = tile * META_TILE + lane;
@@ -388,8 +385,9 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // attend: four waves per workgroup, each wave one split of a (request, KV
 // head) unit's work. The launch holds two kinds of workgroups: the first
 // ceil(S_p / 4) in x take the packed union records, the rest the dense
-// blocks, so both stream at once. Every split carries one online softmax state
-// per query head; merge combines them.
+// blocks, so the dense stream runs beside the latency-bound packed records.
+// Every split carries one online softmax state per query head; merge combines
+// them.
 //
 // Packed items: item (rank, head) of a packed segment is the rank-th block
 // that head selected; an item whose block a lower head of the group also
@@ -411,13 +409,93 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 //   softmax per head, running max over the wave that only moves when a block
 //           exceeds it by 2^8 (so rescales are rare), p = exp2(z - m),
 //           lane-private running sums;
-//   V       lane l accumulates channels 2l, 2l + 1 over the 16 tokens, p_t
-//           read from lane 4 t into a scalar register. Dense rows are read
+//   V       lane l accumulates channels 2l, 2l + 1 over the 16 tokens, the
+//           p_t broadcast through LDS. Dense rows are read
 //           directly; packed values first scatter into the wave's dense tile
 //           [16][128] (a token's kept channels are distinct, so no two lanes
 //           of one token collide; window bytes past a lane's part go to the
 //           lane's slot of a dummy row), which is cleared after use.
 // ----------------------------------------------------------------------------
+// Online-softmax state. Softmax lanes are head-major: lane h*16 + t holds
+// token t of query head h, so each head is one DPP row.
+template <int G>
+struct WaveState {
+    float m;  // running max (log2 units) of the lane's head, uniform within the row
+    float l;  // lane-private partial sum of p
+    __device__ __forceinline__ void init() {
+        m = -INFINITY;
+        l = 0.f;
+    }
+    __device__ __forceinline__ float head_max(int i) const { return lane_value(m, 16 * i); }
+    __device__ __forceinline__ float head_sum(int i) const { return lane_value(row_sum16(l), 16 * i); }
+};
+
+// One online-softmax step over a block of 16 tokens. z is the logit of lane
+// (h, t) = (lane / 16, lane % 16), valid marks real (token, head) pairs. The
+// running max only moves when a block exceeds it by more than 2^8, so
+// rescales are rare. Writes p to zb[t * G + h]; alpha[i] is head i's rescale.
+template <int G>
+__device__ __forceinline__ void softmax16(float z, bool valid, float *zb, WaveState<G> &st, float alpha[G]) {
+    const int lane = lane_id();
+    const float zz = valid ? z : -INFINITY;
+    const float bm = row_max16(zz);
+    const float mh = st.m;
+    float mnew = mh, a = 1.f;
+    if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
+        a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
+        mnew = bm;
+    }
+    const float p = valid ? exp2f(zz - mnew) : 0.f;
+    if (lane < 16 * G) {
+        st.l = st.l * a + p;
+        st.m = mnew;
+        zb[(lane & 15) * G + (lane >> 4)] = p;
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) alpha[i] = lane_value(a, 16 * i);
+}
+
+// 8 consecutive stored values (bf16: one 16-byte load; f32: two)
+template <typename ST>
+struct Vals8;
+template <>
+struct Vals8<Bf16> {
+    uint4 w;
+    __device__ __forceinline__ void load(const char *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void get(float v[8]) const {
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    }
+    __device__ __forceinline__ void raw(uint16_t v[8]) const {
+        v[0] = (uint16_t)w.x; v[1] = (uint16_t)(w.x >> 16);
+        v[2] = (uint16_t)w.y; v[3] = (uint16_t)(w.y >> 16);
+        v[4] = (uint16_t)w.z; v[5] = (uint16_t)(w.z >> 16);
+        v[6] = (uint16_t)w.w; v[7] = (uint16_t)(w.w >> 16);
+    }
+};
+template <>
+struct Vals8<F32> {
+    uint4 a, b;
+    __device__ __forceinline__ void load(const char *p) {
+        a = reinterpret_cast<const uint4 *>(p)[0];
+        b = reinterpret_cast<const uint4 *>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void get(float v[8]) const {
+        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+        v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+        v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    }
+    __device__ __forceinline__ void raw(uint32_t v[8]) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
 // wait until at most N vector-memory loads of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -507,6 +585,7 @@ __device__ __forceinline__ void load_win(const char *rec, const PkGeom<ST, QM> &
 template <typename ST, int G>
 struct PkLds {
     typename ST::bits_t vt[BT + 1][D];
+    float zb[G][BT];  // p of the current record, head-major
 };
 
 template <int G>
@@ -554,10 +633,23 @@ __device__ __forceinline__ float softmax_step(float z, bool valid, PkState<G> &S
     return p;
 }
 
-// acc[I][*] += sum_t p_t * tile[t][2 lane, 2 lane + 1]; p_t sits in lane 4 t
-// of p and is read into a scalar register
+// the 16 weights of one head, broadcast from LDS
+__device__ __forceinline__ void read_p16(const float *zb, float (&p)[BT]) {
+#pragma unroll
+    for (int q = 0; q < BT / 4; ++q) {
+        const float4 v = reinterpret_cast<const float4 *>(zb)[q];
+        p[4 * q] = v.x;
+        p[4 * q + 1] = v.y;
+        p[4 * q + 2] = v.z;
+        p[4 * q + 3] = v.w;
+    }
+}
+
+// acc[I][*] += sum_t p_t * tile[t][2 lane, 2 lane + 1]
 template <typename ST, int G, int I>
-__device__ __forceinline__ void pk_accum(const PkLds<ST, G> &L, PkState<G> &S, float p, int lane) {
+__device__ __forceinline__ void pk_accum(const PkLds<ST, G> &L, PkState<G> &S, int lane) {
+    float p[BT];
+    read_p16(L.zb[I], p);
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
         float a, b;
@@ -570,9 +662,8 @@ __device__ __forceinline__ void pk_accum(const PkLds<ST, G> &L, PkState<G> &S, f
             a = __uint_as_float(w.x);
             b = __uint_as_float(w.y);
         }
-        const float pt = lane_value(p, 4 * t);
-        S.acc[I][0] = fmaf(pt, a, S.acc[I][0]);
-        S.acc[I][1] = fmaf(pt, b, S.acc[I][1]);
+        S.acc[I][0] = fmaf(p[t], a, S.acc[I][0]);
+        S.acc[I][1] = fmaf(p[t], b, S.acc[I][1]);
     }
 }
 
@@ -624,10 +715,8 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM> &W, const PkGeom<ST,
         for (int j = 0; j < QM; ++j) kval[j] = j < gm.cnt ? __uint_as_float(W.kv[j]) : 0.f;
     }
     const bool valid = (lane >> 2) < nv;
-    float pv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        pv[h] = 0.f;
         if (!((hm >> h) & 1)) continue;
         float z = 0.f;
 #pragma unroll
@@ -635,14 +724,15 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM> &W, const PkGeom<ST,
             const int c = (int)((ki[j >> 2] >> (8 * (j & 3))) & 0xFFu);
             z = fmaf(qsh[h][c], kval[j], z);
         }
-        pv[h] = softmax_step<G>(z, valid, S, h);
+        const float p = softmax_step<G>(z, valid, S, h);
+        if ((lane & 3) == 0) L.zb[h][lane >> 2] = p;
     }
     wave_lds_sync();
     // ---- V accumulate over the 16 rows, then clear them
-    if (hm & 1) pk_accum<ST, G, 0>(L, S, pv[0], lane);
-    if constexpr (G > 1) if (hm & 2) pk_accum<ST, G, 1>(L, S, pv[1], lane);
-    if constexpr (G > 2) if (hm & 4) pk_accum<ST, G, 2>(L, S, pv[2], lane);
-    if constexpr (G > 3) if (hm & 8) pk_accum<ST, G, 3>(L, S, pv[3], lane);
+    if (hm & 1) pk_accum<ST, G, 0>(L, S, lane);
+    if constexpr (G > 1) if (hm & 2) pk_accum<ST, G, 1>(L, S, lane);
+    if constexpr (G > 2) if (hm & 4) pk_accum<ST, G, 2>(L, S, lane);
+    if constexpr (G > 3) if (hm & 8) pk_accum<ST, G, 3>(L, S, lane);
     {
         constexpr int n16 = BT * D * ST::bytes / 16;  // 16-byte pieces of rows 0..15
         uint4 *v4 = reinterpret_cast<uint4 *>(&L.vt[0][0]);
@@ -678,105 +768,6 @@ __device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_
     }
 }
 
-// One dense block for one lane: 32 channels of token t's key (lane (t, p)),
-// and channels 2 lane, 2 lane + 1 of all 16 value rows.
-template <typename ST>
-struct DnWin {
-    static constexpr int NK = 32 * ST::bytes / 4;
-    static constexpr int VW = ST::bytes / 2;  // value dwords per row and lane
-    static constexpr int LOADS = load_instrs<NK>() + BT;
-    uint32_t k[NK];
-    uint32_t v[BT][VW];
-};
-
-template <typename ST>
-__device__ __forceinline__ void load_dense(const char *blk, DnWin<ST> &W) {
-    constexpr int sb = ST::bytes;
-    const int lane = lane_id();
-    const int t = lane >> 2, p = lane & 3;
-    load_words(blk + (size_t)(t * D + 32 * p) * sb, W.k);
-    const char *vb = blk + (size_t)BT * D * sb + (size_t)lane * 2 * sb;
-#pragma unroll
-    for (int row = 0; row < BT; ++row) {
-        if constexpr (DnWin<ST>::VW == 1) {
-            W.v[row][0] = *reinterpret_cast<const uint32_t *>(vb + (size_t)row * D * sb);
-        } else {
-            const uint2 x = *reinterpret_cast<const uint2 *>(vb + (size_t)row * D * sb);
-            W.v[row][0] = x.x;
-            W.v[row][1] = x.y;
-        }
-    }
-}
-
-template <typename ST, int G, int WAITN>
-__device__ __forceinline__ void dn_proc(const DnWin<ST> &W, int nv, const float (*qsh)[2 * D], PkState<G> &S) {
-    const int lane = lane_id();
-    const int p = lane & 3;
-    vm_wait<WAITN>();
-    // q' stays in LDS: without this barrier its reads would be hoisted out of
-    // the block loop into 32 G registers
-    asm volatile("" ::: "memory");
-    // K: head by head; the scheduling barrier keeps one head's 32 q' values
-    // live at a time instead of all G heads' (which would not fit)
-    const bool valid = (lane >> 2) < nv;
-    float pv[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float4 *q4 = reinterpret_cast<const float4 *>(&qsh[h][32 * p]);
-        float z = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 q = q4[i];
-            if constexpr (ST::bytes == 2) {
-                z = fmaf(q.x, bf16_lo(W.k[2 * i]), z);
-                z = fmaf(q.y, bf16_hi(W.k[2 * i]), z);
-                z = fmaf(q.z, bf16_lo(W.k[2 * i + 1]), z);
-                z = fmaf(q.w, bf16_hi(W.k[2 * i + 1]), z);
-            } else {
-                z = fmaf(q.x, __uint_as_float(W.k[4 * i]), z);
-                z = fmaf(q.y, __uint_as_float(W.k[4 * i + 1]), z);
-                z = fmaf(q.z, __uint_as_float(W.k[4 * i + 2]), z);
-                z = fmaf(q.w, __uint_as_float(W.k[4 * i + 3]), z);
-            }
-        }
-        pv[h] = softmax_step<G>(z, valid, S, h);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // V: head by head, so that only one head's 16 weights are scalar at a time
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int t = 0; t < BT; ++t) {
-            float a, b;
-            if constexpr (ST::bytes == 2) {
-                a = bf16_lo(W.v[t][0]);
-                b = bf16_hi(W.v[t][0]);
-            } else {
-                a = __uint_as_float(W.v[t][0]);
-                b = __uint_as_float(W.v[t][DnWin<ST>::VW - 1]);
-            }
-            const float pt = lane_value(pv[h], 4 * t);
-            S.acc[h][0] = fmaf(pt, a, S.acc[h][0]);
-            S.acc[h][1] = fmaf(pt, b, S.acc[h][1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// dense blocks [a0, a1) of one segment, one at a time: dense splits run beside
-// the longer packed splits of the same launch, which hide their latency, and
-// a second block buffer would not fit in the registers of four waves per SIMD
-template <typename ST, int G>
-__device__ __forceinline__ void dn_run(const char *seg_base, int a0, int a1, int filled, const float (*qsh)[2 * D],
-                                       PkState<G> &S) {
-    constexpr size_t blk_bytes = (size_t)2 * BT * D * ST::bytes;
-    DnWin<ST> B;
-    for (int i = a0; i < a1; ++i) {
-        load_dense(seg_base + (size_t)i * blk_bytes, B);
-        dn_proc<ST, G, 0>(B, min(BT, filled - i * BT), qsh, S);
-    }
-}
-
 __device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
     const int64_t rec = (int64_t)BT * r * 2 * (sb + 1);
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
@@ -807,30 +798,139 @@ __device__ __forceinline__ void init_state(PkState<G> &S) {
     }
 }
 
-// dense split s of S_d: an equal share of the unit's dense blocks
+// dense split s of S_d: an equal share of the unit's dense blocks. Lane
+// (tg, ch) = (lane / 16, lane % 16) covers tokens tg, tg+4, tg+8, tg+12 on
+// channels 8ch..8ch+7; the K and V loads of a block are issued together.
+// Logits reduce over the 16 lanes of a token group (one DPP row); softmax
+// lanes are head-major (lane h * 16 + t); the V sums stay in registers until
+// the end, where the four token groups add up.
 template <typename ST, int G>
 __device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, int b, int g, int s,
-                                                   const float (*qsh)[2 * D]) {
+                                                   const float (*qsh)[2 * D], float *zb) {
+    const int lane = lane_id();
+    const int tg = lane >> 4, ch = lane & 15;
+    float vacc[G][8];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) vacc[i][c] = 0.f;
+    WaveState<G> st;
+    st.init();
+
     constexpr int sb = ST::bytes;
-    PkState<G> S;
-    init_state<G>(S);
     int64_t nblocks = 0;
     for (int si = 0; si < A.nseg; ++si) {
-        const DSeg &Sg = seg_of(A, bl, si);
-        if (Sg.kind == MKV_SEG_DENSE) nblocks += Sg.nb;
+        const DSeg &S = seg_of(A, bl, si);
+        if (S.kind == MKV_SEG_DENSE) nblocks += S.nb;
     }
     const int64_t i0 = nblocks * s / A.S_d, i1 = nblocks * (s + 1) / A.S_d;
     int64_t before = 0;
     for (int si = 0; si < A.nseg; ++si) {
-        const DSeg &Sg = seg_of(A, bl, si);
-        if (Sg.kind != MKV_SEG_DENSE) continue;
-        const int64_t a0 = max(i0 - before, (int64_t)0), a1 = min(i1 - before, (int64_t)Sg.nb);
-        before += Sg.nb;
+        const DSeg &S = seg_of(A, bl, si);
+        if (S.kind != MKV_SEG_DENSE) continue;
+        const int64_t a0 = max(i0 - before, (int64_t)0), a1 = min(i1 - before, (int64_t)S.nb);
+        before += S.nb;
         if (a0 >= a1) continue;
-        const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * 2 * BT * D * sb;
-        dn_run<ST, G>(seg_base, (int)a0, (int)a1, Sg.filled, qsh, S);
+        const char *seg_base = static_cast<const char *>(S.data) + (size_t)g * S.nbcap * 2 * BT * D * sb;
+        for (int64_t blk = a0; blk < a1; ++blk) {
+            const int nv = min(BT, S.filled - (int)blk * BT);
+            const char *kb = seg_base + (size_t)blk * 2 * BT * D * sb;
+            const char *vb = kb + (size_t)BT * D * sb;
+            Vals8<ST> kr[4], vr[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                kr[ii].load(kb + (size_t)((4 * ii + tg) * D + ch * 8) * sb);
+                vr[ii].load(vb + (size_t)((4 * ii + tg) * D + ch * 8) * sb);
+            }
+            float part[4][G];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                float kv[8];
+                kr[ii].get(kv);
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const float4 qa = *reinterpret_cast<const float4 *>(&qsh[i][ch * 8]);
+                    const float4 qb = *reinterpret_cast<const float4 *>(&qsh[i][ch * 8 + 4]);
+                    float a = qa.x * kv[0];
+                    a = fmaf(qa.y, kv[1], a);
+                    a = fmaf(qa.z, kv[2], a);
+                    a = fmaf(qa.w, kv[3], a);
+                    a = fmaf(qb.x, kv[4], a);
+                    a = fmaf(qb.y, kv[5], a);
+                    a = fmaf(qb.z, kv[6], a);
+                    a = fmaf(qb.w, kv[7], a);
+                    part[ii][i] = a;
+                }
+            }
+            // a token group is one DPP row of 16 lanes
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                for (int i = 0; i < G; ++i) part[ii][i] = row_sum16(part[ii][i]);
+            if (ch < G) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    float v = part[ii][0];
+#pragma unroll
+                    for (int i = 1; i < G; ++i)
+                        if (ch == i) v = part[ii][i];
+                    zb[(4 * ii + tg) * G + ch] = v;
+                }
+            }
+            wave_lds_sync();
+            float alpha[G];
+            {
+                const int h = lane >> 4, t = lane & 15;
+                const bool valid = h < G && t < nv;
+                softmax16<G>(valid ? zb[t * G + h] : 0.f, valid, zb, st, alpha);
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                if (alpha[i] != 1.f) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) vacc[i][c] *= alpha[i];
+                }
+            wave_lds_sync();
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int tt = 4 * ii + tg;
+                float vv[8];
+                vr[ii].get(vv);
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const float p = zb[tt * G + i];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) vacc[i][c] = fmaf(p, vv[c], vacc[i][c]);
+                }
+            }
+            wave_lds_sync();
+        }
     }
-    write_partial<ST, G>(A, b, g, s, S);
+    // partials: m, l and acc[h][c]; acc sums over the four token groups
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float v = vacc[i][c];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            vacc[i][c] = v;
+        }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const float li = st.head_sum(i);
+        const float mi = st.head_max(i);
+        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + s) * PART;
+        if (lane == 0) {
+            pp[0] = mi;
+            pp[1] = li;
+        }
+        if (tg == 0) {
+            float2 *d2 = reinterpret_cast<float2 *>(pp + 2 + ch * 8);  // partials are 8-byte aligned
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) d2[c / 2] = make_float2(vacc[i][c], vacc[i][c + 1]);
+        }
+    }
 }
 
 // packed split s of S_p: an equal share (by bytes) of the unit's union records
@@ -921,8 +1021,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         if (s < A.S_p) attend_packed_split<ST, G, QA, QB>(A, bl, b, g, s, qsh, lds[wave], lists[wave]);
     } else {
         const int s = ((int)blockIdx.x - px) * 4 + wave;
-        if (s < A.S_d) attend_dense_split<ST, G>(A, bl, b, g, s, qsh);
+        if (s < A.S_d) attend_dense_split<ST, G>(A, bl, b, g, s, qsh, lds[wave].zb[0]);
     }
+}
+
+template <typename ST, int G>
+__global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
+    const int z = (int)blockIdx.z;
+    const int bl = z / A.npk, j = z % A.npk;
+    score_tile<ST, G>(A, bl, j, (int)blockIdx.y, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
 }
 
 // ----------------------------------------------------------------------------
@@ -1047,7 +1154,6 @@ hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s) {
 }
 
 hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hipStream_t s) {
-    if (a.npk == 0 || max_tiles <= 0) return hipSuccess;
     const dim3 grid((unsigned)((max_tiles + 3) / 4), (unsigned)a.hkv, (unsigned)(a.n_req * a.npk));
 #define MKV_SCORE(ST, GG) hipLaunchKernelGGL((k_score<ST, GG>), grid, dim3(256), 0, s, a)
     if (dtype == MKV_BF16) {

@@ -380,7 +380,8 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
             Wmax = std::max(Wmax, W);
             Dmax = std::max(Dmax, Dn);
         }
-        // splits of about 64 KB of packed reads and 128 KB of dense reads each
+        // splits of about 64 KB of packed and 128 KB of dense reads each (the
+        // dense splits then share one round of waves with the packed ones)
         A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
         A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 64 * 1024)));
         // select: up to 16 waves, 4 / 16 / 64 keys per lane

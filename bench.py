@@ -128,27 +128,34 @@ def counter_traffic(kernel_key: str):
     k = c.get("kernels", {}).get(kernel_key)
     if not k:
         return None
-    return (k["fetch_kib"] + k["write_kib"]) * 1024.0 * c.get("copy_factor", 1.0)
+    return (k["fetch_kib"] * c["fetch_factor"] + k["write_kib"] * c["write_factor"]) * 1024.0
 
 
-def cpu_baseline(w, K, V, R, T0, steps, n_units, nthreads):
+def cpu_baseline(cfg, scale, R, T0, steps, n_units, nthreads):
     """The oracle as it stands, on a bounded sample: n_units (request, KV head)
     units each run `steps` decode steps (append one token, then decode); the
     per-unit step time is scaled to all units of the workload."""
     from oracle import oracle as orc
+    w = workload(cfg, scale, steps + 64)
     G = w["n_q_heads"] // w["n_kv_heads"]
     dt = w["dtype"]
+    d = w["d"]
     to64 = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if dt == "bf16" else \
         (lambda a: a.astype(np.float64))
     units = [(u // w["n_kv_heads"], u % w["n_kv_heads"]) for u in range(n_units)]
+    npdt = np.uint16 if dt == "bf16" else np.float32
     total, n = 0.0, 0
     for b, g in units:
-        Kr = to64(K[b, g, :T0[b] + steps])
-        Vr = to64(V[b, g, :T0[b] + steps])
+        rows = int(T0[b]) + steps
+        Kb = np.empty((rows, d), npdt)
+        Vb = np.empty((rows, d), npdt)
+        synth.gen_kv_into(cfg, b, g, 0, 0, rows, dt, Kb, d)
+        synth.gen_kv_into(cfg, b, g, 1, 0, rows, dt, Vb, d)
+        Kr, Vr = to64(Kb), to64(Vb)
         Rk, Rv = R[b, g, 0].astype(np.float64), R[b, g, 1].astype(np.float64)
         st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]), dt, nthreads=nthreads)
         for s in range(steps):
-            q = synth.gen_q(w["cfg"], 5000 + s, w["batch"], w["n_q_heads"], dt)[b, g * G:(g + 1) * G]
+            q = synth.gen_q(cfg, 5000 + s, w["batch"], w["n_q_heads"], dt)[b, g * G:(g + 1) * G]
             t0 = time.perf_counter()
             st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]) + s + 1, dt, nthreads=nthreads,
                                    state=st)
@@ -173,7 +180,7 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (default 3: 128K context)")
     ap.add_argument("--scale", type=int, default=1, help="divide token counts (1 = full size)")
     ap.add_argument("--cpu-units", type=int, default=4, help="oracle sample size (0 disables)")
-    ap.add_argument("--cpu-steps", type=int, default=10)
+    ap.add_argument("--cpu-steps", type=int, default=600)
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct layer caches visited round-robin (keeps every call cache-cold)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -293,7 +300,7 @@ def main():
     if args.cpu_units > 0:
         nthreads = synth.host_threads()
         log("oracle CPU baseline on %d units x %d steps, %d threads" % (args.cpu_units, args.cpu_steps, nthreads))
-        cpu = cpu_baseline(w, K, V, R, T0, args.cpu_steps, args.cpu_units, nthreads)
+        cpu = cpu_baseline(args.config, args.scale, R, T0, args.cpu_steps, args.cpu_units, nthreads)
         log("oracle: %.3g tokens/s over %.1f s" % (cpu["value"], cpu["seconds"]))
         cpu.pop("seconds")
 

@@ -102,26 +102,6 @@ __global__ __launch_bounds__(STAGE ? 512 : 128) void k_compress(const CompressAr
     const int se = min(E.e, p0 + BT) - p0;
     const size_t unit = (size_t)E.b * A.n_kv + g;
     const float *R = A.rot + (unit * 2 + wave) * D * D;
-    const float (*Rs)[D + 1] = nullptr;
-    if constexpr (STAGE) {
-        __shared__ float Rst[2][D][D + 1];
-        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + unit * 2 * D * D);
-        float4 v[2 * D * D / 4 / 512];
-#pragma unroll
-        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) v[k] = Rg[threadIdx.x + 512 * k];
-#pragma unroll
-        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) {
-            const int i = (int)threadIdx.x + 512 * k;
-            const int m = i / (D * D / 4), c = (i / (D / 4)) % D, j = (i % (D / 4)) * 4;
-            Rst[m][c][j] = v[k].x;
-            Rst[m][c][j + 1] = v[k].y;
-            Rst[m][c][j + 2] = v[k].z;
-            Rst[m][c][j + 3] = v[k].w;
-        }
-        __syncthreads();
-        if (wave >= 2) return;
-        Rs = Rst[wave];
-    }
     const bits_t *xin = reinterpret_cast<const bits_t *>(wave ? A.v_new : A.k_new) + unit * A.n_max * D;
     __shared__ __align__(16) float xs[2][D];
 
@@ -161,11 +141,43 @@ __global__ __launch_bounds__(STAGE ? 512 : 128) void k_compress(const CompressAr
         }
     }
 
+    // the first token's row is loaded before R is staged, so that the two
+    // (and the block keys above) are in flight together
+    bits_t x0 = 0, x1 = 0;
+    if (wave < 2 && sa < se) {
+        const bits_t *xr = xin + (size_t)(E.row0 + (p0 + sa - E.a)) * D;
+        x0 = xr[lane];
+        x1 = xr[lane + 64];
+    }
+    const float (*Rs)[D + 1] = nullptr;
+    if constexpr (STAGE) {
+        __shared__ float Rst[2][D][D + 1];
+        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + unit * 2 * D * D);
+        float4 v[2 * D * D / 4 / 512];
+#pragma unroll
+        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) v[k] = Rg[threadIdx.x + 512 * k];
+#pragma unroll
+        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) {
+            const int i = (int)threadIdx.x + 512 * k;
+            const int m = i / (D * D / 4), c = (i / (D / 4)) % D, j = (i % (D / 4)) * 4;
+            Rst[m][c][j] = v[k].x;
+            Rst[m][c][j + 1] = v[k].y;
+            Rst[m][c][j + 2] = v[k].z;
+            Rst[m][c][j + 3] = v[k].w;
+        }
+        __syncthreads();
+        if (wave >= 2) return;
+        Rs = Rst[wave];
+    }
+
     for (int slot = sa; slot < se; ++slot) {
-        const int row = E.row0 + (p0 + slot - E.a);
-        const bits_t *xr = xin + (size_t)row * D;
-        xs[wave][lane] = bits_to_float<ST>(xr[lane]);
-        xs[wave][lane + 64] = bits_to_float<ST>(xr[lane + 64]);
+        if (slot > sa) {
+            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot - E.a)) * D;
+            x0 = xr[lane];
+            x1 = xr[lane + 64];
+        }
+        xs[wave][lane] = bits_to_float<ST>(x0);
+        xs[wave][lane + 64] = bits_to_float<ST>(x1);
         wave_lds_sync();
         double v0, v1;
         if constexpr (STAGE) rotate_f64_lds(Rs, xs[wave], lane, v0, v1);

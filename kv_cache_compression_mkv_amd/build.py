@@ -18,6 +18,10 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # no packed-fp32 instructions anywhere in the device code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
+# decode works on finite values only (its inputs are finite by the ABI's
+# precondition; infinities appear only as -inf sentinels, still honoured):
+# max/min then need no NaN canonicalisation
+HIP_FILE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fopenmp", "-D__HIP_PLATFORM_AMD__",
               "-I" + os.path.join(ROCM, "include")]
 
@@ -32,7 +36,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(bdir, src + ".o")
-        cmd = [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + HIP_FLAGS + HIP_FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd += ["-save-temps=obj"]
         if verbose:

@@ -22,6 +22,11 @@ namespace mkv {
 namespace {
 
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
+
+// 2^x with the hardware exponential (results below the smallest normal float
+// flush to zero, which softmax weights tolerate: they are at most 2^8 times
+// the running maximum's weight and such tiny ones do not change any sum)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ const DSeg &seg_of(const DecodeArgs &A, int bl, int si) {
@@ -442,10 +447,10 @@ __device__ __forceinline__ void softmax16(float z, bool valid, float *zb, WaveSt
     const float mh = st.m;
     float mnew = mh, a = 1.f;
     if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
-        a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
+        a = (mh == -INFINITY) ? 0.f : fast_exp2(mh - bm);
         mnew = bm;
     }
-    const float p = valid ? exp2f(zz - mnew) : 0.f;
+    const float p = valid ? fast_exp2(zz - mnew) : 0.f;
     if (lane < 16 * G) {
         st.l = st.l * a + p;
         st.m = mnew;
@@ -622,13 +627,13 @@ __device__ __forceinline__ float softmax_step(float z, bool valid, PkState<G> &S
     const float bm = wave_max_quads(z);
     const float mh = S.m[h];
     if (bm != -INFINITY && (mh == -INFINITY || bm > mh + 8.f)) {
-        const float a = (mh == -INFINITY) ? 0.f : exp2f(mh - bm);
+        const float a = (mh == -INFINITY) ? 0.f : fast_exp2(mh - bm);
         S.m[h] = bm;
         S.acc[h][0] *= a;
         S.acc[h][1] *= a;
         S.l[h] *= a;
     }
-    const float p = valid ? exp2f(z - S.m[h]) : 0.f;
+    const float p = valid ? fast_exp2(z - S.m[h]) : 0.f;
     S.l[h] += p;
     return p;
 }
@@ -1069,7 +1074,7 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     }
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
     if (t < MAX_SPLITS) wsc[t] = w;
     {
         const float v = wave_sum(w * l);

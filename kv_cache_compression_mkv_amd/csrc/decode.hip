@@ -199,15 +199,13 @@ __device__ __forceinline__ void xwave_sum3(SelShared &sh, int &ph, int nw, int &
         sh.v[ph][w][2] = c;
     }
     __syncthreads();
-    int x = 0, y = 0, z = 0;
-    if (lane < nw) {
-        x = sh.v[ph][lane][0];
-        y = sh.v[ph][lane][1];
-        z = sh.v[ph][lane][2];
-    }
-    a = lane_int(row_sum16_i(x), 0);
-    b = lane_int(row_sum16_i(y), 0);
-    c = lane_int(row_sum16_i(z), 0);
+    // DPP row i (lanes 16 i .. 16 i + 15) sums value i over the waves
+    const int wi = lane & 15, vi = lane >> 4;
+    const int x = (vi < 3 && wi < nw) ? sh.v[ph][wi][vi] : 0;
+    const int t = row_sum16_i(x);
+    a = lane_int(t, 0);
+    b = lane_int(t, 16);
+    c = lane_int(t, 32);
     ph ^= 1;
 }
 
@@ -292,26 +290,29 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
         const uint32_t diff = kmn ^ kmx;
         int bit = diff ? 31 - __clz(diff) : -1;
         thr = diff ? (kmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u))) : kmx;
-        while (bit >= 0) {  // invariant: at least k keys are >= thr
+        // Invariant: at least k keys are >= thr. Once exactly k are (cnt == k)
+        // they are the selection, and the remaining bits cannot change it.
+        int cnt = -1;
+        while (bit >= 0 && cnt != k) {
             if (bit >= 1) {
                 const uint32_t c1 = thr | (1u << (bit - 1)), c2 = thr | (2u << (bit - 1)),
                                c3 = thr | (3u << (bit - 1));
                 int n1 = count_ge<KPT>(key, c1), n2 = count_ge<KPT>(key, c2), n3 = count_ge<KPT>(key, c3);
                 xwave_sum3(sh, ph, nw, n1, n2, n3);
-                if (n3 >= k) thr = c3;
-                else if (n2 >= k) thr = c2;
-                else if (n1 >= k) thr = c1;
+                if (n3 >= k) { thr = c3; cnt = n3; }
+                else if (n2 >= k) { thr = c2; cnt = n2; }
+                else if (n1 >= k) { thr = c1; cnt = n1; }
                 bit -= 2;
             } else {
                 int n1 = count_ge<KPT>(key, thr | 1u), n2 = 0, n3 = 0;
                 xwave_sum3(sh, ph, nw, n1, n2, n3);
-                if (n1 >= k) thr |= 1u;
+                if (n1 >= k) { thr |= 1u; cnt = n1; }
                 bit -= 1;
             }
         }
     }
-    // thr > 0 is the k-th largest key: keep every larger key and the first
-    // (k - #larger) equal keys in block order
+    // thr > 0 is the k-th largest key, or has exactly k keys at or above it:
+    // keep every larger key and the first (k - #larger) equal keys in block order
     int ngt = 0, neq = 0, unused = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {

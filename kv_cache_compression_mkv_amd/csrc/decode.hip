@@ -356,7 +356,7 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
                 const int blk = (w * KPT + i) * 64 + lane;
                 sl[pos] = blk;
                 if (so) so[coloff + pos] = blk;
-                atomicOr(mk + blk, 1u << hi);
+                reinterpret_cast<uint8_t *>(mk + blk)[hi] = 1;  // byte hi: head hi chose it
             }
         }
         base += popc64(m);
@@ -984,7 +984,9 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
                 const int rank = (int)(it / G), hl = (int)(it % G);
                 blk = sel[(size_t)hl * kc + rank];
                 if ((unsigned)blk < (unsigned)Sg.nb) {
-                    hm = (int)mk[blk];
+                    // byte i of the word is 1 if head i chose the block
+                    const uint32_t bytes = mk[blk];
+                    hm = (int)((bytes | (bytes >> 7) | (bytes >> 14) | (bytes >> 21)) & 0xFu);
                     keep = !(hm & ((1 << hl) - 1));
                 }
             }

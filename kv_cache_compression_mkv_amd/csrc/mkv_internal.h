@@ -73,7 +73,7 @@ struct DecodeArgs {
     float *qa;        // [B][Hq][D] q' * log2(e) / sqrt(D)
     float *qs;        // [B][Hkv][D][2G] (max(q',0), min(q',0)) / sqrt(D)
     float *scores;    // per packed j: [B][Hq][nbcap_j]
-    uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j]
+    uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j], byte i = 1 if head i of the group chose the block
     int32_t *sel;     // per packed j: [B][Hq][kcap_j]
     float *part;      // [B][Hq][MAX_SPLITS][PART]: dense splits, then packed splits
     int64_t sel_cols;

@@ -63,16 +63,31 @@ __device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const f
 
 // Keep the r channels of largest magnitude (ties to the lower channel).
 // Keys are the magnitude bit patterns (63 bits; order = magnitude order).
-// The r-th largest key is found bit by bit with ballot counts.
+// The threshold is found bit by bit with ballot counts, from the leading bit
+// of the largest key down (higher bits are zero in every key). It keeps the
+// invariant that at least r keys are >= thr; once exactly r are (cnt == r)
+// they are the kept set and lower bits cannot change it, so the search stops.
 __device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane, bool &keep0,
                                           bool &keep1) {
     const uint64_t k0 = (uint64_t)__double_as_longlong(v0) & 0x7FFFFFFFFFFFFFFFull;
     const uint64_t k1 = (uint64_t)__double_as_longlong(v1) & 0x7FFFFFFFFFFFFFFFull;
+    // wave max of the keys' high words (DPP row max, then the four rows)
+    uint32_t hm = (uint32_t)(max(k0, k1) >> 32);
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x121, 0xf, 0xf, false));
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x122, 0xf, 0xf, false));
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x124, 0xf, 0xf, false));
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x128, 0xf, 0xf, false));
+    hm = max(max((uint32_t)__builtin_amdgcn_readlane((int)hm, 0), (uint32_t)__builtin_amdgcn_readlane((int)hm, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)hm, 32), (uint32_t)__builtin_amdgcn_readlane((int)hm, 48)));
     uint64_t thr = 0;
-    for (int bit = 62; bit >= 0; --bit) {
+    int cnt = 2 * 64;  // keys >= thr
+    for (int bit = hm ? 63 - __clz(hm) : 31; bit >= 0 && cnt > r; --bit) {
         const uint64_t cand = thr | (1ull << bit);
-        const int cnt = popc64(ballot(k0 >= cand)) + popc64(ballot(k1 >= cand));
-        if (cnt >= r) thr = cand;
+        const int c = popc64(ballot(k0 >= cand)) + popc64(ballot(k1 >= cand));
+        if (c >= r) {
+            thr = cand;
+            cnt = c;
+        }
     }
     const bool gt0 = k0 > thr, gt1 = k1 > thr;
     const int need = r - popc64(ballot(gt0)) - popc64(ballot(gt1));

@@ -779,13 +779,14 @@ __device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
 }
 
+// a split's partial (m, l, acc[128]) per head into dst [G][PART] (LDS)
 template <typename ST, int G>
-__device__ __forceinline__ void write_partial(const DecodeArgs &A, int b, int g, int split, const PkState<G> &S) {
+__device__ __forceinline__ void write_partial(float *dst, const PkState<G> &S) {
     const int lane = lane_id();
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const float li = wave_sum_all(S.l[i]) * 0.25f;
-        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + split) * PART;
+        float *pp = dst + i * PART;
         if (lane == 0) {
             pp[0] = S.m[i];
             pp[1] = li;
@@ -811,8 +812,8 @@ __device__ __forceinline__ void init_state(PkState<G> &S) {
 // lanes are head-major (lane h * 16 + t); the V sums stay in registers until
 // the end, where the four token groups add up.
 template <typename ST, int G>
-__device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, int b, int g, int s,
-                                                   const float (*qsh)[2 * D], float *zb) {
+__device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, int g, int s,
+                                                   const float (*qsh)[2 * D], float *zb, float *dst) {
     const int lane = lane_id();
     const int tg = lane >> 4, ch = lane & 15;
     float vacc[G][8];
@@ -926,7 +927,7 @@ __device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, 
     for (int i = 0; i < G; ++i) {
         const float li = st.head_sum(i);
         const float mi = st.head_max(i);
-        float *pp = A.part + (((size_t)b * A.hq + g * G + i) * MAX_SPLITS + s) * PART;
+        float *pp = dst + i * PART;
         if (lane == 0) {
             pp[0] = mi;
             pp[1] = li;
@@ -942,7 +943,8 @@ __device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, 
 // packed split s of S_p: an equal share (by bytes) of the unit's union records
 template <typename ST, int G, int QA, int QB>
 __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl, int b, int g, int s,
-                                                    const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list) {
+                                                    const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list,
+                                                    float *dst) {
     constexpr int sb = ST::bytes;
     const int lane = lane_id();
     for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
@@ -1003,7 +1005,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
             wave_lds_sync();
         }
     }
-    write_partial<ST, G>(A, b, g, A.S_d + s, S);
+    write_partial<ST, G>(dst, S);
 }
 
 // QA < QB: packed segments with ceil(r / 4) <= QA run the QA code, the others QB
@@ -1024,12 +1026,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         qsh[h][c] = c < D ? A.qa[((size_t)b * A.hq + g * G + h) * D + c] : 0.f;
     }
     __syncthreads();
-    if ((int)blockIdx.x < px) {
-        const int s = (int)blockIdx.x * 4 + wave;
-        if (s < A.S_p) attend_packed_split<ST, G, QA, QB>(A, bl, b, g, s, qsh, lds[wave], lists[wave]);
-    } else {
-        const int s = ((int)blockIdx.x - px) * 4 + wave;
-        if (s < A.S_d) attend_dense_split<ST, G>(A, bl, b, g, s, qsh, lds[wave].zb[0]);
+    // each wave's split partial goes to its own LDS area once the wave is done with it
+    float *mine = reinterpret_cast<float *>(&lds[wave]);
+    static_assert(sizeof(PkLds<ST, G>) >= G * PART * sizeof(float), "partial fits the wave's LDS");
+    const bool packed = (int)blockIdx.x < px;
+    const int xs = packed ? (int)blockIdx.x : (int)blockIdx.x - px;  // workgroup index within its role
+    const int S = packed ? A.S_p : A.S_d;
+    const int s = xs * 4 + wave;
+    if (s < S) {
+        if (packed) attend_packed_split<ST, G, QA, QB>(A, bl, b, g, s, qsh, lds[wave], lists[wave], mine);
+        else attend_dense_split<ST, G>(A, bl, g, s, qsh, lds[wave].zb[0], mine);
+    }
+    __syncthreads();
+    // Log-sum-exp combine of the workgroup's splits (in wave order) into one
+    // partial per head: wave h takes head h. Dense workgroups' partials come
+    // first, then the packed ones'.
+    const int nvalid = min(4, S - 4 * xs);
+    const int P = packed ? (A.S_d + 3) / 4 + xs : xs;
+    const int lane = lane_id();
+    for (int h = wave; h < G; h += 4) {
+        float mv[4];
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            mv[v] = v < nvalid ? reinterpret_cast<const float *>(&lds[v])[h * PART] : -INFINITY;
+            M = fmaxf(M, mv[v]);
+        }
+        float L = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (v >= nvalid) break;
+            const float *src = reinterpret_cast<const float *>(&lds[v]) + h * PART;
+            const float w = (mv[v] == -INFINITY) ? 0.f : fast_exp2(mv[v] - M);
+            const float2 x = reinterpret_cast<const float2 *>(src + 2)[lane];
+            L = fmaf(w, src[1], L);
+            a0 = fmaf(w, x.x, a0);
+            a1 = fmaf(w, x.y, a1);
+        }
+        float *pp = A.part + (((size_t)b * A.hq + g * G + h) * MAX_SPLITS + P) * PART;
+        if (lane == 0) {
+            pp[0] = M;
+            pp[1] = L;
+        }
+        reinterpret_cast<float2 *>(pp + 2)[lane] = make_float2(a0, a1);
     }
 }
 
@@ -1042,7 +1081,8 @@ __global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
 
 // ----------------------------------------------------------------------------
 // merge: one workgroup per (request, query head): log-sum-exp merge of the
-// head's dense and packed splits in split order, then out_j = sum_c R_v[c][j] o_c.
+// head's partials (one per attend workgroup: dense ones, then packed ones) in
+// order, then out_j = sum_c R_v[c][j] o_c.
 // Thread (cc, j4) = (t / 32, t % 32) loads rows 16 cc .. 16 cc + 15 of R_v at
 // columns 4 j4 .. 4 j4 + 3 first, so those loads overlap the merge.
 // ----------------------------------------------------------------------------
@@ -1052,7 +1092,7 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     const int bl = (int)blockIdx.y, h = (int)blockIdx.x;
     const int b = A.b0 + bl, g = h / G;
     const int t = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x >> 6);
-    const int Stot = A.S_d + A.S_p;
+    const int Stot = (A.S_d + 3) / 4 + (A.S_p + 3) / 4;  // one partial per attend workgroup
     const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_SPLITS * PART;
     __shared__ float wsc[MAX_SPLITS];
     __shared__ float red[2][4];

@@ -75,7 +75,7 @@ struct DecodeArgs {
     float *scores;    // per packed j: [B][Hq][nbcap_j]
     uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j], byte i = 1 if head i of the group chose the block
     int32_t *sel;     // per packed j: [B][Hq][kcap_j]
-    float *part;      // [B][Hq][MAX_SPLITS][PART]: dense splits, then packed splits
+    float *part;      // [B][Hq][MAX_SPLITS][PART]: one partial per attend workgroup (of 4 splits), dense first
     int64_t sel_cols;
     int64_t sc_off[MKV_MAX_SEGMENTS];
     int64_t mk_off[MKV_MAX_SEGMENTS];

@@ -395,10 +395,13 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // Every split carries one online softmax state per query head; merge combines
 // them.
 //
-// Packed items: item (rank, head) of a packed segment is the rank-th block
-// that head selected; an item whose block a lower head of the group also
-// selected is dropped, so every union block is read once and serves each head
-// that chose it. Items are resolved 64 at a time into a compact list.
+// Packed records: in union mode a workgroup takes an exact byte share of the
+// unit's union (blocks some head of the group selected, with the mask of the
+// heads that did) and splits it evenly over its waves; otherwise item (rank,
+// head) of a packed segment is the rank-th block that head selected, an item
+// whose block a lower head of the group also selected is dropped, and items
+// are resolved 64 at a time into a compact list. Either way every union block
+// is read once and serves each head that chose it.
 //
 // Dense blocks and packed records both stream through a two-deep register
 // pipeline (the next one's loads are in flight while one is computed; a
@@ -1008,6 +1011,169 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
     write_partial<ST, G>(dst, S);
 }
 
+// ---- union mode: exact byte-balanced packed splits -------------------------
+// For units whose (at most UNION_MAX_SEGS) packed segments hold at most
+// UNION_SEG_BLOCKS blocks each, a packed workgroup takes an exact
+// byte-weighted share of the unit's union records (blocks with a non-zero head
+// mask; weight = record bytes + 256) and gives each of its waves an equal
+// quarter of it. The workgroup reads the union masks itself: wave v, lane l
+// holds blocks 1024 v + 256 m + 4 l + k (m, k < 4; four coalesced 16-byte
+// loads per segment), and union records are ranked in that order, segment by
+// segment, by one workgroup prefix sum.
+constexpr int UNION_SEG_BLOCKS = 4096;
+constexpr int UNION_MAX_SEGS = 4;
+constexpr int UNION_CAP = 256;  // union entries of one workgroup (bounded on the host)
+
+struct UnionLds {
+    uint32_t ent[UNION_CAP];  // block | head mask << 16, segment by segment
+    uint64_t red[4];
+};
+
+__device__ __forceinline__ int union_block(int i) {
+    return 1024 * (int)(threadIdx.x >> 6) + 256 * (i >> 2) + 4 * lane_id() + (i & 3);
+}
+
+// this thread's 16 union mask words of packed segment j of unit (b, g), as
+// head masks (0 past the stored blocks)
+__device__ __forceinline__ void union_words(const DecodeArgs &A, int j, int b, int g, int nb, uint32_t (&w)[16]) {
+    const uint32_t *mk = A.mask + A.mk_off[j] + ((size_t)b * A.hkv + g) * A.nbcap[j];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int l0 = union_block(4 * m);
+        uint32_t x[4];
+        if (l0 + 3 < nb) {
+            const W4 v = *reinterpret_cast<const W4 *>(mk + l0);  // 4-byte aligned
+            x[0] = v.x;
+            x[1] = v.y;
+            x[2] = v.z;
+            x[3] = v.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = l0 + k < nb ? mk[l0 + k] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[4 * m + k] = (x[k] | (x[k] >> 7) | (x[k] >> 14) | (x[k] >> 21)) & 0xFu;
+    }
+}
+
+// workgroup exclusive prefix of v (four 16-bit counts) in thread order, and
+// the workgroup total
+__device__ __forceinline__ uint64_t wg_excl64(uint64_t v, UnionLds &U, uint64_t &total) {
+    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
+    uint64_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) U.red[wave] = x;
+    __syncthreads();
+    uint64_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint64_t t = U.red[w];
+        if (w < wave) before += t;
+        total += t;
+    }
+    return before + x - v;
+}
+
+// first entry of a segment whose weighted start (Wb + e w) is >= pos
+__device__ __forceinline__ int64_t union_entry(int64_t pos, int64_t Wb, int64_t w, int64_t n) {
+    int64_t e = pos - Wb;
+    e = e <= 0 ? 0 : (e + w - 1) / w;
+    return min(e, n);
+}
+
+template <typename ST, int G, int QA, int QB>
+__device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl, int b, int g, int xs, int wave,
+                                                    const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list,
+                                                    float *dst, UnionLds &U) {
+    constexpr int sb = ST::bytes;
+    const int lane = lane_id();
+    const int npk = A.npk;
+    uint32_t w[UNION_MAX_SEGS][16];
+#pragma unroll
+    for (int j = 0; j < UNION_MAX_SEGS; ++j)
+        if (j < npk) union_words(A, j, b, g, seg_of(A, bl, A.pseg[j]).nb, w[j]);
+    for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
+    PkState<G> S;
+    init_state<G>(S);
+    // union records of each segment: this thread's rank base and the totals
+    uint64_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < UNION_MAX_SEGS; ++j) {
+        if (j >= npk) break;
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c += w[j][i] != 0u;
+        cnt |= (uint64_t)c << (16 * j);
+    }
+    uint64_t tot;
+    const uint64_t pre = wg_excl64(cnt, U, tot);
+    auto count = [&](int j) { return (int64_t)((tot >> (16 * j)) & 0xFFFFu); };
+    int64_t W = 0;
+    for (int j = 0; j < npk; ++j) W += count(j) * packed_weight(seg_of(A, bl, A.pseg[j]).r, sb, 1);
+    const int P = A.S_p / 4;
+    const int64_t wlo = W * xs / P, whi = W * (xs + 1) / P;
+    const int64_t vlo = wlo + (whi - wlo) * wave / 4, vhi = wlo + (whi - wlo) * (wave + 1) / 4;
+    // the workgroup's entries into LDS, segment by segment
+    {
+        int64_t Wb = 0;
+        int off = 0;
+#pragma unroll
+        for (int j = 0; j < UNION_MAX_SEGS; ++j) {
+            if (j >= npk) break;
+            const int64_t wj = packed_weight(seg_of(A, bl, A.pseg[j]).r, sb, 1), nj = count(j);
+            const int e0 = (int)union_entry(wlo, Wb, wj, nj), e1 = (int)union_entry(whi, Wb, wj, nj);
+            Wb += nj * wj;
+            int u = (int)((pre >> (16 * j)) & 0xFFFFu);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (w[j][i] != 0u) {
+                    const int at = off + u - e0;
+                    if (u >= e0 && u < e1 && at < UNION_CAP) U.ent[at] = (uint32_t)union_block(i) | (w[j][i] << 16);
+                    ++u;
+                }
+            }
+            off += e1 - e0;
+        }
+    }
+    __syncthreads();
+    // this wave's quarter, 64 entries at a time
+    int64_t Wb = 0;
+    int off = 0;
+    for (int j = 0; j < npk; ++j) {
+        const DSeg &Sg = seg_of(A, bl, A.pseg[j]);
+        const int r = Sg.r;
+        const int64_t wj = packed_weight(r, sb, 1), nj = count(j);
+        const int e0 = (int)union_entry(wlo, Wb, wj, nj), e1 = (int)union_entry(whi, Wb, wj, nj);
+        const int v0 = (int)union_entry(vlo, Wb, wj, nj), v1 = (int)union_entry(vhi, Wb, wj, nj);
+        Wb += nj * wj;
+        const size_t rec = (size_t)BT * r * 2 * (sb + 1);
+        const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
+        for (int base = v0; base < v1; base += 64) {
+            // (the host bounds the workgroup's entries by UNION_CAP; the clamp
+            // only keeps reads inside the table)
+            const int n = min(min(64, v1 - base), UNION_CAP - (off + base - e0));
+            if (n <= 0) break;
+            if (lane < n) {
+                const uint32_t e = U.ent[off + base - e0 + lane];
+                list[lane] = make_int2((int)(e & 0xFFFFu), (int)(e >> 16));
+            }
+            wave_lds_sync();
+            if (((r + 3) >> 2) <= QA)
+                pk_run<ST, G, QA>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+            else
+                pk_run<ST, G, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+            wave_lds_sync();
+        }
+        off += e1 - e0;
+    }
+    write_partial<ST, G>(dst, S);
+}
+
 // QA < QB: packed segments with ceil(r / 4) <= QA run the QA code, the others QB
 template <typename ST, int G, int QA, int QB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_attend(const DecodeArgs A) {
@@ -1033,7 +1199,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const int xs = packed ? (int)blockIdx.x : (int)blockIdx.x - px;  // workgroup index within its role
     const int S = packed ? A.S_p : A.S_d;
     const int s = xs * 4 + wave;
-    if (s < S) {
+    if (packed && A.union_mode) {
+        __shared__ UnionLds U;
+        attend_packed_union<ST, G, QA, QB>(A, bl, b, g, xs, wave, qsh, lds[wave], lists[wave], mine, U);
+    } else if (s < S) {
         if (packed) attend_packed_split<ST, G, QA, QB>(A, bl, b, g, s, qsh, lds[wave], lists[wave], mine);
         else attend_dense_split<ST, G>(A, bl, g, s, qsh, lds[wave].zb[0], mine);
     }

@@ -384,6 +384,33 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
         // dense splits then share one round of waves with the packed ones)
         A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
         A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 64 * 1024)));
+        // Union mode (exact byte-balanced packed workgroups) when every packed
+        // segment has at most 4096 blocks and a workgroup's share of the union
+        // provably fits its 256-entry table: a share holds at most
+        // U w_max / (P w_min) + npk entries, U = max over requests of the sum
+        // over packed segments of min(G k, nb).
+        A.union_mode = 0;
+        if (m.npk > 0 && m.npk <= 4 && max_nb <= 4096) {
+            const int32_t sp4 = (int32_t)std::min<int64_t>(((int64_t)A.S_p + 3) / 4 * 4, (MAX_SPLITS - A.S_d) / 4 * 4);
+            int64_t U = 0, wmin = INT64_MAX, wmax = 0;
+            for (int i = 0; i < n_req; ++i) {
+                int64_t u = 0;
+                for (int j = 0; j < c->n_segments; ++j) {
+                    const DSeg &D_ = A.seg[i * c->n_segments + j];
+                    if (D_.kind != MKV_SEG_PACKED) continue;
+                    u += std::min<int64_t>((int64_t)G * D_.k, D_.nb);
+                    const int64_t w = (int64_t)BT * D_.r * 2 * (sb + 1) + 256;
+                    wmin = std::min(wmin, w);
+                    wmax = std::max(wmax, w);
+                }
+                U = std::max(U, u);
+            }
+            const int64_t P = sp4 / 4;
+            if (P >= 1 && ceil_div(U * wmax, P * wmin) + m.npk <= 256) {
+                A.union_mode = 1;
+                A.S_p = sp4;
+            }
+        }
         // select: up to 16 waves, 4 / 16 / 64 keys per lane
         const int kpt = max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
         A.sel_kpt = kpt;

@@ -88,6 +88,7 @@ struct DecodeArgs {
     int32_t S_p;       // packed attention splits per unit (>= 1), S_d + S_p <= MAX_SPLITS
     int32_t sel_kpt;   // keys per lane in select
     int32_t sel_waves; // waves per select workgroup
+    int32_t union_mode; // packed workgroups take exact byte shares of the union (S_p a multiple of 4)
 };
 
 // ---- launchers (defined in the .hip files) --------------------------------

@@ -1033,8 +1033,8 @@ __device__ __forceinline__ int union_block(int i) {
     return 1024 * (int)(threadIdx.x >> 6) + 256 * (i >> 2) + 4 * lane_id() + (i & 3);
 }
 
-// this thread's 16 union mask words of packed segment j of unit (b, g), as
-// head masks (0 past the stored blocks)
+// this thread's 16 union mask words of packed segment j of unit (b, g) (0
+// past the stored blocks; byte h is 1 if head h chose the block)
 __device__ __forceinline__ void union_words(const DecodeArgs &A, int j, int b, int g, int nb, uint32_t (&w)[16]) {
     const uint32_t *mk = A.mask + A.mk_off[j] + ((size_t)b * A.hkv + g) * A.nbcap[j];
 #pragma unroll
@@ -1052,7 +1052,7 @@ __device__ __forceinline__ void union_words(const DecodeArgs &A, int j, int b, i
             for (int k = 0; k < 4; ++k) x[k] = l0 + k < nb ? mk[l0 + k] : 0u;
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w[4 * m + k] = (x[k] | (x[k] >> 7) | (x[k] >> 14) | (x[k] >> 21)) & 0xFu;
+        for (int k = 0; k < 4; ++k) w[4 * m + k] = x[k];
     }
 }
 
@@ -1080,12 +1080,13 @@ __device__ __forceinline__ uint64_t wg_excl64(uint64_t v, UnionLds &U, uint64_t 
 }
 
 // first entry of a segment whose weighted start (Wb + e w) is >= pos
-__device__ __forceinline__ int64_t union_entry(int64_t pos, int64_t Wb, int64_t w, int64_t n) {
-    int64_t e = pos - Wb;
-    e = e <= 0 ? 0 : (e + w - 1) / w;
+__device__ __forceinline__ int union_entry(uint32_t pos, uint32_t Wb, uint32_t w, int n) {
+    const int e = pos <= Wb ? 0 : (int)((pos - Wb + w - 1) / w);
     return min(e, n);
 }
 
+// Weighted positions stay below 2^32: at most 4 segments x 4096 records x
+// (16 r 2 (s + 1) + 256 <= 20736) bytes.
 template <typename ST, int G, int QA, int QB>
 __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl, int b, int g, int xs, int wave,
                                                     const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list,
@@ -1093,11 +1094,25 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
     constexpr int sb = ST::bytes;
     const int lane = lane_id();
     const int npk = A.npk;
+    // per packed segment: stored blocks, kept elements and record weight
+    int nbj[UNION_MAX_SEGS], rj[UNION_MAX_SEGS];
+    uint32_t wj[UNION_MAX_SEGS];
+#pragma unroll
+    for (int j = 0; j < UNION_MAX_SEGS; ++j) {
+        const DSeg &Sg = seg_of(A, bl, A.pseg[min(j, npk - 1)]);
+        nbj[j] = j < npk ? Sg.nb : 0;
+        rj[j] = Sg.r;
+        wj[j] = (uint32_t)(BT * Sg.r * 2 * (sb + 1) + 256);
+    }
     uint32_t w[UNION_MAX_SEGS][16];
 #pragma unroll
     for (int j = 0; j < UNION_MAX_SEGS; ++j)
-        if (j < npk) union_words(A, j, b, g, seg_of(A, bl, A.pseg[j]).nb, w[j]);
-    for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
+        if (j < npk) union_words(A, j, b, g, nbj[j], w[j]);
+    {
+        uint4 *v4 = reinterpret_cast<uint4 *>(&L.vt[0][0]);  // rows 0..15 of the tile
+#pragma unroll
+        for (int i = 0; i < BT * D * sb / 16 / 64; ++i) v4[lane + 64 * i] = make_uint4(0, 0, 0, 0);
+    }
     PkState<G> S;
     init_state<G>(S);
     // union records of each segment: this thread's rank base and the totals
@@ -1112,54 +1127,70 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
     }
     uint64_t tot;
     const uint64_t pre = wg_excl64(cnt, U, tot);
-    auto count = [&](int j) { return (int64_t)((tot >> (16 * j)) & 0xFFFFu); };
-    int64_t W = 0;
-    for (int j = 0; j < npk; ++j) W += count(j) * packed_weight(seg_of(A, bl, A.pseg[j]).r, sb, 1);
-    const int P = A.S_p / 4;
-    const int64_t wlo = W * xs / P, whi = W * (xs + 1) / P;
-    const int64_t vlo = wlo + (whi - wlo) * wave / 4, vhi = wlo + (whi - wlo) * (wave + 1) / 4;
-    // the workgroup's entries into LDS, segment by segment
+    int nj[UNION_MAX_SEGS];
+    uint32_t W = 0;
+#pragma unroll
+    for (int j = 0; j < UNION_MAX_SEGS; ++j) {
+        nj[j] = j < npk ? (int)((tot >> (16 * j)) & 0xFFFFu) : 0;
+        W += (uint32_t)nj[j] * wj[j];
+    }
+    const uint32_t P = (uint32_t)A.S_p / 4, q = W / P, rm = W % P;
+    const uint32_t wlo = q * xs + rm * xs / P, whi = q * (xs + 1) + rm * (xs + 1) / P;
+    const uint32_t vlo = wlo + (whi - wlo) * wave / 4, vhi = wlo + (whi - wlo) * (wave + 1) / 4;
+    int e0[UNION_MAX_SEGS], e1[UNION_MAX_SEGS], off[UNION_MAX_SEGS];
     {
-        int64_t Wb = 0;
-        int off = 0;
+        uint32_t Wb = 0;
+        int o = 0;
 #pragma unroll
         for (int j = 0; j < UNION_MAX_SEGS; ++j) {
-            if (j >= npk) break;
-            const int64_t wj = packed_weight(seg_of(A, bl, A.pseg[j]).r, sb, 1), nj = count(j);
-            const int e0 = (int)union_entry(wlo, Wb, wj, nj), e1 = (int)union_entry(whi, Wb, wj, nj);
-            Wb += nj * wj;
-            int u = (int)((pre >> (16 * j)) & 0xFFFFu);
+            e0[j] = union_entry(wlo, Wb, wj[j], nj[j]);
+            e1[j] = union_entry(whi, Wb, wj[j], nj[j]);
+            off[j] = o;
+            o += e1[j] - e0[j];
+            Wb += (uint32_t)nj[j] * wj[j];
+        }
+    }
+    // the workgroup's entries into LDS, segment by segment (only the threads
+    // whose records overlap the workgroup's share)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (w[j][i] != 0u) {
-                    const int at = off + u - e0;
-                    if (u >= e0 && u < e1 && at < UNION_CAP) U.ent[at] = (uint32_t)union_block(i) | (w[j][i] << 16);
-                    ++u;
+    for (int j = 0; j < UNION_MAX_SEGS; ++j) {
+        if (j >= npk) break;
+        int u = (int)((pre >> (16 * j)) & 0xFFFFu);
+        const int c = (int)((cnt >> (16 * j)) & 0xFFFFu);
+        if (u + c <= e0[j] || u >= e1[j]) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t x = w[j][i];
+            if (x != 0u) {
+                const int at = off[j] + u - e0[j];
+                if (u >= e0[j] && u < e1[j] && at < UNION_CAP) {
+                    const uint32_t hm = (x | (x >> 7) | (x >> 14) | (x >> 21)) & 0xFu;  // byte h -> bit h
+                    U.ent[at] = (uint32_t)union_block(i) | (hm << 16);
                 }
+                ++u;
             }
-            off += e1 - e0;
         }
     }
     __syncthreads();
     // this wave's quarter, 64 entries at a time
-    int64_t Wb = 0;
-    int off = 0;
-    for (int j = 0; j < npk; ++j) {
+    uint32_t Wb = 0;
+#pragma unroll
+    for (int j = 0; j < UNION_MAX_SEGS; ++j) {
+        if (j >= npk) break;
+        const int v0 = union_entry(vlo, Wb, wj[j], nj[j]), v1 = union_entry(vhi, Wb, wj[j], nj[j]);
+        Wb += (uint32_t)nj[j] * wj[j];
+        if (v0 >= v1) continue;
         const DSeg &Sg = seg_of(A, bl, A.pseg[j]);
-        const int r = Sg.r;
-        const int64_t wj = packed_weight(r, sb, 1), nj = count(j);
-        const int e0 = (int)union_entry(wlo, Wb, wj, nj), e1 = (int)union_entry(whi, Wb, wj, nj);
-        const int v0 = (int)union_entry(vlo, Wb, wj, nj), v1 = (int)union_entry(vhi, Wb, wj, nj);
-        Wb += nj * wj;
+        const int r = rj[j];
         const size_t rec = (size_t)BT * r * 2 * (sb + 1);
         const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
         for (int base = v0; base < v1; base += 64) {
             // (the host bounds the workgroup's entries by UNION_CAP; the clamp
             // only keeps reads inside the table)
-            const int n = min(min(64, v1 - base), UNION_CAP - (off + base - e0));
+            const int n = min(min(64, v1 - base), UNION_CAP - (off[j] + base - e0[j]));
             if (n <= 0) break;
             if (lane < n) {
-                const uint32_t e = U.ent[off + base - e0 + lane];
+                const uint32_t e = U.ent[off[j] + base - e0[j] + lane];
                 list[lane] = make_int2((int)(e & 0xFFFFu), (int)(e >> 16));
             }
             wave_lds_sync();
@@ -1169,7 +1200,6 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
                 pk_run<ST, G, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
             wave_lds_sync();
         }
-        off += e1 - e0;
     }
     write_partial<ST, G>(dst, S);
 }

@@ -1015,7 +1015,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
 // For units whose (at most UNION_MAX_SEGS) packed segments hold at most
 // UNION_SEG_BLOCKS blocks each, a packed workgroup takes an exact
 // byte-weighted share of the unit's union records (blocks with a non-zero head
-// mask; weight = record bytes + 256) and gives each of its waves an equal
+// mask; weight = record bytes + UNION_RECORD_FIXED) and gives each of its waves an equal
 // quarter of it. The workgroup reads the union masks itself: wave v, lane l
 // holds blocks 1024 v + 256 m + 4 l + k (m, k < 4; four coalesced 16-byte
 // loads per segment), and union records are ranked in that order, segment by
@@ -1085,8 +1085,8 @@ __device__ __forceinline__ int union_entry(uint32_t pos, uint32_t Wb, uint32_t w
     return min(e, n);
 }
 
-// Weighted positions stay below 2^32: at most 4 segments x 4096 records x
-// (16 r 2 (s + 1) + 256 <= 20736) bytes.
+// Weighted positions stay below 2^32 / 4: at most 4 segments x 4096 records
+// x (16 r 2 (s + 1) + UNION_RECORD_FIXED <= 20480 + 16384) bytes.
 template <typename ST, int G, int QA, int QB>
 __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl, int b, int g, int xs, int wave,
                                                     const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list,
@@ -1102,7 +1102,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
         const DSeg &Sg = seg_of(A, bl, A.pseg[min(j, npk - 1)]);
         nbj[j] = j < npk ? Sg.nb : 0;
         rj[j] = Sg.r;
-        wj[j] = (uint32_t)(BT * Sg.r * 2 * (sb + 1) + 256);
+        wj[j] = (uint32_t)(BT * Sg.r * 2 * (sb + 1) + UNION_RECORD_FIXED);
     }
     uint32_t w[UNION_MAX_SEGS][16];
 #pragma unroll

@@ -399,7 +399,7 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
                     const DSeg &D_ = A.seg[i * c->n_segments + j];
                     if (D_.kind != MKV_SEG_PACKED) continue;
                     u += std::min<int64_t>((int64_t)G * D_.k, D_.nb);
-                    const int64_t w = (int64_t)BT * D_.r * 2 * (sb + 1) + 256;
+                    const int64_t w = (int64_t)BT * D_.r * 2 * (sb + 1) + UNION_RECORD_FIXED;
                     wmin = std::min(wmin, w);
                     wmax = std::max(wmax, w);
                 }

@@ -18,6 +18,10 @@ constexpr int TABLE = 64;       // (request, segment) entries per launch
 constexpr int META_TILE = 64;   // blocks per meta tile
 constexpr int MAX_SPLITS = 256; // attention splits per (request, KV head)
 constexpr int PART = D + 2;     // floats per split partial: m, l, acc[D]
+// Union-mode weight of a packed record: its bytes plus a fixed per-record
+// cost (records are latency-bound, so a record costs more than its bytes).
+constexpr int UNION_RECORD_FIXED = 256;
+static_assert(UNION_RECORD_FIXED <= 16384, "union weights of a unit stay below 2^32 / 4");
 
 // ---- compression ----------------------------------------------------------
 struct CompressEntry {

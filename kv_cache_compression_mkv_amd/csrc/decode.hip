@@ -1022,7 +1022,6 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
 // segment, by one workgroup prefix sum.
 constexpr int UNION_SEG_BLOCKS = 4096;
 constexpr int UNION_MAX_SEGS = 4;
-constexpr int UNION_CAP = 256;  // union entries of one workgroup (bounded on the host)
 
 struct UnionLds {
     uint32_t ent[UNION_CAP];  // block | head mask << 16, segment by segment

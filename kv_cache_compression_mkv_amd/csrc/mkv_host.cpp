@@ -380,13 +380,15 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
             Wmax = std::max(Wmax, W);
             Dmax = std::max(Dmax, Dn);
         }
-        // splits of about 64 KB of packed and 128 KB of dense reads each (the
-        // dense splits then share one round of waves with the packed ones)
+        // splits of about 96 KB of packed and 128 KB of dense reads each: both
+        // kinds fit one round of resident waves with room to spare (measured
+        // on the 128K workload: 88-104 KB packed splits are the fastest; 64 KB
+        // fills every wave slot and is slower, 128 KB leaves too few waves)
         A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
-        A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 64 * 1024)));
+        A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 96 * 1024)));
         // Union mode (exact byte-balanced packed workgroups) when every packed
         // segment has at most 4096 blocks and a workgroup's share of the union
-        // provably fits its 256-entry table: a share holds at most
+        // provably fits its UNION_CAP-entry table: a share holds at most
         // U w_max / (P w_min) + npk entries, U = max over requests of the sum
         // over packed segments of min(G k, nb).
         A.union_mode = 0;
@@ -406,7 +408,7 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
                 U = std::max(U, u);
             }
             const int64_t P = sp4 / 4;
-            if (P >= 1 && ceil_div(U * wmax, P * wmin) + m.npk <= 256) {
+            if (P >= 1 && ceil_div(U * wmax, P * wmin) + m.npk <= UNION_CAP) {
                 A.union_mode = 1;
                 A.S_p = sp4;
             }

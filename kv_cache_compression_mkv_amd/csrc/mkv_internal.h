@@ -21,6 +21,7 @@ constexpr int PART = D + 2;     // floats per split partial: m, l, acc[D]
 // Union-mode weight of a packed record: its bytes plus a fixed per-record
 // cost (records are latency-bound, so a record costs more than its bytes).
 constexpr int UNION_RECORD_FIXED = 256;
+constexpr int UNION_CAP = 1024;  // union records one packed workgroup can take
 static_assert(UNION_RECORD_FIXED <= 16384, "union weights of a unit stay below 2^32 / 4");
 
 // ---- compression ----------------------------------------------------------

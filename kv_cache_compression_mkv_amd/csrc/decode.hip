@@ -150,6 +150,8 @@ constexpr int SEL_MAX_WAVES = 16;
 
 struct SelShared {
     int v[2][SEL_MAX_WAVES][3];
+    uint32_t act[64];  // keys still undecided when the search is handed to one wave
+    uint32_t thr;
 };
 
 // DPP row (16-lane) reductions on integers; every lane of the row gets the result
@@ -247,6 +249,55 @@ __device__ __forceinline__ int count_ge(const uint32_t (&key)[KPT], uint32_t can
     return n;
 }
 
+// The nact (1..64) keys in [thr, thr + 2^(bit + 1)) go to LDS; wave 0 then
+// finds, bit by bit with ballots and no barriers, the threshold t in that
+// range with at least need of them >= t (largest such t, or one with exactly
+// need), and every wave gets it back. With cnt_hi keys above the range and
+// need = k - cnt_hi this is the threshold the workgroup-wide search reaches.
+template <int KPT>
+__device__ __forceinline__ uint32_t select_compact(SelShared &sh, int &ph, int nw, const uint32_t (&key)[KPT],
+                                                   uint32_t thr, int bit, int nact, int need) {
+    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
+    const int sft = bit + 1;  // 1..31
+    const uint32_t pre = thr >> sft;
+    int cw = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) cw += popc64(ballot((key[i] >> sft) == pre));
+    int base = xwave_excl(sh, ph, nw, cw);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const bool a = (key[i] >> sft) == pre;
+        const uint64_t m = ballot(a);
+        const int at = base + rank_below(m);
+        if (a && at < 64) sh.act[at] = key[i];  // (never 64 or more: nact <= 64)
+        base += popc64(m);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // inactive lanes hold 0, below every candidate (thr > 0)
+        const uint32_t x = lane < nact ? sh.act[lane] : 0u;
+        uint32_t t = thr;
+        int c = nact, b = bit;
+        while (b >= 0 && c != need) {
+            if (b >= 1) {
+                const uint32_t c1 = t | (1u << (b - 1)), c2 = t | (2u << (b - 1)), c3 = t | (3u << (b - 1));
+                const int n1 = popc64(ballot(x >= c1)), n2 = popc64(ballot(x >= c2)), n3 = popc64(ballot(x >= c3));
+                if (n3 >= need) { t = c3; c = n3; }
+                else if (n2 >= need) { t = c2; c = n2; }
+                else if (n1 >= need) { t = c1; c = n1; }
+                b -= 2;
+            } else {
+                const int n1 = popc64(ballot(x >= (t | 1u)));
+                if (n1 >= need) { t |= 1u; c = n1; }
+                b -= 1;
+            }
+        }
+        if (lane == 0) sh.thr = t;
+    }
+    __syncthreads();
+    return sh.thr;
+}
+
 template <int G, int KPT>
 __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
     const int z = (int)blockIdx.z;
@@ -292,7 +343,9 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
         thr = diff ? (kmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u))) : kmx;
         // Invariant: at least k keys are >= thr. Once exactly k are (cnt == k)
         // they are the selection, and the remaining bits cannot change it.
-        int cnt = -1;
+        // cnt_hi counts the keys at or above the range's upper end
+        // thr + 2^(bit + 1), all of which are kept.
+        int cnt = -1, cnt_hi = 0;
         while (bit >= 0 && cnt != k) {
             if (bit >= 1) {
                 const uint32_t c1 = thr | (1u << (bit - 1)), c2 = thr | (2u << (bit - 1)),
@@ -300,14 +353,21 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
                 int n1 = count_ge<KPT>(key, c1), n2 = count_ge<KPT>(key, c2), n3 = count_ge<KPT>(key, c3);
                 xwave_sum3(sh, ph, nw, n1, n2, n3);
                 if (n3 >= k) { thr = c3; cnt = n3; }
-                else if (n2 >= k) { thr = c2; cnt = n2; }
-                else if (n1 >= k) { thr = c1; cnt = n1; }
+                else if (n2 >= k) { thr = c2; cnt = n2; cnt_hi = n3; }
+                else if (n1 >= k) { thr = c1; cnt = n1; cnt_hi = n2; }
+                else cnt_hi = n1;
                 bit -= 2;
             } else {
                 int n1 = count_ge<KPT>(key, thr | 1u), n2 = 0, n3 = 0;
                 xwave_sum3(sh, ph, nw, n1, n2, n3);
                 if (n1 >= k) { thr |= 1u; cnt = n1; }
+                else cnt_hi = n1;
                 bit -= 1;
+            }
+            // at most 64 keys left undecided: one wave finishes the search
+            if (nw > 1 && bit >= 0 && cnt > k && cnt - cnt_hi <= 64) {
+                thr = select_compact<KPT>(sh, ph, nw, key, thr, bit, cnt - cnt_hi, k - cnt_hi);
+                break;
             }
         }
     }

@@ -104,6 +104,10 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // ---- wave64 primitives ------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
+// number of set bits of m at lanes below this one (mbcnt: no 64-bit mask held)
+__device__ __forceinline__ int rank_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 

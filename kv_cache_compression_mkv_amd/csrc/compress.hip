@@ -10,8 +10,8 @@
 // vectors up to date (the Quest-style block keys of the reading notes' Quest
 // paragraph and the paper's section 5.2).
 //
-// One workgroup of two waves handles one block of one (request, segment, KV
-// head): wave 0 the keys, wave 1 the values. Lane l owns channels l and l+64,
+// One wave per matrix handles one block of one (request, segment, KV head):
+// the keys, and (in the same or another workgroup) the values. Lane l owns channels l and l+64,
 // so the top-r selection is a wave-wide radix search with ballots and the
 // packing order falls out of a ballot prefix count.
 #include "device_util.hpp"
@@ -99,18 +99,23 @@ __device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane,
     keep1 = gt1 || ((k1 == thr) && rank1 < need);
 }
 
-// STAGE (appends of a few tokens): 512 threads first copy R_k and R_v into
-// LDS with one round of coalesced 16-byte loads, then waves 0 and 1 compute
-// from LDS; without it (bulk appends) each lane reads its R rows, which the
-// 16 tokens of the block reuse through the caches.
+// STAGE (appends of a few tokens): one workgroup per (block, matrix); its 256
+// threads first copy R_k or R_v into LDS with one round of coalesced 16-byte
+// loads, then wave 0 computes from LDS; the K and V workgroups run side by
+// side. Without it (bulk appends) one workgroup per block, each lane reading
+// its R rows, which the 16 tokens of the block reuse through the caches.
 template <typename ST, bool STAGE>
-__global__ __launch_bounds__(STAGE ? 512 : 128) void k_compress(const CompressArgs A) {
+__global__ __launch_bounds__(STAGE ? 256 : 128) void k_compress(const CompressArgs A) {
     using bits_t = typename ST::bits_t;
     const CompressEntry &E = A.ent[blockIdx.z];
-    if ((int)blockIdx.x >= E.nblk) return;
-    const int blk = E.blk0 + (int)blockIdx.x;
+    // STAGE: workgroup x = 2 block + matrix (0: K, 1: V), wave 0 computes;
+    // otherwise workgroup x = block, wave 0 the keys and wave 1 the values
+    const int bx = STAGE ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
+    if (bx >= E.nblk) return;
+    const int blk = E.blk0 + bx;
     const int g = (int)blockIdx.y;
-    const int wave = (int)(threadIdx.x >> 6);  // 0: K, 1: V
+    const int wave = STAGE ? (int)(blockIdx.x & 1) + 2 * (int)(threadIdx.x >> 6)
+                           : (int)(threadIdx.x >> 6);  // 0: K, 1: V (>= 2: staging only)
     const int lane = lane_id();
     const int p0 = blk * BT;
     const int sa = max(E.a, p0) - p0;
@@ -166,23 +171,23 @@ __global__ __launch_bounds__(STAGE ? 512 : 128) void k_compress(const CompressAr
     }
     const float (*Rs)[D + 1] = nullptr;
     if constexpr (STAGE) {
-        __shared__ float Rst[2][D][D + 1];
-        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + unit * 2 * D * D);
-        float4 v[2 * D * D / 4 / 512];
+        __shared__ float Rst[D][D + 1];
+        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + (unit * 2 + (blockIdx.x & 1)) * D * D);
+        float4 v[D * D / 4 / 256];
 #pragma unroll
-        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) v[k] = Rg[threadIdx.x + 512 * k];
+        for (int k = 0; k < D * D / 4 / 256; ++k) v[k] = Rg[threadIdx.x + 256 * k];
 #pragma unroll
-        for (int k = 0; k < 2 * D * D / 4 / 512; ++k) {
-            const int i = (int)threadIdx.x + 512 * k;
-            const int m = i / (D * D / 4), c = (i / (D / 4)) % D, j = (i % (D / 4)) * 4;
-            Rst[m][c][j] = v[k].x;
-            Rst[m][c][j + 1] = v[k].y;
-            Rst[m][c][j + 2] = v[k].z;
-            Rst[m][c][j + 3] = v[k].w;
+        for (int k = 0; k < D * D / 4 / 256; ++k) {
+            const int i = (int)threadIdx.x + 256 * k;
+            const int c = i / (D / 4), j = (i % (D / 4)) * 4;
+            Rst[c][j] = v[k].x;
+            Rst[c][j + 1] = v[k].y;
+            Rst[c][j + 2] = v[k].z;
+            Rst[c][j + 3] = v[k].w;
         }
         __syncthreads();
         if (wave >= 2) return;
-        Rs = Rst[wave];
+        Rs = Rst;
     }
 
     for (int slot = sa; slot < se; ++slot) {
@@ -301,14 +306,15 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
 
 hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s) {
     if (a.n_ent <= 0 || max_blk <= 0) return hipSuccess;
-    const dim3 grid((unsigned)max_blk, (unsigned)a.n_kv, (unsigned)a.n_ent);
-    // a block of work per (entry, KV head) at most twice: stage R in LDS
+    // a block of work per (entry, KV head) at most twice: stage R in LDS, one
+    // workgroup per matrix
     const bool stage = max_blk <= 2;
+    const dim3 grid((unsigned)(stage ? 2 * max_blk : max_blk), (unsigned)a.n_kv, (unsigned)a.n_ent);
     if (dtype == MKV_BF16) {
-        if (stage) hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(512), 0, s, a);
+        if (stage) hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((k_compress<Bf16, false>), grid, dim3(128), 0, s, a);
     } else {
-        if (stage) hipLaunchKernelGGL((k_compress<F32, true>), grid, dim3(512), 0, s, a);
+        if (stage) hipLaunchKernelGGL((k_compress<F32, true>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((k_compress<F32, false>), grid, dim3(128), 0, s, a);
     }
     return hipGetLastError();

@@ -19,8 +19,10 @@ constexpr int META_TILE = 64;   // blocks per meta tile
 constexpr int MAX_SPLITS = 256; // attention splits per (request, KV head)
 constexpr int PART = D + 2;     // floats per split partial: m, l, acc[D]
 // Union-mode weight of a packed record: its bytes plus a fixed per-record
-// cost (records are latency-bound, so a record costs more than its bytes).
-constexpr int UNION_RECORD_FIXED = 256;
+// cost. A wave holds about one record in flight, so a record's time is mostly
+// its load latency and only a little its size; the constant is the measured
+// balance point at 96 KB shares (its cost is worth about 3 KB of bytes).
+constexpr int UNION_RECORD_FIXED = 3072;
 constexpr int UNION_CAP = 1024;  // union records one packed workgroup can take
 static_assert(UNION_RECORD_FIXED <= 16384, "union weights of a unit stay below 2^32 / 4");
 

@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the MosaicKV hot path on one MI355X.
 
-One step = mkv_compress_append of one new token per request (rotate in
-float64, top-r, pack, block-key update) followed by mkv_decode_attn (query
-rotation, block scoring, top-k, sparse attention, merge, inverse rotation).
+One step = one mkv_append_decode call: the append of one new token per
+request (rotate in float64, top-r, pack, block-key update) and then the decode
+(query rotation, block scoring, top-k, sparse attention, merge, inverse
+rotation), with the query rotation running inside the append's launch.
 
 Default workload (128K context): GQA layer with 32 query / 8 KV heads, d=128,
 batch 4, T=131072 tokens per request, bf16 storage, segments: 64 dense sink,
@@ -245,9 +246,8 @@ def main():
     def run_step():
         nonlocal step
         c = caches[step % n_layers]
-        c.append(newk[step], newv[step], ones)
+        c.append_decode(newk[step], newv[step], ones, qs[step], out=out)
         tokens.append(sum(c.lengths))
-        c.decode(qs[step], out=out)
         step += 1
 
     for _ in range(W_steps):

@@ -197,11 +197,26 @@ int64_t mkv_decode_sel_cols(const mkv_cache *c);
 mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32_t *sel_out,
                            int64_t sel_cols, void *workspace, size_t ws_bytes, void *stream);
 
+/* One serving step in one call: mkv_compress_append(c, k_new, v_new, n_new,
+ * n_max) and then mkv_decode_attn(c, q, out, sel_out, sel_cols, workspace,
+ * ws_bytes), with the same arguments, meaning and results bit for bit ([N]
+ * Eq. 7-9 and 12-14; [S] 4.2, 5.2-5.3). When the append is small (at most two
+ * blocks per request and segment), the query rotation q' = R_k q runs in the
+ * append's launch instead of a launch of its own. Every argument of both
+ * parts is checked before anything is enqueued (the decode's at the lengths
+ * after the append), so an argument error leaves the cache unchanged; after
+ * MKV_ERR_HIP the append may have been enqueued and c->len advanced.
+ * Errors: those of both calls. */
+mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
+                             int32_t n_max, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
+                             void *workspace, size_t ws_bytes, void *stream);
+
 /* Optional kernel timing (a diagnostic, not thread-safe): while enabled, every
  * kernel the library launches is bracketed by HIP events on its stream.
  * mkv_timing_read synchronises those events and returns, per stage, the summed
  * milliseconds and the number of launches since the last read, then clears
- * them. Stages: 0 compress, 1 block_meta, 2 q_rotate, 3 score, 4 select,
+ * them. Stages: 0 compress (with the query rotation when mkv_append_decode
+ * runs it there), 1 block_meta, 2 q_rotate, 3 score, 4 select,
  * 5 attend (dense blocks and selected packed blocks), 6 merge (split merge +
  * inverse rotation). */
 #define MKV_N_STAGES 7

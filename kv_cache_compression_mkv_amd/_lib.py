@@ -27,7 +27,7 @@ MKV_N_STAGES = 7
 
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
            "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",
-           "mkv_timing_enable", "mkv_timing_read", "mkv_stage_name"]
+           "mkv_append_decode", "mkv_timing_enable", "mkv_timing_read", "mkv_stage_name"]
 
 
 class mkv_segment(ctypes.Structure):
@@ -70,6 +70,8 @@ def _load():
     L.mkv_decode_sel_cols.argtypes = [ctypes.POINTER(mkv_cache)]
     L.mkv_decode_attn.restype = ctypes.c_int
     L.mkv_decode_attn.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I64, P, SZ, P]
+    L.mkv_append_decode.restype = ctypes.c_int
+    L.mkv_append_decode.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P, P, P, I64, P, SZ, P]
     L.mkv_timing_enable.restype = ctypes.c_int
     L.mkv_timing_enable.argtypes = [I32]
     L.mkv_timing_read.restype = ctypes.c_int
@@ -123,6 +125,12 @@ def mkv_decode_attn(cache: mkv_cache, q_ptr: int, out_ptr: int, sel_ptr, sel_col
                     ws_bytes: int, stream: int):
     _check(LIB.mkv_decode_attn(ctypes.byref(cache), q_ptr, out_ptr, sel_ptr, sel_cols, ws_ptr, ws_bytes,
                                stream), "mkv_decode_attn")
+
+
+def mkv_append_decode(cache: mkv_cache, k_ptr: int, v_ptr: int, n_new_ptr: int, n_max: int, q_ptr: int,
+                      out_ptr: int, sel_ptr, sel_cols: int, ws_ptr: int, ws_bytes: int, stream: int):
+    _check(LIB.mkv_append_decode(ctypes.byref(cache), k_ptr, v_ptr, n_new_ptr, n_max, q_ptr, out_ptr, sel_ptr,
+                                 sel_cols, ws_ptr, ws_bytes, stream), "mkv_append_decode")
 
 
 def mkv_timing_enable(on: bool):

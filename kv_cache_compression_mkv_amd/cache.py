@@ -106,3 +106,33 @@ class Cache:
         L.mkv_decode_attn(self.c, q.data_ptr(), out.data_ptr(), sel.data_ptr() if sel is not None else None,
                           cols, ws.data_ptr(), ws.numel(), _stream())
         return (out, sel) if want_sel else out
+
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, n_new, q: torch.Tensor,
+                      out: torch.Tensor | None = None, want_sel: bool = False, sel_cols: int | None = None):
+        """append(k_new, v_new, n_new) then decode(q) in one library call (same results)."""
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        assert k_new.element_size() == self.sbytes and k_new.shape[:2] == (self.batch, self.hkv)
+        assert q.dtype == torch.float32 and q.is_contiguous()
+        n_max = int(k_new.shape[2])
+        nn = (ctypes.c_int32 * self.batch)(*[int(x) for x in n_new])
+        if out is None:
+            out = torch.empty((self.batch, self.hq, self.d), dtype=torch.float32, device=self.device)
+        sel = None
+        cols = 0
+        if want_sel:
+            if sel_cols is None:  # columns needed at the lengths after the append
+                self._len_add(n_new)
+                cols = self.sel_cols()
+                self._len_add([-int(x) for x in n_new])
+            else:
+                cols = sel_cols
+            sel = torch.empty((self.batch, self.hq, max(cols, 1)), dtype=torch.int32, device=self.device)
+        ws = self.workspace()
+        L.mkv_append_decode(self.c, k_new.data_ptr(), v_new.data_ptr(), ctypes.addressof(nn), n_max, q.data_ptr(),
+                            out.data_ptr(), sel.data_ptr() if sel is not None else None, cols, ws.data_ptr(),
+                            ws.numel(), _stream())
+        return (out, sel) if want_sel else out
+
+    def _len_add(self, n):
+        for b in range(self.batch):
+            self._len[b] += int(n[b])

@@ -14,8 +14,11 @@
 // the keys, and (in the same or another workgroup) the values. Lane l owns channels l and l+64,
 // so the top-r selection is a wave-wide radix search with ballots and the
 // packing order falls out of a ballot prefix count.
+#include <algorithm>
+
 #include "device_util.hpp"
 #include "mkv_internal.h"
+#include "qrot.hpp"
 
 namespace mkv {
 
@@ -107,6 +110,20 @@ __device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane,
 template <typename ST, bool STAGE>
 __global__ __launch_bounds__(STAGE ? 256 : 128) void k_compress(const CompressArgs A) {
     using bits_t = typename ST::bits_t;
+    if constexpr (STAGE) {
+        // the optional query rotation: workgroups past the append table
+        if ((int)blockIdx.z >= A.n_ent) {
+            if (blockIdx.x >= D / 32) return;
+            __shared__ __align__(16) float qsh[4][D];
+            const int b = (int)blockIdx.z - A.n_ent, g = (int)blockIdx.y, cb = (int)blockIdx.x;
+            switch (A.q_G) {
+            case 1: qrot_block<1>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+            case 2: qrot_block<2>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+            default: qrot_block<4>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+            }
+            return;
+        }
+    }
     const CompressEntry &E = A.ent[blockIdx.z];
     // STAGE: workgroup x = 2 block + matrix (0: K, 1: V), wave 0 computes;
     // otherwise workgroup x = block, wave 0 the keys and wave 1 the values
@@ -305,11 +322,16 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s) {
-    if (a.n_ent <= 0 || max_blk <= 0) return hipSuccess;
+    if (a.n_ent <= 0 || max_blk <= 0) return a.q_req > 0 ? hipErrorInvalidValue : hipSuccess;
     // a block of work per (entry, KV head) at most twice: stage R in LDS, one
     // workgroup per matrix
-    const bool stage = max_blk <= 2;
-    const dim3 grid((unsigned)(stage ? 2 * max_blk : max_blk), (unsigned)a.n_kv, (unsigned)a.n_ent);
+    const bool stage = compress_stages(max_blk);
+    // a query rotation rides along only on staged launches (256 threads)
+    if (a.q_req > 0 && (!stage || !a.q || !a.qa || !a.qs || (a.q_G != 1 && a.q_G != 2 && a.q_G != 4) ||
+                        a.q_hq != a.q_G * a.n_kv))
+        return hipErrorInvalidValue;
+    const unsigned gx = stage ? (unsigned)std::max(2 * max_blk, a.q_req > 0 ? D / 32 : 0) : (unsigned)max_blk;
+    const dim3 grid(gx, (unsigned)a.n_kv, (unsigned)(a.n_ent + std::max(a.q_req, 0)));
     if (dtype == MKV_BF16) {
         if (stage) hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((k_compress<Bf16, false>), grid, dim3(128), 0, s, a);

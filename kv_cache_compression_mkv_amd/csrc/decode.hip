@@ -16,70 +16,28 @@
 
 #include "device_util.hpp"
 #include "mkv_internal.h"
+#include "qrot.hpp"
 
 namespace mkv {
 
 namespace {
 
-constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
-
 // 2^x with the hardware exponential (results below the smallest normal float
 // flush to zero, which softmax weights tolerate: they are at most 2^8 times
 // the running maximum's weight and such tiny ones do not change any sum)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ const DSeg &seg_of(const DecodeArgs &A, int bl, int si) {
     return A.seg[bl * A.nseg + si];
 }
 
 // ----------------------------------------------------------------------------
-// q_rotate: four workgroups per (request, KV head), 32 channels each. The 8
-// lanes of channel c sum 16 columns each of R_k[c] . q (one round of 16-byte
-// loads per lane) and add up with DPP (quad swaps, then the half-row mirror).
+// q_rotate: four workgroups per (request, KV head), 32 channels each.
 // ----------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void k_qrot(const DecodeArgs A) {
-    const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
-    const int b = A.b0 + bl;
-    const int tid = (int)threadIdx.x;
-    const int k = tid & 7;
-    const int c = (int)blockIdx.x * 32 + (tid >> 3);
     __shared__ __align__(16) float qsh[G][D];
-    const float4 *Rr = reinterpret_cast<const float4 *>(A.rot + (((size_t)b * A.hkv + g) * 2) * D * D +
-                                                        (size_t)c * D + 16 * k);
-    float4 r[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = Rr[u];
-    for (int i = tid; i < G * D; i += 256) qsh[i / D][i % D] = A.q[((size_t)b * A.hq + g * G) * D + i];
-    __syncthreads();
-    float acc[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(&qsh[i][16 * k]);
-        float a = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float4 x = x4[u];
-            a = fmaf(r[u].x, x.x, a);
-            a = fmaf(r[u].y, x.y, a);
-            a = fmaf(r[u].z, x.z, a);
-            a = fmaf(r[u].w, x.w, a);
-        }
-        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xf, 0xf, false));
-        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xf, 0xf, false));
-        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xf, 0xf, false));
-        acc[i] = a;
-    }
-    if (k == 0) {
-        float *qs = A.qs + (((size_t)b * A.hkv + g) * D + c) * 2 * G;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            A.qa[((size_t)b * A.hq + g * G + i) * D + c] = acc[i] * (kRsqrtD * kLog2e);
-            qs[i] = fmaxf(acc[i], 0.f) * kRsqrtD;
-            qs[G + i] = fminf(acc[i], 0.f) * kRsqrtD;
-        }
-    }
+    qrot_block<G>(A.rot, A.q, A.qa, A.qs, A.hq, A.hkv, A.b0 + (int)blockIdx.z, (int)blockIdx.y, (int)blockIdx.x, qsh);
 }
 
 // ----------------------------------------------------------------------------

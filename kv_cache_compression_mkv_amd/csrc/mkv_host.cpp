@@ -176,53 +176,38 @@ int64_t sel_cols_now(const mkv_cache *c) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char *mkv_status_str(mkv_status s) {
-    switch (s) {
-    case MKV_OK: return "ok";
-    case MKV_ERR_ARG: return "invalid argument";
-    case MKV_ERR_UNSUPPORTED: return "unsupported configuration";
-    case MKV_ERR_CAPACITY: return "append exceeds segment capacity";
-    case MKV_ERR_WORKSPACE: return "workspace missing or too small";
-    case MKV_ERR_NOCONVERGE: return "eigensolver did not converge";
-    case MKV_ERR_HIP: return "HIP runtime error";
-    }
-    return "unknown status";
-}
-
-size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads, int64_t t_cap,
-                         size_t *meta_bytes_out) {
-    if (meta_bytes_out) *meta_bytes_out = 0;
-    if ((dtype != MKV_F32 && dtype != MKV_BF16) || d < 1 || n_kv_heads < 1 || t_cap < 1) return 0;
-    const size_t s = elem_bytes(dtype);
-    const size_t nb = (size_t)ceil_div(t_cap, BT);
-    if (kind == MKV_SEG_DENSE) return (size_t)n_kv_heads * nb * 2 * BT * d * s;
-    if (kind != MKV_SEG_PACKED || r < 1 || r > d) return 0;
-    if (meta_bytes_out) {
-        const size_t ntile = ceil_div((int64_t)nb, META_TILE);
-        *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * d * s;
-    }
-    return (size_t)n_kv_heads * nb * BT * r * 2 * (s + 1) + MKV_PACKED_TAIL_BYTES;
-}
-
-mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
-                               int32_t n_max, void *stream) {
-    mkv_status st = check_cache(c);
-    if (st != MKV_OK) return st;
+// Argument checks of an append; *any tells whether any request appends.
+mkv_status append_check(const mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
+                        int32_t n_max, bool *any) {
     if (!n_new || n_max < 0) return MKV_ERR_ARG;
-    bool any = false;
+    *any = false;
     for (int b = 0; b < c->batch; ++b) {
         if (n_new[b] < 0 || n_new[b] > n_max) return MKV_ERR_ARG;
         int64_t cap = 0;
         for (int j = 0; j < c->n_segments; ++j) cap += segof(c, b, j).t_cap;
         if (c->len[b] + n_new[b] > cap) return MKV_ERR_CAPACITY;
-        any = any || n_new[b] > 0;
+        *any = *any || n_new[b] > 0;
     }
-    if (!any) return MKV_OK;
-    if (!k_new || !v_new) return MKV_ERR_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (*any && (!k_new || !v_new)) return MKV_ERR_ARG;
+    return MKV_OK;
+}
 
+// Query rotation to run beside an append: q and the decode workspace's q'
+// buffers (every request of the cache).
+struct QrotFuse {
+    const float *q;
+    float *qa;
+    float *qs;
+};
+
+// Enqueue a checked, non-empty append and advance c->len. With `fuse`, the
+// first launch also rotates the queries when it is a staged launch; *rotated
+// then reports it.
+mkv_status append_enqueue(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new, int32_t n_max,
+                          hipStream_t s, const QrotFuse *fuse, bool *rotated) {
+    if (rotated) *rotated = false;
     std::vector<CompressEntry> ents;
     for (int b = 0; b < c->batch; ++b) {
         const int64_t p0 = c->len[b], p1 = c->len[b] + n_new[b];
@@ -261,63 +246,36 @@ mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_ne
         A.n_ent = (int32_t)n;
         A.n_kv = c->n_kv_heads;
         A.n_max = n_max;
-        st = timed(0, s, [&] { return launch_compress(A, c->dtype, max_blk, s); });
+        if (fuse && i0 == 0 && compress_stages(max_blk)) {
+            A.q = fuse->q;
+            A.qa = fuse->qa;
+            A.qs = fuse->qs;
+            A.q_req = c->batch;
+            A.q_hq = c->n_q_heads;
+            A.q_G = c->n_q_heads / c->n_kv_heads;
+            if (rotated) *rotated = true;
+        }
+        mkv_status st = timed(0, s, [&] { return launch_compress(A, c->dtype, max_blk, s); });
         if (st != MKV_OK) return st;
     }
     for (int b = 0; b < c->batch; ++b) c->len[b] += n_new[b];
     return MKV_OK;
 }
 
-mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
-    mkv_status st = check_cache(c);
-    if (st != MKV_OK) return st;
-    if (seg < 0 || seg >= c->n_segments || segof(c, 0, seg).kind != MKV_SEG_PACKED) return MKV_ERR_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int b0 = 0; b0 < c->batch; b0 += TABLE) {
-        MetaArgs A;
-        memset(&A, 0, sizeof(A));
-        const int n = std::min(TABLE, c->batch - b0);
-        int max_nb = 0;
-        for (int i = 0; i < n; ++i) {
-            const mkv_segment &sg = segof(c, b0 + i, seg);
-            MetaEntry &E = A.ent[i];
-            E.data = sg.data;
-            E.meta = sg.meta;
-            E.filled = (int32_t)seg_filled(c, b0 + i, seg);
-            E.nb = (int32_t)ceil_div(E.filled, BT);
-            E.r = sg.r;
-            E.b = b0 + i;
-            E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
-            max_nb = std::max(max_nb, E.nb);
-        }
-        A.n_ent = n;
-        A.n_kv = c->n_kv_heads;
-        st = timed(1, s, [&] { return launch_block_meta(A, c->dtype, max_nb, s); });
-        if (st != MKV_OK) return st;
-    }
+// Argument checks of a decode at the cache's current lengths.
+mkv_status decode_check(const mkv_cache *c, const float *q, const float *out, const int32_t *sel_out,
+                        int64_t sel_cols, const void *workspace, size_t ws_bytes) {
+    if (!q || !out) return MKV_ERR_ARG;
+    if (sel_out && sel_cols < sel_cols_now(c)) return MKV_ERR_ARG;
+    if (!workspace || ws_bytes < ws_map(c).total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return MKV_ERR_WORKSPACE;
     return MKV_OK;
 }
 
-size_t mkv_decode_workspace_bytes(const mkv_cache *c) {
-    if (check_cache(c) != MKV_OK) return 0;
-    return ws_map(c).total;
-}
-
-int64_t mkv_decode_sel_cols(const mkv_cache *c) {
-    if (check_cache(c) != MKV_OK) return -1;
-    return sel_cols_now(c);
-}
-
-mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
-                           void *workspace, size_t ws_bytes, void *stream) {
-    mkv_status st = check_cache(c);
-    if (st != MKV_OK) return st;
-    if (!q || !out) return MKV_ERR_ARG;
-    if (sel_out && sel_cols < sel_cols_now(c)) return MKV_ERR_ARG;
+// Enqueue a checked decode; `rotated`: q' is already in the workspace.
+mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
+                          void *workspace, bool rotated, hipStream_t s) {
     const WsMap m = ws_map(c);
-    if (!workspace || ws_bytes < m.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
-        return MKV_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const int G = c->n_q_heads / c->n_kv_heads;
     const int sb = elem_bytes(c->dtype);
     char *ws = static_cast<char *>(workspace);
@@ -418,8 +376,11 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
         A.sel_kpt = kpt;
         A.sel_waves = (int32_t)std::max<int64_t>(1, ceil_div(max_nb, 64 * kpt));
 
-        st = timed(2, s, [&] { return launch_qrot(A, G, s); });
-        if (st != MKV_OK) return st;
+        mkv_status st = MKV_OK;
+        if (!rotated) {
+            st = timed(2, s, [&] { return launch_qrot(A, G, s); });
+            if (st != MKV_OK) return st;
+        }
         if (m.npk > 0) {
             st = timed(3, s, [&] { return launch_score(A, c->dtype, G, max_tiles, s); });
             if (st != MKV_OK) return st;
@@ -433,6 +394,123 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
         if (st != MKV_OK) return st;
     }
     return MKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mkv_status_str(mkv_status s) {
+    switch (s) {
+    case MKV_OK: return "ok";
+    case MKV_ERR_ARG: return "invalid argument";
+    case MKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MKV_ERR_CAPACITY: return "append exceeds segment capacity";
+    case MKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case MKV_ERR_NOCONVERGE: return "eigensolver did not converge";
+    case MKV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads, int64_t t_cap,
+                         size_t *meta_bytes_out) {
+    if (meta_bytes_out) *meta_bytes_out = 0;
+    if ((dtype != MKV_F32 && dtype != MKV_BF16) || d < 1 || n_kv_heads < 1 || t_cap < 1) return 0;
+    const size_t s = elem_bytes(dtype);
+    const size_t nb = (size_t)ceil_div(t_cap, BT);
+    if (kind == MKV_SEG_DENSE) return (size_t)n_kv_heads * nb * 2 * BT * d * s;
+    if (kind != MKV_SEG_PACKED || r < 1 || r > d) return 0;
+    if (meta_bytes_out) {
+        const size_t ntile = ceil_div((int64_t)nb, META_TILE);
+        *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * d * s;
+    }
+    return (size_t)n_kv_heads * nb * BT * r * 2 * (s + 1) + MKV_PACKED_TAIL_BYTES;
+}
+
+mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
+                               int32_t n_max, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    bool any = false;
+    st = append_check(c, k_new, v_new, n_new, n_max, &any);
+    if (st != MKV_OK || !any) return st;
+    return append_enqueue(c, k_new, v_new, n_new, n_max, static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    if (seg < 0 || seg >= c->n_segments || segof(c, 0, seg).kind != MKV_SEG_PACKED) return MKV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int b0 = 0; b0 < c->batch; b0 += TABLE) {
+        MetaArgs A;
+        memset(&A, 0, sizeof(A));
+        const int n = std::min(TABLE, c->batch - b0);
+        int max_nb = 0;
+        for (int i = 0; i < n; ++i) {
+            const mkv_segment &sg = segof(c, b0 + i, seg);
+            MetaEntry &E = A.ent[i];
+            E.data = sg.data;
+            E.meta = sg.meta;
+            E.filled = (int32_t)seg_filled(c, b0 + i, seg);
+            E.nb = (int32_t)ceil_div(E.filled, BT);
+            E.r = sg.r;
+            E.b = b0 + i;
+            E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
+            max_nb = std::max(max_nb, E.nb);
+        }
+        A.n_ent = n;
+        A.n_kv = c->n_kv_heads;
+        st = timed(1, s, [&] { return launch_block_meta(A, c->dtype, max_nb, s); });
+        if (st != MKV_OK) return st;
+    }
+    return MKV_OK;
+}
+
+size_t mkv_decode_workspace_bytes(const mkv_cache *c) {
+    if (check_cache(c) != MKV_OK) return 0;
+    return ws_map(c).total;
+}
+
+int64_t mkv_decode_sel_cols(const mkv_cache *c) {
+    if (check_cache(c) != MKV_OK) return -1;
+    return sel_cols_now(c);
+}
+
+mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
+                           void *workspace, size_t ws_bytes, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    st = decode_check(c, q, out, sel_out, sel_cols, workspace, ws_bytes);
+    if (st != MKV_OK) return st;
+    return decode_enqueue(c, q, out, sel_out, sel_cols, workspace, false, static_cast<hipStream_t>(stream));
+}
+
+mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
+                             int32_t n_max, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
+                             void *workspace, size_t ws_bytes, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    bool any = false;
+    st = append_check(c, k_new, v_new, n_new, n_max, &any);
+    if (st != MKV_OK) return st;
+    // the decode's arguments are checked at the lengths after the append
+    std::vector<int64_t> len0(c->len, c->len + c->batch);
+    for (int b = 0; b < c->batch; ++b) c->len[b] += n_new[b];
+    st = decode_check(c, q, out, sel_out, sel_cols, workspace, ws_bytes);
+    for (int b = 0; b < c->batch; ++b) c->len[b] = len0[b];
+    if (st != MKV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool rotated = false;
+    if (any) {
+        const WsMap m = ws_map(c);
+        char *ws = static_cast<char *>(workspace);
+        const QrotFuse f{q, reinterpret_cast<float *>(ws + m.qa), reinterpret_cast<float *>(ws + m.qs)};
+        st = append_enqueue(c, k_new, v_new, n_new, n_max, s, &f, &rotated);
+        if (st != MKV_OK) return st;
+    }
+    return decode_enqueue(c, q, out, sel_out, sel_cols, workspace, rotated, s);
 }
 
 mkv_status mkv_timing_enable(int32_t on) {

@@ -47,7 +47,14 @@ struct CompressArgs {
     const void *v_new;
     const float *rot;
     int32_t n_ent, n_kv, n_max, pad;
+    // optional query rotation run beside the append (staged launches only):
+    // workgroups z = n_ent .. n_ent + q_req - 1, x < 4, rotate request z - n_ent
+    const float *q;
+    float *qa;
+    float *qs;
+    int32_t q_req, q_hq, q_G, pad2;
 };
+static_assert(sizeof(CompressArgs) <= 4096, "kernel arguments stay below 4 KB");
 
 struct MetaEntry {
     const void *data;
@@ -97,6 +104,10 @@ struct DecodeArgs {
     int32_t sel_waves; // waves per select workgroup
     int32_t union_mode; // packed workgroups take exact byte shares of the union (S_p a multiple of 4)
 };
+
+// Appends touching at most this many blocks per (entry, KV head) stage R in
+// LDS, one 256-thread workgroup per matrix (and may carry a query rotation).
+constexpr bool compress_stages(int max_blk) { return max_blk <= 2; }
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s);

@@ -24,44 +24,33 @@ namespace mkv {
 
 namespace {
 
-// Compute x' = R x for the wave's token staged in xs (float, exact copy of
-// the stored input). Lane owns channels c0 = lane and c1 = lane + 64.
-__device__ __forceinline__ void rotate_f64(const float *__restrict__ R, const float *xs, int lane,
-                                           double &acc0, double &acc1) {
-    const float4 *r0 = reinterpret_cast<const float4 *>(R + (size_t)lane * D);
-    const float4 *r1 = reinterpret_cast<const float4 *>(R + (size_t)(lane + 64) * D);
-    const float4 *x4 = reinterpret_cast<const float4 *>(xs);
-    double a0 = 0.0, a1 = 0.0;
-#pragma unroll 4
-    for (int j = 0; j < D / 4; ++j) {
-        const float4 u = r0[j], v = r1[j], x = x4[j];
-        a0 = fma((double)u.x, (double)x.x, a0);
-        a0 = fma((double)u.y, (double)x.y, a0);
-        a0 = fma((double)u.z, (double)x.z, a0);
-        a0 = fma((double)u.w, (double)x.w, a0);
-        a1 = fma((double)v.x, (double)x.x, a1);
-        a1 = fma((double)v.y, (double)x.y, a1);
-        a1 = fma((double)v.z, (double)x.z, a1);
-        a1 = fma((double)v.w, (double)x.w, a1);
-    }
-    acc0 = a0;
-    acc1 = a1;
-}
-
-// The same product sum with R staged in LDS (rows padded to D + 1 floats, so
-// the 64 lanes reading 64 rows at one column hit distinct banks). Identical
-// operation order, hence identical bits.
-__device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const float *xs, int lane,
-                                               double &acc0, double &acc1) {
-    double a0 = 0.0, a1 = 0.0;
+// Compute x' = R x for one token (xs: its input as doubles in LDS, exact
+// copies of the stored values), or for two tokens at once (xs and ys), which
+// then share every R element read from LDS and converted. R is staged in LDS
+// with rows padded to D + 1 floats, so the 64 lanes reading 64 rows at one
+// column hit distinct banks. Lane owns channels lane and lane + 64; each sum
+// is one fp64 chain over j ascending, and every product of two floats is
+// exact in fp64.
+template <bool TWO>
+__device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const double *xs, const double *ys, int lane,
+                                               double &a0, double &a1, double &b0, double &b1) {
+    double p0 = 0.0, p1 = 0.0, q0 = 0.0, q1 = 0.0;
 #pragma unroll 8
     for (int j = 0; j < D; ++j) {
-        const double x = (double)xs[j];
-        a0 = fma((double)Rs[lane][j], x, a0);
-        a1 = fma((double)Rs[lane + 64][j], x, a1);
+        const double r0 = (double)Rs[lane][j], r1 = (double)Rs[lane + 64][j];
+        const double x = xs[j];
+        p0 = fma(r0, x, p0);
+        p1 = fma(r1, x, p1);
+        if constexpr (TWO) {
+            const double y = ys[j];
+            q0 = fma(r0, y, q0);
+            q1 = fma(r1, y, q1);
+        }
     }
-    acc0 = a0;
-    acc1 = a1;
+    a0 = p0;
+    a1 = p1;
+    b0 = q0;
+    b1 = q1;
 }
 
 // Keep the r channels of largest magnitude (ties to the lower channel).
@@ -102,46 +91,31 @@ __device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane,
     keep1 = gt1 || ((k1 == thr) && rank1 < need);
 }
 
-// STAGE (appends of a few tokens): one workgroup per (block, matrix); its 256
-// threads first copy R_k or R_v into LDS with one round of coalesced 16-byte
-// loads, then wave 0 computes from LDS; the K and V workgroups run side by
-// side. Without it (bulk appends) one workgroup per block, each lane reading
-// its R rows, which the 16 tokens of the block reuse through the caches.
-template <typename ST, bool STAGE>
-__global__ __launch_bounds__(STAGE ? 256 : 128) void k_compress(const CompressArgs A) {
+// Per-block state of one wave's append into block blk of one (entry, KV head,
+// matrix): destination pointers, the new slots [sa, se), the running keys of
+// a packed segment's block (keys matrix only) and the first new row.
+template <typename ST>
+struct BlockJob {
+    typename ST::bits_t *vals;
+    uint8_t *idxs;
+    char *meta_tile;
+    const typename ST::bits_t *xin;
+    int p0, sa, se, r, G16, cpg;
+    bool packed, do_meta;
+    uint32_t mn0, mx0, mn1, mx1;
+    typename ST::bits_t x0, x1, y0, y1;  // rows of the first two new tokens (lane's channels)
+};
+
+// Pointers of block blk, its stored keys (when it already holds tokens) and
+// the first new token's row: the loads are issued here, not waited for.
+template <typename ST>
+__device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs &A, const CompressEntry &E,
+                                            size_t unit, int g, int blk, int wave, int lane) {
     using bits_t = typename ST::bits_t;
-    if constexpr (STAGE) {
-        // the optional query rotation: workgroups past the append table
-        if ((int)blockIdx.z >= A.n_ent) {
-            if (blockIdx.x >= D / 32) return;
-            __shared__ __align__(16) float qsh[4][D];
-            const int b = (int)blockIdx.z - A.n_ent, g = (int)blockIdx.y, cb = (int)blockIdx.x;
-            switch (A.q_G) {
-            case 1: qrot_block<1>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
-            case 2: qrot_block<2>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
-            default: qrot_block<4>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
-            }
-            return;
-        }
-    }
-    const CompressEntry &E = A.ent[blockIdx.z];
-    // STAGE: workgroup x = 2 block + matrix (0: K, 1: V), wave 0 computes;
-    // otherwise workgroup x = block, wave 0 the keys and wave 1 the values
-    const int bx = STAGE ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
-    if (bx >= E.nblk) return;
-    const int blk = E.blk0 + bx;
-    const int g = (int)blockIdx.y;
-    const int wave = STAGE ? (int)(blockIdx.x & 1) + 2 * (int)(threadIdx.x >> 6)
-                           : (int)(threadIdx.x >> 6);  // 0: K, 1: V (>= 2: staging only)
-    const int lane = lane_id();
     const int p0 = blk * BT;
     const int sa = max(E.a, p0) - p0;
     const int se = min(E.e, p0 + BT) - p0;
-    const size_t unit = (size_t)E.b * A.n_kv + g;
-    const float *R = A.rot + (unit * 2 + wave) * D * D;
     const bits_t *xin = reinterpret_cast<const bits_t *>(wave ? A.v_new : A.k_new) + unit * A.n_max * D;
-    __shared__ __align__(16) float xs[2][D];
-
     const bool packed = E.kind == MKV_SEG_PACKED;
     const int r = E.r;
     char *blkbase;
@@ -180,46 +154,54 @@ __global__ __launch_bounds__(STAGE ? 256 : 128) void k_compress(const CompressAr
 
     // the first token's row is loaded before R is staged, so that the two
     // (and the block keys above) are in flight together
-    bits_t x0 = 0, x1 = 0;
-    if (wave < 2 && sa < se) {
+    bits_t x0 = 0, x1 = 0, y0 = 0, y1 = 0;
+    if (sa < se) {
         const bits_t *xr = xin + (size_t)(E.row0 + (p0 + sa - E.a)) * D;
         x0 = xr[lane];
         x1 = xr[lane + 64];
     }
-    const float (*Rs)[D + 1] = nullptr;
-    if constexpr (STAGE) {
-        __shared__ float Rst[D][D + 1];
-        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + (unit * 2 + (blockIdx.x & 1)) * D * D);
-        float4 v[D * D / 4 / 256];
-#pragma unroll
-        for (int k = 0; k < D * D / 4 / 256; ++k) v[k] = Rg[threadIdx.x + 256 * k];
-#pragma unroll
-        for (int k = 0; k < D * D / 4 / 256; ++k) {
-            const int i = (int)threadIdx.x + 256 * k;
-            const int c = i / (D / 4), j = (i % (D / 4)) * 4;
-            Rst[c][j] = v[k].x;
-            Rst[c][j + 1] = v[k].y;
-            Rst[c][j + 2] = v[k].z;
-            Rst[c][j + 3] = v[k].w;
-        }
-        __syncthreads();
-        if (wave >= 2) return;
-        Rs = Rst;
+    if (sa + 1 < se) {
+        const bits_t *xr = xin + (size_t)(E.row0 + (p0 + sa + 1 - E.a)) * D;
+        y0 = xr[lane];
+        y1 = xr[lane + 64];
     }
+    J.vals = vals;
+    J.idxs = idxs;
+    J.meta_tile = meta_tile;
+    J.xin = xin;
+    J.p0 = p0;
+    J.sa = sa;
+    J.se = se;
+    J.r = r;
+    J.G16 = G16;
+    J.cpg = cpg;
+    J.packed = packed;
+    J.do_meta = do_meta;
+    J.mn0 = mn0; J.mx0 = mx0; J.mn1 = mn1; J.mx1 = mx1;
+    J.x0 = x0;
+    J.x1 = x1;
+    J.y0 = y0;
+    J.y1 = y1;
+}
 
-    for (int slot = sa; slot < se; ++slot) {
-        if (slot > sa) {
-            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot - E.a)) * D;
-            x0 = xr[lane];
-            x1 = xr[lane + 64];
-        }
-        xs[wave][lane] = bits_to_float<ST>(x0);
-        xs[wave][lane + 64] = bits_to_float<ST>(x1);
-        wave_lds_sync();
-        double v0, v1;
-        if constexpr (STAGE) rotate_f64_lds(Rs, xs[wave], lane, v0, v1);
-        else rotate_f64(R, xs[wave], lane, v0, v1);
-        wave_lds_sync();
+// Rotate, rank, round and store the block's new tokens, two at a time while
+// two remain (R from LDS; xs is the wave's two LDS rows of doubles), clear the
+// slots after the last token of a block this call starts, and write the block
+// keys back.
+template <typename ST>
+__device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &E, int blk, int lane,
+                                          const float (*Rs)[D + 1], double (*xs)[D]) {
+    using bits_t = typename ST::bits_t;
+    bits_t *vals = J.vals;
+    uint8_t *idxs = J.idxs;
+    char *meta_tile = J.meta_tile;
+    const bits_t *xin = J.xin;
+    const int p0 = J.p0, sa = J.sa, se = J.se, r = J.r, cpg = J.cpg;
+    const bool packed = J.packed, do_meta = J.do_meta;
+    uint32_t mn0 = J.mn0, mx0 = J.mx0, mn1 = J.mn1, mx1 = J.mx1;
+    bits_t x0 = J.x0, x1 = J.x1, y0 = J.y0, y1 = J.y1;
+    // top-r, rounding and the stores of token `slot` from its rotated channels
+    auto store = [&](int slot, double v0, double v1) {
         const bits_t s0 = round_store<ST>(v0), s1 = round_store<ST>(v1);
         if (packed) {
             bool keep0, keep1;
@@ -249,6 +231,34 @@ __global__ __launch_bounds__(STAGE ? 256 : 128) void k_compress(const CompressAr
             vrow[lane] = s0;
             vrow[lane + 64] = s1;
         }
+    };
+    for (int slot = sa; slot < se;) {
+        const bool two = slot + 1 < se;
+        xs[0][lane] = (double)bits_to_float<ST>(x0);
+        xs[0][lane + 64] = (double)bits_to_float<ST>(x1);
+        if (two) {
+            xs[1][lane] = (double)bits_to_float<ST>(y0);
+            xs[1][lane + 64] = (double)bits_to_float<ST>(y1);
+        }
+        wave_lds_sync();
+        // the next two tokens' rows load while these are rotated
+        if (slot + 2 < se) {
+            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 2 - E.a)) * D;
+            x0 = xr[lane];
+            x1 = xr[lane + 64];
+        }
+        if (slot + 3 < se) {
+            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 3 - E.a)) * D;
+            y0 = xr[lane];
+            y1 = xr[lane + 64];
+        }
+        double a0, a1, b0, b1;
+        if (two) rotate_f64_lds<true>(Rs, xs[0], xs[1], lane, a0, a1, b0, b1);
+        else rotate_f64_lds<false>(Rs, xs[0], xs[0], lane, a0, a1, b0, b1);
+        wave_lds_sync();
+        store(slot, a0, a1);
+        if (two) store(slot + 1, b0, b1);
+        slot += two ? 2 : 1;
     }
 
     // a block started by this call: clear the slots after its last token
@@ -272,6 +282,66 @@ __global__ __launch_bounds__(STAGE ? 256 : 128) void k_compress(const CompressAr
             pr[0] = key_to_bits<ST>(h == 0 ? mn0 : mn1);
             pr[1] = key_to_bits<ST>(h == 0 ? mx0 : mx1);
         }
+    }
+}
+
+// One workgroup per (chunk of blocks, matrix) of an (entry, KV head): its 256
+// threads copy R_k or R_v into LDS (rows padded to D + 1 floats, so the 64
+// lanes reading 64 rows at one column hit distinct banks) with one round of
+// coalesced 16-byte loads; wave w then rotates blocks w, w + 4, ... of the
+// chunk (counted from the entry's first block E.blk0) from LDS, a token at a
+// time. Each wave's first block has its keys
+// and first row requested before the copy, so those loads overlap it. Appends
+// of a token or two use one-block chunks (one computing wave per matrix; the
+// K and V workgroups run side by side); bulk appends use A.chunk_blocks, so R
+// is read once per chunk rather than once per block.
+// Workgroups past the append table (z >= n_ent) rotate queries instead.
+template <typename ST>
+__global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
+    if ((int)blockIdx.z >= A.n_ent) {
+        if (blockIdx.x >= D / 32) return;
+        __shared__ __align__(16) float qsh[4][D];
+        const int b = (int)blockIdx.z - A.n_ent, g = (int)blockIdx.y, cb = (int)blockIdx.x;
+        switch (A.q_G) {
+        case 1: qrot_block<1>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+        case 2: qrot_block<2>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+        default: qrot_block<4>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+        }
+        return;
+    }
+    const CompressEntry &E = A.ent[blockIdx.z];
+    const int c0 = ((int)blockIdx.x >> 1) * A.chunk_blocks;
+    if (c0 >= E.nblk) return;
+    const int c1 = min(c0 + A.chunk_blocks, E.nblk);
+    const int mat = (int)blockIdx.x & 1;  // 0: keys (R_k), 1: values (R_v)
+    const int g = (int)blockIdx.y;
+    const int w = (int)(threadIdx.x >> 6);
+    const int lane = lane_id();
+    const size_t unit = (size_t)E.b * A.n_kv + g;
+    __shared__ __align__(16) double xs[4][2][D];
+    __shared__ float Rst[D][D + 1];
+    BlockJob<ST> J;
+    int bx = c0 + w;  // block index within the entry's range; the block is E.blk0 + bx
+    if (bx < c1) block_begin<ST>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
+    {
+        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + (unit * 2 + mat) * D * D);
+        float4 v[D * D / 4 / 256];
+#pragma unroll
+        for (int k = 0; k < D * D / 4 / 256; ++k) v[k] = Rg[threadIdx.x + 256 * k];
+#pragma unroll
+        for (int k = 0; k < D * D / 4 / 256; ++k) {
+            const int i = (int)threadIdx.x + 256 * k;
+            const int c = i / (D / 4), j = (i % (D / 4)) * 4;
+            Rst[c][j] = v[k].x;
+            Rst[c][j + 1] = v[k].y;
+            Rst[c][j + 2] = v[k].z;
+            Rst[c][j + 3] = v[k].w;
+        }
+    }
+    __syncthreads();
+    for (; bx < c1; bx += 4) {
+        if (bx != c0 + w) block_begin<ST>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
+        block_run<ST>(J, E, E.blk0 + bx, lane, Rst, xs[w]);
     }
 }
 
@@ -323,22 +393,20 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
 
 hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s) {
     if (a.n_ent <= 0 || max_blk <= 0) return a.q_req > 0 ? hipErrorInvalidValue : hipSuccess;
-    // a block of work per (entry, KV head) at most twice: stage R in LDS, one
-    // workgroup per matrix
-    const bool stage = compress_stages(max_blk);
-    // a query rotation rides along only on staged launches (256 threads)
-    if (a.q_req > 0 && (!stage || !a.q || !a.qa || !a.qs || (a.q_G != 1 && a.q_G != 2 && a.q_G != 4) ||
+    const bool small = compress_stages(max_blk);
+    // a query rotation rides along only on one-block-chunk launches
+    if (a.q_req > 0 && (!small || !a.q || !a.qa || !a.qs || (a.q_G != 1 && a.q_G != 2 && a.q_G != 4) ||
                         a.q_hq != a.q_G * a.n_kv))
         return hipErrorInvalidValue;
-    const unsigned gx = stage ? (unsigned)std::max(2 * max_blk, a.q_req > 0 ? D / 32 : 0) : (unsigned)max_blk;
+    CompressArgs b = a;
+    b.chunk_blocks = small ? 1 : COMPRESS_CHUNK;
+    const int nchunk = (max_blk + b.chunk_blocks - 1) / b.chunk_blocks;
+    const unsigned gx = (unsigned)std::max(2 * nchunk, a.q_req > 0 ? D / 32 : 0);
     const dim3 grid(gx, (unsigned)a.n_kv, (unsigned)(a.n_ent + std::max(a.q_req, 0)));
-    if (dtype == MKV_BF16) {
-        if (stage) hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_compress<Bf16, false>), grid, dim3(128), 0, s, a);
-    } else {
-        if (stage) hipLaunchKernelGGL((k_compress<F32, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_compress<F32, false>), grid, dim3(128), 0, s, a);
-    }
+    if (dtype == MKV_BF16)
+        hipLaunchKernelGGL(k_compress<Bf16>, grid, dim3(256), 0, s, b);
+    else
+        hipLaunchKernelGGL(k_compress<F32>, grid, dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

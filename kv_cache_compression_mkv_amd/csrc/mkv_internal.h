@@ -46,7 +46,8 @@ struct CompressArgs {
     const void *k_new;
     const void *v_new;
     const float *rot;
-    int32_t n_ent, n_kv, n_max, pad;
+    int32_t n_ent, n_kv, n_max;
+    int32_t chunk_blocks;  // blocks per workgroup (set by the launcher)
     // optional query rotation run beside the append (staged launches only):
     // workgroups z = n_ent .. n_ent + q_req - 1, x < 4, rotate request z - n_ent
     const float *q;
@@ -105,9 +106,10 @@ struct DecodeArgs {
     int32_t union_mode; // packed workgroups take exact byte shares of the union (S_p a multiple of 4)
 };
 
-// Appends touching at most this many blocks per (entry, KV head) stage R in
-// LDS, one 256-thread workgroup per matrix (and may carry a query rotation).
+// Appends touching at most two blocks per (entry, KV head) take one block per
+// workgroup and may carry a query rotation; larger ones take COMPRESS_CHUNK.
 constexpr bool compress_stages(int max_blk) { return max_blk <= 2; }
+constexpr int COMPRESS_CHUNK = 32;
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStream_t s);

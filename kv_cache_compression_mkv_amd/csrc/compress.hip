@@ -108,7 +108,7 @@ struct BlockJob {
 
 // Pointers of block blk, its stored keys (when it already holds tokens) and
 // the first new token's row: the loads are issued here, not waited for.
-template <typename ST>
+template <typename ST, bool BULK>
 __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs &A, const CompressEntry &E,
                                             size_t unit, int g, int blk, int wave, int lane) {
     using bits_t = typename ST::bits_t;
@@ -160,7 +160,7 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
         x0 = xr[lane];
         x1 = xr[lane + 64];
     }
-    if (sa + 1 < se) {
+    if (BULK && sa + 1 < se) {
         const bits_t *xr = xin + (size_t)(E.row0 + (p0 + sa + 1 - E.a)) * D;
         y0 = xr[lane];
         y1 = xr[lane + 64];
@@ -188,7 +188,7 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
 // two remain (R from LDS; xs is the wave's two LDS rows of doubles), clear the
 // slots after the last token of a block this call starts, and write the block
 // keys back.
-template <typename ST>
+template <typename ST, bool BULK>
 __device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &E, int blk, int lane,
                                           const float (*Rs)[D + 1], double (*xs)[D]) {
     using bits_t = typename ST::bits_t;
@@ -233,7 +233,7 @@ __device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &
         }
     };
     for (int slot = sa; slot < se;) {
-        const bool two = slot + 1 < se;
+        const bool two = BULK && slot + 1 < se;
         xs[0][lane] = (double)bits_to_float<ST>(x0);
         xs[0][lane + 64] = (double)bits_to_float<ST>(x1);
         if (two) {
@@ -241,19 +241,24 @@ __device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &
             xs[1][lane + 64] = (double)bits_to_float<ST>(y1);
         }
         wave_lds_sync();
-        // the next two tokens' rows load while these are rotated
-        if (slot + 2 < se) {
+        // the next tokens' rows load while these are rotated
+        if (!BULK && slot + 1 < se) {
+            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 1 - E.a)) * D;
+            x0 = xr[lane];
+            x1 = xr[lane + 64];
+        }
+        if (BULK && slot + 2 < se) {
             const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 2 - E.a)) * D;
             x0 = xr[lane];
             x1 = xr[lane + 64];
         }
-        if (slot + 3 < se) {
+        if (BULK && slot + 3 < se) {
             const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 3 - E.a)) * D;
             y0 = xr[lane];
             y1 = xr[lane + 64];
         }
         double a0, a1, b0, b1;
-        if (two) rotate_f64_lds<true>(Rs, xs[0], xs[1], lane, a0, a1, b0, b1);
+        if (BULK && two) rotate_f64_lds<true>(Rs, xs[0], xs[1], lane, a0, a1, b0, b1);
         else rotate_f64_lds<false>(Rs, xs[0], xs[0], lane, a0, a1, b0, b1);
         wave_lds_sync();
         store(slot, a0, a1);
@@ -296,7 +301,9 @@ __device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &
 // K and V workgroups run side by side); bulk appends use A.chunk_blocks, so R
 // is read once per chunk rather than once per block.
 // Workgroups past the append table (z >= n_ent) rotate queries instead.
-template <typename ST>
+// BULK: chunks of A.chunk_blocks blocks and two tokens per rotation pass;
+// otherwise one-block chunks, one token per pass.
+template <typename ST, bool BULK>
 __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     if ((int)blockIdx.z >= A.n_ent) {
         if (blockIdx.x >= D / 32) return;
@@ -318,11 +325,11 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     const int w = (int)(threadIdx.x >> 6);
     const int lane = lane_id();
     const size_t unit = (size_t)E.b * A.n_kv + g;
-    __shared__ __align__(16) double xs[4][2][D];
+    __shared__ __align__(16) double xs[4][BULK ? 2 : 1][D];
     __shared__ float Rst[D][D + 1];
     BlockJob<ST> J;
     int bx = c0 + w;  // block index within the entry's range; the block is E.blk0 + bx
-    if (bx < c1) block_begin<ST>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
+    if (bx < c1) block_begin<ST, BULK>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
     {
         const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + (unit * 2 + mat) * D * D);
         float4 v[D * D / 4 / 256];
@@ -340,8 +347,8 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     }
     __syncthreads();
     for (; bx < c1; bx += 4) {
-        if (bx != c0 + w) block_begin<ST>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
-        block_run<ST>(J, E, E.blk0 + bx, lane, Rst, xs[w]);
+        if (bx != c0 + w) block_begin<ST, BULK>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
+        block_run<ST, BULK>(J, E, E.blk0 + bx, lane, Rst, xs[w]);
     }
 }
 
@@ -403,10 +410,13 @@ hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStr
     const int nchunk = (max_blk + b.chunk_blocks - 1) / b.chunk_blocks;
     const unsigned gx = (unsigned)std::max(2 * nchunk, a.q_req > 0 ? D / 32 : 0);
     const dim3 grid(gx, (unsigned)a.n_kv, (unsigned)(a.n_ent + std::max(a.q_req, 0)));
-    if (dtype == MKV_BF16)
-        hipLaunchKernelGGL(k_compress<Bf16>, grid, dim3(256), 0, s, b);
-    else
-        hipLaunchKernelGGL(k_compress<F32>, grid, dim3(256), 0, s, b);
+    if (dtype == MKV_BF16) {
+        if (small) hipLaunchKernelGGL((k_compress<Bf16, false>), grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(256), 0, s, b);
+    } else {
+        if (small) hipLaunchKernelGGL((k_compress<F32, false>), grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL((k_compress<F32, true>), grid, dim3(256), 0, s, b);
+    }
     return hipGetLastError();
 }
 

@@ -192,7 +192,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload 1-5 (default 3: 128K context)")
+    ap.add_argument("--config", type=int, default=3, help="workload id: 1 single head 4K fp32, 2 32K layer, 3 128K batch 4 (default), 4 1M tokens, 5 serving batch 32")
     ap.add_argument("--scale", type=int, default=1, help="divide token counts (1 = full size)")
     ap.add_argument("--cpu-units", type=int, default=4, help="oracle sample size (0 disables)")
     ap.add_argument("--cpu-steps", type=int, default=600)
@@ -349,9 +349,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "config%d: GQA %d/%d heads d=%d, batch %d, T=%d/request at start, %s storage; "
-                        "step = append 1 token/request + decode attention" % (args.config, hq, hkv, d, B,
-                                                                              int(T0[0]), dt),
+            "workload": "GQA %d/%d heads d=%d, batch %d, T=%d/request at start, %s storage; "
+                        "step = append 1 token/request + decode attention" % (hq, hkv, d, B, int(T0[0]), dt),
             "global_batch": B,
             "seq_len": int(T0.max()),
             "segments": seg_desc,

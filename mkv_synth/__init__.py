@@ -185,13 +185,17 @@ def _stack(parts):
     return out
 
 
-def config5_lengths(batch: int = 32, lo: int = 16384, hi: int = 98304) -> np.ndarray:
+def serving_lengths(batch: int = 32, lo: int = 16384, hi: int = 98304) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5, 999])))
     return rng.integers(lo, hi + 1, size=batch).astype(np.int64)
 
 
 def workload(cfg: int, scale: int = 1, extra_cap: int = 0, batch: int | None = None):
-    """Describe one of the five workloads.
+    """Describe one of the five workloads, by id (the id also seeds its streams):
+    1 single head, T = 4096, fp32; 2 GQA 32/8 layer, T = 32768, bf16;
+    3 the same layer at T = 131072, batch 4, two packed segments; 4 the same
+    layer at T = 1048576 (one layer's share at million-token context);
+    5 serving, batch 32, T uniform in [16384, 98304].
 
     scale divides every token count (1 = full size); extra_cap adds capacity to
     the last segment (decode-step growth). Returns a dict with keys:
@@ -236,7 +240,7 @@ def workload(cfg: int, scale: int = 1, extra_cap: int = 0, batch: int | None = N
     elif cfg == 5:
         B = 32 if batch is None else batch
         hq, hk, dt = 32, 8, "bf16"
-        Ts = config5_lengths(32)[:B] // scale
+        Ts = serving_lengths(32)[:B] // scale
         sink = max(64 // scale, 1)
         layouts = [_stack([(DENSE, sink, 0, 0, 0),
                            (PACKED, int(t) - sink + 256 + extra_cap, 38, 100000, 0)]) for t in Ts]

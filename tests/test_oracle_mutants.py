@@ -1,0 +1,84 @@
+"""The oracle's pins reject plausible mistakes (CPU only).
+
+Each case copies oracle.c, plants one mistake by text substitution (a dropped
+term, a transposed operand, a wrong tie or rounding rule), builds the copy as
+a separate library and runs the pins that should catch it with the oracle
+module pointed at that library. The case passes when at least one of those
+pins fails. The committed oracle source is never modified.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+import pytest
+
+from oracle import oracle as orc
+
+import test_oracle_pins as pins
+
+_SRC = os.path.join(os.path.dirname(orc.__file__), "oracle.c")
+
+# (name, original text, planted text, pins expected to catch it)
+MUTANTS = [
+    # block score keeps only the q'*min term: the min/max bound no longer
+    # covers the block's tokens
+    ("score_min_only", "s += a > b ? a : b;", "s += b;",
+     [pins.test_P5_quest_score_equals_eq12_at_block_size_one]),
+    # logits and scores without the 1/sqrt(d) factor
+    ("score_unscaled", "sc[noff + l] = s * scale;", "sc[noff + l] = s;",
+     [pins.test_P5_quest_score_equals_eq12_at_block_size_one]),
+    # top-r ties go to the higher channel instead of the lower
+    ("topr_ties_high", "return x->c - y->c;", "return y->c - x->c;",
+     [pins.test_P3_worked_example_d4]),
+    # storage rounding rounds halves up instead of to even
+    ("round_half_up", "if (rem > half || (rem == half && (kept & 1))) kept++;", "if (rem >= half) kept++;",
+     [pins.test_round_bf16_is_nearest_even, pins.test_round_f32_matches_ieee_cast]),
+    # the rotation multiplies by R^T instead of R
+    ("rotation_transposed", "s += R[c * d + j] * x[j];", "s += R[j * d + c] * x[j];",
+     [pins.test_P4_full_retention_equals_dense_attention]),
+    # the inverse rotation multiplies by R_v instead of R_v^T
+    ("inverse_rotation_transposed", "s += Rv[c * d + jj] * o[c];", "s += Rv[jj * d + c] * o[c];",
+     [pins.test_P4_full_retention_equals_dense_attention]),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    with open(_SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation site not unique in oracle.c: %r" % old
+    path = tmp_path / ("oracle_%s.c" % name)
+    path.write_text(src.replace(old, new))
+    so = str(tmp_path / ("liboracle_%s.so" % name))
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                           "-shared", "-o", so, str(path), "-lm"])
+    return so
+
+
+@pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_planted_mistake(tmp_path, name, old, new, catchers):
+    so = _build_mutant(tmp_path, name, old, new)
+    saved_so, saved_lib = orc._SO, orc._LIB
+    caught = []
+    try:
+        orc._SO, orc._LIB = so, None
+        for pin in catchers:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(pin.__name__)
+    finally:
+        orc._SO, orc._LIB = saved_so, saved_lib
+    assert caught, "no pin caught the planted mistake %s" % name
+
+
+def test_unmutated_copy_passes_the_same_pins(tmp_path):
+    """The harness itself: a copy built the same way with no change passes every pin used above."""
+    so = _build_mutant(tmp_path, "none", "return x->c - y->c;", "return x->c - y->c;")
+    saved_so, saved_lib = orc._SO, orc._LIB
+    try:
+        orc._SO, orc._LIB = so, None
+        for pin in {p for m in MUTANTS for p in m[3]}:
+            pin()
+    finally:
+        orc._SO, orc._LIB = saved_so, saved_lib

@@ -8,6 +8,7 @@ pins fails. The committed oracle source is never modified.
 """
 from __future__ import annotations
 
+import inspect
 import os
 import subprocess
 
@@ -37,6 +38,19 @@ MUTANTS = [
     # the rotation multiplies by R^T instead of R
     ("rotation_transposed", "s += R[c * d + j] * x[j];", "s += R[j * d + c] * x[j];",
      [pins.test_P4_full_retention_equals_dense_attention]),
+    # the block count rounds down instead of up
+    ("keep_floor", "else k = ((int64_t)keep_ppm * n + 999999) / 1000000;",
+     "else k = ((int64_t)keep_ppm * n) / 1000000;", [pins.test_block_keep_rule]),
+    # top-k ties go to the higher block instead of the lower
+    ("topk_ties_high", "return x->l < y->l ? -1 : (x->l > y->l ? 1 : 0);",
+     "return x->l > y->l ? -1 : (x->l < y->l ? 1 : 0);", [pins.test_P6_topk_matches_subset_enumeration]),
+    # sigma reported as the eigenvalue itself, not its square root
+    ("sigma_not_sqrt", "if (sigma) sigma[c] = sqrt(lam > 0.0 ? lam : 0.0);",
+     "if (sigma) sigma[c] = lam > 0.0 ? lam : 0.0;", [pins.test_P2_energy_closed_form_and_singular_values]),
+    # R stored with the singular vectors as columns instead of rows
+    ("rotation_vectors_as_columns", "for (int j = 0; j < d; ++j) R[c * d + j] = sg * V[j * d + col];",
+     "for (int j = 0; j < d; ++j) R[j * d + c] = sg * V[j * d + col];",
+     [pins.test_P2_energy_closed_form_and_singular_values, pins.test_rotation_matches_library_svd_vectors]),
     # the inverse rotation multiplies by R_v instead of R_v^T
     ("inverse_rotation_transposed", "s += Rv[c * d + jj] * o[c];", "s += Rv[jj * d + c] * o[c];",
      [pins.test_P4_full_retention_equals_dense_attention]),
@@ -55,6 +69,17 @@ def _build_mutant(tmp_path, name, old, new):
     return so
 
 
+def _call(pin):
+    """Run a pin against whichever oracle library is current; pins that take
+    the rotation case get one computed by that library."""
+    if "rot_case" in inspect.signature(pin).parameters:
+        K, _ = pins._unit_inputs(3000)
+        R, sig = orc.rotation(K)
+        pin((K, R, sig))
+    else:
+        pin()
+
+
 @pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_reject_planted_mistake(tmp_path, name, old, new, catchers):
     so = _build_mutant(tmp_path, name, old, new)
@@ -64,7 +89,7 @@ def test_pins_reject_planted_mistake(tmp_path, name, old, new, catchers):
         orc._SO, orc._LIB = so, None
         for pin in catchers:
             try:
-                pin()
+                _call(pin)
             except AssertionError:
                 caught.append(pin.__name__)
     finally:
@@ -79,6 +104,6 @@ def test_unmutated_copy_passes_the_same_pins(tmp_path):
     try:
         orc._SO, orc._LIB = so, None
         for pin in {p for m in MUTANTS for p in m[3]}:
-            pin()
+            _call(pin)
     finally:
         orc._SO, orc._LIB = saved_so, saved_lib

@@ -22,8 +22,8 @@
  *     hipStream_t; NULL is the null stream); calls return after the enqueue.
  *     Faults of enqueued work surface at the caller's next synchronisation.
  *   - The library allocates no device memory and keeps no state between calls
- *     apart from the optional kernel-timing facility below. The caller owns
- *     every buffer. Calls on distinct caches are thread-safe; one cache must be
+ *     apart from the optional kernel-timing facility below (thread-safe).
+ *     The caller owns every buffer. Calls on distinct caches are thread-safe; one cache must be
  *     used from one stream at a time.
  *   - Inputs must be finite (NaN/Inf behaviour is unspecified).
  *   - The GPU path supports head_dim == 128, storage MKV_F32 or MKV_BF16, and
@@ -139,7 +139,9 @@ const char *mkv_status_str(mkv_status s);
  * eigenvalue and makes the largest-magnitude entry of each row positive (ties
  * to the lower index). R_out [d][d] host float32 (row c = c-th vector),
  * sigma_out [d] host float64 (nullable) = sqrt(max(eigenvalue, 0)).
- * Synchronous host computation (OpenMP); d in 1..256, T >= 0.
+ * Synchronous host computation (OpenMP); d in 1..256, T >= 0. The Gram sums
+ * run in a fixed order, so R and sigma are bitwise the same whatever the
+ * number of host threads.
  * Errors: MKV_ERR_ARG, MKV_ERR_NOCONVERGE. */
 mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtype, int64_t T, int32_t d,
                                      float *R_out, double *sigma_out);
@@ -211,8 +213,10 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
                              int32_t n_max, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
                              void *workspace, size_t ws_bytes, void *stream);
 
-/* Optional kernel timing (a diagnostic, not thread-safe): while enabled, every
- * kernel the library launches is bracketed by HIP events on its stream.
+/* Optional kernel timing (a diagnostic; process-wide, thread-safe): while
+ * enabled, every kernel the library launches, from any thread, is bracketed
+ * by HIP events on its stream. This is the library's only state kept between
+ * calls: a pool of HIP events and the pairs not yet read.
  * mkv_timing_read synchronises those events and returns, per stage, the summed
  * milliseconds and the number of launches since the last read, then clears
  * them. Stages: 0 compress (with the query rotation when mkv_append_decode

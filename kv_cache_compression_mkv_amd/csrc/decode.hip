@@ -1310,6 +1310,10 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     const int t = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x >> 6);
     const int Stot = (A.S_d + 3) / 4 + (A.S_p + 3) / 4;  // one partial per attend workgroup
     const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_SPLITS * PART;
+    if (A.npk == 0 && A.sel_out) {  // no packed segment, no select launch: all of sel_out is padding
+        int32_t *so = A.sel_out + ((size_t)b * A.hq + h) * A.sel_cols;
+        for (int64_t c = t; c < A.sel_cols; c += 256) so[c] = -1;
+    }
     __shared__ float wsc[MAX_SPLITS];
     __shared__ float red[2][4];
     __shared__ __align__(16) float part_o[8][D];

@@ -40,21 +40,44 @@ hipEvent_t take_event(Timing &t) {
     return e;
 }
 
+void give_back(Timing &t, hipEvent_t a, hipEvent_t b) {
+    std::lock_guard<std::mutex> g(t.mu);
+    if (a) t.pool.push_back(a);
+    if (b) t.pool.push_back(b);
+}
+
+// Run one launch; while timing is enabled, bracket it with a pair of events on
+// its stream. Every access to the shared timing state holds its mutex, and the
+// events go back to the pool when a record or the launch fails.
 template <class F>
 mkv_status timed(int stage, hipStream_t s, F &&launch) {
     Timing &t = timing();
     hipEvent_t a = nullptr, b = nullptr;
-    if (t.on) {
+    {
         std::lock_guard<std::mutex> g(t.mu);
-        a = take_event(t);
-        b = take_event(t);
-        if (!a || !b) return MKV_ERR_HIP;
-        if (hipEventRecord(a, s) != hipSuccess) return MKV_ERR_HIP;
+        if (t.on) {
+            a = take_event(t);
+            b = a ? take_event(t) : nullptr;
+            if (!a || !b) {
+                if (a) t.pool.push_back(a);
+                return MKV_ERR_HIP;
+            }
+        }
     }
-    if (launch() != hipSuccess) return MKV_ERR_HIP;
-    if (t.on) {
+    if (a && hipEventRecord(a, s) != hipSuccess) {
+        give_back(t, a, b);
+        return MKV_ERR_HIP;
+    }
+    if (launch() != hipSuccess) {
+        give_back(t, a, b);
+        return MKV_ERR_HIP;
+    }
+    if (a) {
+        if (hipEventRecord(b, s) != hipSuccess) {
+            give_back(t, a, b);
+            return MKV_ERR_HIP;
+        }
         std::lock_guard<std::mutex> g(t.mu);
-        if (hipEventRecord(b, s) != hipSuccess) return MKV_ERR_HIP;
         t.pending[stage].push_back({a, b});
     }
     return MKV_OK;

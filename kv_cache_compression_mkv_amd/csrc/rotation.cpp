@@ -1,8 +1,8 @@
 // Host-side rotation from prefill vectors ("MosaicKV 阅读笔记" reading notes,
 // Eq. 4 and 6-8; paper summary section 2.3): R = V^T with X^T X = V S^2 V^T.
 //
-// G = X^T X is accumulated in float64 (per-thread partial Gram matrices over
-// token chunks), reduced to tridiagonal form by Householder reflections and
+// G = X^T X is accumulated in float64 (partial Gram matrices over fixed token
+// ranges, added in a fixed order), reduced to tridiagonal form by Householder reflections and
 // diagonalised by the implicit symmetric QR iteration with Wilkinson shifts
 // (Golub and Van Loan, "Matrix Computations", sections 8.3.1 and 8.3.3).
 #include <math.h>
@@ -27,36 +27,47 @@ double elem(const void *x, int32_t dtype, int64_t i) {
 }
 
 // Upper triangle of X^T X, X given row-major [T][d] in the storage dtype.
+// The tokens are cut into GRAM_PARTS contiguous ranges of whole 64-token
+// chunks; each range sums its chunks in order into its own partial, and the
+// partials are added in range order. Neither depends on the thread count, so
+// G (and R) is bitwise the same on every host.
+constexpr int GRAM_PARTS = 64;
+
 void gram(const void *x, int32_t dtype, int64_t T, int d, std::vector<double> &G) {
-    const int nthr = std::max(1, std::min(omp_get_max_threads(), 64));
-    std::vector<std::vector<double>> partial(nthr);
     const int64_t chunk = 64;
+    const int64_t nchunk = (T + chunk - 1) / chunk;
+    std::vector<std::vector<double>> partial(GRAM_PARTS);
+    const int nthr = std::max(1, std::min(omp_get_max_threads(), GRAM_PARTS));
 #pragma omp parallel num_threads(nthr)
     {
-        const int tid = omp_get_thread_num();
-        std::vector<double> &acc = partial[tid];
-        acc.assign((size_t)d * d, 0.0);
         std::vector<double> xt((size_t)d * chunk);  // chunk transposed: [d][chunk]
-#pragma omp for schedule(static)
-        for (int64_t t0 = 0; t0 < T; t0 += chunk) {
-            const int64_t n = std::min<int64_t>(chunk, T - t0);
-            for (int64_t t = 0; t < n; ++t)
-                for (int c = 0; c < d; ++c) xt[(size_t)c * chunk + t] = elem(x, dtype, (t0 + t) * d + c);
-            for (int i = 0; i < d; ++i) {
-                const double *xi = &xt[(size_t)i * chunk];
-                for (int j = i; j < d; ++j) {
-                    const double *xj = &xt[(size_t)j * chunk];
-                    double s = 0.0;
-                    for (int64_t t = 0; t < n; ++t) s += xi[t] * xj[t];
-                    acc[(size_t)i * d + j] += s;
+#pragma omp for schedule(dynamic)
+        for (int p = 0; p < GRAM_PARTS; ++p) {
+            const int64_t c0 = nchunk * p / GRAM_PARTS, c1 = nchunk * (p + 1) / GRAM_PARTS;
+            if (c0 >= c1) continue;
+            std::vector<double> &acc = partial[p];
+            acc.assign((size_t)d * d, 0.0);
+            for (int64_t ci = c0; ci < c1; ++ci) {
+                const int64_t t0 = ci * chunk;
+                const int64_t n = std::min<int64_t>(chunk, T - t0);
+                for (int64_t t = 0; t < n; ++t)
+                    for (int c = 0; c < d; ++c) xt[(size_t)c * chunk + t] = elem(x, dtype, (t0 + t) * d + c);
+                for (int i = 0; i < d; ++i) {
+                    const double *xi = &xt[(size_t)i * chunk];
+                    for (int j = i; j < d; ++j) {
+                        const double *xj = &xt[(size_t)j * chunk];
+                        double s = 0.0;
+                        for (int64_t t = 0; t < n; ++t) s += xi[t] * xj[t];
+                        acc[(size_t)i * d + j] += s;
+                    }
                 }
             }
         }
     }
     G.assign((size_t)d * d, 0.0);
-    for (int tid = 0; tid < nthr; ++tid)
-        if (!partial[tid].empty())
-            for (size_t k = 0; k < G.size(); ++k) G[k] += partial[tid][k];
+    for (int p = 0; p < GRAM_PARTS; ++p)
+        if (!partial[p].empty())
+            for (size_t k = 0; k < G.size(); ++k) G[k] += partial[p][k];
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < i; ++j) G[(size_t)i * d + j] = G[(size_t)j * d + i];
 }

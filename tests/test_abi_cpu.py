@@ -179,3 +179,27 @@ def test_host_rotation_edge_cases(L):
         L.mkv_rotation_from_prefill(x.ctypes.data, L.MKV_F32, 2, 0, R.ctypes.data, None)
     with pytest.raises(L.MkvError):
         L.mkv_rotation_from_prefill(None, L.MKV_F32, 2, 4, R.ctypes.data, None)
+
+
+def test_host_rotation_is_bitwise_independent_of_thread_count():
+    """The Gram sums run in a fixed order, so R and sigma are the same bits at 1
+    host thread and at several."""
+    import hashlib
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys, hashlib, numpy as np\n"
+        "sys.path.insert(0, %r)\n"
+        "import mkv_synth as synth\n"
+        "from kv_cache_compression_mkv_amd import _lib as L\n"
+        "_, bits = synth.gen_kv(3, 0, 1, 1, 0, 20001, 'bf16')\n"
+        "R = np.empty((128, 128), np.float32); s = np.empty(128, np.float64)\n"
+        "L.mkv_rotation_from_prefill(bits.ctypes.data, L.MKV_BF16, 20001, 128, R.ctypes.data, s.ctypes.data)\n"
+        "print(hashlib.sha256(R.tobytes() + s.tobytes()).hexdigest())\n" % root)
+    digests = set()
+    for n in (1, 3, 8):
+        env = dict(os.environ, OMP_NUM_THREADS=str(n))
+        out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
+        digests.add(out.stdout.strip().splitlines()[-1])
+    assert len(digests) == 1

@@ -54,6 +54,23 @@ MUTANTS = [
     # the inverse rotation multiplies by R_v instead of R_v^T
     ("inverse_rotation_transposed", "s += Rv[c * d + jj] * o[c];", "s += Rv[jj * d + c] * o[c];",
      [pins.test_P4_full_retention_equals_dense_attention]),
+    # forced selection: every packed segment reads the first segment's columns
+    ("forced_offset_dropped", "sh[koff + i] = forced_sel[h * ksum + koff + i];",
+     "sh[koff + i] = forced_sel[h * ksum + i];",
+     [pins.test_forced_random_selection_equals_dense_reconstruction,
+      pins.test_forced_selection_of_own_choice_is_identical]),
+    # the threshold reported is the (k+1)-th score instead of the k-th
+    ("tau_next_score", "tau[h * npacked + pj] = k > 0 ? tmp[k - 1].s : NAN;",
+     "tau[h * npacked + pj] = k > 0 ? tmp[k].s : NAN;", [pins.test_tau_is_kth_largest_score]),
+    # incremental appends rebuild block keys from the block after the one the
+    # previous call left partly filled
+    ("incremental_keys_skip_open_block", "const int64_t from = t_from > t_begin[j] ? (t_from - t_begin[j]) / block : 0;",
+     "const int64_t from = t_from > t_begin[j] ? (t_from - t_begin[j]) / block + 1 : 0;",
+     [pins.test_incremental_compression_equals_bulk]),
+    # incremental appends skip the first new token
+    ("incremental_skips_first_token", "for (int64_t t = t_from; t < len; ++t) {\n        const int j",
+     "for (int64_t t = t_from + 1; t < len; ++t) {\n        const int j",
+     [pins.test_incremental_compression_equals_bulk]),
 ]
 
 

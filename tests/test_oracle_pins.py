@@ -348,3 +348,140 @@ def test_P9_P10_bytes_model_reproduces_printed_values():
     assert bm.quest_key_overhead(16) * 100 == vals["quest_key_overhead"][0]
     assert round(bm.theoretical_speedup(0.10, 0.30), 1) == vals["theoretical_speedup"][0]
     assert int(mb(bm.dense_kv_bytes(128000, 128, 2))) == vals["h800_head_bytes"][0]
+
+
+# ------------------------------------------ forced selection and threshold --
+def _decode_case(seed, d=16, T=310, dtype="bf16"):
+    """A unit with two dense and two packed segments (one by keep ratio, one by
+    absolute count), compressed by the oracle, and four query heads."""
+    rng = np.random.default_rng(seed)
+    K = orc.round_to(rng.standard_normal((T, d)), dtype)
+    V = orc.round_to(rng.standard_normal((T, d)), dtype)
+    Rk, _ = orc.rotation(rng.standard_normal((64, d)))
+    Rv, _ = orc.rotation(rng.standard_normal((64, d)))
+    segs = [synth.seg(0, 0, 10), synth.seg(1, 10, 130, 4, 250000, 0),
+            synth.seg(1, 140, 120, 7, 0, 3), synth.seg(0, 260, 60)]
+    comp = orc.compress_unit(K, V, Rk, Rv, segs, T, dtype)
+    q = rng.standard_normal((4, d))
+    return comp, q, Rk, Rv, segs
+
+
+def _token_mask(segs, length, sel_per_seg, h):
+    """Tokens attended by head h: every filled dense token and every valid token
+    of each given block of each packed segment."""
+    att = np.zeros(length, bool)
+    pj = 0
+    for s in segs:
+        filled = min(max(length - s["t_begin"], 0), s["t_cap"])
+        if s["kind"] == synth.DENSE:
+            att[s["t_begin"]:s["t_begin"] + filled] = True
+            continue
+        for l in sel_per_seg[pj][h]:
+            t0 = s["t_begin"] + 16 * int(l)
+            att[t0:min(t0 + 16, s["t_begin"] + filled)] = True
+        pj += 1
+    return att
+
+
+def test_forced_selection_of_own_choice_is_identical():
+    """Forcing the oracle's own top-k reproduces every output bit for bit: the
+    forced mode changes only where the block list comes from."""
+    for seed in (21, 22, 23):
+        comp, q, Rk, Rv, _ = _decode_case(seed)
+        own = orc.decode_unit(comp, q, Rk, Rv)
+        forced = orc.decode_unit(comp, q, Rk, Rv, forced_sel=own["sel"])
+        assert np.array_equal(own["out"].view(np.uint64), forced["out"].view(np.uint64))
+        for a, b in zip(own["sel"], forced["sel"]):
+            assert np.array_equal(a, b)
+
+
+def test_forced_random_selection_equals_dense_reconstruction():
+    """Any valid forced block list gives softmax(q' K^T / sqrt d) V^ over exactly
+    those tokens (zero-filled K^, V^ and float64 matrix products, reading notes
+    Eq. 13), rotated back by R_v (Eq. 14); q' is recomputed as R_k q here."""
+    rng = np.random.default_rng(31)
+    comp, q, Rk, Rv, segs = _decode_case(24)
+    T, d = comp["length"], q.shape[1]
+    nk = orc.seg_blocks(segs, T)
+    for trial in range(12):
+        forced = [np.stack([np.sort(rng.choice(nb, size=k, replace=False)) for _ in range(4)]).astype(np.int32)
+                  for nb, k in nk]
+        res = orc.decode_unit(comp, q, Rk, Rv, forced_sel=forced)
+        for a, b in zip(res["sel"], forced):
+            assert np.array_equal(a, b)
+        for h in range(4):
+            att = _token_mask(segs, T, forced, h)
+            qr = Rk @ q[h]
+            o = brute.attention_dense(comp["Khat"][:T], comp["Vhat"][:T], qr, att, d)
+            ref = o @ Rv
+            assert np.abs(res["out"][h] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_tau_is_kth_largest_score():
+    """tau of a (head, packed segment) is its k-th largest block score: fewer than
+    k scores lie above it and at least k at or above it, and it is the smallest
+    score of the best k-subset found by enumeration."""
+    rng = np.random.default_rng(41)
+    for seed in range(6):
+        comp, q, Rk, Rv, segs = _decode_case(50 + seed, T=int(rng.integers(120, 310)))
+        res = orc.decode_unit(comp, q, Rk, Rv)
+        for pj, (nb, k) in enumerate(orc.seg_blocks(segs, comp["length"])):
+            sc = res["scores"][pj]
+            for h in range(4):
+                tau = res["tau"][h, pj]
+                assert np.sum(sc[h] > tau) < k <= np.sum(sc[h] >= tau)
+                assert tau == np.sort(sc[h])[::-1][k - 1]
+                if nb <= 12:
+                    assert tau == sc[h][brute.topk_subsets(sc[h], k)].min()
+
+
+# ------------------------------------------------- incremental compression --
+def _incremental_unit(dtype="bf16", seed=61):
+    rng = np.random.default_rng(seed)
+    d, T = 16, 300
+    K = orc.round_to(rng.standard_normal((T, d)), dtype)
+    V = orc.round_to(rng.standard_normal((T, d)), dtype)
+    Rk, _ = orc.rotation(rng.standard_normal((64, d)))
+    Rv, _ = orc.rotation(rng.standard_normal((64, d)))
+    # packed segments start off the 16-token grid of positions, so block
+    # boundaries of the two packed segments fall at different positions
+    segs = [synth.seg(0, 0, 8), synth.seg(1, 8, 150, 5, 200000, 0), synth.seg(1, 158, 72, 3, 0, 2),
+            synth.seg(0, 230, 70)]
+    return K, V, Rk, Rv, segs
+
+
+def _same_bits(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint64), np.asarray(b).view(np.uint64))
+
+
+def _assert_same_state(st, bulk, length):
+    for key in ("Khat", "Vhat"):
+        assert _same_bits(st[key][:length], bulk[key][:length]), key
+    for key in ("Kidx", "Vidx"):
+        assert np.array_equal(st[key][:length], bulk[key][:length]), key
+    assert _same_bits(st["meta_flat"], bulk["meta_flat"])
+    for a, b in zip(st["meta"], bulk["meta"]):
+        assert _same_bits(a, b)
+
+
+def test_incremental_compression_equals_bulk():
+    """Compressing a unit in ragged pieces (a piece ending inside a block, pieces
+    that continue a partly filled block, one crossing the boundary of two packed
+    segments, single tokens) gives the same stored vectors, indices and block
+    keys, bit for bit, as one call over all tokens."""
+    K, V, Rk, Rv, segs = _incremental_unit()
+    T = K.shape[0]
+    cuts = [3, 8, 13, 24, 25, 31, 40, 41, 100, 157, 163, 164, 174, 200, 229, 231, 300]
+    st = None
+    for c in cuts:
+        st = orc.compress_unit(K, V, Rk, Rv, segs, c, "bf16", state=st)
+        bulk = orc.compress_unit(K, V, Rk, Rv, segs, c, "bf16")
+        _assert_same_state(st, bulk, c)
+    rng = np.random.default_rng(62)
+    for trial in range(4):
+        cuts = np.unique(np.concatenate([rng.integers(1, T, 12), [T]]))
+        st = None
+        for c in cuts:
+            st = orc.compress_unit(K, V, Rk, Rv, segs, int(c), "f32" if trial % 2 else "bf16", state=st)
+        bulk = orc.compress_unit(K, V, Rk, Rv, segs, T, "f32" if trial % 2 else "bf16")
+        _assert_same_state(st, bulk, T)

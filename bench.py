@@ -146,45 +146,83 @@ def prefill_summary(ms, vectors, d):
                          "frac": round(tf / PEAK_FP64_TFLOPS, 4), "flops_per_token_head": 4 * d * d}}
 
 
-def cpu_baseline(cfg, scale, R, T0, steps, n_units, nthreads):
-    """The oracle as it stands, on a bounded sample: n_units (request, KV head)
-    units each run `steps` decode steps (append one token, then decode); the
-    per-unit step time is scaled to all units of the workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, scale, R, T0, steps, n_units, workers, steps_1t):
+    """The oracle as it stands, on a bounded sample of the workload's
+    (request, KV head) units. Each unit is compressed up to its prompt length
+    (not timed), then runs decode steps (append one token, then decode its G
+    query heads) with one oracle thread per unit:
+      * all cores: `workers` units at once, one per thread (the oracle's own
+        threading only spans the 4 heads of a unit, so units run side by side);
+      * one thread: one unit alone.
+    A step of the whole workload is B * Hkv unit-steps; tokens/s = sum_b T_b
+    over that step time."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from oracle import oracle as orc
-    w = workload(cfg, scale, steps + 64)
+    w = workload(cfg, scale, 2 * steps + steps_1t + 64)
     G = w["n_q_heads"] // w["n_kv_heads"]
-    dt = w["dtype"]
-    d = w["d"]
+    dt, d, hkv = w["dtype"], w["d"], w["n_kv_heads"]
+    n_all = w["batch"] * hkv
     to64 = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if dt == "bf16" else \
         (lambda a: a.astype(np.float64))
-    units = [(u // w["n_kv_heads"], u % w["n_kv_heads"]) for u in range(n_units)]
     npdt = np.uint16 if dt == "bf16" else np.float32
-    total, n = 0.0, 0
+    # spread the sample over the workload's units
+    units = [divmod(int(u * n_all // n_units), hkv) for u in range(n_units)]
+    prep_threads = synth.host_threads()
+    states = []
     for b, g in units:
-        rows = int(T0[b]) + steps
+        rows = int(T0[b]) + 2 * steps + steps_1t + 1
         Kb = np.empty((rows, d), npdt)
         Vb = np.empty((rows, d), npdt)
         synth.gen_kv_into(cfg, b, g, 0, 0, rows, dt, Kb, d)
         synth.gen_kv_into(cfg, b, g, 1, 0, rows, dt, Vb, d)
         Kr, Vr = to64(Kb), to64(Vb)
         Rk, Rv = R[b, g, 0].astype(np.float64), R[b, g, 1].astype(np.float64)
-        st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]), dt, nthreads=nthreads)
-        for s in range(steps):
-            q = synth.gen_q(cfg, 5000 + s, w["batch"], w["n_q_heads"], dt)[b, g * G:(g + 1) * G]
-            t0 = time.perf_counter()
-            st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]) + s + 1, dt, nthreads=nthreads,
-                                   state=st)
-            orc.decode_unit(st, q.astype(np.float64), Rk, Rv, nthreads=nthreads)
-            total += time.perf_counter() - t0
-            n += 1
-    per_unit_step = total / n
-    full_step = per_unit_step * w["batch"] * w["n_kv_heads"]
-    return dict(value=float(np.sum(T0) / full_step), unit="tokens/s", cores=nthreads, kind="oracle",
-                sample="%d (request, KV head) units x %d steps of append-1-token + decode at T=%d; "
-                       "per-unit step %.2f ms scaled to %d units" % (n_units, steps, int(T0[0]),
-                                                                  per_unit_step * 1e3,
-                                                                  w["batch"] * w["n_kv_heads"]),
-                seconds=float(total))
+        st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], int(T0[b]), dt, nthreads=prep_threads)
+        qs = [synth.gen_q(cfg, 5000 + s, w["batch"], w["n_q_heads"], dt)[b, g * G:(g + 1) * G].astype(np.float64)
+              for s in range(steps + steps_1t)]
+        states.append([b, Kr, Vr, Rk, Rv, st, qs])
+
+    def run(i, n, q0):
+        b, Kr, Vr, Rk, Rv, st, qs = states[i]
+        for s in range(n):
+            st = orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], st["length"] + 1, dt, nthreads=1, state=st)
+            orc.decode_unit(st, qs[q0 + s], Rk, Rv, nthreads=1)
+        states[i][5] = st
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda i: run(i, steps, 0), range(n_units)))
+    wall = time.perf_counter() - t0
+    unit_steps_per_s = n_units * steps / wall
+    t1 = time.perf_counter()
+    run(0, steps_1t, steps)
+    one = (time.perf_counter() - t1) / steps_1t
+    total_T = float(np.sum(T0))
+    return dict(value=total_T / (n_all / unit_steps_per_s), unit="tokens/s", cores=min(workers, n_units),
+                kind="oracle", cpu_model=cpu_model(), host_cpus_visible=len(os.sched_getaffinity(0)),
+                sample="%d of %d (request, KV head) units x %d decode steps each (append 1 token + decode "
+                       "its %d query heads) at T=%d, one oracle thread per unit, %d units at once: %.1f s; "
+                       "scaled to all %d units" % (n_units, n_all, steps, G, int(T0[0]), min(workers, n_units),
+                                                   wall, n_all),
+                one_thread={"value": total_T / (n_all * one), "cores": 1,
+                            "sample": "1 unit x %d decode steps, %.2f ms per unit-step" % (steps_1t, one * 1e3)},
+                seconds=float(wall + one * steps_1t))
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a, np.float64), q))
 
 
 def main():
@@ -192,10 +230,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload id: 1 single head 4K fp32, 2 32K layer, 3 128K batch 4 (default), 4 1M tokens, 5 serving batch 32")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload id: 1 single head 4K fp32, 2 32K layer, 3 128K batch 4 (default), "
+                         "4 1M tokens, 5 serving batch 32")
     ap.add_argument("--scale", type=int, default=1, help="divide token counts (1 = full size)")
-    ap.add_argument("--cpu-units", type=int, default=4, help="oracle sample size (0 disables)")
-    ap.add_argument("--cpu-steps", type=int, default=600)
+    ap.add_argument("--cpu-units", type=int, default=-1,
+                    help="oracle sample: units run side by side (-1: one per host thread; 0 disables)")
+    ap.add_argument("--cpu-steps", type=int, default=600, help="oracle decode steps per unit")
+    ap.add_argument("--cpu-steps-1t", type=int, default=300, help="oracle decode steps of the 1-thread run")
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct layer caches visited round-robin (keeps every call cache-cold)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -211,9 +253,9 @@ def main():
     w = workload(args.config, args.scale, cap_extra)
     T0 = np.asarray(w["lengths"], np.int64)
     B, hq, hkv, d, dt = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["d"], w["dtype"]
-    G = hq // hkv
     n_step_total = W_steps + 2 * K_steps + 1
-    log("workload cfg=%d scale=%d B=%d T=%s dtype=%s" % (args.config, args.scale, B, list(T0), dt))
+    log("workload cfg=%d scale=%d B=%d T=[%d..%d] dtype=%s" % (args.config, args.scale, B, int(T0.min()),
+                                                              int(T0.max()), dt))
 
     t = time.time()
     K, V = gen_rows(w, int(T0.max()) + n_step_total)
@@ -247,13 +289,14 @@ def main():
         caches.append(c)
     del kpre, vpre
     prefill_ms = float(np.median(prefill_all))
-    log("prefill compress of %d tokens per layer cache: %s ms" % (int(T0.sum()) * hkv,
-                                                              ", ".join("%.2f" % t for t in prefill_all)))
+    log("prefill compress of %d (token, KV head) pairs per layer cache: %s ms" % (
+        int(T0.sum()) * hkv, ", ".join("%.2f" % t for t in prefill_all)))
 
     # per-step inputs, resident in HBM before timing
     newk = [dev(torch, np.stack([K[b, :, T0[b] + s:T0[b] + s + 1] for b in range(B)])) for s in range(n_step_total)]
     newv = [dev(torch, np.stack([V[b, :, T0[b] + s:T0[b] + s + 1] for b in range(B)])) for s in range(n_step_total)]
     qs = [torch.from_numpy(synth.gen_q(args.config, s, B, hq, dt)).cuda() for s in range(n_step_total)]
+    del K, V
     out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
     ones = [1] * B
     step = 0
@@ -270,19 +313,21 @@ def main():
         run_step()
     torch.cuda.synchronize()
     tok0 = len(tokens)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps + 1)]
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(K_steps):
+    evs[0].record()
+    for i in range(K_steps):
         run_step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(K_steps)]
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = wall * 1e3 / K_steps
     mean_len = float(np.mean(tokens[tok0:tok0 + K_steps]))
     value = mean_len / (ms_per_step / 1e3)
-    log("timed %d steps: %.3f ms/step wall, %.3f ms/step GPU events" % (K_steps, ms_per_step, gpu_ms / K_steps))
+    log("timed %d steps: %.4f ms/step wall, %.4f ms/step GPU events (p10 %.4f, p50 %.4f, p90 %.4f)" % (
+        K_steps, ms_per_step, gpu_ms / K_steps, pct(step_ms, 10), pct(step_ms, 50), pct(step_ms, 90)))
 
     # per-kernel durations, live: HIP events around every launch of the same steps
     L.mkv_timing_enable(True)
@@ -302,22 +347,46 @@ def main():
     summ = union_summary(w, lens_now, sel.cpu().numpy())
     sb = 2 if dt == "bf16" else 4
     call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
-    append_bytes = B * hkv * 2 * (d * d * 4 + d * sb)
-    step_bytes = call["total"] + append_bytes
+    r_new = [s["r"] for s in w["segs"][0] if s["kind"] == synth.PACKED][-1]
+    append = bm.append_bytes(d, sb, hkv, B, r_new)
+    step_bytes = call["total"] + append
+    # algorithmic bytes each kernel of the step must move (the query rotation
+    # runs in the append's launch: it reads R_k and the queries, writes q')
+    qrot_bytes = B * hkv * d * d * 4 + B * hq * d * 4
     cand = {"attend": call["records"] + call["dense"], "score": call["meta"], "select": 0,
-            "merge": 0, "q_rotate": 0}
-    dom = max(cand, key=lambda k: stage_ms.get(k, 0.0))
+            "merge": B * hkv * d * d * 4 + B * hq * d * 4, "compress": append + qrot_bytes, "q_rotate": qrot_bytes}
+    kernels = {}
+    for k, ms in stage_ms.items():
+        if not ms:
+            continue
+        a = cand.get(k, 0)
+        kernels[k] = {"avg_launch_ms": round(ms, 5), "alg_bytes": int(a),
+                      "gbps": round(a / (ms * 1e-3) / 1e9, 1) if a else None,
+                      "frac": round(a / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4) if a else None}
+    dom = max(("attend", "score"), key=lambda k: stage_ms.get(k, 0.0))
     dom_ms = stage_ms[dom]
     achieved = cand[dom] / (dom_ms * 1e-3) / 1e9
     traffic = counter_traffic(dom)
     dense_equiv = bm.dense_kv_bytes(int(np.sum(lens_now)), d, sb) * hkv
+    dec_ms = sum(stage_ms.get(k, 0.0) for k in ("q_rotate", "score", "select", "attend", "merge"))
+    if not stage_ms.get("q_rotate"):
+        # the query rotation ran inside the append's launch: count the decode
+        # from score on, and its bytes without the rotation's R_k read
+        dec_bytes = call["total"] - B * hkv * d * d * 4
+    else:
+        dec_bytes = call["total"]
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
 
     cpu = None
-    if args.cpu_units > 0:
-        nthreads = synth.host_threads()
-        log("oracle CPU baseline on %d units x %d steps, %d threads" % (args.cpu_units, args.cpu_steps, nthreads))
-        cpu = cpu_baseline(args.config, args.scale, R, T0, args.cpu_steps, args.cpu_units, nthreads)
-        log("oracle: %.3g tokens/s over %.1f s" % (cpu["value"], cpu["seconds"]))
+    if args.cpu_units != 0:
+        workers = synth.host_threads()
+        n_units = workers if args.cpu_units < 0 else args.cpu_units
+        n_units = min(n_units, B * hkv)
+        log("oracle CPU baseline: %d units x %d steps on %d threads, then 1 unit x %d steps on 1 thread" % (
+            n_units, args.cpu_steps, min(workers, n_units), args.cpu_steps_1t))
+        cpu = cpu_baseline(args.config, args.scale, R, T0, args.cpu_steps, n_units, workers, args.cpu_steps_1t)
+        log("oracle: %.3g tokens/s on %d threads, %.3g on 1 thread (%.1f s)" % (
+            cpu["value"], cpu["cores"], cpu["one_thread"]["value"], cpu["seconds"]))
         cpu.pop("seconds")
 
     if args.copy_mib > 0:
@@ -335,6 +404,10 @@ def main():
                                               s["r"], ("%d blocks" % s["k_abs"]) if s["k_abs"] else
                                               ("%g%%" % (s["keep_ppm"] / 1e4))))
                          for s in w["segs"][0])
+    if args.config == 5:
+        seg_desc += " (request 0; every request: D[0,64) then one packed segment)"
+    names = {1: "single head, T=4096, fp32", 2: "32K-token GQA layer", 3: "128K-token GQA layer, batch 4",
+             4: "1M-token GQA layer share", 5: "serving batch 32, T uniform in [16K, 96K]"}
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -349,8 +422,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "GQA %d/%d heads d=%d, batch %d, T=%d/request at start, %s storage; "
-                        "step = append 1 token/request + decode attention" % (hq, hkv, d, B, int(T0[0]), dt),
+            "workload": "%s: GQA %d/%d heads d=%d, batch %d, T=%d..%d/request at start, %s storage; "
+                        "step = append 1 token/request + decode attention" % (
+                            names.get(args.config, "workload %d" % args.config), hq, hkv, d, B, int(T0.min()),
+                            int(T0.max()), dt),
             "global_batch": B,
             "seq_len": int(T0.max()),
             "segments": seg_desc,
@@ -358,11 +433,17 @@ def main():
             "parallelism": "single GPU",
             "layer_caches": n_layers,
         },
+        "step_ms_p10_p50_p90": [round(pct(step_ms, 10), 4), round(pct(step_ms, 50), 4), round(pct(step_ms, 90), 4)],
         "achieved_step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_alg_bytes": int(step_bytes),
+        "append_alg_bytes": int(append),
         "decode_alg_bytes": {k: int(v) for k, v in call.items()},
+        "decode_roofline": {"kernels": "q_rotate+score+select+attend+merge (summed launch times)",
+                            "bound": "hbm", "alg_bytes": int(dec_bytes), "ms": round(dec_ms, 5),
+                            "achieved": round(dec_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(dec_gbps / PEAK_GBPS, 4)},
+        "kernels": kernels,
         "dense_equiv_bytes": int(dense_equiv),
-        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items() if v},
         "gpu_event_ms_per_step": round(gpu_ms / K_steps, 4),
         "prefill_compress_ms": round(prefill_ms, 3),
         "prefill": prefill_summary(prefill_ms, int(T0.sum()) * hkv, d),

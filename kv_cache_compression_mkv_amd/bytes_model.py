@@ -76,3 +76,12 @@ def decode_call_bytes(d: int, s: int, hkv: int, batch: int, hq: int, seg_summary
     qo = 2 * batch * hq * d * 4
     return dict(meta=meta, records=records, dense=dense, rot=rot, qo=qo,
                 total=meta + records + dense + rot + qo)
+
+
+def append_bytes(d: int, s: int, hkv: int, batch: int, r: int) -> int:
+    """Algorithmic bytes of appending one token per request to a packed
+    segment: per (request, KV head) read R_k and R_v (float32) and the raw key
+    and value, write the two packed vectors (r values and r u8 indices each)
+    and read and write the block's min/max keys."""
+    per_unit = 2 * d * d * 4 + 2 * d * s + 2 * r * (s + 1) + 2 * meta_block_bytes(d, s)
+    return batch * hkv * per_unit

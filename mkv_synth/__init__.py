@@ -101,11 +101,16 @@ def _lib():
 
 
 def host_threads() -> int:
+    """Host threads to use: every CPU this process may run on, bounded by the
+    OMP_NUM_THREADS the environment grants (a GPU job's share of its host)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def _haar(cfg: int, b: int, g: int, kind: int, d: int) -> np.ndarray:

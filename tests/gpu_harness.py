@@ -210,3 +210,84 @@ def check_decode_unit(w, comp, Rk, Rv, q_unit, out_gpu, sel_gpu_unit, tol, lengt
         else:
             assert err / nr <= tol, "b=%d g=%d h=%d rel L2 %.3g > %.3g" % (b, g, h, err / nr, tol)
     return n_exempt
+
+
+def _pidx(segs, j):
+    """Index of segment j among the packed segments."""
+    return sum(1 for s in segs[:j] if s["kind"] == synth.PACKED)
+
+
+def compare_packed_blocks(cache, w, comp, b, g, j, blocks, length):
+    """Bit-exact comparison of the given blocks of packed segment j of unit (b, g)
+    with the oracle: indices and values of every valid slot, zeros in the slots
+    after the last token, and the blocks' keys."""
+    from kv_cache_compression_mkv_amd import layout
+    dt, d = w["dtype"], w.get("d", 128)
+    sb = 2 if dt == "bf16" else 4
+    s = w["segs"][b][j]
+    r, tb = s["r"], s["t_begin"]
+    nbcap = -(-s["t_cap"] // 16)
+    rec = 16 * r * 2 * (sb + 1)
+    filled = min(max(length - tb, 0), s["t_cap"])
+    data = cache.data[b][j]
+    for l in blocks:
+        off = (g * nbcap + l) * rec
+        P = layout.unpack_packed(data[off:off + rec].cpu().numpy(), 1, 1, r, dt)
+        nv = min(16, filled - 16 * l)
+        for hat, idx, gb, gi, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
+                                       (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
+            ei = idx[tb + 16 * l:tb + 16 * l + nv, :r].astype(np.int64)
+            assert np.array_equal(gi[0, 0, :nv].astype(np.int64), ei), "%s idx b=%d g=%d seg=%d block=%d" % (
+                name, b, g, j, l)
+            ev = bits_of(np.take_along_axis(hat[tb + 16 * l:tb + 16 * l + nv], ei, axis=1), dt)
+            assert np.array_equal(gb[0, 0, :nv], ev), "%s val b=%d g=%d seg=%d block=%d" % (name, b, g, j, l)
+            assert np.all(gb[0, 0, nv:] == 0) and np.all(gi[0, 0, nv:] == 0), "padding b=%d block=%d" % (b, l)
+    ng = 2 * d * sb // 16
+    ntile = -(-nbcap // 64)
+    mraw = _head_bytes(cache.meta[b][j], g, ntile * ng * 64 * 16)
+    _, mbits = layout.unpack_meta(mraw, 1, nbcap, dt, d)
+    om = comp["meta"][_pidx(w["segs"][b], j)]
+    for l in blocks:
+        assert np.array_equal(mbits[0, l], bits_of(om[l], dt)), "keys b=%d g=%d seg=%d block=%d" % (b, g, j, l)
+
+
+class Snapshot:
+    """Device copy of a cache's segment buffers, to find which blocks a step changed."""
+
+    def __init__(self, cache):
+        self.data = [[t.clone() for t in row] for row in cache.data]
+        self.meta = [[t.clone() if t is not None else None for t in row] for row in cache.meta]
+
+    @staticmethod
+    def _diff(cur, prev):
+        return torch_nonzero_offsets(cur, prev)
+
+    def changed(self, cache, w, b, j):
+        """Sorted (KV head, block) pairs whose stored bytes (data or keys) differ
+        from the snapshot in segment j of request b; (-1, -1) marks bytes past
+        the last block."""
+        dt, d, hkv = w["dtype"], w.get("d", 128), w["n_kv_heads"]
+        sb = 2 if dt == "bf16" else 4
+        s = w["segs"][b][j]
+        nbcap = -(-s["t_cap"] // 16)
+        out = set()
+        if s["kind"] == synth.PACKED:
+            per = 16 * s["r"] * 2 * (sb + 1)
+        else:
+            per = 2 * 16 * d * sb
+        for off in self._diff(cache.data[b][j], self.data[b][j]):
+            g, rem = divmod(int(off), nbcap * per)
+            out.add((g, rem // per) if g < hkv else (-1, -1))
+        if s["kind"] == synth.PACKED:
+            ntile = -(-nbcap // 64)
+            tile_bytes = (2 * d * sb // 16) * 64 * 16
+            for off in self._diff(cache.meta[b][j], self.meta[b][j]):
+                g, rem = divmod(int(off), ntile * tile_bytes)
+                tile, rem = divmod(rem, tile_bytes)
+                out.add((g, tile * 64 + (rem % 1024) // 16))
+        return sorted(out)
+
+
+def torch_nonzero_offsets(cur, prev):
+    """Byte offsets where two equally sized device byte tensors differ (host list)."""
+    return (cur != prev).nonzero().flatten().cpu().tolist()

@@ -147,3 +147,31 @@ def test_serving_steps_append_then_decode():
         units = [(b, g) for b in range(w["batch"]) for g in (0, 5)] if s % 5 else None
         _decode_and_check(w, c, raw, R, q, units=units)
     assert c.lengths == [t + steps for t in T0]
+
+
+def test_all_dense_cache_pads_selection():
+    """Without packed segments nothing is selected: every column of sel_out, at
+    any width, is -1; the outputs still match the oracle."""
+    from kv_cache_compression_mkv_amd import _lib as L
+    segs = [synth.seg(synth.DENSE, 0, 64), synth.seg(synth.DENSE, 64, 200)]
+    w = dict(cfg=2, batch=2, n_q_heads=8, n_kv_heads=2, d=128, dtype="bf16", lengths=np.array([150, 90]),
+             segs=[segs, segs])
+    c, raw, R = build(torch, w)
+    assert c.sel_cols() == 0
+    q = synth.gen_q(2, 7, 2, 8, "bf16")
+    qd = torch.from_numpy(q).cuda()
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
+    sel = torch.full((2, 8, 7), 12345, dtype=torch.int32, device="cuda")
+    ws = c.workspace()
+    L.mkv_decode_attn(c.c, qd.data_ptr(), out.data_ptr(), sel.data_ptr(), 7, ws.data_ptr(), ws.numel(),
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.all(sel == -1)
+    out = out.cpu().numpy()
+    for b in range(2):
+        for g in range(2):
+            comp, Rk, Rv = oracle_unit(w, raw, R, b, g, c.lengths[b])
+            ref = orc.decode_unit(comp, q[b, 4 * g:4 * g + 4].astype(np.float64), Rk, Rv)["out"]
+            for h in range(4):
+                err = np.linalg.norm(out[b, 4 * g + h] - ref[h]) / np.linalg.norm(ref[h])
+                assert err <= TOL["bf16"]

@@ -213,6 +213,25 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
                              int32_t n_max, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* Decode attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, meaning and results, bit
+ * for bit, as mkv_decode_attn with the workspace replaced by the library's own
+ * scratch array of MKV_SCRATCH_BYTES bytes: a file-scope device array each
+ * device holds from the library's first use on it until the process ends
+ * (its address is looked up once per device, on the first call whose stream
+ * belongs to that device). The call allocates and frees nothing.
+ * Every call on one device shares that device's array, so calls that overlap
+ * on one device (concurrent streams or threads) race and must be serialised
+ * by the caller; the array keeps the last call's contents, and every byte a
+ * call reads it has written earlier in the same call.
+ * Errors: those of mkv_decode_attn; MKV_ERR_WORKSPACE when the cache needs
+ * more than MKV_SCRATCH_BYTES (mkv_decode_workspace_bytes() tells), checked
+ * before anything is enqueued. */
+#define MKV_SCRATCH_BYTES (128ull << 20)
+mkv_status mkv_decode_attn_noalloc(const mkv_cache *c, const float *q, float *out, int32_t *sel_out,
+                                   int64_t sel_cols, void *stream);
+
 /* Optional kernel timing (a diagnostic; process-wide, thread-safe): while
  * enabled, every kernel the library launches, from any thread, is bracketed
  * by HIP events on its stream. This is the library's only state kept between

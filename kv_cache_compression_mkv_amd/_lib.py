@@ -24,10 +24,12 @@ MKV_MAX_SEGMENTS = 8
 MKV_MAX_PACKED_BLOCKS = 65536
 MKV_PACKED_TAIL_BYTES = 256
 MKV_N_STAGES = 7
+MKV_SCRATCH_BYTES = 128 << 20
 
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
            "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",
-           "mkv_append_decode", "mkv_timing_enable", "mkv_timing_read", "mkv_stage_name"]
+           "mkv_append_decode", "mkv_decode_attn_noalloc", "mkv_timing_enable", "mkv_timing_read",
+           "mkv_stage_name"]
 
 
 class mkv_segment(ctypes.Structure):
@@ -72,6 +74,8 @@ def _load():
     L.mkv_decode_attn.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I64, P, SZ, P]
     L.mkv_append_decode.restype = ctypes.c_int
     L.mkv_append_decode.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P, P, P, I64, P, SZ, P]
+    L.mkv_decode_attn_noalloc.restype = ctypes.c_int
+    L.mkv_decode_attn_noalloc.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I64, P]
     L.mkv_timing_enable.restype = ctypes.c_int
     L.mkv_timing_enable.argtypes = [I32]
     L.mkv_timing_read.restype = ctypes.c_int
@@ -131,6 +135,11 @@ def mkv_append_decode(cache: mkv_cache, k_ptr: int, v_ptr: int, n_new_ptr: int, 
                       out_ptr: int, sel_ptr, sel_cols: int, ws_ptr: int, ws_bytes: int, stream: int):
     _check(LIB.mkv_append_decode(ctypes.byref(cache), k_ptr, v_ptr, n_new_ptr, n_max, q_ptr, out_ptr, sel_ptr,
                                  sel_cols, ws_ptr, ws_bytes, stream), "mkv_append_decode")
+
+
+def mkv_decode_attn_noalloc(cache: mkv_cache, q_ptr: int, out_ptr: int, sel_ptr, sel_cols: int, stream: int):
+    _check(LIB.mkv_decode_attn_noalloc(ctypes.byref(cache), q_ptr, out_ptr, sel_ptr, sel_cols, stream),
+           "mkv_decode_attn_noalloc")
 
 
 def mkv_timing_enable(on: bool):

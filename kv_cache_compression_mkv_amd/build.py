@@ -12,7 +12,7 @@ OUT = os.path.join(HERE, "libmkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["compress.hip", "decode.hip"]
+HIP_SOURCES = ["compress.hip", "decode.hip", "noalloc.hip"]
 HOST_SOURCES = ["mkv_host.cpp", "rotation.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # no packed-fp32 instructions anywhere in the device code

@@ -1279,7 +1279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
             a0 = fmaf(w, x.x, a0);
             a1 = fmaf(w, x.y, a1);
         }
-        float *pp = A.part + (((size_t)b * A.hq + g * G + h) * MAX_SPLITS + P) * PART;
+        float *pp = A.part + (((size_t)b * A.hq + g * G + h) * MAX_PARTS + P) * PART;
         if (lane == 0) {
             pp[0] = M;
             pp[1] = L;
@@ -1304,17 +1304,17 @@ __global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
 // ----------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
-    static_assert(MAX_SPLITS <= 256, "one thread per split");
+    static_assert(MAX_PARTS <= 256, "one thread per partial");
     const int bl = (int)blockIdx.y, h = (int)blockIdx.x;
     const int b = A.b0 + bl, g = h / G;
     const int t = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x >> 6);
     const int Stot = (A.S_d + 3) / 4 + (A.S_p + 3) / 4;  // one partial per attend workgroup
-    const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_SPLITS * PART;
+    const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_PARTS * PART;
     if (A.npk == 0 && A.sel_out) {  // no packed segment, no select launch: all of sel_out is padding
         int32_t *so = A.sel_out + ((size_t)b * A.hq + h) * A.sel_cols;
         for (int64_t c = t; c < A.sel_cols; c += 256) so[c] = -1;
     }
-    __shared__ float wsc[MAX_SPLITS];
+    __shared__ float wsc[256];
     __shared__ float red[2][4];
     __shared__ __align__(16) float part_o[8][D];
     __shared__ __align__(16) float osh[D];
@@ -1324,7 +1324,7 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) rv[u] = Rv4[(size_t)(cc * 16 + u) * (D / 4) + j4];
 
-    // split weights: w_s = exp2(m_s - M), L = sum_s w_s l_s (MAX_SPLITS == 256 threads)
+    // partial weights: w_s = exp2(m_s - M), L = sum_s w_s l_s (one thread per partial)
     float m = -INFINITY, l = 0.f;
     if (t < Stot) {
         m = pp[(size_t)t * PART];
@@ -1338,7 +1338,7 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-    if (t < MAX_SPLITS) wsc[t] = w;
+    wsc[t] = w;
     {
         const float v = wave_sum(w * l);
         if (lane == 0) red[1][wave] = v;

@@ -178,7 +178,7 @@ WsMap ws_map(const mkv_cache *c) {
     m.sel = off;
     off = align256(off + (size_t)sl * 4);
     m.part = off;
-    off = align256(off + B * Hq * MAX_SPLITS * PART * 4);
+    off = align256(off + B * Hq * MAX_PARTS * PART * 4);
     m.total = off;
     return m;
 }
@@ -394,6 +394,7 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                 A.S_p = sp4;
             }
         }
+        if ((A.S_d + 3) / 4 + (A.S_p + 3) / 4 > MAX_PARTS) return MKV_ERR_UNSUPPORTED;  // (never: S_d + S_p <= 256)
         // select: up to 16 waves, 4 / 16 / 64 keys per lane
         const int kpt = max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
         A.sel_kpt = kpt;
@@ -508,6 +509,21 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
     st = decode_check(c, q, out, sel_out, sel_cols, workspace, ws_bytes);
     if (st != MKV_OK) return st;
     return decode_enqueue(c, q, out, sel_out, sel_cols, workspace, false, static_cast<hipStream_t>(stream));
+}
+
+mkv_status mkv_decode_attn_noalloc(const mkv_cache *c, const float *q, float *out, int32_t *sel_out,
+                                   int64_t sel_cols, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    if (ws_map(c).total > MKV_SCRATCH_BYTES) return MKV_ERR_WORKSPACE;
+    if (!q || !out) return MKV_ERR_ARG;
+    if (sel_out && sel_cols < sel_cols_now(c)) return MKV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (scratch_address(s, &ws) != hipSuccess) return MKV_ERR_HIP;
+    st = decode_check(c, q, out, sel_out, sel_cols, ws, MKV_SCRATCH_BYTES);
+    if (st != MKV_OK) return st;
+    return decode_enqueue(c, q, out, sel_out, sel_cols, ws, false, s);
 }
 
 mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,

@@ -17,6 +17,9 @@ constexpr int BT = MKV_BLOCK_TOKENS;
 constexpr int TABLE = 64;       // (request, segment) entries per launch
 constexpr int META_TILE = 64;   // blocks per meta tile
 constexpr int MAX_SPLITS = 256; // attention splits per (request, KV head)
+// Partials per (request, query head): one per attend workgroup of 4 splits.
+// With S_d + S_p <= MAX_SPLITS there are ceil(S_d / 4) + ceil(S_p / 4) <= 65.
+constexpr int MAX_PARTS = MAX_SPLITS / 4 + 1;
 constexpr int PART = D + 2;     // floats per split partial: m, l, acc[D]
 // Union-mode weight of a packed record: its bytes plus a fixed per-record
 // cost. A wave holds about one record in flight, so a record's time is mostly
@@ -90,7 +93,7 @@ struct DecodeArgs {
     float *scores;    // per packed j: [B][Hq][nbcap_j]
     uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j], byte i = 1 if head i of the group chose the block
     int32_t *sel;     // per packed j: [B][Hq][kcap_j]
-    float *part;      // [B][Hq][MAX_SPLITS][PART]: one partial per attend workgroup (of 4 splits), dense first
+    float *part;      // [B][Hq][MAX_PARTS][PART]: one partial per attend workgroup (of 4 splits), dense first
     int64_t sel_cols;
     int64_t sc_off[MKV_MAX_SEGMENTS];
     int64_t mk_off[MKV_MAX_SEGMENTS];
@@ -119,5 +122,10 @@ hipError_t launch_score(const DecodeArgs &a, int dtype, int G, int max_tiles, hi
 hipError_t launch_select(const DecodeArgs &a, int G, hipStream_t s);
 hipError_t launch_attend(const DecodeArgs &a, int dtype, int G, int qmax, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s);
+
+// ---- allocation-free decode (noalloc.hip) ----------------------------------
+// Device address of the library's scratch array on the device of `stream`
+// (looked up once per device, then cached). Bytes: MKV_SCRATCH_BYTES.
+hipError_t scratch_address(hipStream_t stream, void **ptr);
 
 }  // namespace mkv

@@ -203,3 +203,23 @@ def test_host_rotation_is_bitwise_independent_of_thread_count():
         out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
         digests.add(out.stdout.strip().splitlines()[-1])
     assert len(digests) == 1
+
+
+def test_noalloc_rejects_caches_beyond_its_scratch(L):
+    """mkv_decode_attn_noalloc refuses, before any device work, a cache whose
+    decode needs more than MKV_SCRATCH_BYTES of scratch (64 requests of a
+    million-token packed segment: 64 x 32 heads x 65536 fp32 scores alone are
+    512 MiB). The device pointers are never dereferenced."""
+    B, ns = 64, 1
+    segs = (L.mkv_segment * (B * ns))()
+    lens = (ctypes.c_int64 * B)(*([1000] * B))
+    for b in range(B):
+        e = segs[b]
+        e.kind, e.r, e.keep_ppm, e.k_abs, e.t_begin, e.t_cap = L.MKV_SEG_PACKED, 32, 40000, 0, 0, 1 << 20
+        e.data, e.meta = 4096, 8192
+    c = L.mkv_cache(B, 32, 8, 128, L.MKV_BF16, ns, ctypes.cast(segs, ctypes.POINTER(L.mkv_segment)),
+                    ctypes.cast(lens, ctypes.POINTER(ctypes.c_int64)), 4096)
+    assert L.mkv_decode_workspace_bytes(c) > L.MKV_SCRATCH_BYTES
+    with pytest.raises(L.MkvError) as e:
+        L.mkv_decode_attn_noalloc(c, 4096, 4096, None, 0, None)
+    assert e.value.status == L.MKV_ERR_WORKSPACE

@@ -49,7 +49,7 @@ def log(msg):
 
 
 def workload(cfg: int, scale: int, extra: int):
-    w = synth.workload(cfg, scale=scale)
+    w = synth.workload(cfg, scale=scale, extra_cap=extra if cfg == 5 else 0)
     if cfg != 5:
         w = synth.with_update_segment(w, cap=extra)
     return w
@@ -236,8 +236,10 @@ def main():
     ap.add_argument("--scale", type=int, default=1, help="divide token counts (1 = full size)")
     ap.add_argument("--cpu-units", type=int, default=-1,
                     help="oracle sample: units run side by side (-1: one per host thread; 0 disables)")
-    ap.add_argument("--cpu-steps", type=int, default=600, help="oracle decode steps per unit")
-    ap.add_argument("--cpu-steps-1t", type=int, default=300, help="oracle decode steps of the 1-thread run")
+    ap.add_argument("--cpu-steps", type=int, default=-1,
+                    help="oracle decode steps per unit (-1: 600 at 128K context, scaled inversely with context)")
+    ap.add_argument("--cpu-steps-1t", type=int, default=-1, help="oracle decode steps of the 1-thread run "
+                                                                 "(-1: half of --cpu-steps)")
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct layer caches visited round-robin (keeps every call cache-cold)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -378,6 +380,10 @@ def main():
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
 
     cpu = None
+    if args.cpu_steps < 0:
+        args.cpu_steps = int(max(20, min(600, 600 * 131072 / float(np.mean(T0)))))
+    if args.cpu_steps_1t < 0:
+        args.cpu_steps_1t = max(10, args.cpu_steps // 2)
     if args.cpu_units != 0:
         workers = synth.host_threads()
         n_units = workers if args.cpu_units < 0 else args.cpu_units

@@ -95,22 +95,7 @@ __device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, i
     }
 }
 
-// ----------------------------------------------------------------------------
-// select: one workgroup of up to 16 waves per (request, query head, packed
-// segment). Lane l of wave w holds the keys of blocks (w*KPT + i)*64 + l, so
-// block order is (wave, i, lane) order. Counting is done with ballots and
-// scalar popcounts; the k-th largest key is found two bits at a time below
-// the bits every key shares. Blocks above it are kept, equal ones by
-// ascending block index; ballot prefix counts give each kept block its place
-// in the ascending output.
-// ----------------------------------------------------------------------------
 constexpr int SEL_MAX_WAVES = 16;
-
-struct SelShared {
-    int v[2][SEL_MAX_WAVES][3];
-    uint32_t act[64];  // keys still undecided when the search is handed to one wave
-    uint32_t thr;
-};
 
 // DPP row (16-lane) reductions on integers; every lane of the row gets the result
 #define MKV_RORI(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), ctrl, 0xf, 0xf, false)
@@ -150,7 +135,8 @@ __device__ __forceinline__ void wave_minmax_u(uint32_t &mn, uint32_t &mx) {
 // Cross-wave helpers (nw <= 16 waves): after the barrier, lane i of every
 // wave reads wave i's entry and a DPP row reduction combines them.
 // sum three wave-uniform values over the workgroup's waves
-__device__ __forceinline__ void xwave_sum3(SelShared &sh, int &ph, int nw, int &a, int &b, int &c) {
+template <class SH>
+__device__ __forceinline__ void xwave_sum3(SH &sh, int &ph, int nw, int &a, int &b, int &c) {
     if (nw == 1) return;
     const int w = (int)(threadIdx.x >> 6), lane = lane_id();
     if (lane == 0) {
@@ -170,7 +156,8 @@ __device__ __forceinline__ void xwave_sum3(SelShared &sh, int &ph, int nw, int &
 }
 
 // exclusive prefix over waves of a wave-uniform value
-__device__ __forceinline__ int xwave_excl(SelShared &sh, int &ph, int nw, int v) {
+template <class SH>
+__device__ __forceinline__ int xwave_excl(SH &sh, int &ph, int nw, int v) {
     if (nw == 1) return 0;
     const int w = (int)(threadIdx.x >> 6), lane = lane_id();
     if (lane == 0) sh.v[ph][w][0] = v;
@@ -180,7 +167,8 @@ __device__ __forceinline__ int xwave_excl(SelShared &sh, int &ph, int nw, int v)
     return lane_int(row_sum16_i(x), 0);
 }
 
-__device__ __forceinline__ void xwave_minmax(SelShared &sh, int &ph, int nw, uint32_t &mn, uint32_t &mx) {
+template <class SH>
+__device__ __forceinline__ void xwave_minmax(SH &sh, int &ph, int nw, uint32_t &mn, uint32_t &mx) {
     wave_minmax_u(mn, mx);
     if (nw == 1) return;
     const int w = (int)(threadIdx.x >> 6), lane = lane_id();
@@ -212,8 +200,8 @@ __device__ __forceinline__ int count_ge(const uint32_t (&key)[KPT], uint32_t can
 // range with at least need of them >= t (largest such t, or one with exactly
 // need), and every wave gets it back. With cnt_hi keys above the range and
 // need = k - cnt_hi this is the threshold the workgroup-wide search reaches.
-template <int KPT>
-__device__ __forceinline__ uint32_t select_compact(SelShared &sh, int &ph, int nw, const uint32_t (&key)[KPT],
+template <int KPT, class SH>
+__device__ __forceinline__ uint32_t select_compact(SH &sh, int &ph, int nw, const uint32_t (&key)[KPT],
                                                    uint32_t thr, int bit, int nact, int need) {
     const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
     const int sft = bit + 1;  // 1..31
@@ -256,6 +244,89 @@ __device__ __forceinline__ uint32_t select_compact(SelShared &sh, int &ph, int n
     return sh.thr;
 }
 
+// Exact threshold of the k largest keys, 2 bits at a time, over keys known to
+// lie in [kmn, kmx] from the k-th largest on (every key above kmx counts as
+// kept): the largest t with at least k keys >= t. Counting uses ballots and
+// one cross-wave sum per step; once at most 64 keys remain undecided one wave
+// finishes with ballots and no barriers.
+template <int KPT, class SH>
+__device__ __forceinline__ uint32_t radix_threshold(SH &sh, int &ph, int nw, const uint32_t (&key)[KPT], uint32_t kmn,
+                                                    uint32_t kmx, int k) {
+    const uint32_t diff = kmn ^ kmx;
+    int bit = diff ? 31 - __clz(diff) : -1;
+    uint32_t thr = diff ? (kmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u))) : kmx;
+    // Invariant: at least k keys are >= thr. Once exactly k are (cnt == k)
+    // they are the selection, and the remaining bits cannot change it.
+    // cnt_hi counts the keys at or above the range's upper end
+    // thr + 2^(bit + 1), all of which are kept.
+    // keys at or above the range's upper end (none when [kmn, kmx] spans
+    // every key; keys of higher bins otherwise)
+    const uint64_t upper = (uint64_t)thr + (bit >= 0 ? (2ull << bit) : 1ull);
+    int cnt = -1, cnt_hi = upper > 0xFFFFFFFFull ? 0 : count_ge<KPT>(key, (uint32_t)upper);
+    {
+        int u1 = 0, u2 = 0;
+        xwave_sum3(sh, ph, nw, cnt_hi, u1, u2);
+    }
+    while (bit >= 0 && cnt != k) {
+        if (bit >= 1) {
+            const uint32_t c1 = thr | (1u << (bit - 1)), c2 = thr | (2u << (bit - 1)), c3 = thr | (3u << (bit - 1));
+            int n1 = count_ge<KPT>(key, c1), n2 = count_ge<KPT>(key, c2), n3 = count_ge<KPT>(key, c3);
+            xwave_sum3(sh, ph, nw, n1, n2, n3);
+            if (n3 >= k) { thr = c3; cnt = n3; }
+            else if (n2 >= k) { thr = c2; cnt = n2; cnt_hi = n3; }
+            else if (n1 >= k) { thr = c1; cnt = n1; cnt_hi = n2; }
+            else cnt_hi = n1;
+            bit -= 2;
+        } else {
+            int n1 = count_ge<KPT>(key, thr | 1u), n2 = 0, n3 = 0;
+            xwave_sum3(sh, ph, nw, n1, n2, n3);
+            if (n1 >= k) { thr |= 1u; cnt = n1; }
+            else cnt_hi = n1;
+            bit -= 1;
+        }
+        // at most 64 keys left undecided: one wave finishes the search
+        if (nw > 1 && bit >= 0 && cnt > k && cnt - cnt_hi <= 64) {
+            thr = select_compact<KPT>(sh, ph, nw, key, thr, bit, cnt - cnt_hi, k - cnt_hi);
+            break;
+        }
+    }
+    return thr;
+}
+
+// the score of an order key (inverse of score_key)
+__device__ __forceinline__ float key_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// bin of a score between smin and smax: monotone in the score (a subtraction,
+// a product by a positive factor and a truncation each preserve order), so
+// every key of a higher bin exceeds every key of a lower one
+__device__ __forceinline__ int score_bin(uint32_t key, float smin, float inv) {
+    return min(255, (int)((key_score(key) - smin) * inv));
+}
+
+// ----------------------------------------------------------------------------
+// select: one workgroup of up to 16 waves per (request, query head, packed
+// segment). Lane l of wave w holds the keys of blocks (w * KPT + i) * 64 + l,
+// so block order is (wave, i, lane) order. The k-th largest score is located
+// in one histogram pass: scores are binned linearly between their minimum
+// and maximum into 256 bins (per-wave histograms, LDS atomics), and one wave
+// finds the bin holding the k-th largest from the top. Usually that bin's
+// keys are all needed, or at most 64 of them remain; those are compacted to
+// LDS and one wave finds the exact threshold with ballots. Otherwise (many
+// near-equal scores) the exact 2-bit search runs from that bin's key range.
+// Blocks above the threshold are kept, equal ones by ascending block index;
+// ballot prefix counts give each kept block its place in the ascending output.
+// ----------------------------------------------------------------------------
+struct SelShared {
+    int v[2][SEL_MAX_WAVES][3];
+    uint32_t hist[SEL_MAX_WAVES][256];  // one histogram per wave (no cross-wave atomics)
+    uint32_t act[64];                   // candidate keys handed to one wave
+    uint32_t thr;
+    int res[3];                         // bin, keys above it, keys in it
+    int ncand;
+};
+
 template <int G, int KPT>
 __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
     const int z = (int)blockIdx.z;
@@ -265,7 +336,8 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
     const DSeg &S = seg_of(A, bl, A.pseg[j]);
     const int n = S.nb, k = S.k;
     const int nbc = A.nbcap[j];
-    const int nw = (int)(blockDim.x >> 6), w = (int)(threadIdx.x >> 6), lane = lane_id();
+    const int nw = (int)(blockDim.x >> 6), lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     __shared__ SelShared sh;
     int ph = 0;
 
@@ -278,84 +350,146 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
     }
     if (n <= 0 || k <= 0) return;
 
-    // keys; 0 marks a missing block (every finite score has a key above 0x007FFFFF)
+    // keys; 0 marks a missing block (every finite score has a key above
+    // 0x007FFFFF). Every load is issued first (lanes past the last block
+    // reread it), so they are in flight together.
     const float *sc = A.scores + A.sc_off[j] + ((size_t)b * A.hq + h) * nbc;
     uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) key[i] = __float_as_uint(sc[min((w * KPT + i) * 64 + lane, n - 1)]);
+    for (int i = (int)threadIdx.x; i < nw * 256; i += (int)blockDim.x) (&sh.hist[0][0])[i] = 0u;
+    if (threadIdx.x == 0) sh.ncand = 0;
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const int blk = (w * KPT + i) * 64 + lane;
-        key[i] = blk < n ? score_key(sc[blk]) : 0u;
-        if (blk < n) {
+        const bool valid = (w * KPT + i) * 64 + lane < n;
+        key[i] = valid ? score_key(__uint_as_float(key[i])) : 0u;
+        if (valid) {
             kmn = min(kmn, key[i]);
             kmx = max(kmx, key[i]);
         }
     }
     xwave_minmax(sh, ph, nw, kmn, kmx);
-    uint32_t thr;
-    if (k >= n) {
-        thr = kmn;
-    } else {
-        const uint32_t diff = kmn ^ kmx;
-        int bit = diff ? 31 - __clz(diff) : -1;
-        thr = diff ? (kmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u))) : kmx;
-        // Invariant: at least k keys are >= thr. Once exactly k are (cnt == k)
-        // they are the selection, and the remaining bits cannot change it.
-        // cnt_hi counts the keys at or above the range's upper end
-        // thr + 2^(bit + 1), all of which are kept.
-        int cnt = -1, cnt_hi = 0;
-        while (bit >= 0 && cnt != k) {
-            if (bit >= 1) {
-                const uint32_t c1 = thr | (1u << (bit - 1)), c2 = thr | (2u << (bit - 1)),
-                               c3 = thr | (3u << (bit - 1));
-                int n1 = count_ge<KPT>(key, c1), n2 = count_ge<KPT>(key, c2), n3 = count_ge<KPT>(key, c3);
-                xwave_sum3(sh, ph, nw, n1, n2, n3);
-                if (n3 >= k) { thr = c3; cnt = n3; }
-                else if (n2 >= k) { thr = c2; cnt = n2; cnt_hi = n3; }
-                else if (n1 >= k) { thr = c1; cnt = n1; cnt_hi = n2; }
-                else cnt_hi = n1;
-                bit -= 2;
+    if (nw == 1) wave_lds_sync();
+
+    // Kept: every key above thr and the first (k - #above) equal to thr in
+    // block order; or, when by_bin, every key in bin bstar or above.
+    uint32_t thr = kmn;
+    bool by_bin = false;
+    int bstar = 0;
+    float smin = 0.f, inv = 0.f;
+    if (k < n && kmn != kmx) {
+        smin = key_score(kmn);
+        const float range = key_score(kmx) - smin;
+        inv = 256.f / range;
+        if (range > 0.f && inv > 0.f && inv < 3.0e38f) {
+            uint32_t *hist = sh.hist[w];
+#pragma unroll
+            for (int i = 0; i < KPT; ++i)
+                if (key[i] != 0u) atomicAdd(&hist[score_bin(key[i], smin, inv)], 1u);
+            __syncthreads();
+            if (w == 0) {
+                // lane holds bins 4 lane .. 4 lane + 3, summed over the waves
+                uint4 hv = make_uint4(0u, 0u, 0u, 0u);
+                for (int v = 0; v < nw; ++v) {
+                    const uint4 x = reinterpret_cast<const uint4 *>(sh.hist[v])[lane];
+                    hv.x += x.x;
+                    hv.y += x.y;
+                    hv.z += x.z;
+                    hv.w += x.w;
+                }
+                const uint32_t tot = hv.x + hv.y + hv.z + hv.w;
+                uint32_t suf = tot;  // keys in the bins of lanes >= lane
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t y = __shfl_down(suf, o, 64);
+                    if (lane + o < 64) suf += y;
+                }
+                const uint32_t a3 = suf - tot, s3 = a3 + hv.w, s2 = s3 + hv.z, s1 = s2 + hv.y, s0 = s1 + hv.x;
+                // highest bin whose keys and those above it reach k
+                const uint64_t m = ballot(s0 >= (uint32_t)k);
+                const int L = 63 - __clzll(m);
+                if (lane == L) {
+                    int bin;
+                    uint32_t above, cnt;
+                    if (s3 >= (uint32_t)k) { bin = 4 * L + 3; above = a3; cnt = hv.w; }
+                    else if (s2 >= (uint32_t)k) { bin = 4 * L + 2; above = s3; cnt = hv.z; }
+                    else if (s1 >= (uint32_t)k) { bin = 4 * L + 1; above = s2; cnt = hv.y; }
+                    else { bin = 4 * L; above = s1; cnt = hv.x; }
+                    sh.res[0] = bin;
+                    sh.res[1] = (int)above;
+                    sh.res[2] = (int)cnt;
+                }
+            }
+            __syncthreads();
+            bstar = sh.res[0];
+            const int above = sh.res[1], cnt = sh.res[2], need = k - above;
+            if (cnt == need) {
+                by_bin = true;
+            } else if (cnt <= 64) {
+                // the need-th largest of the bin's keys, found by one wave
+#pragma unroll
+                for (int i = 0; i < KPT; ++i)
+                    if (key[i] != 0u && score_bin(key[i], smin, inv) == bstar) sh.act[atomicAdd(&sh.ncand, 1)] = key[i];
+                __syncthreads();
+                if (w == 0) {
+                    const uint32_t x = lane < cnt ? sh.act[lane] : 0u;  // candidates are > 0
+                    uint32_t t = 0u;
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t c = t | (1u << bit);
+                        if (popc64(ballot(x >= c)) >= need) t = c;
+                    }
+                    if (lane == 0) sh.thr = t;
+                }
+                __syncthreads();
+                thr = sh.thr;
             } else {
-                int n1 = count_ge<KPT>(key, thr | 1u), n2 = 0, n3 = 0;
-                xwave_sum3(sh, ph, nw, n1, n2, n3);
-                if (n1 >= k) { thr |= 1u; cnt = n1; }
-                else cnt_hi = n1;
-                bit -= 1;
+                // many near-equal scores: exact search over the bin's key range
+                uint32_t cmn = 0xFFFFFFFFu, cmx = 0u;
+#pragma unroll
+                for (int i = 0; i < KPT; ++i)
+                    if (key[i] != 0u && score_bin(key[i], smin, inv) == bstar) {
+                        cmn = min(cmn, key[i]);
+                        cmx = max(cmx, key[i]);
+                    }
+                xwave_minmax(sh, ph, nw, cmn, cmx);
+                thr = radix_threshold<KPT>(sh, ph, nw, key, cmn, cmx, k);
             }
-            // at most 64 keys left undecided: one wave finishes the search
-            if (nw > 1 && bit >= 0 && cnt > k && cnt - cnt_hi <= 64) {
-                thr = select_compact<KPT>(sh, ph, nw, key, thr, bit, cnt - cnt_hi, k - cnt_hi);
-                break;
-            }
+        } else {
+            thr = radix_threshold<KPT>(sh, ph, nw, key, kmn, kmx, k);
         }
     }
-    // thr > 0 is the k-th largest key, or has exactly k keys at or above it:
-    // keep every larger key and the first (k - #larger) equal keys in block order
-    int ngt = 0, neq = 0, unused = 0;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        ngt += popc64(ballot(key[i] > thr));
-        neq += popc64(ballot(key[i] == thr));
-    }
-    xwave_sum3(sh, ph, nw, ngt, neq, unused);
-    const int need = k - ngt;
     const uint64_t below = lanes_below(lane);
     uint64_t selm = 0;
-    if (neq <= need) {
+    if (by_bin || k >= n) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i)
-            if (key[i] >= thr) selm |= 1ull << i;
+            if (key[i] != 0u && (k >= n || score_bin(key[i], smin, inv) >= bstar)) selm |= 1ull << i;
     } else {
-        int eqw = 0;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) eqw += popc64(ballot(key[i] == thr));
-        int run = xwave_excl(sh, ph, nw, eqw);
+        int ngt = 0, neq = 0, unused = 0;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const uint64_t em = ballot(key[i] == thr);
-            const int rank = run + popc64(em & below);
-            if (key[i] > thr || (key[i] == thr && rank < need)) selm |= 1ull << i;
-            run += popc64(em);
+            ngt += popc64(ballot(key[i] > thr));
+            neq += popc64(ballot(key[i] == thr));
+        }
+        xwave_sum3(sh, ph, nw, ngt, neq, unused);
+        const int need = k - ngt;
+        if (neq <= need) {
+#pragma unroll
+            for (int i = 0; i < KPT; ++i)
+                if (key[i] >= thr) selm |= 1ull << i;
+        } else {
+            int eqw = 0;
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) eqw += popc64(ballot(key[i] == thr));
+            int run = xwave_excl(sh, ph, nw, eqw);
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const uint64_t em = ballot(key[i] == thr);
+                const int rank = run + popc64(em & below);
+                if (key[i] > thr || (key[i] == thr && rank < need)) selm |= 1ull << i;
+                run += popc64(em);
+            }
         }
     }
     int cw = 0;
@@ -795,6 +929,15 @@ __device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_
     }
 }
 
+// the records of one packed segment, with the windows code of their r
+template <typename ST, int G, int QA, int QB>
+__device__ __forceinline__ void run_records(const int2 *list, int n, const char *seg_base, size_t rec, int r,
+                                            int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L,
+                                            PkState<G> &S) {
+    if (((r + 3) >> 2) <= QA) pk_run<ST, G, QA>(list, n, seg_base, rec, r, filled, qsh, L, S);
+    else pk_run<ST, G, QB>(list, n, seg_base, rec, r, filled, qsh, L, S);
+}
+
 __device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
     const int64_t rec = (int64_t)BT * r * 2 * (sb + 1);
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
@@ -1017,12 +1160,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
             if (keep) list[popc64(km & lanes_below(lane))] = make_int2(blk, hm);
             const int n = popc64(km);
             wave_lds_sync();
-            if (n > 0) {
-                if (((r + 3) >> 2) <= QA)
-                    pk_run<ST, G, QA>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
-                else
-                    pk_run<ST, G, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
-            }
+            if (n > 0) run_records<ST, G, QA, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
             wave_lds_sync();
         }
     }
@@ -1211,10 +1349,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
                 list[lane] = make_int2((int)(e & 0xFFFFu), (int)(e >> 16));
             }
             wave_lds_sync();
-            if (((r + 3) >> 2) <= QA)
-                pk_run<ST, G, QA>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
-            else
-                pk_run<ST, G, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+            run_records<ST, G, QA, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
             wave_lds_sync();
         }
     }

@@ -366,7 +366,7 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
         // on the 128K workload: 88-104 KB packed splits are the fastest; 64 KB
         // fills every wave slot and is slower, 128 KB leaves too few waves)
         A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
-        A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, 96 * 1024)));
+        A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, PACKED_SPLIT)));
         // Union mode (exact byte-balanced packed workgroups) when every packed
         // segment has at most 4096 blocks and a workgroup's share of the union
         // provably fits its UNION_CAP-entry table: a share holds at most
@@ -395,8 +395,9 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
             }
         }
         if ((A.S_d + 3) / 4 + (A.S_p + 3) / 4 > MAX_PARTS) return MKV_ERR_UNSUPPORTED;  // (never: S_d + S_p <= 256)
-        // select: up to 16 waves, 4 / 16 / 64 keys per lane
-        const int kpt = max_nb <= 4096 ? 4 : max_nb <= 16384 ? 16 : 64;
+        // select: 4 keys per lane up to 1024 blocks, 16 up to 16384 (at most
+        // 16 waves), 64 beyond
+        const int kpt = max_nb <= 1024 ? 4 : max_nb <= 16384 ? 16 : 64;
         A.sel_kpt = kpt;
         A.sel_waves = (int32_t)std::max<int64_t>(1, ceil_div(max_nb, 64 * kpt));
 

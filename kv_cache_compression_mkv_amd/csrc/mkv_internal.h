@@ -27,6 +27,8 @@ constexpr int PART = D + 2;     // floats per split partial: m, l, acc[D]
 // balance point at 96 KB shares (its cost is worth about 3 KB of bytes).
 constexpr int UNION_RECORD_FIXED = 3072;
 constexpr int UNION_CAP = 1024;  // union records one packed workgroup can take
+// Bytes of packed records per attention split.
+constexpr int64_t PACKED_SPLIT = 96 * 1024;
 static_assert(UNION_RECORD_FIXED <= 16384, "union weights of a unit stay below 2^32 / 4");
 
 // ---- compression ----------------------------------------------------------

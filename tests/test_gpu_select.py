@@ -1,0 +1,102 @@
+"""GPU block selection on adversarial score distributions.
+
+The block keys (per-block min/max) of one packed segment are overwritten, on
+the device through the documented meta layout and in the oracle's state, with
+crafted values: every channel of block l holds the same value a_l, so its
+score is a_l * sum(q') / sqrt(d), and the score order is the order of a_l
+(or its reverse). Cases: many exact ties at the k-th score (ties go to the
+lower block), one outlier far above the rest (every other score falls into
+one bin of a value histogram, so the exact bit search decides), mixed signs,
+and a segment where every block ties. Selections must equal the oracle's
+exactly; outputs match the oracle on the GPU's selection.
+"""
+import numpy as np
+import pytest
+
+import mkv_synth as synth
+from oracle import oracle as orc
+
+from gpu_harness import build, check_decode_unit, log, oracle_unit
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_compression_mkv_amd import _lib  # noqa: F401
+
+
+def _bf16(x):
+    """bf16 bit patterns of float64 values exactly representable in bf16."""
+    b = (np.asarray(x, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(synth.bf16_bits_to_f32(b).astype(np.float64), np.asarray(x, np.float64))
+    return b
+
+
+def _pack_meta_head(bits, nbcap, d=128):
+    """[nb][2][d] bf16 bits (min, max) -> one head's meta bytes in the device layout
+    [ceil(nbcap/64)][2d*2/16][64][16 B]: per 16-byte group, (min, max) pairs of 4 channels."""
+    ntile = -(-nbcap // 64)
+    ng = 2 * d * 2 // 16
+    out = np.zeros((ntile, ng, 64, 4, 2), np.uint16)
+    nb = bits.shape[0]
+    full = np.zeros((ntile * 64, 2, d), np.uint16)
+    full[:nb] = bits
+    # full[l][m][c] -> out[l // 64][c // 4][l % 64][c % 4][m]
+    x = full.reshape(ntile, 64, 2, ng, 4).transpose(0, 3, 1, 4, 2)
+    out[:] = x
+    return out.reshape(-1).view(np.uint8)
+
+
+def _set_block_values(c, w, comp, b, g, j, a):
+    """Every channel of block l: min = max = a[l] (device meta and oracle state)."""
+    seg = w["segs"][b][j]
+    nbcap = -(-seg["t_cap"] // 16)
+    nb = len(a)
+    bits = np.repeat(_bf16(a)[:, None, None], 2 * 128, axis=1).reshape(nb, 2, 128)
+    raw = _pack_meta_head(bits, nbcap)
+    per_head = raw.size
+    c.meta[b][j][g * per_head:(g + 1) * per_head].copy_(torch.from_numpy(raw).cuda())
+    vals = np.repeat(np.asarray(a, np.float64)[:, None, None], 2 * 128, axis=1).reshape(nb, 2, 128)
+    pj = sum(1 for s in w["segs"][b][:j] if s["kind"] == synth.PACKED)
+    comp["meta"][pj][:] = vals
+    off = sum(-(-s["t_cap"] // 16) for s in w["segs"][b][:j] if s["kind"] == synth.PACKED)
+    comp["meta_flat"][off:off + nb] = vals
+
+
+@pytest.mark.parametrize("case", ["ties", "outlier", "mixed_sign", "all_equal"])
+def test_select_adversarial_scores(case):
+    segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * 3000, 38, 100000, 0),
+            synth.seg(synth.DENSE, 32 + 16 * 3000, 64)]
+    T = 32 + 16 * 3000 + 40
+    w = dict(cfg=2, batch=1, n_q_heads=8, n_kv_heads=2, d=128, dtype="bf16", lengths=np.array([T]), segs=[segs])
+    c, raw, R = build(torch, w)
+    nb = 3000
+    rng = np.random.default_rng({"ties": 1, "outlier": 2, "mixed_sign": 3, "all_equal": 4}[case])
+    if case == "ties":
+        a = np.round(rng.uniform(1.0, 2.0, nb) * 8) / 8          # 9 distinct values, ~330 blocks each
+    elif case == "outlier":
+        a = 1.0 + rng.integers(0, 127, nb) / 128.0                # 127 values in [1, 2)
+        a[1234] = 2.0 ** 60                                       # far above: the rest share one bin
+    elif case == "mixed_sign":
+        a = rng.choice([-1, 1], nb) * 2.0 ** rng.integers(-20, 20, nb) * (1 + rng.integers(0, 8, nb) / 8)
+    else:
+        a = np.full(nb, 0.75)
+    q = synth.gen_q(2, 11, 1, 8, "bf16")
+    ex = 0
+    for g in range(2):
+        comp, Rk, Rv = oracle_unit(w, raw, R, 0, g, T)
+        _set_block_values(c, w, comp, 0, g, 1, a)
+        out, sel = c.decode(torch.from_numpy(q).cuda(), want_sel=True)
+        torch.cuda.synchronize()
+        out, sel = out.cpu().numpy(), sel.cpu().numpy()
+        hs = slice(4 * g, 4 * g + 4)
+        own = orc.decode_unit(comp, q[0, hs].astype(np.float64), Rk, Rv)
+        for h in range(4):
+            assert sel[0, 4 * g + h, :own["sel"][0].shape[1]].tolist() == own["sel"][0][h].tolist(), \
+                "%s: g=%d h=%d selection differs" % (case, g, h)
+        ex += check_decode_unit(w, comp, Rk, Rv, q[0, hs].astype(np.float64), out[0, hs], sel[0, hs], 5e-3, T, 0, g)
+    log("adversarial select (%s): selections equal the oracle's" % case)

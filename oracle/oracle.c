@@ -15,8 +15,13 @@
  *       Long-Context LLM with Dynamic Two-D KV Cache Compression"):
  *       section 4.2 (two-stage compression: top-r elements, then top-k token
  *       blocks by query-to-block-key scores), 5.2 (per-block keys), 5.3
- *       (PackedAttention; inverse rotation merged into the query), 6.3
- *       (Quest per-block keys at block size 16).
+ *       (PackedAttention; inverse rotation merged into the query), 5.4
+ *       (heterogeneous double compression buffering: a finished segment is
+ *       recompressed on the CPU with its own SVD rotation and swapped in),
+ *       6.3 (Quest per-block keys at block size 16).
+ *   [N] also describes the double buffering (its heterogeneous double
+ *       buffering section and Fig. 4): the swapped-in segment is packed with
+ *       a per-segment rotation.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - rotation arithmetic: x'_c = sum_j R[c][j] x_j in fp64, j ascending;
@@ -270,16 +275,20 @@ static int64_t n_blocks_of(int64_t filled, int block) { return (filled + block -
 /* Compress tokens [t_from, len) of a unit and rebuild the per-block keys of
  * every block holding one of them (tokens before t_from are already stored).
  *   Kraw, Vraw [len][d]: stored raw inputs (as exact doubles)
- *   Rk, Rv [d][d]
+ *   Rk, Rv [d][d]: the unit's rotation
+ *   segR (nullable): per segment, NULL or its own [2][d][d] rotation (R_k then
+ *        R_v) that replaces Rk, Rv for the tokens of that segment (the paper's
+ *        per-segment SVD of recompressed segments, section 5.4; the reading
+ *        notes' heterogeneous double buffering)
  *   Khat, Vhat [len][d]: stored values, 0 at dropped channels
  *   Kidx, Vidx [len][d]: kept channels ascending, then -1 (dense tokens: 0..d-1)
  *   meta: packed segments one after the other, each [ceil(t_cap/block)][2][d] (mn, mx)
  * Returns 0, or 1 when a token falls outside every segment. */
 int orc_compress_unit(int d, int64_t len, int64_t t_from, int dtype, int block,
                       const double *Kraw, const double *Vraw, const double *Rk, const double *Rv,
-                      int nseg, const int32_t *kind, const int64_t *t_begin, const int64_t *t_cap,
-                      const int32_t *r, double *Khat, double *Vhat, int16_t *Kidx, int16_t *Vidx,
-                      double *meta, int nthreads) {
+                      const double *const *segR, int nseg, const int32_t *kind, const int64_t *t_begin,
+                      const int64_t *t_cap, const int32_t *r, double *Khat, double *Vhat, int16_t *Kidx,
+                      int16_t *Vidx, double *meta, int nthreads) {
     if (t_from < 0) t_from = 0;
     for (int64_t t = t_from; t < len; ++t)
         if (find_segment(nseg, t_begin, t_cap, t) < 0) return 1;
@@ -288,7 +297,7 @@ int orc_compress_unit(int d, int64_t len, int64_t t_from, int dtype, int block,
         const int j = find_segment(nseg, t_begin, t_cap, t);
         for (int which = 0; which < 2; ++which) {
             const double *x = (which == 0 ? Kraw : Vraw) + t * d;
-            const double *R = which == 0 ? Rk : Rv;
+            const double *R = (segR && segR[j]) ? segR[j] + (int64_t)which * d * d : (which == 0 ? Rk : Rv);
             double *hat = (which == 0 ? Khat : Vhat) + t * d;
             int16_t *ix = (which == 0 ? Kidx : Vidx) + t * d;
             double xr[256];
@@ -380,11 +389,17 @@ static int ascending_i32(const void *a, const void *b) {
  *   z_i = (1/sqrt d) q'[I_i]^T k^_i over dense tokens and selected blocks
  *   o = softmax(z) V^                            ([N] Eq. 13)
  *   out_j = sum_c R_v[c][j] o_c                  ([N] Eq. 14)
+ * A segment with its own rotation (segR[j] != NULL, [2][d][d]) stores its
+ * tokens in its own rotated space: its scores and logits use q'_j = R_k,j q,
+ * and its share of o is rotated back by its own R_v,j. Since the softmax
+ * weights are shared and the inverse rotation is linear,
+ *   out = sum over segments j of R_v,j^T (sum_{i in j} p_i v^_i).
  * forced_sel (nullable) replaces the top-k by a given selection.
  * Outputs: qrot [G][d], scores [G][nsum], sel [G][ksum], tau [G][npacked]
  * (the k-th largest score; NAN when k = 0), out [G][d]. */
 int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, const double *Vhat,
-                    const int16_t *Kidx, const int16_t *Vidx, const double *meta, int nseg,
+                    const int16_t *Kidx, const int16_t *Vidx, const double *meta, const double *const *segR,
+                    int nseg,
                     const int32_t *kind, const int64_t *t_begin, const int64_t *t_cap,
                     const int32_t *r, const int32_t *keep_ppm, const int32_t *k_abs, const double *q,
                     const double *Rk, const double *Rv, const int32_t *forced_sel, double *qrot,
@@ -405,13 +420,23 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
     for (int h = 0; h < G; ++h) {
         double *qr = qrot + (int64_t)h * d;
         rotate(Rk, q + (int64_t)h * d, d, qr);
+        /* q' in the rotated space of each segment: the unit's, or its own */
+        double *qseg = (double *)malloc(sizeof(double) * (size_t)nseg * d);
+        if (!qseg) {
+            status = 1;
+            continue;
+        }
+        for (int j = 0; j < nseg; ++j) {
+            if (segR && segR[j]) rotate(segR[j], q + (int64_t)h * d, d, qseg + (int64_t)j * d);
+            else memcpy(qseg + (int64_t)j * d, qr, sizeof(double) * d);
+        }
         double *sc = scores + h * nsum;
         int32_t *sh = sel + h * ksum;
         scored *tmp = (scored *)malloc(sizeof(scored) * (size_t)(nsum > 0 ? nsum : 1));
         char *chosen = (char *)calloc((size_t)(nsum > 0 ? nsum : 1), 1);
         if (!tmp || !chosen) {
             status = 1;
-            free(tmp); free(chosen);
+            free(tmp); free(chosen); free(qseg);
             continue;
         }
         int64_t noff = 0, koff = 0, moff = 0;
@@ -420,11 +445,12 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
             if (kind[j] != ORC_PACKED) continue;
             const int64_t nb = n_blocks_of(seg_filled(len, t_begin[j], t_cap[j]), block);
             const int64_t k = orc_block_keep(nb, keep_ppm[j], k_abs[j]);
+            const double *qj = qseg + (int64_t)j * d;
             for (int64_t l = 0; l < nb; ++l) {
                 const double *mn = meta + (moff + l) * 2 * d, *mx = mn + d;
                 double s = 0.0;
                 for (int c = 0; c < d; ++c) {
-                    const double a = qr[c] * mx[c], b = qr[c] * mn[c];
+                    const double a = qj[c] * mx[c], b = qj[c] * mn[c];
                     s += a > b ? a : b;
                 }
                 sc[noff + l] = s * scale;
@@ -454,7 +480,7 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
         char *att = (char *)calloc((size_t)(len > 0 ? len : 1), 1);
         if (!z || !att) {
             status = 1;
-            free(z); free(att); free(tmp); free(chosen);
+            free(z); free(att); free(tmp); free(chosen); free(qseg);
             continue;
         }
         noff = 0;
@@ -475,29 +501,40 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
         double zmax = -INFINITY;
         for (int64_t t = 0; t < len; ++t) {
             if (!att[t]) continue;
+            const double *qj = qseg + (int64_t)find_segment(nseg, t_begin, t_cap, t) * d;
             double s = 0.0;
             const int16_t *ix = Kidx + t * d;
-            for (int m = 0; m < d && ix[m] >= 0; ++m) s += qr[ix[m]] * Khat[t * d + ix[m]];
+            for (int m = 0; m < d && ix[m] >= 0; ++m) s += qj[ix[m]] * Khat[t * d + ix[m]];
             z[t] = s * scale;
             if (z[t] > zmax) zmax = z[t];
         }
+        /* o_j: the weighted sum of segment j's stored values, in its space */
+        double *o = (double *)calloc((size_t)nseg * d, sizeof(double));
+        if (!o) {
+            status = 1;
+            free(z); free(att); free(tmp); free(chosen); free(qseg);
+            continue;
+        }
         double denom = 0.0;
-        double o[256];
-        for (int c = 0; c < d; ++c) o[c] = 0.0;
         for (int64_t t = 0; t < len; ++t) {
             if (!att[t]) continue;
             const double w = exp(z[t] - zmax);
             denom += w;
+            double *oj = o + (int64_t)find_segment(nseg, t_begin, t_cap, t) * d;
             const int16_t *ix = Vidx + t * d;
-            for (int m = 0; m < d && ix[m] >= 0; ++m) o[ix[m]] += w * Vhat[t * d + ix[m]];
+            for (int m = 0; m < d && ix[m] >= 0; ++m) oj[ix[m]] += w * Vhat[t * d + ix[m]];
         }
-        for (int c = 0; c < d; ++c) o[c] = denom > 0.0 ? o[c] / denom : 0.0;
-        for (int jj = 0; jj < d; ++jj) {
-            double s = 0.0;
-            for (int c = 0; c < d; ++c) s += Rv[c * d + jj] * o[c];
-            out[(int64_t)h * d + jj] = s;
+        for (int jj = 0; jj < d; ++jj) out[(int64_t)h * d + jj] = 0.0;
+        for (int j = 0; j < nseg; ++j) {
+            const double *Rvj = (segR && segR[j]) ? segR[j] + (int64_t)d * d : Rv;
+            const double *oj = o + (int64_t)j * d;
+            for (int jj = 0; jj < d; ++jj) {
+                double s = 0.0;
+                for (int c = 0; c < d; ++c) s += Rvj[c * d + jj] * (denom > 0.0 ? oj[c] / denom : 0.0);
+                out[(int64_t)h * d + jj] += s;
+            }
         }
-        free(z); free(att); free(tmp); free(chosen);
+        free(o); free(z); free(att); free(tmp); free(chosen); free(qseg);
     }
     return status;
 }

@@ -53,10 +53,10 @@ def _lib():
         L.orc_block_keep.restype = I64
         L.orc_block_keep.argtypes = [I64, I32, I32]
         L.orc_compress_unit.restype = ctypes.c_int
-        L.orc_compress_unit.argtypes = [ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P, P,
+        L.orc_compress_unit.argtypes = [ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P,
                                         ctypes.c_int, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         L.orc_decode_unit.restype = ctypes.c_int
-        L.orc_decode_unit.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P,
+        L.orc_decode_unit.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
                                       ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                       ctypes.c_int]
         _LIB = L
@@ -139,14 +139,27 @@ def seg_blocks(segs, length: int, block: int = BLOCK):
     return out
 
 
+def _seg_rot_table(seg_rot, nseg, d):
+    """(ctypes pointer array, kept arrays) for per-segment rotations: seg_rot is
+    None or a list (per segment) of None or (R_k, R_v) [d][d]."""
+    if seg_rot is None:
+        return None, []
+    assert len(seg_rot) == nseg
+    keep = [None if x is None else _c(np.stack([x[0], x[1]]), np.float64).reshape(2, d, d) for x in seg_rot]
+    tab = (ctypes.c_void_p * nseg)(*[None if a is None else a.ctypes.data for a in keep])
+    return tab, keep
+
+
 def compress_unit(Kraw, Vraw, Rk, Rv, segs, length: int, dtype: str, block: int = BLOCK,
-                  nthreads: int | None = None, state=None):
+                  nthreads: int | None = None, state=None, seg_rot=None):
     """Compress one (request, KV head) unit. Returns a dict with Khat, Vhat, Kidx, Vidx
     ([len][d]) and meta: list (one per packed segment) of [n_blocks][2][d].
 
     state: a dict returned by an earlier call on the same unit; then only the
     tokens from its length on are compressed, into the same arrays (their row
-    capacity is the row count of the raw inputs given the first time)."""
+    capacity is the row count of the raw inputs given the first time).
+    seg_rot: per segment, None or its own (R_k, R_v), which then replace Rk, Rv
+    for that segment's tokens (kept in the state for decode_unit)."""
     if Kraw.shape[0] < length or Vraw.shape[0] < length:
         raise ValueError("compress_unit: %d input rows for length %d" % (min(Kraw.shape[0], Vraw.shape[0]), length))
     d = Kraw.shape[1]
@@ -157,16 +170,19 @@ def compress_unit(Kraw, Vraw, Rk, Rv, segs, length: int, dtype: str, block: int 
         rows = max(Kraw.shape[0], length, 1)
         st = dict(Khat=np.zeros((rows, d)), Vhat=np.zeros((rows, d)), Kidx=np.full((rows, d), -1, np.int16),
                   Vidx=np.full((rows, d), -1, np.int16), meta_flat=np.zeros((max(sum(nbcaps), 1), 2, d)),
-                  length=0, segs=segs, dtype=dtype, block=block)
+                  length=0, segs=segs, dtype=dtype, block=block, seg_rot=seg_rot)
     else:
         st = state
         if st["Khat"].shape[0] < length:
             raise ValueError("compress_unit: state holds %d rows, need %d" % (st["Khat"].shape[0], length))
+        if seg_rot is not None:
+            st["seg_rot"] = seg_rot
+    tab, _rot_arrays = _seg_rot_table(st.get("seg_rot"), len(segs), d)
     t_from = st["length"]
     Kin = _c(Kraw[:length], np.float64)
     Vin = _c(Vraw[:length], np.float64)
     rc = _lib().orc_compress_unit(d, length, t_from, DTYPES[dtype], block, Kin.ctypes.data, Vin.ctypes.data,
-                                  Rk.ctypes.data, Rv.ctypes.data, len(segs), kind.ctypes.data,
+                                  Rk.ctypes.data, Rv.ctypes.data, tab, len(segs), kind.ctypes.data,
                                   tb.ctypes.data, cap.ctypes.data, r.ctypes.data, st["Khat"].ctypes.data,
                                   st["Vhat"].ctypes.data, st["Kidx"].ctypes.data, st["Vidx"].ctypes.data,
                                   st["meta_flat"].ctypes.data, nthreads or threads())
@@ -182,7 +198,8 @@ def compress_unit(Kraw, Vraw, Rk, Rv, segs, length: int, dtype: str, block: int 
 
 
 def decode_unit(comp, q, Rk, Rv, forced_sel=None, nthreads: int | None = None):
-    """Decode attention for the G query heads q [G][d] of one compressed unit.
+    """Decode attention for the G query heads q [G][d] of one compressed unit
+    (with the per-segment rotations the unit was compressed with, if any).
 
     forced_sel: optional list (per packed segment) of [G][k] block lists that
     replace the top-k. Returns dict(qrot [G][d], scores [list per seg of [G][n]],
@@ -204,9 +221,10 @@ def decode_unit(comp, q, Rk, Rv, forced_sel=None, nthreads: int | None = None):
             if npk else np.zeros((G, 1), np.int32)
         fs = _c(fs, np.int32)
         assert fs.shape[1] == max(ksum, 1) or (ksum == 0)
+    tab, _rot_arrays = _seg_rot_table(comp.get("seg_rot"), len(segs), d)
     rc = _lib().orc_decode_unit(d, length, G, block, comp["Khat"].ctypes.data, comp["Vhat"].ctypes.data,
                                 comp["Kidx"].ctypes.data, comp["Vidx"].ctypes.data,
-                                comp["meta_flat"].ctypes.data, len(segs), kind.ctypes.data,
+                                comp["meta_flat"].ctypes.data, tab, len(segs), kind.ctypes.data,
                                 tb.ctypes.data, cap.ctypes.data, r.ctypes.data, keep.ctypes.data,
                                 kabs.ctypes.data, q.ctypes.data, _c(Rk, np.float64).ctypes.data,
                                 _c(Rv, np.float64).ctypes.data,

@@ -52,7 +52,7 @@ MUTANTS = [
      "for (int j = 0; j < d; ++j) R[j * d + c] = sg * V[j * d + col];",
      [pins.test_P2_energy_closed_form_and_singular_values, pins.test_rotation_matches_library_svd_vectors]),
     # the inverse rotation multiplies by R_v instead of R_v^T
-    ("inverse_rotation_transposed", "s += Rv[c * d + jj] * o[c];", "s += Rv[jj * d + c] * o[c];",
+    ("inverse_rotation_transposed", "s += Rvj[c * d + jj] *", "s += Rvj[jj * d + c] *",
      [pins.test_P4_full_retention_equals_dense_attention]),
     # forced selection: every packed segment reads the first segment's columns
     ("forced_offset_dropped", "sh[koff + i] = forced_sel[h * ksum + koff + i];",
@@ -67,6 +67,21 @@ MUTANTS = [
     ("incremental_keys_skip_open_block", "const int64_t from = t_from > t_begin[j] ? (t_from - t_begin[j]) / block : 0;",
      "const int64_t from = t_from > t_begin[j] ? (t_from - t_begin[j]) / block + 1 : 0;",
      [pins.test_incremental_compression_equals_bulk]),
+    # a segment with its own rotation is scored and attended with the unit's q'
+    ("segment_query_not_rotated", "if (segR && segR[j]) rotate(segR[j], q + (int64_t)h * d, d, qseg + (int64_t)j * d);",
+     "if (0) rotate(segR[j], q + (int64_t)h * d, d, qseg + (int64_t)j * d);",
+     [pins.test_P4_per_segment_rotations_equal_dense_attention,
+      pins.test_per_segment_rotation_matches_unrotated_reconstruction]),
+    # a segment's share of the output is rotated back by the unit's R_v
+    ("segment_inverse_rotation_unit", "const double *Rvj = (segR && segR[j]) ? segR[j] + (int64_t)d * d : Rv;",
+     "const double *Rvj = Rv;",
+     [pins.test_P4_per_segment_rotations_equal_dense_attention,
+      pins.test_per_segment_rotation_matches_unrotated_reconstruction]),
+    # a segment with its own rotation is compressed with the unit's
+    ("segment_compressed_with_unit_rotation",
+     "const double *R = (segR && segR[j]) ? segR[j] + (int64_t)which * d * d : (which == 0 ? Rk : Rv);",
+     "const double *R = which == 0 ? Rk : Rv;",
+     [pins.test_P4_per_segment_rotations_equal_dense_attention]),
     # incremental appends skip the first new token
     ("incremental_skips_first_token", "for (int64_t t = t_from; t < len; ++t) {\n        const int j",
      "for (int64_t t = t_from + 1; t < len; ++t) {\n        const int j",

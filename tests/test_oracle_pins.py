@@ -485,3 +485,66 @@ def test_incremental_compression_equals_bulk():
             st = orc.compress_unit(K, V, Rk, Rv, segs, int(c), "f32" if trial % 2 else "bf16", state=st)
         bulk = orc.compress_unit(K, V, Rk, Rv, segs, T, "f32" if trial % 2 else "bf16")
         _assert_same_state(st, bulk, T)
+
+
+# ------------------------------------------------------ per-segment rotation --
+def _haar(rng, d):
+    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def test_P4_per_segment_rotations_equal_dense_attention():
+    """Segments stored in their own rotated spaces (a recompressed segment's
+    own SVD rotation, paper section 5.4) change nothing when every element and
+    block is kept in binary64: the output is still softmax(q k^T / sqrt d) v on
+    the raw data (reading notes Eq. 1), since each R is orthogonal and each
+    segment's queries and outputs use its own R."""
+    d, T = 32, 420
+    rng = np.random.default_rng(71)
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    Rk, _ = orc.rotation(K)
+    Rv, _ = orc.rotation(V)
+    segs = [synth.seg(0, 0, 20), synth.seg(1, 20, 200, d, 1000000, 0), synth.seg(1, 220, 150, d, 1000000, 0),
+            synth.seg(0, 370, 50)]
+    seg_rot = [None, (_haar(rng, d), _haar(rng, d)), (orc.rotation(K[220:370])[0], orc.rotation(V[220:370])[0]),
+               (_haar(rng, d), _haar(rng, d))]
+    comp = orc.compress_unit(K, V, Rk, Rv, segs, T, "f64", seg_rot=seg_rot)
+    q = rng.standard_normal((3, d))
+    res = orc.decode_unit(comp, q, Rk, Rv)
+    for h in range(3):
+        z = K @ q[h] / math.sqrt(d)
+        p = np.exp(z - z.max())
+        ref = (p / p.sum()) @ V
+        assert np.linalg.norm(res["out"][h] - ref) / np.linalg.norm(ref) <= 1e-12
+
+
+def test_per_segment_rotation_matches_unrotated_reconstruction():
+    """With top-r storage and per-segment rotations, the oracle's output equals a
+    masked softmax in the original space over the stored vectors rotated back
+    one by one (row k^ R_j for a token of segment j, reading notes Eq. 7-8),
+    computed with float64 matrix products -- a different path from the
+    oracle's per-segment query rotation and per-segment inverse rotation."""
+    d, T = 16, 300
+    rng = np.random.default_rng(72)
+    K = orc.round_to(rng.standard_normal((T, d)), "bf16")
+    V = orc.round_to(rng.standard_normal((T, d)), "bf16")
+    Rk, _ = orc.rotation(rng.standard_normal((64, d)))
+    Rv, _ = orc.rotation(rng.standard_normal((64, d)))
+    segs = [synth.seg(0, 0, 10), synth.seg(1, 10, 130, 4, 250000, 0),
+            synth.seg(1, 140, 120, 7, 0, 3), synth.seg(0, 260, 50)]
+    own = [None, (_haar(rng, d), _haar(rng, d)), None, (_haar(rng, d), _haar(rng, d))]
+    comp = orc.compress_unit(K, V, Rk, Rv, segs, T, "bf16", seg_rot=own)
+    q = rng.standard_normal((4, d))
+    res = orc.decode_unit(comp, q, Rk, Rv)
+    Kor = np.empty((T, d))
+    Vor = np.empty((T, d))
+    for j, s in enumerate(segs):
+        t0, t1 = s["t_begin"], min(s["t_begin"] + s["t_cap"], T)
+        Rkj, Rvj = own[j] if own[j] is not None else (Rk, Rv)
+        Kor[t0:t1] = comp["Khat"][t0:t1] @ Rkj
+        Vor[t0:t1] = comp["Vhat"][t0:t1] @ Rvj
+    for h in range(4):
+        att = _token_mask(segs, T, res["sel"], h)
+        o = brute.attention_dense(Kor, Vor, q[h], att, d)
+        assert np.abs(o - res["out"][h]).max() <= 1e-12 * max(1.0, np.abs(o).max())

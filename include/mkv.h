@@ -76,8 +76,16 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1 } mkv_seg_kind;
  * data      device buffer of mkv_segment_bytes() bytes (layout below).
  * meta      device buffer of the meta bytes reported by mkv_segment_bytes()
  *           (packed only; NULL for dense).
+ * rot       NULL: the segment's tokens are rotated by the cache's rotation of
+ *           the request. Otherwise the segment's own rotation, device float32
+ *           [n_kv_heads][2][d][d] (R_k then R_v per KV head, rows as for the
+ *           cache's), 16-byte aligned: appends to the segment rotate by it,
+ *           and decode scores and attends the segment with q' = R_k,seg q and
+ *           rotates its share of the output back by its own R_v,seg ([S] 5.4:
+ *           a finished segment recompressed with its own SVD rotation; see
+ *           mkv_recompress_segment and mkv_swap_segment).
  * Across the requests of one cache, segment j must have the same kind, r,
- * keep_ppm and k_abs; t_begin and t_cap may differ per request.
+ * keep_ppm and k_abs; t_begin, t_cap and rot may differ per request.
  *
  * Device layouts (s = bytes per stored element, nb = ceil(t_cap / 16),
  * block l holds positions t_begin + 16 l .. t_begin + 16 l + 15, slot = position - block start):
@@ -105,6 +113,7 @@ typedef struct mkv_segment {
     int64_t t_cap;
     void *data;
     void *meta;
+    const float *rot;
 } mkv_segment;
 
 /* A compressed cache for one attention layer of a batch of requests.
@@ -173,7 +182,9 @@ mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_ne
 mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream);
 
 /* Workspace bytes mkv_decode_attn needs for this cache (sized from capacities,
- * so it does not change as the cache fills). */
+ * so it does not change as the cache fills; it grows with the number of
+ * segment indices whose segment carries its own rotation in some request, so
+ * query it again after mkv_swap_segment gives a segment its first own one). */
 size_t mkv_decode_workspace_bytes(const mkv_cache *c);
 
 /* Columns of sel_out needed at the current lengths: max over requests of the
@@ -212,6 +223,46 @@ mkv_status mkv_decode_attn(const mkv_cache *c, const float *q, float *out, int32
 mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
                              int32_t n_max, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
                              void *workspace, size_t ws_bytes, void *stream);
+
+/* Exact recompression of one finished packed segment on the host: the
+ * CPU side of the paper's heterogeneous double compression buffering ([S]
+ * 5.4; [N] its double-buffering section and Fig. 4), where a segment first
+ * compressed on arrival with the request's rotation is re-packed with a
+ * rotation of its own and swapped in without blocking decode.
+ * For each KV head g: R_k,g and R_v,g from the segment's raw keys and values
+ * exactly as mkv_rotation_from_prefill computes them; then every token is
+ * rotated in float64 with exact products (summed in ascending input channel),
+ * keeps its r largest elements (ties to the lower channel), rounded once to
+ * nearest even, and the per-block min/max keys are formed -- the arithmetic
+ * of mkv_compress_append, so the result is what the GPU would store with
+ * these rotations.
+ * k_host, v_host: [n_kv_heads][n_tokens][d] in `dtype` (f32 values or bf16
+ *   bit patterns), n_tokens in 1..t_cap.
+ * Outputs in the documented device layouts, in host memory the caller owns:
+ *   data_out [mkv_segment_bytes(dtype, MKV_SEG_PACKED, r, d, n_kv_heads, t_cap)]
+ *     (slots after the last token zero; the tail bytes are left as they are),
+ *   meta_out [that call's meta bytes] (blocks past the last one zero),
+ *   rot_out float32 [n_kv_heads][2][d][d].
+ * Synchronous host computation (OpenMP); d == MKV_HEAD_DIM, dtype MKV_F32 or
+ * MKV_BF16, r in 1..d. Errors: MKV_ERR_ARG, MKV_ERR_UNSUPPORTED,
+ * MKV_ERR_NOCONVERGE. */
+mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
+                                  int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t r, void *data_out,
+                                  void *meta_out, float *rot_out);
+
+/* Stream-ordered swap of packed segment `seg` of request b to new device
+ * buffers (data, meta, rot: as mkv_segment's, e.g. mkv_recompress_segment's
+ * outputs copied to the device), without any host wait: if ready_event (a
+ * hipEvent_t, nullable) is given, `stream` is made to wait for it (e.g. the
+ * end of the copies on another stream), then the descriptor of (b, seg) is
+ * pointed at the new buffers. Work enqueued on `stream` before the call reads
+ * the old buffers, work enqueued after it the new ones; the caller keeps the
+ * old buffers alive until that earlier work is done. The segment must be
+ * full (c->len[b] >= t_begin + t_cap) and keep its kind, r and capacity.
+ * Errors: MKV_ERR_ARG, MKV_ERR_HIP (the wait could not be enqueued; nothing
+ * changed). */
+mkv_status mkv_swap_segment(mkv_cache *c, int32_t b, int32_t seg, void *data, void *meta, const float *rot,
+                            void *ready_event, void *stream);
 
 /* Decode attention without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

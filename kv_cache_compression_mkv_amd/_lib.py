@@ -28,14 +28,14 @@ MKV_SCRATCH_BYTES = 128 << 20
 
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
            "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",
-           "mkv_append_decode", "mkv_decode_attn_noalloc", "mkv_timing_enable", "mkv_timing_read",
-           "mkv_stage_name"]
+           "mkv_append_decode", "mkv_decode_attn_noalloc", "mkv_recompress_segment", "mkv_swap_segment",
+           "mkv_timing_enable", "mkv_timing_read", "mkv_stage_name"]
 
 
 class mkv_segment(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("keep_ppm", ctypes.c_int32),
                 ("k_abs", ctypes.c_int32), ("t_begin", ctypes.c_int64), ("t_cap", ctypes.c_int64),
-                ("data", ctypes.c_void_p), ("meta", ctypes.c_void_p)]
+                ("data", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("rot", ctypes.c_void_p)]
 
 
 class mkv_cache(ctypes.Structure):
@@ -74,6 +74,10 @@ def _load():
     L.mkv_decode_attn.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I64, P, SZ, P]
     L.mkv_append_decode.restype = ctypes.c_int
     L.mkv_append_decode.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P, P, P, I64, P, SZ, P]
+    L.mkv_recompress_segment.restype = ctypes.c_int
+    L.mkv_recompress_segment.argtypes = [P, P, I32, I32, I32, I64, I64, I32, P, P, P]
+    L.mkv_swap_segment.restype = ctypes.c_int
+    L.mkv_swap_segment.argtypes = [ctypes.POINTER(mkv_cache), I32, I32, P, P, P, P, P]
     L.mkv_decode_attn_noalloc.restype = ctypes.c_int
     L.mkv_decode_attn_noalloc.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I64, P]
     L.mkv_timing_enable.restype = ctypes.c_int
@@ -135,6 +139,18 @@ def mkv_append_decode(cache: mkv_cache, k_ptr: int, v_ptr: int, n_new_ptr: int, 
                       out_ptr: int, sel_ptr, sel_cols: int, ws_ptr: int, ws_bytes: int, stream: int):
     _check(LIB.mkv_append_decode(ctypes.byref(cache), k_ptr, v_ptr, n_new_ptr, n_max, q_ptr, out_ptr, sel_ptr,
                                  sel_cols, ws_ptr, ws_bytes, stream), "mkv_append_decode")
+
+
+def mkv_recompress_segment(k_ptr: int, v_ptr: int, dtype: int, d: int, n_kv_heads: int, n_tokens: int, t_cap: int,
+                           r: int, data_ptr: int, meta_ptr: int, rot_ptr: int):
+    _check(LIB.mkv_recompress_segment(k_ptr, v_ptr, dtype, d, n_kv_heads, n_tokens, t_cap, r, data_ptr, meta_ptr,
+                                      rot_ptr), "mkv_recompress_segment")
+
+
+def mkv_swap_segment(cache: mkv_cache, b: int, seg: int, data_ptr: int, meta_ptr: int, rot_ptr: int, event,
+                     stream: int):
+    _check(LIB.mkv_swap_segment(ctypes.byref(cache), b, seg, data_ptr, meta_ptr, rot_ptr, event, stream),
+           "mkv_swap_segment")
 
 
 def mkv_decode_attn_noalloc(cache: mkv_cache, q_ptr: int, out_ptr: int, sel_ptr, sel_cols: int, stream: int):

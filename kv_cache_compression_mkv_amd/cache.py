@@ -52,6 +52,7 @@ class Cache:
                 e.meta = mt.data_ptr() if mt is not None else None
             self.data.append(drow)
             self.meta.append(mrow)
+        self.seg_rot = [[None] * self.nseg for _ in range(batch)]  # segments' own rotations (device tensors)
         self.rot = torch.zeros((batch, n_kv_heads, 2, head_dim, head_dim), dtype=torch.float32, device=device)
         self.c = L.mkv_cache(batch, n_q_heads, n_kv_heads, head_dim, self.code, self.nseg,
                              ctypes.cast(self._segs, ctypes.POINTER(L.mkv_segment)),
@@ -66,6 +67,47 @@ class Cache:
     def set_rotation(self, R):
         """R: [batch][n_kv][2][d][d] float32 (numpy or torch)."""
         self.rot.copy_(torch.as_tensor(np.asarray(R, np.float32)).to(self.device))
+
+    def set_segment_rotation(self, b: int, j: int, R):
+        """Give segment j of request b its own rotation before any token reaches it:
+        R [n_kv][2][d][d] float32 (numpy or torch)."""
+        t = torch.as_tensor(np.asarray(R, np.float32)).to(self.device).contiguous()
+        self.seg_rot[b][j] = t
+        self._segs[b * self.nseg + j].rot = t.data_ptr()
+
+    def recompress_segment(self, b: int, j: int, k_host, v_host):
+        """Host recompression of segment j of request b (mkv_recompress_segment) from
+        its raw keys and values, numpy [n_kv][n_tokens][d] (float32, or bf16 bits as
+        uint16). Returns host (data, meta, rot) in the device layouts."""
+        s = self.seg_list[b][j]
+        nbytes, mbytes = L.mkv_segment_bytes(self.code, s["kind"], s["r"], self.d, self.hkv, s["t_cap"])
+        data = np.zeros(nbytes, np.uint8)
+        meta = np.zeros(mbytes, np.uint8)
+        rot = np.zeros((self.hkv, 2, self.d, self.d), np.float32)
+        k = np.ascontiguousarray(k_host)
+        v = np.ascontiguousarray(v_host)
+        L.mkv_recompress_segment(k.ctypes.data, v.ctypes.data, self.code, self.d, self.hkv, int(k.shape[1]),
+                                 s["t_cap"], s["r"], data.ctypes.data, meta.ctypes.data, rot.ctypes.data)
+        return data, meta, rot
+
+    def swap_segment(self, b: int, j: int, data, meta, rot, copy_stream=None):
+        """Copy host (data, meta, rot) to new device buffers on copy_stream (a side
+        stream by default) and swap them in for segment j of request b
+        (mkv_swap_segment): the current stream waits for the copies, the host does
+        not. Returns the previous device buffers, which must outlive the work
+        enqueued before the swap."""
+        copy_stream = copy_stream or torch.cuda.Stream()
+        ev = torch.cuda.Event()
+        with torch.cuda.stream(copy_stream):
+            dt = torch.from_numpy(np.asarray(data, np.uint8)).pin_memory().to(self.device, non_blocking=True)
+            mt = torch.from_numpy(np.asarray(meta, np.uint8)).pin_memory().to(self.device, non_blocking=True)
+            rt = torch.from_numpy(np.asarray(rot, np.float32)).pin_memory().to(self.device, non_blocking=True)
+            ev.record(copy_stream)
+        old = (self.data[b][j], self.meta[b][j], self.seg_rot[b][j])
+        L.mkv_swap_segment(self.c, b, j, dt.data_ptr(), mt.data_ptr(), rt.data_ptr(), ev.cuda_event, _stream())
+        self.data[b][j], self.meta[b][j], self.seg_rot[b][j] = dt, mt, rt
+        self._keep = (ev, copy_stream)
+        return old
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, n_new):
         """k_new, v_new: device tensors [batch][n_kv][n_max][d] of the storage dtype

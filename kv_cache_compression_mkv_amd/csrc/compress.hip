@@ -309,10 +309,15 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
         if (blockIdx.x >= D / 32) return;
         __shared__ __align__(16) float qsh[4][D];
         const int b = (int)blockIdx.z - A.n_ent, g = (int)blockIdx.y, cb = (int)blockIdx.x;
+        // the cache's rotation: q' slot 0 of the request
+        const float *Rb = A.rot + (size_t)b * A.n_kv * 2 * D * D;
+        const float *qb = A.q + (size_t)b * A.q_hq * D;
+        float *qa = A.qa + (size_t)b * A.q_ns * A.q_hq * D;
+        float *qs = A.qs + (size_t)b * A.q_ns * A.n_kv * D * 2 * A.q_G;
         switch (A.q_G) {
-        case 1: qrot_block<1>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
-        case 2: qrot_block<2>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
-        default: qrot_block<4>(A.rot, A.q, A.qa, A.qs, A.q_hq, A.n_kv, b, g, cb, qsh); break;
+        case 1: qrot_block<1>(Rb, qb, qa, qs, g, cb, qsh); break;
+        case 2: qrot_block<2>(Rb, qb, qa, qs, g, cb, qsh); break;
+        default: qrot_block<4>(Rb, qb, qa, qs, g, cb, qsh); break;
         }
         return;
     }
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     int bx = c0 + w;  // block index within the entry's range; the block is E.blk0 + bx
     if (bx < c1) block_begin<ST, BULK>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
     {
-        const float4 *Rg = reinterpret_cast<const float4 *>(A.rot + (unit * 2 + mat) * D * D);
+        const float4 *Rg = reinterpret_cast<const float4 *>(E.rot + ((size_t)g * 2 + mat) * D * D);
         float4 v[D * D / 4 / 256];
 #pragma unroll
         for (int k = 0; k < D * D / 4 / 256; ++k) v[k] = Rg[threadIdx.x + 256 * k];
@@ -403,7 +408,7 @@ hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStr
     const bool small = compress_stages(max_blk);
     // a query rotation rides along only on one-block-chunk launches
     if (a.q_req > 0 && (!small || !a.q || !a.qa || !a.qs || (a.q_G != 1 && a.q_G != 2 && a.q_G != 4) ||
-                        a.q_hq != a.q_G * a.n_kv))
+                        a.q_hq != a.q_G * a.n_kv || a.q_ns < 1))
         return hipErrorInvalidValue;
     CompressArgs b = a;
     b.chunk_blocks = small ? 1 : COMPRESS_CHUNK;

@@ -34,10 +34,28 @@ __device__ __forceinline__ const DSeg &seg_of(const DecodeArgs &A, int bl, int s
 // ----------------------------------------------------------------------------
 // q_rotate: four workgroups per (request, KV head), 32 channels each.
 // ----------------------------------------------------------------------------
+// the rotations [n_kv][2][D][D] of rotation slot `slot` for request bl of the
+// launch: the cache's for slot 0 and for requests whose segment of that slot
+// has no rotation of its own, else the segment's
+__device__ __forceinline__ const float *slot_rot(const DecodeArgs &A, int bl, int slot) {
+    const float *own = nullptr;
+    if (slot > 0)
+        for (int j = 0; j < A.nseg; ++j) {
+            const DSeg &S = seg_of(A, bl, j);
+            if (S.slot == slot) own = S.rot;
+        }
+    return own ? own : A.rot + (size_t)(A.b0 + bl) * A.hkv * 2 * D * D;
+}
+
+// q' of every rotation slot from qrot_from on: grid z = request * nslot + slot
 template <int G>
 __global__ __launch_bounds__(256) void k_qrot(const DecodeArgs A) {
     __shared__ __align__(16) float qsh[G][D];
-    qrot_block<G>(A.rot, A.q, A.qa, A.qs, A.hq, A.hkv, A.b0 + (int)blockIdx.z, (int)blockIdx.y, (int)blockIdx.x, qsh);
+    const int bl = (int)blockIdx.z / A.nslot, slot = (int)blockIdx.z % A.nslot;
+    if (slot < A.qrot_from) return;
+    const int b = A.b0 + bl;
+    qrot_block<G>(slot_rot(A, bl, slot), A.q + (size_t)b * A.hq * D, A.qa + ((size_t)b * A.nslot + slot) * A.hq * D,
+                  A.qs + ((size_t)b * A.nslot + slot) * A.hkv * D * 2 * G, (int)blockIdx.y, (int)blockIdx.x, qsh);
 }
 
 // ----------------------------------------------------------------------------
@@ -59,7 +77,7 @@ __device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, i
     const int ntile_cap = (S.nbcap + META_TILE - 1) / META_TILE;
     const uint4 *mt = reinterpret_cast<const uint4 *>(static_cast<const char *>(S.meta) +
                                                       ((size_t)g * ntile_cap + tile) * NG * META_TILE * 16);
-    const float *__restrict__ qs = A.qs + (((size_t)b * A.hkv + g) * D) * 2 * G;
+    const float *__restrict__ qs = A.qs + ((((size_t)b * A.nslot + S.slot) * A.hkv + g) * D) * 2 * G;
     float acc[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.f;
@@ -992,13 +1010,13 @@ __device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, 
     int64_t nblocks = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &S = seg_of(A, bl, si);
-        if (S.kind == MKV_SEG_DENSE) nblocks += S.nb;
+        if (S.kind == MKV_SEG_DENSE && S.slot == A.cur_slot) nblocks += S.nb;
     }
     const int64_t i0 = nblocks * s / A.S_d, i1 = nblocks * (s + 1) / A.S_d;
     int64_t before = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &S = seg_of(A, bl, si);
-        if (S.kind != MKV_SEG_DENSE) continue;
+        if (S.kind != MKV_SEG_DENSE || S.slot != A.cur_slot) continue;
         const int64_t a0 = max(i0 - before, (int64_t)0), a1 = min(i1 - before, (int64_t)S.nb);
         before += S.nb;
         if (a0 >= a1) continue;
@@ -1117,7 +1135,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
     int64_t W = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &Sg = seg_of(A, bl, si);
-        if (Sg.kind == MKV_SEG_PACKED) W += (int64_t)G * Sg.k * packed_weight(Sg.r, sb, G);
+        if (Sg.kind == MKV_SEG_PACKED && Sg.slot == A.cur_slot) W += (int64_t)G * Sg.k * packed_weight(Sg.r, sb, G);
     }
     const int64_t lo = W * s / A.S_p, hi = W * (s + 1) / A.S_p;
     int64_t Wb = 0;
@@ -1126,6 +1144,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
         const DSeg &Sg = seg_of(A, bl, si);
         if (Sg.kind != MKV_SEG_PACKED) continue;
         const int myj = pj++;
+        if (Sg.slot != A.cur_slot) continue;
         const int64_t w = packed_weight(Sg.r, sb, G);
         const int64_t items = (int64_t)G * Sg.k;
         int64_t i0 = lo - Wb, i1 = hi - Wb;
@@ -1255,7 +1274,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
 #pragma unroll
     for (int j = 0; j < UNION_MAX_SEGS; ++j) {
         const DSeg &Sg = seg_of(A, bl, A.pseg[min(j, npk - 1)]);
-        nbj[j] = j < npk ? Sg.nb : 0;
+        nbj[j] = (j < npk && Sg.slot == A.cur_slot) ? Sg.nb : 0;
         rj[j] = Sg.r;
         wj[j] = (uint32_t)(BT * Sg.r * 2 * (sb + 1) + UNION_RECORD_FIXED);
     }
@@ -1371,7 +1390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     __shared__ int2 lists[4][64];
     for (int i = (int)threadIdx.x; i < G * 2 * D; i += 256) {
         const int h = i / (2 * D), c = i % (2 * D);
-        qsh[h][c] = c < D ? A.qa[((size_t)b * A.hq + g * G + h) * D + c] : 0.f;
+        qsh[h][c] = c < D ? A.qa[(((size_t)b * A.nslot + A.cur_slot) * A.hq + g * G + h) * D + c] : 0.f;
     }
     __syncthreads();
     // each wave's split partial goes to its own LDS area once the wave is done with it
@@ -1414,7 +1433,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
             a0 = fmaf(w, x.x, a0);
             a1 = fmaf(w, x.y, a1);
         }
-        float *pp = A.part + (((size_t)b * A.hq + g * G + h) * MAX_PARTS + P) * PART;
+        float *pp = A.part + ((((size_t)b * A.hq + g * G + h) * A.nslot + A.cur_slot) * MAX_PARTS + P) * PART;
         if (lane == 0) {
             pp[0] = M;
             pp[1] = L;
@@ -1432,10 +1451,13 @@ __global__ __launch_bounds__(256) void k_score(const DecodeArgs A) {
 
 // ----------------------------------------------------------------------------
 // merge: one workgroup per (request, query head): log-sum-exp merge of the
-// head's partials (one per attend workgroup: dense ones, then packed ones) in
-// order, then out_j = sum_c R_v[c][j] o_c.
-// Thread (cc, j4) = (t / 32, t % 32) loads rows 16 cc .. 16 cc + 15 of R_v at
-// columns 4 j4 .. 4 j4 + 3 first, so those loads overlap the merge.
+// head's partials (one per attend workgroup: dense ones, then packed ones,
+// rotation slot by rotation slot) in order, then out_j = sum over slots of
+// sum_c R_v,slot[c][j] o_slot,c -- each slot's share is rotated back by its
+// own R_v (one slot unless segments carry rotations of their own).
+// Thread (cc, j4) = (t / 32, t % 32) loads rows 16 cc .. 16 cc + 15 of the
+// cache's R_v at columns 4 j4 .. 4 j4 + 3 first, so those loads overlap the
+// merge.
 // ----------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
@@ -1443,28 +1465,28 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     const int bl = (int)blockIdx.y, h = (int)blockIdx.x;
     const int b = A.b0 + bl, g = h / G;
     const int t = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x >> 6);
-    const int Stot = (A.S_d + 3) / 4 + (A.S_p + 3) / 4;  // one partial per attend workgroup
-    const float *pp = A.part + ((size_t)b * A.hq + h) * MAX_PARTS * PART;
+    const int ns = A.nslot;
+    const float *pp = A.part + ((size_t)b * A.hq + h) * ns * MAX_PARTS * PART;
     if (A.npk == 0 && A.sel_out) {  // no packed segment, no select launch: all of sel_out is padding
         int32_t *so = A.sel_out + ((size_t)b * A.hq + h) * A.sel_cols;
         for (int64_t c = t; c < A.sel_cols; c += 256) so[c] = -1;
     }
-    __shared__ float wsc[256];
+    __shared__ float wsc[MAX_SLOTS * MAX_PARTS];
     __shared__ float red[2][4];
     __shared__ __align__(16) float part_o[8][D];
     __shared__ __align__(16) float osh[D];
     const int j4 = t & 31, cc = t >> 5;
-    const float4 *Rv4 = reinterpret_cast<const float4 *>(A.rot + (((size_t)b * A.hkv + g) * 2 + 1) * D * D);
     float4 rv[16];
+    {
+        const float4 *Rv4 = reinterpret_cast<const float4 *>(A.rot + (((size_t)b * A.hkv + g) * 2 + 1) * D * D);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) rv[u] = Rv4[(size_t)(cc * 16 + u) * (D / 4) + j4];
-
-    // partial weights: w_s = exp2(m_s - M), L = sum_s w_s l_s (one thread per partial)
-    float m = -INFINITY, l = 0.f;
-    if (t < Stot) {
-        m = pp[(size_t)t * PART];
-        l = pp[(size_t)t * PART + 1];
+        for (int u = 0; u < 16; ++u) rv[u] = Rv4[(size_t)(cc * 16 + u) * (D / 4) + j4];
     }
+
+    // partial weights: w_p = exp2(m_p - M), L = sum_p w_p l_p over every slot
+    float m = -INFINITY;
+    for (int i = t; i < ns * MAX_PARTS; i += 256)
+        if (i % MAX_PARTS < A.nparts[i / MAX_PARTS]) m = fmaxf(m, pp[(size_t)i * PART]);
     {
         float v = row_max16(m);
         v = fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
@@ -1472,41 +1494,56 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     }
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-    wsc[t] = w;
+    float wl = 0.f;
+    for (int i = t; i < ns * MAX_PARTS; i += 256) {
+        float w = 0.f;
+        if (i % MAX_PARTS < A.nparts[i / MAX_PARTS]) {
+            const float mi = pp[(size_t)i * PART];
+            w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
+            wl = fmaf(w, pp[(size_t)i * PART + 1], wl);
+        }
+        wsc[i] = w;
+    }
     {
-        const float v = wave_sum(w * l);
+        const float v = wave_sum(wl);
         if (lane == 0) red[1][wave] = v;
     }
     __syncthreads();
     const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-    {
-        // thread (grp, quad): channels 4 quad .. 4 quad + 3 over splits grp, grp + 8, ...
-        const int quad = t & 31, grp = t >> 5;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int slot = 0; slot < ns; ++slot) {
+        const float *ps = pp + (size_t)slot * MAX_PARTS * PART;
+        const int np = A.nparts[slot];
+        {
+            // thread (grp, quad): channels 4 quad .. 4 quad + 3 over partials grp, grp + 8, ...
+            const int quad = t & 31, grp = t >> 5;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
-        for (int y = grp; y < Stot; y += 8) {
-            const float wy = wsc[y];
-            const float *src = pp + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
-            const float2 x0 = *reinterpret_cast<const float2 *>(src);
-            const float2 x1 = *reinterpret_cast<const float2 *>(src + 2);
-            o.x = fmaf(wy, x0.x, o.x);
-            o.y = fmaf(wy, x0.y, o.y);
-            o.z = fmaf(wy, x1.x, o.z);
-            o.w = fmaf(wy, x1.y, o.w);
+            for (int y = grp; y < np; y += 8) {
+                const float wy = wsc[slot * MAX_PARTS + y];
+                const float *src = ps + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
+                const float2 x0 = *reinterpret_cast<const float2 *>(src);
+                const float2 x1 = *reinterpret_cast<const float2 *>(src + 2);
+                o.x = fmaf(wy, x0.x, o.x);
+                o.y = fmaf(wy, x0.y, o.y);
+                o.z = fmaf(wy, x1.x, o.z);
+                o.w = fmaf(wy, x1.y, o.w);
+            }
+            *reinterpret_cast<float4 *>(&part_o[grp][quad * 4]) = o;
         }
-        *reinterpret_cast<float4 *>(&part_o[grp][quad * 4]) = o;
-    }
-    __syncthreads();
-    if (t < D) {
-        float o = 0.f;
+        __syncthreads();
+        if (t < D) {
+            float o = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o += part_o[k][t];
-        osh[t] = L > 0.f ? o / L : 0.f;
-    }
-    __syncthreads();
-    {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int k = 0; k < 8; ++k) o += part_o[k][t];
+            osh[t] = L > 0.f ? o / L : 0.f;
+        }
+        __syncthreads();
+        if (slot > 0) {
+            const float4 *Rv4 = reinterpret_cast<const float4 *>(slot_rot(A, bl, slot) + ((size_t)g * 2 + 1) * D * D);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) rv[u] = Rv4[(size_t)(cc * 16 + u) * (D / 4) + j4];
+        }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const float oc = osh[cc * 16 + u];
@@ -1515,8 +1552,8 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
             acc.z = fmaf(rv[u].z, oc, acc.z);
             acc.w = fmaf(rv[u].w, oc, acc.w);
         }
-        *reinterpret_cast<float4 *>(&part_o[cc][4 * j4]) = acc;
     }
+    *reinterpret_cast<float4 *>(&part_o[cc][4 * j4]) = acc;
     __syncthreads();
     if (t < D) {
         float o = 0.f;
@@ -1546,7 +1583,7 @@ hipError_t select_launch(const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_qrot(const DecodeArgs &a, int G, hipStream_t s) {
-    const dim3 grid(D / 32, (unsigned)a.hkv, (unsigned)a.n_req);
+    const dim3 grid(D / 32, (unsigned)a.hkv, (unsigned)(a.n_req * a.nslot));
     switch (G) {
     case 1: hipLaunchKernelGGL(k_qrot<1>, grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_qrot<2>, grid, dim3(256), 0, s, a); break;

@@ -124,7 +124,8 @@ mkv_status check_cache(const mkv_cache *c) {
                 if (s.k_abs == 0 && (s.keep_ppm < 1 || s.keep_ppm > 1000000)) return MKV_ERR_ARG;
                 if (ceil_div(s.t_cap, BT) > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
             }
-            if ((reinterpret_cast<uintptr_t>(s.data) & 15) || (reinterpret_cast<uintptr_t>(s.meta) & 15))
+            if ((reinterpret_cast<uintptr_t>(s.data) & 15) || (reinterpret_cast<uintptr_t>(s.meta) & 15) ||
+                (reinterpret_cast<uintptr_t>(s.rot) & 15))
                 return MKV_ERR_ARG;
             t += s.t_cap;
         }
@@ -134,12 +135,30 @@ mkv_status check_cache(const mkv_cache *c) {
     return MKV_OK;
 }
 
+// Rotation slots: slot 0 is the cache's rotation; every segment index whose
+// segment carries its own rotation in some request gets a slot of its own
+// (slot_of[j], 0 for the others). Returns the number of slots.
+int rot_slots(const mkv_cache *c, int (&slot_of)[MKV_MAX_SEGMENTS]) {
+    int ns = 1;
+    for (int j = 0; j < c->n_segments; ++j) {
+        slot_of[j] = 0;
+        for (int b = 0; b < c->batch; ++b)
+            if (segof(c, b, j).rot) {
+                slot_of[j] = ns++;
+                break;
+            }
+    }
+    return ns;
+}
+
 // ---------------------------------------------------------- workspace map --
 struct WsMap {
     size_t qa, qs, scores, mask, sel, part, total;
     int64_t sc_off[MKV_MAX_SEGMENTS], mk_off[MKV_MAX_SEGMENTS], sl_off[MKV_MAX_SEGMENTS];
     int32_t nbcap[MKV_MAX_SEGMENTS], kcap[MKV_MAX_SEGMENTS], pseg[MKV_MAX_SEGMENTS];
     int npk;
+    int nslot;
+    int slot_of[MKV_MAX_SEGMENTS];
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -150,6 +169,8 @@ WsMap ws_map(const mkv_cache *c) {
     const int G = (int)(Hq / Hkv);
     int64_t sc = 0, mk = 0, sl = 0;
     m.npk = 0;
+    m.nslot = rot_slots(c, m.slot_of);
+    const size_t NS = (size_t)m.nslot;
     for (int j = 0; j < c->n_segments; ++j) {
         if (segof(c, 0, j).kind != MKV_SEG_PACKED) continue;
         int64_t nbc = 0;
@@ -168,9 +189,9 @@ WsMap ws_map(const mkv_cache *c) {
     }
     size_t off = 0;
     m.qa = off;
-    off = align256(off + B * Hq * D * 4);
+    off = align256(off + B * NS * Hq * D * 4);
     m.qs = off;
-    off = align256(off + B * Hkv * D * 2 * G * 4);
+    off = align256(off + B * NS * Hkv * D * 2 * G * 4);
     m.scores = off;
     off = align256(off + (size_t)sc * 4);
     m.mask = off;
@@ -178,7 +199,7 @@ WsMap ws_map(const mkv_cache *c) {
     m.sel = off;
     off = align256(off + (size_t)sl * 4);
     m.part = off;
-    off = align256(off + B * Hq * MAX_PARTS * PART * 4);
+    off = align256(off + B * Hq * NS * MAX_PARTS * PART * 4);
     m.total = off;
     return m;
 }
@@ -223,6 +244,7 @@ struct QrotFuse {
     const float *q;
     float *qa;
     float *qs;
+    int nslot;
 };
 
 // Enqueue a checked, non-empty append and advance c->len. With `fuse`, the
@@ -242,12 +264,13 @@ mkv_status append_enqueue(mkv_cache *c, const void *k_new, const void *v_new, co
             CompressEntry E{};
             E.data = sg.data;
             E.meta = sg.meta;
+            E.rot = sg.rot ? sg.rot : c->rot + (size_t)b * c->n_kv_heads * 2 * D * D;
             E.a = (int32_t)a;
             E.e = (int32_t)e;
             E.row0 = (int32_t)(sg.t_begin + a - p0);
             E.b = b;
-            E.r = sg.r;
-            E.kind = sg.kind;
+            E.r = (int16_t)sg.r;
+            E.kind = (int16_t)sg.kind;
             E.blk0 = (int32_t)(a / BT);
             E.nblk = (int32_t)((e - 1) / BT - a / BT + 1);
             E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
@@ -276,6 +299,7 @@ mkv_status append_enqueue(mkv_cache *c, const void *k_new, const void *v_new, co
             A.q_req = c->batch;
             A.q_hq = c->n_q_heads;
             A.q_G = c->n_q_heads / c->n_kv_heads;
+            A.q_ns = fuse->nslot;
             if (rotated) *rotated = true;
         }
         mkv_status st = timed(0, s, [&] { return launch_compress(A, c->dtype, max_blk, s); });
@@ -295,7 +319,66 @@ mkv_status decode_check(const mkv_cache *c, const float *q, const float *out, co
     return MKV_OK;
 }
 
-// Enqueue a checked decode; `rotated`: q' is already in the workspace.
+// Attention splits of one rotation slot's launch: the dense and packed work of
+// the segments in that slot, for every request of the launch.
+void plan_splits(DecodeArgs &A, const mkv_cache *c, int slot, int G, int sb, int npk) {
+    int max_nb = 0;
+    int64_t Wmax = 0, Dmax = 0;
+    int npk_slot = 0;
+    for (int i = 0; i < A.n_req; ++i) {
+        int64_t W = 0, Dn = 0;
+        for (int j = 0; j < c->n_segments; ++j) {
+            const DSeg &D_ = A.seg[i * c->n_segments + j];
+            if (D_.slot != slot) continue;
+            if (D_.kind == MKV_SEG_PACKED) {
+                const int64_t rec = (int64_t)BT * D_.r * 2 * (sb + 1);
+                W += (int64_t)G * D_.k * ((G > 1 ? rec * 4 / 5 : rec) + 256);
+                max_nb = std::max(max_nb, D_.nb);
+            } else {
+                Dn += (int64_t)D_.nb * 2 * BT * D * sb;
+            }
+        }
+        Wmax = std::max(Wmax, W);
+        Dmax = std::max(Dmax, Dn);
+    }
+    for (int j = 0; j < c->n_segments; ++j)
+        if (A.seg[j].kind == MKV_SEG_PACKED && A.seg[j].slot == slot) ++npk_slot;
+    // splits of about 96 KB of packed and 128 KB of dense reads each: both
+    // kinds fit one round of resident waves with room to spare (measured
+    // on the 128K workload: 88-104 KB packed splits are the fastest; 64 KB
+    // fills every wave slot and is slower, 128 KB leaves too few waves)
+    A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
+    A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, PACKED_SPLIT)));
+    // Union mode (exact byte-balanced packed workgroups) when every packed
+    // segment has at most 4096 blocks and a workgroup's share of the union
+    // provably fits its UNION_CAP-entry table: a share holds at most
+    // U w_max / (P w_min) + npk entries, U = max over requests of the sum
+    // over packed segments of min(G k, nb).
+    A.union_mode = 0;
+    if (npk > 0 && npk <= 4 && max_nb <= 4096 && npk_slot > 0) {
+        const int32_t sp4 = (int32_t)std::min<int64_t>(((int64_t)A.S_p + 3) / 4 * 4, (MAX_SPLITS - A.S_d) / 4 * 4);
+        int64_t U = 0, wmin = INT64_MAX, wmax = 0;
+        for (int i = 0; i < A.n_req; ++i) {
+            int64_t u = 0;
+            for (int j = 0; j < c->n_segments; ++j) {
+                const DSeg &D_ = A.seg[i * c->n_segments + j];
+                if (D_.kind != MKV_SEG_PACKED || D_.slot != slot) continue;
+                u += std::min<int64_t>((int64_t)G * D_.k, D_.nb);
+                const int64_t w = (int64_t)BT * D_.r * 2 * (sb + 1) + UNION_RECORD_FIXED;
+                wmin = std::min(wmin, w);
+                wmax = std::max(wmax, w);
+            }
+            U = std::max(U, u);
+        }
+        const int64_t P = sp4 / 4;
+        if (P >= 1 && ceil_div(U * wmax, P * wmin) + npk <= UNION_CAP) {
+            A.union_mode = 1;
+            A.S_p = sp4;
+        }
+    }
+}
+
+// Enqueue a checked decode; `rotated`: q' of slot 0 is already in the workspace.
 mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_t *sel_out, int64_t sel_cols,
                           void *workspace, bool rotated, hipStream_t s) {
     const WsMap m = ws_map(c);
@@ -333,16 +416,20 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
         A.npk = m.npk;
         A.hq = c->n_q_heads;
         A.hkv = c->n_kv_heads;
+        A.nslot = m.nslot;
         int max_tiles = 0, max_nb = 0, max_r = 1;
-        int64_t Wmax = 0, Dmax = 0;
         for (int i = 0; i < n_req; ++i) {
-            int64_t W = 0, Dn = 0;
             for (int j = 0; j < c->n_segments; ++j) {
                 const mkv_segment &sg = segof(c, b0 + i, j);
                 DSeg &D_ = A.seg[i * c->n_segments + j];
                 D_.data = sg.data;
                 D_.meta = sg.meta;
-                D_.kind = sg.kind;
+                D_.rot = sg.rot;
+                D_.kind = (int16_t)sg.kind;
+                // a segment index with a slot of its own keeps that slot in
+                // every request; requests whose segment has no own rotation
+                // there use the cache's, through the slot's launch
+                D_.slot = (int16_t)m.slot_of[j];
                 D_.r = sg.r;
                 D_.filled = (int32_t)seg_filled(c, b0 + i, j);
                 D_.nb = (int32_t)ceil_div(D_.filled, BT);
@@ -352,49 +439,9 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                     max_tiles = std::max(max_tiles, (int)ceil_div(D_.nb, META_TILE));
                     max_nb = std::max(max_nb, D_.nb);
                     max_r = std::max(max_r, (int)sg.r);
-                    const int64_t rec = (int64_t)BT * sg.r * 2 * (sb + 1);
-                    W += (int64_t)G * D_.k * ((G > 1 ? rec * 4 / 5 : rec) + 256);
-                } else {
-                    Dn += (int64_t)D_.nb * 2 * BT * D * sb;
                 }
             }
-            Wmax = std::max(Wmax, W);
-            Dmax = std::max(Dmax, Dn);
         }
-        // splits of about 96 KB of packed and 128 KB of dense reads each: both
-        // kinds fit one round of resident waves with room to spare (measured
-        // on the 128K workload: 88-104 KB packed splits are the fastest; 64 KB
-        // fills every wave slot and is slower, 128 KB leaves too few waves)
-        A.S_d = (int32_t)std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(Dmax, 128 * 1024)));
-        A.S_p = (int32_t)std::max<int64_t>(1, std::min<int64_t>(MAX_SPLITS - A.S_d, ceil_div(Wmax, PACKED_SPLIT)));
-        // Union mode (exact byte-balanced packed workgroups) when every packed
-        // segment has at most 4096 blocks and a workgroup's share of the union
-        // provably fits its UNION_CAP-entry table: a share holds at most
-        // U w_max / (P w_min) + npk entries, U = max over requests of the sum
-        // over packed segments of min(G k, nb).
-        A.union_mode = 0;
-        if (m.npk > 0 && m.npk <= 4 && max_nb <= 4096) {
-            const int32_t sp4 = (int32_t)std::min<int64_t>(((int64_t)A.S_p + 3) / 4 * 4, (MAX_SPLITS - A.S_d) / 4 * 4);
-            int64_t U = 0, wmin = INT64_MAX, wmax = 0;
-            for (int i = 0; i < n_req; ++i) {
-                int64_t u = 0;
-                for (int j = 0; j < c->n_segments; ++j) {
-                    const DSeg &D_ = A.seg[i * c->n_segments + j];
-                    if (D_.kind != MKV_SEG_PACKED) continue;
-                    u += std::min<int64_t>((int64_t)G * D_.k, D_.nb);
-                    const int64_t w = (int64_t)BT * D_.r * 2 * (sb + 1) + UNION_RECORD_FIXED;
-                    wmin = std::min(wmin, w);
-                    wmax = std::max(wmax, w);
-                }
-                U = std::max(U, u);
-            }
-            const int64_t P = sp4 / 4;
-            if (P >= 1 && ceil_div(U * wmax, P * wmin) + m.npk <= UNION_CAP) {
-                A.union_mode = 1;
-                A.S_p = sp4;
-            }
-        }
-        if ((A.S_d + 3) / 4 + (A.S_p + 3) / 4 > MAX_PARTS) return MKV_ERR_UNSUPPORTED;  // (never: S_d + S_p <= 256)
         // select: 4 keys per lane up to 1024 blocks, 16 up to 16384 (at most
         // 16 waves), 64 beyond
         const int kpt = max_nb <= 1024 ? 4 : max_nb <= 16384 ? 16 : 64;
@@ -402,7 +449,8 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
         A.sel_waves = (int32_t)std::max<int64_t>(1, ceil_div(max_nb, 64 * kpt));
 
         mkv_status st = MKV_OK;
-        if (!rotated) {
+        A.qrot_from = rotated ? 1 : 0;
+        if (A.qrot_from < m.nslot) {
             st = timed(2, s, [&] { return launch_qrot(A, G, s); });
             if (st != MKV_OK) return st;
         }
@@ -412,9 +460,17 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
             st = timed(4, s, [&] { return launch_select(A, G, s); });
             if (st != MKV_OK) return st;
         }
+        // one attend launch per rotation slot, each over its slot's segments
         const int qmax = (max_r + 3) / 4;
-        st = timed(5, s, [&] { return launch_attend(A, c->dtype, G, qmax, s); });
-        if (st != MKV_OK) return st;
+        for (int slot = 0; slot < m.nslot; ++slot) {
+            DecodeArgs As = A;
+            As.cur_slot = slot;
+            plan_splits(As, c, slot, G, sb, m.npk);
+            if ((As.S_d + 3) / 4 + (As.S_p + 3) / 4 > MAX_PARTS) return MKV_ERR_UNSUPPORTED;  // (never: S_d + S_p <= 256)
+            A.nparts[slot] = (As.S_d + 3) / 4 + (As.S_p + 3) / 4;
+            st = timed(5, s, [&] { return launch_attend(As, c->dtype, G, qmax, s); });
+            if (st != MKV_OK) return st;
+        }
         st = timed(6, s, [&] { return launch_merge(A, G, s); });
         if (st != MKV_OK) return st;
     }
@@ -493,6 +549,26 @@ mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
     return MKV_OK;
 }
 
+mkv_status mkv_swap_segment(mkv_cache *c, int32_t b, int32_t seg, void *data, void *meta, const float *rot,
+                            void *ready_event, void *stream) {
+    mkv_status st = check_cache(c);
+    if (st != MKV_OK) return st;
+    if (b < 0 || b >= c->batch || seg < 0 || seg >= c->n_segments) return MKV_ERR_ARG;
+    mkv_segment &sg = c->segs[(size_t)b * c->n_segments + seg];
+    if (sg.kind != MKV_SEG_PACKED || !data || !meta || !rot) return MKV_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(data) & 15) || (reinterpret_cast<uintptr_t>(meta) & 15) ||
+        (reinterpret_cast<uintptr_t>(rot) & 15))
+        return MKV_ERR_ARG;
+    if (c->len[b] < sg.t_begin + sg.t_cap) return MKV_ERR_ARG;  // only a finished segment is swapped
+    if (ready_event &&
+        hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ready_event), 0) != hipSuccess)
+        return MKV_ERR_HIP;
+    sg.data = data;
+    sg.meta = meta;
+    sg.rot = rot;
+    return MKV_OK;
+}
+
 size_t mkv_decode_workspace_bytes(const mkv_cache *c) {
     if (check_cache(c) != MKV_OK) return 0;
     return ws_map(c).total;
@@ -546,7 +622,7 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
     if (any) {
         const WsMap m = ws_map(c);
         char *ws = static_cast<char *>(workspace);
-        const QrotFuse f{q, reinterpret_cast<float *>(ws + m.qa), reinterpret_cast<float *>(ws + m.qs)};
+        const QrotFuse f{q, reinterpret_cast<float *>(ws + m.qa), reinterpret_cast<float *>(ws + m.qs), m.nslot};
         st = append_enqueue(c, k_new, v_new, n_new, n_max, s, &f, &rotated);
         if (st != MKV_OK) return st;
     }

@@ -33,17 +33,17 @@ static_assert(UNION_RECORD_FIXED <= 16384, "union weights of a unit stay below 2
 
 // ---- compression ----------------------------------------------------------
 struct CompressEntry {
-    void *data;      // segment data
-    void *meta;      // packed meta or nullptr
-    int32_t a, e;    // new tokens occupy local positions [a, e) of the segment
-    int32_t row0;    // input row of local position a
-    int32_t b;       // request
-    int32_t r;       // kept elements (packed)
-    int32_t kind;    // MKV_SEG_*
-    int32_t blk0;    // first block touched
-    int32_t nblk;    // blocks touched
-    int32_t nbcap;   // block capacity of the segment
-    int32_t pad;
+    void *data;       // segment data
+    void *meta;       // packed meta or nullptr
+    const float *rot; // the request's rotations [n_kv][2][D][D]: the segment's own or the cache's
+    int32_t a, e;     // new tokens occupy local positions [a, e) of the segment
+    int32_t row0;     // input row of local position a
+    int32_t b;        // request
+    int32_t blk0;     // first block touched
+    int32_t nblk;     // blocks touched
+    int32_t nbcap;    // block capacity of the segment
+    int16_t r;        // kept elements (packed)
+    int16_t kind;     // MKV_SEG_*
 };  // 56 bytes
 
 struct CompressArgs {
@@ -55,11 +55,13 @@ struct CompressArgs {
     int32_t chunk_blocks;  // blocks per workgroup (set by the launcher)
     // optional query rotation run beside the append (staged launches only):
     // workgroups z = n_ent .. n_ent + q_req - 1, x < 4, rotate request z - n_ent
+    // with the cache's rotation (q' slot 0 of q_ns)
     const float *q;
     float *qa;
     float *qs;
-    int32_t q_req, q_hq, q_G, pad2;
+    int32_t q_req, q_hq, q_G, q_ns;
 };
+static_assert(sizeof(CompressEntry) == 56, "compress entry layout");
 static_assert(sizeof(CompressArgs) <= 4096, "kernel arguments stay below 4 KB");
 
 struct MetaEntry {
@@ -77,12 +79,15 @@ struct MetaArgs {
 struct DSeg {
     const void *data;
     const void *meta;
-    int32_t kind, r;
-    int32_t filled;  // tokens stored
-    int32_t nb;      // blocks stored
-    int32_t k;       // blocks kept (packed)
-    int32_t nbcap;   // block capacity (layout stride)
-};  // 40 bytes
+    const float *rot; // the segment's own rotations [n_kv][2][D][D], or nullptr (the cache's)
+    int16_t kind;
+    int16_t slot;     // rotation slot: 0 the cache's rotation, else that of the segment index
+    int32_t r;
+    int32_t filled;   // tokens stored
+    int32_t nb;       // blocks stored
+    int32_t k;        // blocks kept (packed)
+    int32_t nbcap;    // block capacity (layout stride)
+};  // 48 bytes
 
 struct DecodeArgs {
     DSeg seg[TABLE];  // [n_req][nseg]
@@ -90,12 +95,13 @@ struct DecodeArgs {
     const float *q;
     float *out;
     int32_t *sel_out;
-    float *qa;        // [B][Hq][D] q' * log2(e) / sqrt(D)
-    float *qs;        // [B][Hkv][D][2G] (max(q',0), min(q',0)) / sqrt(D)
+    float *qa;        // [B][nslot][Hq][D] q' * log2(e) / sqrt(D), per rotation slot
+    float *qs;        // [B][nslot][Hkv][D][2G] (max(q',0), min(q',0)) / sqrt(D)
     float *scores;    // per packed j: [B][Hq][nbcap_j]
     uint32_t *mask;   // per packed j: [B][Hkv][nbcap_j], byte i = 1 if head i of the group chose the block
     int32_t *sel;     // per packed j: [B][Hq][kcap_j]
-    float *part;      // [B][Hq][MAX_PARTS][PART]: one partial per attend workgroup (of 4 splits), dense first
+    float *part;      // [B][Hq][nslot][MAX_PARTS][PART]: one partial per attend workgroup (of 4
+                      // splits) of the slot's launch, dense first
     int64_t sel_cols;
     int64_t sc_off[MKV_MAX_SEGMENTS];
     int64_t mk_off[MKV_MAX_SEGMENTS];
@@ -109,7 +115,15 @@ struct DecodeArgs {
     int32_t sel_kpt;   // keys per lane in select
     int32_t sel_waves; // waves per select workgroup
     int32_t union_mode; // packed workgroups take exact byte shares of the union (S_p a multiple of 4)
+    int32_t nslot;      // rotation slots (1 + segment indices with own rotations)
+    int32_t cur_slot;   // attend: the slot whose segments this launch attends
+    int32_t qrot_from;  // q_rotate: first slot to rotate (1 when the append's launch did slot 0)
+    int32_t nparts[MKV_MAX_SEGMENTS + 1];  // merge: partials per slot
 };
+
+static_assert(sizeof(DSeg) == 48, "decode segment layout");
+static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments stay below 4 KB");
+constexpr int MAX_SLOTS = MKV_MAX_SEGMENTS + 1;
 
 // Appends touching at most two blocks per (entry, KV head) take one block per
 // workgroup and may carry a query rotation; larger ones take COMPRESS_CHUNK.

@@ -1,0 +1,122 @@
+"""GPU checks of segments that carry a rotation of their own: the paper's
+heterogeneous double compression buffering (section 5.4), where a finished
+segment is recompressed on the host with its own SVD rotation and swapped in
+without blocking decode.
+
+* swap: decodes enqueued before and after mkv_swap_segment on one stream, with
+  no host wait between them; the earlier one reads the old segment (bit for
+  bit the output of a decode without any swap), the later one the
+  recompressed segment -- its stored bytes, selections and outputs match the
+  oracle compressed with that segment's rotation;
+* a segment given its own rotation before any token reaches it: appends
+  rotate by it, and mkv_append_decode equals separate append and decode calls
+  and matches the oracle at every step.
+"""
+import numpy as np
+import pytest
+
+import mkv_synth as synth
+from oracle import oracle as orc
+
+from gpu_harness import build, check_decode_unit, compare_compress, gen_raw, log, raw_to_f64, rotations, to_device
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_compression_mkv_amd import _lib  # noqa: F401
+
+
+def _oracle(w, K, V, R, b, g, length, seg_rot):
+    Kr = raw_to_f64(K[b, g, :length], w["dtype"])
+    Vr = raw_to_f64(V[b, g, :length], w["dtype"])
+    Rk, Rv = R[b, g, 0].astype(np.float64), R[b, g, 1].astype(np.float64)
+    return orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], length, w["dtype"], seg_rot=seg_rot), Rk, Rv
+
+
+def test_swap_recompressed_segment():
+    segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * 120, 26, 100000, 0),
+            synth.seg(synth.PACKED, 32 + 16 * 120, 16 * 100, 38, 100000, 0),
+            synth.seg(synth.DENSE, 32 + 16 * 220, 128)]
+    T = 32 + 16 * 220 + 40
+    B = 3
+    w = dict(cfg=3, batch=B, n_q_heads=32, n_kv_heads=8, d=128, dtype="bf16", lengths=np.array([T] * B),
+             segs=[segs] * B)
+    c, raw, R = build(torch, w)
+    K, V, _ = raw
+    q1 = torch.from_numpy(synth.gen_q(3, 50, B, 32, "bf16")).cuda()
+    q2n = synth.gen_q(3, 51, B, 32, "bf16")
+    q2 = torch.from_numpy(q2n).cuda()
+    ref1 = c.decode(q1).clone()
+    torch.cuda.synchronize()
+    t0, t1 = segs[1]["t_begin"], segs[1]["t_begin"] + segs[1]["t_cap"]
+    swapped = (0, 2)  # request 1 keeps the cache's rotation in that segment
+    host = {b: c.recompress_segment(b, 1, K[b, :, t0:t1], V[b, :, t0:t1]) for b in swapped}
+    log("recompressed segment 1 of requests %s on the host" % (swapped,))
+    out1 = c.decode(q1)  # enqueued before the swaps: the old buffers
+    old = [c.swap_segment(b, 1, *host[b]) for b in swapped]
+    out2, sel2 = c.decode(q2, want_sel=True)
+    torch.cuda.synchronize()
+    del old
+    assert torch.equal(out1.view(torch.int32), ref1.view(torch.int32))
+    out2, sel2 = out2.cpu().numpy(), sel2.cpu().numpy()
+    ex = 0
+    for b, g in ((0, 0), (0, 5), (1, 3), (2, 7)):
+        seg_rot = [None] * 4
+        if b in swapped:
+            rot = host[b][2]
+            seg_rot[1] = (rot[g, 0].astype(np.float64), rot[g, 1].astype(np.float64))
+        comp, Rk, Rv = _oracle(w, K, V, R, b, g, T, seg_rot)
+        compare_compress(c, w, comp, b, g, T)
+        ex += check_decode_unit(w, comp, Rk, Rv, q2n[b, 4 * g:4 * g + 4].astype(np.float64), out2[b, 4 * g:4 * g + 4],
+                                sel2[b, 4 * g:4 * g + 4], 5e-3, T, b, g)
+    log("swap: decode before it unchanged, after it matches the oracle (%d exempt blocks)" % ex)
+
+
+def test_segment_rotation_from_the_start():
+    segs = [synth.seg(synth.DENSE, 0, 16), synth.seg(synth.PACKED, 16, 16 * 60, 38, 100000, 0),
+            synth.seg(synth.DENSE, 16 + 16 * 60, 32), synth.seg(synth.PACKED, 16 + 16 * 62, 96, 38, 250000, 0)]
+    T0 = 16 + 16 * 62
+    B, hkv = 2, 8
+    w = dict(cfg=2, batch=B, n_q_heads=32, n_kv_heads=hkv, d=128, dtype="bf16", lengths=np.array([T0] * B),
+             segs=[segs] * B)
+    steps = [1, 1, 1, 20, 1, 1]
+    K, V, n = gen_raw(w, [T0 + sum(steps)] * B)
+    from kv_cache_compression_mkv_amd import _lib as L
+    R = rotations(L, w, K, V, [T0] * B)
+    # the update segment's own rotation: that of another stretch of vectors
+    Rseg = np.empty((B, hkv, 2, 128, 128), np.float32)
+    for b in range(B):
+        for g in range(hkv):
+            for kind, arr in ((0, K), (1, V)):
+                x = np.ascontiguousarray(arr[b, g, 100:700])
+                L.mkv_rotation_from_prefill(x.ctypes.data, L.MKV_BF16, 600, 128, Rseg[b, g, kind].ctypes.data, None)
+    a, raw, _ = build(torch, w, lengths=[T0] * B, raw=(K, V, n), R=R)
+    t, _, _ = build(torch, w, lengths=[T0] * B, raw=(K, V, n), R=R)
+    for cc in (a, t):
+        for b in range(B):
+            cc.set_segment_rotation(b, 3, Rseg[b])
+    lens = [T0] * B
+    for i, nn in enumerate(steps):
+        kk = np.ascontiguousarray(K[:, :, lens[0]:lens[0] + nn])
+        vv = np.ascontiguousarray(V[:, :, lens[0]:lens[0] + nn])
+        q = synth.gen_q(2, 300 + i, B, 32, "bf16")
+        o1, s1 = a.append_decode(to_device(torch, kk), to_device(torch, vv), [nn] * B, torch.from_numpy(q).cuda(),
+                                 want_sel=True)
+        t.append(to_device(torch, kk), to_device(torch, vv), [nn] * B)
+        o2, s2 = t.decode(torch.from_numpy(q).cuda(), want_sel=True)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2) and torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+        lens = a.lengths
+        out, sel = o1.cpu().numpy(), s1.cpu().numpy()
+        for b, g in ((0, 1), (1, 6)):
+            seg_rot = [None, None, None, (Rseg[b, g, 0].astype(np.float64), Rseg[b, g, 1].astype(np.float64))]
+            comp, Rk, Rv = _oracle(w, K, V, R, b, g, lens[b], seg_rot)
+            compare_compress(a, w, comp, b, g, lens[b])
+            check_decode_unit(w, comp, Rk, Rv, q[b, 4 * g:4 * g + 4].astype(np.float64), out[b, 4 * g:4 * g + 4],
+                              sel[b, 4 * g:4 * g + 4], 5e-3, lens[b], b, g)
+        log("own-rotation segment, step %d (+%d tokens): append_decode = separate calls = oracle" % (i, nn))

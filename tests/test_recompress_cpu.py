@@ -1,0 +1,79 @@
+"""Host recompression of a finished segment (mkv_recompress_segment) against
+the oracle, on the CPU: the library computes each KV head's own rotation from
+the segment's vectors and re-packs the segment; the oracle, compressing the
+same raw vectors with that segment rotation, must store the same bits --
+indices, values, zero slots and blocks, and block keys."""
+import numpy as np
+import pytest
+
+import mkv_synth as synth
+from oracle import oracle as orc
+
+
+@pytest.fixture(scope="module")
+def L():
+    from kv_cache_compression_mkv_amd import _lib
+    return _lib
+
+
+def _bits(v, dtype):
+    f = np.asarray(v, np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else f.view(np.uint32)
+
+
+@pytest.mark.parametrize("dtype,r,n,cap", [("bf16", 26, 500, 520), ("bf16", 38, 1024, 1024), ("f32", 32, 333, 400)])
+def test_recompress_matches_oracle(L, dtype, r, n, cap):
+    from kv_cache_compression_mkv_amd import layout
+    hkv, d = 2, 128
+    code = L.MKV_BF16 if dtype == "bf16" else L.MKV_F32
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    K = np.empty((hkv, n, d), npdt)
+    V = np.empty((hkv, n, d), npdt)
+    for g in range(hkv):
+        synth.gen_kv_into(7, 0, g, 0, 1000, 1000 + n, dtype, K[g], d)
+        synth.gen_kv_into(7, 0, g, 1, 1000, 1000 + n, dtype, V[g], d)
+    nbytes, mbytes = L.mkv_segment_bytes(code, L.MKV_SEG_PACKED, r, d, hkv, cap)
+    data = np.full(nbytes, 0xAB, np.uint8)
+    meta = np.full(mbytes, 0xCD, np.uint8)
+    rot = np.empty((hkv, 2, d, d), np.float32)
+    L.mkv_recompress_segment(K.ctypes.data, V.ctypes.data, code, d, hkv, n, cap, r, data.ctypes.data,
+                             meta.ctypes.data, rot.ctypes.data)
+    nbcap, nb = -(-cap // 16), -(-n // 16)
+    s = 2 if dtype == "bf16" else 4
+    P = layout.unpack_packed(data, hkv, nbcap, r, dtype)
+    _, mbits = layout.unpack_meta(meta, hkv, nbcap, dtype, d)
+    to64 = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if dtype == "bf16" else \
+        (lambda a: a.astype(np.float64))
+    segs = [synth.seg(1, 0, cap, r, 100000, 0)]
+    for g in range(hkv):
+        Kr, Vr = to64(K[g]), to64(V[g])
+        # the segment's rotation is the one the library computes from its vectors
+        Ro, _ = orc.rotation(Kr)
+        assert np.abs(rot[g, 0].astype(np.float64) - Ro).max() <= 1e-6
+        Rk, Rv = rot[g, 0].astype(np.float64), rot[g, 1].astype(np.float64)
+        comp = orc.compress_unit(Kr, Vr, np.eye(d), np.eye(d), segs, n, dtype, seg_rot=[(Rk, Rv)])
+        for hat, idx, gb, gi in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"]),
+                                 (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"])):
+            ei = idx[:n, :r].astype(np.int64)
+            assert np.array_equal(gi[g].reshape(-1, r)[:n].astype(np.int64), ei)
+            ev = _bits(np.take_along_axis(hat[:n], ei, axis=1), dtype)
+            assert np.array_equal(gb[g].reshape(-1, r)[:n], ev)
+            assert np.all(gb[g].reshape(-1, r)[n:] == 0) and np.all(gi[g].reshape(-1, r)[n:] == 0)
+        assert np.array_equal(mbits[g, :nb], _bits(comp["meta"][0], dtype))
+        assert np.all(mbits[g, nb:] == 0)
+    # the tail bytes after the last record are not written
+    assert np.all(data[hkv * nbcap * 16 * r * 2 * (s + 1):] == 0xAB)
+
+
+def test_recompress_rejects_bad_arguments(L):
+    buf = np.zeros(16, np.uint8)
+    with pytest.raises(L.MkvError):
+        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 0, 16, 8, buf.ctypes.data,
+                                 buf.ctypes.data, buf.ctypes.data)
+    with pytest.raises(L.MkvError):
+        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 17, 16, 8, buf.ctypes.data,
+                                 buf.ctypes.data, buf.ctypes.data)
+    with pytest.raises(L.MkvError) as e:
+        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 64, 1, 4, 16, 8, buf.ctypes.data,
+                                 buf.ctypes.data, buf.ctypes.data)
+    assert e.value.status == L.MKV_ERR_UNSUPPORTED

@@ -25,32 +25,75 @@ namespace mkv {
 namespace {
 
 // Compute x' = R x for one token (xs: its input as doubles in LDS, exact
-// copies of the stored values), or for two tokens at once (xs and ys), which
-// then share every R element read from LDS and converted. R is staged in LDS
-// with rows padded to D + 1 floats, so the 64 lanes reading 64 rows at one
-// column hit distinct banks. Lane owns channels lane and lane + 64; each sum
-// is one fp64 chain over j ascending, and every product of two floats is
-// exact in fp64.
-template <bool TWO>
-__device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const double *xs, const double *ys, int lane,
-                                               double &a0, double &a1, double &b0, double &b1) {
-    double p0 = 0.0, p1 = 0.0, q0 = 0.0, q1 = 0.0;
+// copies of the stored values). R is staged in LDS with rows padded to D + 1
+// floats, so the 64 lanes reading 64 rows at one column hit distinct banks.
+// Lane owns channels lane and lane + 64; each sum is one fp64 chain over j
+// ascending, and every product of two floats is exact in fp64.
+__device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const double *xs, int lane, double &a0,
+                                               double &a1) {
+    double p0 = 0.0, p1 = 0.0;
 #pragma unroll 8
     for (int j = 0; j < D; ++j) {
-        const double r0 = (double)Rs[lane][j], r1 = (double)Rs[lane + 64][j];
         const double x = xs[j];
-        p0 = fma(r0, x, p0);
-        p1 = fma(r1, x, p1);
-        if constexpr (TWO) {
-            const double y = ys[j];
-            q0 = fma(r0, y, q0);
-            q1 = fma(r1, y, q1);
-        }
+        p0 = fma((double)Rs[lane][j], x, p0);
+        p1 = fma((double)Rs[lane + 64][j], x, p1);
     }
     a0 = p0;
     a1 = p1;
-    b0 = q0;
-    b1 = q1;
+}
+
+// x' = R x for NT tokens at once (xs: their inputs as doubles in LDS): every
+// R element read from LDS and converted serves 2 NT fused multiply-adds. Lane
+// owns channels lane and lane + 64; each sum is one fp64 chain over j
+// ascending (products of two floats are exact in fp64). Columns go in pairs,
+// and the next pair's R elements and inputs are read while the current pair
+// is multiplied, so the LDS latency overlaps the arithmetic.
+template <int NT>
+struct RotCols {  // two columns' R elements (rows lane, lane + 64) and NT inputs
+    float r0[2], r1[2];
+    double2 x[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ void rot_load(const float (*Rs)[D + 1], const double (*xs)[D], int lane, int j,
+                                         RotCols<NT> &c) {
+    c.r0[0] = Rs[lane][j];
+    c.r0[1] = Rs[lane][j + 1];
+    c.r1[0] = Rs[lane + 64][j];
+    c.r1[1] = Rs[lane + 64][j + 1];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) c.x[t] = *reinterpret_cast<const double2 *>(&xs[t][j]);
+}
+
+template <int NT>
+__device__ __forceinline__ void rot_fma(const RotCols<NT> &c, double (&a0)[NT], double (&a1)[NT]) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const double u = (double)c.r0[k], v = (double)c.r1[k];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const double x = k ? c.x[t].y : c.x[t].x;
+            a0[t] = fma(u, x, a0[t]);
+            a1[t] = fma(v, x, a1[t]);
+        }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void rotate_nt(const float (*Rs)[D + 1], const double (*xs)[D], int lane,
+                                          double (&a0)[NT], double (&a1)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) a0[t] = a1[t] = 0.0;
+    // two register sets in turn: one is read from LDS while the other is used
+    RotCols<NT> A, B;
+    rot_load<NT>(Rs, xs, lane, 0, A);
+#pragma unroll 1
+    for (int j = 0; j < D; j += 4) {
+        rot_load<NT>(Rs, xs, lane, j + 2, B);
+        rot_fma<NT>(A, a0, a1);
+        rot_load<NT>(Rs, xs, lane, min(j + 4, D - 2), A);  // the last pass rereads a pair (unused)
+        rot_fma<NT>(B, a0, a1);
+    }
 }
 
 // Keep the r channels of largest magnitude (ties to the lower channel).
@@ -103,7 +146,7 @@ struct BlockJob {
     int p0, sa, se, r, G16, cpg;
     bool packed, do_meta;
     uint32_t mn0, mx0, mn1, mx1;
-    typename ST::bits_t x0, x1, y0, y1;  // rows of the first two new tokens (lane's channels)
+    typename ST::bits_t x0, x1;  // row of the first new token (lane's channels; one-token appends)
 };
 
 // Pointers of block blk, its stored keys (when it already holds tokens) and
@@ -152,18 +195,14 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
         }
     }
 
-    // the first token's row is loaded before R is staged, so that the two
-    // (and the block keys above) are in flight together
-    bits_t x0 = 0, x1 = 0, y0 = 0, y1 = 0;
-    if (sa < se) {
+    // one-token appends: the first token's row is loaded before R is staged,
+    // so that the two (and the block keys above) are in flight together (bulk
+    // appends load their rows themselves)
+    bits_t x0 = 0, x1 = 0;
+    if (!BULK && sa < se) {
         const bits_t *xr = xin + (size_t)(E.row0 + (p0 + sa - E.a)) * D;
         x0 = xr[lane];
         x1 = xr[lane + 64];
-    }
-    if (BULK && sa + 1 < se) {
-        const bits_t *xr = xin + (size_t)(E.row0 + (p0 + sa + 1 - E.a)) * D;
-        y0 = xr[lane];
-        y1 = xr[lane + 64];
     }
     J.vals = vals;
     J.idxs = idxs;
@@ -180,130 +219,106 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     J.mn0 = mn0; J.mx0 = mx0; J.mn1 = mn1; J.mx1 = mx1;
     J.x0 = x0;
     J.x1 = x1;
-    J.y0 = y0;
-    J.y1 = y1;
 }
 
-// Rotate, rank, round and store the block's new tokens, two at a time while
-// two remain (R from LDS; xs is the wave's two LDS rows of doubles), clear the
-// slots after the last token of a block this call starts, and write the block
-// keys back.
-template <typename ST, bool BULK>
-__device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &E, int blk, int lane,
-                                          const float (*Rs)[D + 1], double (*xs)[D]) {
+// top-r, rounding and the stores of token `slot` of J's block from its
+// rotated channels (lane: channels lane and lane + 64); packed segments fold
+// the stored key into the block's running min/max
+template <typename ST>
+__device__ __forceinline__ void store_token(BlockJob<ST> &J, int slot, double v0, double v1, int lane) {
     using bits_t = typename ST::bits_t;
-    bits_t *vals = J.vals;
-    uint8_t *idxs = J.idxs;
-    char *meta_tile = J.meta_tile;
-    const bits_t *xin = J.xin;
-    const int p0 = J.p0, sa = J.sa, se = J.se, r = J.r, cpg = J.cpg;
-    const bool packed = J.packed, do_meta = J.do_meta;
-    uint32_t mn0 = J.mn0, mx0 = J.mx0, mn1 = J.mn1, mx1 = J.mx1;
-    bits_t x0 = J.x0, x1 = J.x1, y0 = J.y0, y1 = J.y1;
-    // top-r, rounding and the stores of token `slot` from its rotated channels
-    auto store = [&](int slot, double v0, double v1) {
-        const bits_t s0 = round_store<ST>(v0), s1 = round_store<ST>(v1);
-        if (packed) {
-            bool keep0, keep1;
-            topr_keep(v0, v1, r, lane, keep0, keep1);
-            const uint64_t m0 = ballot(keep0), m1 = ballot(keep1);
-            const uint64_t below = lanes_below(lane);
-            bits_t *vrow = vals + (size_t)slot * r;
-            uint8_t *irow = idxs + (size_t)slot * r;
-            if (keep0) {
-                const int pos = popc64(m0 & below);
-                vrow[pos] = s0;
-                irow[pos] = (uint8_t)lane;
-            }
-            if (keep1) {
-                const int pos = popc64(m0) + popc64(m1 & below);
-                vrow[pos] = s1;
-                irow[pos] = (uint8_t)(lane + 64);
-            }
-            if (do_meta) {
-                const uint32_t q0 = order_key<ST>(keep0 ? s0 : (bits_t)0);
-                const uint32_t q1 = order_key<ST>(keep1 ? s1 : (bits_t)0);
-                mn0 = min(mn0, q0); mx0 = max(mx0, q0);
-                mn1 = min(mn1, q1); mx1 = max(mx1, q1);
+    const bits_t s0 = round_store<ST>(v0), s1 = round_store<ST>(v1);
+    if (J.packed) {
+        bool keep0, keep1;
+        topr_keep(v0, v1, J.r, lane, keep0, keep1);
+        const uint64_t m0 = ballot(keep0), m1 = ballot(keep1);
+        const uint64_t below = lanes_below(lane);
+        bits_t *vrow = J.vals + (size_t)slot * J.r;
+        uint8_t *irow = J.idxs + (size_t)slot * J.r;
+        if (keep0) {
+            const int pos = popc64(m0 & below);
+            vrow[pos] = s0;
+            irow[pos] = (uint8_t)lane;
+        }
+        if (keep1) {
+            const int pos = popc64(m0) + popc64(m1 & below);
+            vrow[pos] = s1;
+            irow[pos] = (uint8_t)(lane + 64);
+        }
+        if (J.do_meta) {
+            const uint32_t q0 = order_key<ST>(keep0 ? s0 : (bits_t)0);
+            const uint32_t q1 = order_key<ST>(keep1 ? s1 : (bits_t)0);
+            J.mn0 = min(J.mn0, q0); J.mx0 = max(J.mx0, q0);
+            J.mn1 = min(J.mn1, q1); J.mx1 = max(J.mx1, q1);
+        }
+    } else {
+        bits_t *vrow = J.vals + (size_t)slot * D;
+        vrow[lane] = s0;
+        vrow[lane + 64] = s1;
+    }
+}
+
+// After a block's new tokens: clear the slots after its last token when this
+// call started the block, and write the block keys back.
+template <typename ST>
+__device__ __forceinline__ void block_finish(const BlockJob<ST> &J, int blk, int lane) {
+    using bits_t = typename ST::bits_t;
+    if (J.sa == 0 && J.se < BT) {
+        if (J.packed) {
+            for (int i = J.se * J.r + lane; i < BT * J.r; i += 64) {
+                J.vals[i] = (bits_t)0;
+                J.idxs[i] = 0;
             }
         } else {
-            bits_t *vrow = vals + (size_t)slot * D;
-            vrow[lane] = s0;
-            vrow[lane + 64] = s1;
-        }
-    };
-    for (int slot = sa; slot < se;) {
-        const bool two = BULK && slot + 1 < se;
-        xs[0][lane] = (double)bits_to_float<ST>(x0);
-        xs[0][lane + 64] = (double)bits_to_float<ST>(x1);
-        if (two) {
-            xs[1][lane] = (double)bits_to_float<ST>(y0);
-            xs[1][lane + 64] = (double)bits_to_float<ST>(y1);
-        }
-        wave_lds_sync();
-        // the next tokens' rows load while these are rotated
-        if (!BULK && slot + 1 < se) {
-            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 1 - E.a)) * D;
-            x0 = xr[lane];
-            x1 = xr[lane + 64];
-        }
-        if (BULK && slot + 2 < se) {
-            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 2 - E.a)) * D;
-            x0 = xr[lane];
-            x1 = xr[lane + 64];
-        }
-        if (BULK && slot + 3 < se) {
-            const bits_t *xr = xin + (size_t)(E.row0 + (p0 + slot + 3 - E.a)) * D;
-            y0 = xr[lane];
-            y1 = xr[lane + 64];
-        }
-        double a0, a1, b0, b1;
-        if (BULK && two) rotate_f64_lds<true>(Rs, xs[0], xs[1], lane, a0, a1, b0, b1);
-        else rotate_f64_lds<false>(Rs, xs[0], xs[0], lane, a0, a1, b0, b1);
-        wave_lds_sync();
-        store(slot, a0, a1);
-        if (two) store(slot + 1, b0, b1);
-        slot += two ? 2 : 1;
-    }
-
-    // a block started by this call: clear the slots after its last token
-    if (sa == 0 && se < BT) {
-        if (packed) {
-            for (int i = se * r + lane; i < BT * r; i += 64) {
-                vals[i] = (bits_t)0;
-                idxs[i] = 0;
-            }
-        } else {
-            for (int i = se * D + lane; i < BT * D; i += 64) vals[i] = (bits_t)0;
+            for (int i = J.se * D + lane; i < BT * D; i += 64) J.vals[i] = (bits_t)0;
         }
     }
-
-    if (do_meta && se > sa) {
+    if (J.do_meta && J.se > J.sa) {
         const int bl = blk % META_TILE;
         for (int h = 0; h < 2; ++h) {
             const int c = lane + 64 * h;
-            bits_t *pr = reinterpret_cast<bits_t *>(meta_tile + ((size_t)(c / cpg) * META_TILE + bl) * 16 +
-                                                    (c % cpg) * 2 * ST::bytes);
-            pr[0] = key_to_bits<ST>(h == 0 ? mn0 : mn1);
-            pr[1] = key_to_bits<ST>(h == 0 ? mx0 : mx1);
+            bits_t *pr = reinterpret_cast<bits_t *>(J.meta_tile + ((size_t)(c / J.cpg) * META_TILE + bl) * 16 +
+                                                    (c % J.cpg) * 2 * ST::bytes);
+            pr[0] = key_to_bits<ST>(h == 0 ? J.mn0 : J.mn1);
+            pr[1] = key_to_bits<ST>(h == 0 ? J.mx0 : J.mx1);
         }
     }
 }
 
-// One workgroup per (chunk of blocks, matrix) of an (entry, KV head): its 256
-// threads copy R_k or R_v into LDS (rows padded to D + 1 floats, so the 64
-// lanes reading 64 rows at one column hit distinct banks) with one round of
-// coalesced 16-byte loads; wave w then rotates blocks w, w + 4, ... of the
-// chunk (counted from the entry's first block E.blk0) from LDS, a token at a
-// time. Each wave's first block has its keys
-// and first row requested before the copy, so those loads overlap it. Appends
-// of a token or two use one-block chunks (one computing wave per matrix; the
-// K and V workgroups run side by side); bulk appends use A.chunk_blocks, so R
-// is read once per chunk rather than once per block.
+// Rotate, rank, round and store the block's new tokens one at a time (R from
+// LDS; xs is the wave's LDS row of doubles), the next row loading while one
+// is rotated; then finish the block.
+template <typename ST>
+__device__ __forceinline__ void block_run(BlockJob<ST> &J, const CompressEntry &E, int blk, int lane,
+                                          const float (*Rs)[D + 1], double (*xs)[D]) {
+    using bits_t = typename ST::bits_t;
+    bits_t x0 = J.x0, x1 = J.x1;
+    for (int slot = J.sa; slot < J.se; ++slot) {
+        xs[0][lane] = (double)bits_to_float<ST>(x0);
+        xs[0][lane + 64] = (double)bits_to_float<ST>(x1);
+        wave_lds_sync();
+        if (slot + 1 < J.se) {
+            const bits_t *xr = J.xin + (size_t)(E.row0 + (J.p0 + slot + 1 - E.a)) * D;
+            x0 = xr[lane];
+            x1 = xr[lane + 64];
+        }
+        double a0, a1;
+        rotate_f64_lds(Rs, xs[0], lane, a0, a1);
+        wave_lds_sync();
+        store_token<ST>(J, slot, a0, a1, lane);
+    }
+    block_finish<ST>(J, blk, lane);
+}
+
+// One workgroup per (block, matrix) of an (entry, KV head), for appends of a
+// token or two: its 256 threads copy R_k or R_v into LDS (rows padded to
+// D + 1 floats, so the 64 lanes reading 64 rows at one column hit distinct
+// banks) with one round of coalesced 16-byte loads; wave 0 then rotates the
+// block's new tokens from LDS, a token at a time. The block's keys and first
+// row are requested before the copy, so those loads overlap it; the K and V
+// workgroups run side by side.
 // Workgroups past the append table (z >= n_ent) rotate queries instead.
-// BULK: chunks of A.chunk_blocks blocks and two tokens per rotation pass;
-// otherwise one-block chunks, one token per pass.
-template <typename ST, bool BULK>
+template <typename ST>
 __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     if ((int)blockIdx.z >= A.n_ent) {
         if (blockIdx.x >= D / 32) return;
@@ -322,19 +337,17 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
         return;
     }
     const CompressEntry &E = A.ent[blockIdx.z];
-    const int c0 = ((int)blockIdx.x >> 1) * A.chunk_blocks;
-    if (c0 >= E.nblk) return;
-    const int c1 = min(c0 + A.chunk_blocks, E.nblk);
+    const int bx = (int)blockIdx.x >> 1;  // block index within the entry's range
+    if (bx >= E.nblk) return;
     const int mat = (int)blockIdx.x & 1;  // 0: keys (R_k), 1: values (R_v)
     const int g = (int)blockIdx.y;
     const int w = (int)(threadIdx.x >> 6);
     const int lane = lane_id();
     const size_t unit = (size_t)E.b * A.n_kv + g;
-    __shared__ __align__(16) double xs[4][BULK ? 2 : 1][D];
+    __shared__ __align__(16) double xs[1][D];
     __shared__ float Rst[D][D + 1];
     BlockJob<ST> J;
-    int bx = c0 + w;  // block index within the entry's range; the block is E.blk0 + bx
-    if (bx < c1) block_begin<ST, BULK>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
+    if (w == 0) block_begin<ST, false>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
     {
         const float4 *Rg = reinterpret_cast<const float4 *>(E.rot + ((size_t)g * 2 + mat) * D * D);
         float4 v[D * D / 4 / 256];
@@ -351,9 +364,102 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
         }
     }
     __syncthreads();
-    for (; bx < c1; bx += 4) {
-        if (bx != c0 + w) block_begin<ST, BULK>(J, A, E, unit, g, E.blk0 + bx, mat, lane);
-        block_run<ST, BULK>(J, E, E.blk0 + bx, lane, Rst, xs[w]);
+    if (w == 0) block_run<ST>(J, E, E.blk0 + bx, lane, Rst, xs);
+}
+
+// Bulk appends (prefill): one workgroup of 8 waves per (chunk of
+// COMPRESS_CHUNK blocks, matrix) of an (entry, KV head). R is copied into LDS
+// once per chunk; wave w takes blocks w, w + 8, ... of the chunk and rotates
+// their tokens BULK_NT at a time, so each R element read from LDS serves
+// 2 BULK_NT multiply-adds; the rows of a wave's next pass (in the same or its
+// next block) load while the current pass is rotated.
+constexpr int BULK_NT = 8;
+constexpr int BULK_WAVES = 8;
+
+template <typename ST>
+__global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const CompressArgs A) {
+    using bits_t = typename ST::bits_t;
+    const CompressEntry &E = A.ent[blockIdx.z];
+    const int c0 = ((int)blockIdx.x >> 1) * A.chunk_blocks;
+    if (c0 >= E.nblk) return;
+    const int c1 = min(c0 + A.chunk_blocks, E.nblk);
+    const int mat = (int)blockIdx.x & 1;  // 0: keys (R_k), 1: values (R_v)
+    const int g = (int)blockIdx.y;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = lane_id();
+    const size_t unit = (size_t)E.b * A.n_kv + g;
+    __shared__ __align__(16) double xs[BULK_WAVES][BULK_NT][D];
+    __shared__ float Rst[D][D + 1];
+    {
+        const float4 *Rg = reinterpret_cast<const float4 *>(E.rot + ((size_t)g * 2 + mat) * D * D);
+        constexpr int PER = D * D / 4 / (64 * BULK_WAVES);
+        float4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[k] = Rg[threadIdx.x + 64 * BULK_WAVES * k];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = (int)threadIdx.x + 64 * BULK_WAVES * k;
+            const int c = i / (D / 4), j = (i % (D / 4)) * 4;
+            Rst[c][j] = v[k].x;
+            Rst[c][j + 1] = v[k].y;
+            Rst[c][j + 2] = v[k].z;
+            Rst[c][j + 3] = v[k].w;
+        }
+    }
+    __syncthreads();
+    // this wave's blocks: c0 + w, c0 + w + BULK_WAVES, ... (E.blk0-relative)
+    const bits_t *xin = reinterpret_cast<const bits_t *>(mat ? A.v_new : A.k_new) + unit * A.n_max * D;
+    auto row_of = [&](int blk, int slot) { return xin + (size_t)(E.row0 + (blk * BT + slot - E.a)) * D; };
+    auto slots_of = [&](int blk, int &sa, int &se) {
+        sa = max(E.a, blk * BT) - blk * BT;
+        se = min(E.e, blk * BT + BT) - blk * BT;
+    };
+    // rows of the next pass: block nb_blk, slots [n_slot, n_slot + BULK_NT)
+    bits_t nx0[BULK_NT], nx1[BULK_NT];
+    auto load_pass = [&](int blk, int slot, int se) {
+#pragma unroll
+        for (int t = 0; t < BULK_NT; ++t)
+            if (slot + t < se) {
+                const bits_t *xr = row_of(blk, slot + t);
+                nx0[t] = xr[lane];
+                nx1[t] = xr[lane + 64];
+            }
+    };
+    int bx = c0 + w;
+    if (bx >= c1) return;
+    {
+        int sa, se;
+        slots_of(E.blk0 + bx, sa, se);
+        load_pass(E.blk0 + bx, sa, se);
+    }
+    for (; bx < c1; bx += BULK_WAVES) {
+        const int blk = E.blk0 + bx;
+        BlockJob<ST> J;
+        block_begin<ST, true>(J, A, E, unit, g, blk, mat, lane);
+        for (int slot = J.sa; slot < J.se; slot += BULK_NT) {
+            const int nt = min(BULK_NT, J.se - slot);
+#pragma unroll
+            for (int t = 0; t < BULK_NT; ++t) {
+                xs[w][t][lane] = t < nt ? (double)bits_to_float<ST>(nx0[t]) : 0.0;
+                xs[w][t][lane + 64] = t < nt ? (double)bits_to_float<ST>(nx1[t]) : 0.0;
+            }
+            wave_lds_sync();
+            // the next pass's rows: this block's next slots, else the next block's first
+            if (slot + BULK_NT < J.se) {
+                load_pass(blk, slot + BULK_NT, J.se);
+            } else if (bx + BULK_WAVES < c1) {
+                int sa2, se2;
+                slots_of(blk + BULK_WAVES, sa2, se2);
+                load_pass(blk + BULK_WAVES, sa2, se2);
+            }
+            double a0[BULK_NT], a1[BULK_NT];
+            rotate_nt<BULK_NT>(Rst, xs[w], lane, a0, a1);
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < BULK_NT; ++t)
+                if (t < nt) store_token<ST>(J, slot + t, a0[t], a1[t], lane);
+        }
+        block_finish<ST>(J, blk, lane);
     }
 }
 
@@ -416,11 +522,11 @@ hipError_t launch_compress(const CompressArgs &a, int dtype, int max_blk, hipStr
     const unsigned gx = (unsigned)std::max(2 * nchunk, a.q_req > 0 ? D / 32 : 0);
     const dim3 grid(gx, (unsigned)a.n_kv, (unsigned)(a.n_ent + std::max(a.q_req, 0)));
     if (dtype == MKV_BF16) {
-        if (small) hipLaunchKernelGGL((k_compress<Bf16, false>), grid, dim3(256), 0, s, b);
-        else hipLaunchKernelGGL((k_compress<Bf16, true>), grid, dim3(256), 0, s, b);
+        if (small) hipLaunchKernelGGL(k_compress<Bf16>, grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL(k_compress_bulk<Bf16>, grid, dim3(64 * BULK_WAVES), 0, s, b);
     } else {
-        if (small) hipLaunchKernelGGL((k_compress<F32, false>), grid, dim3(256), 0, s, b);
-        else hipLaunchKernelGGL((k_compress<F32, true>), grid, dim3(256), 0, s, b);
+        if (small) hipLaunchKernelGGL(k_compress<F32>, grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL(k_compress_bulk<F32>, grid, dim3(64 * BULK_WAVES), 0, s, b);
     }
     return hipGetLastError();
 }

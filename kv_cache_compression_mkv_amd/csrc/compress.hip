@@ -134,6 +134,97 @@ __device__ __forceinline__ void topr_keep(double v0, double v1, int r, int lane,
     keep1 = gt1 || ((k1 == thr) && rank1 < need);
 }
 
+// The same selection for NT tokens at once (v0/v1[t]: token t's channels
+// lane and lane + 64; tokens t >= nt are padding), with the same kept set.
+// The threshold is the largest key T with at least r keys >= T, found in
+// three steps that each fix more of its bits: its exponent (scanning down
+// from the largest exponent present), the 20 mantissa bits of the keys' high
+// words (compares of high words only), then, only while some token still has
+// more than r keys >= its threshold, the low words. The NT searches run side
+// by side, so each token's ballot-to-scalar latency is covered by the others;
+// a token with exactly r keys >= its threshold is settled (later steps cannot
+// change its kept set).
+template <int NT>
+__device__ __forceinline__ void topr_keep_nt(const double (&v0)[NT], const double (&v1)[NT], int nt, int r, int lane,
+                                             bool (&keep0)[NT], bool (&keep1)[NT]) {
+    uint64_t k0[NT], k1[NT];
+    uint32_t h0[NT], h1[NT], th[NT];
+    int cnt[NT];
+    uint32_t hm = 0, found = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        k0[t] = (uint64_t)__double_as_longlong(v0[t]) & 0x7FFFFFFFFFFFFFFFull;
+        k1[t] = (uint64_t)__double_as_longlong(v1[t]) & 0x7FFFFFFFFFFFFFFFull;
+        h0[t] = (uint32_t)(k0[t] >> 32);
+        h1[t] = (uint32_t)(k1[t] >> 32);
+        hm = max(hm, max(h0[t], h1[t]));
+        th[t] = 0;
+        cnt[t] = t < nt ? 2 * 64 : r;  // padding tokens count as settled
+        found |= (t < nt ? 0u : 1u) << t;
+    }
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x121, 0xf, 0xf, false));
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x122, 0xf, 0xf, false));
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x124, 0xf, 0xf, false));
+    hm = max(hm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hm, 0x128, 0xf, 0xf, false));
+    hm = max(max((uint32_t)__builtin_amdgcn_readlane((int)hm, 0), (uint32_t)__builtin_amdgcn_readlane((int)hm, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)hm, 32), (uint32_t)__builtin_amdgcn_readlane((int)hm, 48)));
+    // exponent: every key is >= 0, so the scan ends at exponent 0 at the latest
+    constexpr uint32_t ALL = (1u << NT) - 1;
+    for (int e = (int)(hm >> 20); e >= 0 && found != ALL; --e) {
+        const uint32_t cand = (uint32_t)e << 20;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int c = popc64(ballot(h0[t] >= cand)) + popc64(ballot(h1[t] >= cand));
+            const bool take = !((found >> t) & 1u) && c >= r;
+            th[t] = take ? cand : th[t];
+            cnt[t] = take ? c : cnt[t];
+            found |= (take ? 1u : 0u) << t;
+        }
+    }
+    int excess = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) excess += cnt[t] - r;
+    // high-word mantissa bits (k >= T with T's low word zero iff high(k) >= high(T))
+    for (int bit = 19; bit >= 0 && excess > 0; --bit) {
+        excess = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t cand = th[t] | (1u << bit);
+            const int c = popc64(ballot(h0[t] >= cand)) + popc64(ballot(h1[t] >= cand));
+            const bool take = c >= r;
+            th[t] = take ? cand : th[t];
+            cnt[t] = take ? c : cnt[t];
+            excess += cnt[t] - r;
+        }
+    }
+    uint64_t thr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) thr[t] = (uint64_t)th[t] << 32;
+    for (int bit = 31; bit >= 0 && excess > 0; --bit) {
+        excess = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint64_t cand = thr[t] | (1ull << bit);
+            const int c = popc64(ballot(k0[t] >= cand)) + popc64(ballot(k1[t] >= cand));
+            const bool take = c >= r;
+            thr[t] = take ? cand : thr[t];
+            cnt[t] = take ? c : cnt[t];
+            excess += cnt[t] - r;
+        }
+    }
+    const uint64_t below = lanes_below(lane);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const bool gt0 = k0[t] > thr[t], gt1 = k1[t] > thr[t];
+        const int need = r - popc64(ballot(gt0)) - popc64(ballot(gt1));
+        const uint64_t e0 = ballot(k0[t] == thr[t]), e1 = ballot(k1[t] == thr[t]);
+        const int rank0 = popc64(e0 & below);
+        const int rank1 = popc64(e0) + popc64(e1 & below);
+        keep0[t] = gt0 || ((k0[t] == thr[t]) && rank0 < need);
+        keep1[t] = gt1 || ((k1[t] == thr[t]) && rank1 < need);
+    }
+}
+
 // Per-block state of one wave's append into block blk of one (entry, KV head,
 // matrix): destination pointers, the new slots [sa, se), the running keys of
 // a packed segment's block (keys matrix only) and the first new row.
@@ -221,16 +312,16 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     J.x1 = x1;
 }
 
-// top-r, rounding and the stores of token `slot` of J's block from its
-// rotated channels (lane: channels lane and lane + 64); packed segments fold
-// the stored key into the block's running min/max
+// Rounding and the stores of token `slot` of J's block from its rotated
+// channels (lane: channels lane and lane + 64) and, for packed segments, its
+// kept channels keep0/keep1; packed segments fold the stored key into the
+// block's running min/max.
 template <typename ST>
-__device__ __forceinline__ void store_token(BlockJob<ST> &J, int slot, double v0, double v1, int lane) {
+__device__ __forceinline__ void store_kept(BlockJob<ST> &J, int slot, double v0, double v1, bool keep0, bool keep1,
+                                           int lane) {
     using bits_t = typename ST::bits_t;
     const bits_t s0 = round_store<ST>(v0), s1 = round_store<ST>(v1);
     if (J.packed) {
-        bool keep0, keep1;
-        topr_keep(v0, v1, J.r, lane, keep0, keep1);
         const uint64_t m0 = ballot(keep0), m1 = ballot(keep1);
         const uint64_t below = lanes_below(lane);
         bits_t *vrow = J.vals + (size_t)slot * J.r;
@@ -256,6 +347,14 @@ __device__ __forceinline__ void store_token(BlockJob<ST> &J, int slot, double v0
         vrow[lane] = s0;
         vrow[lane + 64] = s1;
     }
+}
+
+// top-r selection, then the stores, of one token
+template <typename ST>
+__device__ __forceinline__ void store_token(BlockJob<ST> &J, int slot, double v0, double v1, int lane) {
+    bool keep0 = false, keep1 = false;
+    if (J.packed) topr_keep(v0, v1, J.r, lane, keep0, keep1);
+    store_kept<ST>(J, slot, v0, v1, keep0, keep1, lane);
 }
 
 // After a block's new tokens: clear the slots after its last token when this
@@ -455,9 +554,16 @@ __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const Compres
             double a0[BULK_NT], a1[BULK_NT];
             rotate_nt<BULK_NT>(Rst, xs[w], lane, a0, a1);
             wave_lds_sync();
+            bool keep0[BULK_NT], keep1[BULK_NT];
+            if (J.packed) {
+                topr_keep_nt<BULK_NT>(a0, a1, nt, J.r, lane, keep0, keep1);
+            } else {
+#pragma unroll
+                for (int t = 0; t < BULK_NT; ++t) keep0[t] = keep1[t] = false;
+            }
 #pragma unroll
             for (int t = 0; t < BULK_NT; ++t)
-                if (t < nt) store_token<ST>(J, slot + t, a0[t], a1[t], lane);
+                if (t < nt) store_kept<ST>(J, slot + t, a0[t], a1[t], keep0[t], keep1[t], lane);
         }
         block_finish<ST>(J, blk, lane);
     }

@@ -150,3 +150,65 @@ def test_rounding_edge_cases(dtype):
     xf = x[0, 0].astype(np.float64)
     comp = orc.compress_unit(xf, xf, R[0, 0, 0].astype(np.float64), R[0, 0, 1].astype(np.float64), segs, 64, dtype)
     compare_compress(c, w, comp, 0, 0, 64)
+
+
+def _tie_inputs(rng, n, dtype):
+    """Rows of several kinds, by row index mod 7: magnitudes from {0, 1/2, 1, 2}
+    (many exact ties), all zero, all of magnitude 1, normal values, three
+    nonzero values only, powers of two over a wide exponent range, and
+    magnitudes 1 + k 2^-23 that share their leading 20 mantissa bits (f32;
+    with bf16 storage these round to 1 and tie)."""
+    x = np.zeros((n, 128), np.float32)
+    for t in range(n):
+        kind = t % 7
+        sgn = rng.choice([-1.0, 1.0], 128)
+        if kind == 0:
+            x[t] = sgn * rng.choice([0.0, 0.5, 1.0, 2.0], 128)
+        elif kind == 2:
+            x[t] = sgn
+        elif kind == 3:
+            x[t] = rng.standard_normal(128)
+        elif kind == 4:
+            x[t, rng.choice(128, 3, replace=False)] = rng.standard_normal(3) + 3.0
+        elif kind == 5:
+            x[t] = sgn * np.exp2(rng.integers(-120, 120, 128).astype(np.float64))
+        elif kind == 6:
+            x[t] = sgn * (1.0 + rng.integers(0, 8, 128) * 2.0 ** -23)
+    if dtype == "bf16":
+        xb = synth.f32_to_bf16_bits(x)
+        return synth.bf16_bits_to_f32(xb).reshape(x.shape), xb
+    return x, None
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bulk_selection_ties_and_extremes(dtype):
+    """Prefill-sized appends (the many-block kernel) whose rotated magnitudes
+    tie exactly, are all zero, span a wide exponent range or differ only in
+    the low word of their binary64 bits: kept channels and values equal the
+    oracle's, with ties to the lower channel, for r from 1 to 127."""
+    n = 7 * 16 * 5  # 35 blocks per segment
+    rs = (1, 5, 64, 127)
+    segs = [synth.seg(synth.PACKED, i * n, n, r, 1000000, 0) for i, r in enumerate(rs)]
+    total = n * len(rs)
+    c = _one_head_cache(dtype, segs)
+    rng = np.random.default_rng(11)
+    R = np.zeros((1, 1, 2, 128, 128), np.float32)
+    # keys: a signed permutation (rotated values are exact copies, so ties stay ties)
+    perm = rng.permutation(128)
+    R[0, 0, 0, np.arange(128), perm] = rng.choice([-1.0, 1.0], 128)
+    # values: the same plus k 2^-40 x_0 in rows that do not already read x_0,
+    # so equal copies split in the low word when x_0 != 0
+    R[0, 0, 1] = R[0, 0, 0]
+    rows = np.nonzero(perm != 0)[0]
+    R[0, 0, 1, rows, 0] = (rng.integers(0, 4, rows.size) * 2.0 ** -40).astype(np.float32)
+    c.set_rotation(R)
+    x, xb = _tie_inputs(rng, total, dtype)
+    log("bulk ties dtype=%s tokens=%d r=%s" % (dtype, total, rs))
+    kin = to_device(torch, (xb if xb is not None else x).reshape(1, 1, total, 128))
+    c.append(kin, kin.clone(), [total])
+    torch.cuda.synchronize()
+    w = dict(dtype=dtype, n_kv_heads=1, segs=[segs])
+    xf = x.astype(np.float64)
+    comp = orc.compress_unit(xf, xf, R[0, 0, 0].astype(np.float64), R[0, 0, 1].astype(np.float64), segs, total,
+                             dtype)
+    compare_compress(c, w, comp, 0, 0, total)

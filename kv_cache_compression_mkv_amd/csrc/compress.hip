@@ -42,61 +42,109 @@ __device__ __forceinline__ void rotate_f64_lds(const float (*Rs)[D + 1], const d
     a1 = p1;
 }
 
-// x' = R x for NT tokens at once (xs: their inputs as doubles in LDS): every
-// R element read from LDS and converted serves 2 NT fused multiply-adds. Lane
-// owns channels lane and lane + 64; each sum is one fp64 chain over j
-// ascending (products of two floats are exact in fp64). Columns go in pairs,
-// and the next pair's R elements and inputs are read while the current pair
-// is multiplied, so the LDS latency overlaps the arithmetic.
-template <int NT>
-struct RotCols {  // two columns' R elements (rows lane, lane + 64) and NT inputs
-    float r0[2], r1[2];
-    double2 x[NT];
-};
-
-template <int NT>
-__device__ __forceinline__ void rot_load(const float (*Rs)[D + 1], const double (*xs)[D], int lane, int j,
-                                         RotCols<NT> &c) {
-    c.r0[0] = Rs[lane][j];
-    c.r0[1] = Rs[lane][j + 1];
-    c.r1[0] = Rs[lane + 64][j];
-    c.r1[1] = Rs[lane + 64][j + 1];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) c.x[t] = *reinterpret_cast<const double2 *>(&xs[t][j]);
+// ---- bulk rotation: inputs in registers, broadcast across lanes by DPP ----
+// Lane l owns channels l and l + 64. In row q (16 lanes) lane n holds inputs
+// 8n .. 8n + 7 of each token, one per register (the four rows hold the same
+// copy), so input j = 8n + m is register m of lane n of every row; the
+// fused multiply-add reads it with a row broadcast of lane n, and no input
+// goes through LDS. R is held in LDS as binary64 pairs (R[c][j], R[c+64][j])
+// at [j][c], one 16-byte read per column per lane.
+//
+// The multiply-adds are written as ordered assembly statements because the
+// compiler does not fuse the broadcast into the f64 multiply-add. A DPP read
+// needs two wait states after a vector-ALU write of any register it reads:
+// inputs are fenced by dpp_fence after their conversion, R values come from
+// LDS reads, zeroed accumulators are fenced too, and an accumulator is
+// rewritten only 2 NT statements later.
+template <int N>
+__device__ __forceinline__ void fma_row_bcast(double &acc, double x, double r) {
+    asm volatile("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(x), "v"(r), "n"(N));
 }
 
-template <int NT>
-__device__ __forceinline__ void rot_fma(const RotCols<NT> &c, double (&a0)[NT], double (&a1)[NT]) {
+__device__ __forceinline__ void dpp_fence(double (&X)[8]) {
+    asm volatile("s_nop 1"
+                 : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3]), "+v"(X[4]), "+v"(X[5]), "+v"(X[6]), "+v"(X[7]));
+}
+
+// one token's inputs 8n .. 8n + 7 (raw storage words) and their binary64 values
+template <typename ST>
+struct Row8 {
+    uint4 w[ST::bytes / 2];
+};
+
+template <typename ST>
+__device__ __forceinline__ void row8_load(Row8<ST> &raw, const typename ST::bits_t *xr, int n) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(xr) + n * (ST::bytes / 2);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const double u = (double)c.r0[k], v = (double)c.r1[k];
+    for (int k = 0; k < ST::bytes / 2; ++k) raw.w[k] = p[k];
+}
+
+__device__ __forceinline__ void row8_f64(const Row8<Bf16> &raw, double (&X)[8]) {
+    const uint32_t u[4] = {raw.w[0].x, raw.w[0].y, raw.w[0].z, raw.w[0].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        X[2 * k] = (double)bf16_lo(u[k]);
+        X[2 * k + 1] = (double)bf16_hi(u[k]);
+    }
+}
+
+__device__ __forceinline__ void row8_f64(const Row8<F32> &raw, double (&X)[8]) {
+    const uint32_t u[8] = {raw.w[0].x, raw.w[0].y, raw.w[0].z, raw.w[0].w,
+                           raw.w[1].x, raw.w[1].y, raw.w[1].z, raw.w[1].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) X[k] = (double)__uint_as_float(u[k]);
+}
+
+// columns 8n .. 8n + 7 of the rotation of NT tokens (one fp64 chain per
+// channel and token, j ascending across calls)
+template <int NT, int N, int PF>
+__device__ __forceinline__ void rotate_cols8(const double2 *Rl, double2 (&ring)[PF], const double (&X)[NT][8],
+                                             double (&a0)[NT], double (&a1)[NT]) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int j = 8 * N + m;
+        const double2 rc = ring[j % PF];
+        if (j + PF < D) ring[j % PF] = Rl[(j + PF) * 64];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const double x = k ? c.x[t].y : c.x[t].x;
-            a0[t] = fma(u, x, a0[t]);
-            a1[t] = fma(v, x, a1[t]);
+            fma_row_bcast<N>(a0[t], X[t][m], rc.x);
+            fma_row_bcast<N>(a1[t], X[t][m], rc.y);
         }
     }
 }
 
 template <int NT>
-__device__ __forceinline__ void rotate_nt(const float (*Rs)[D + 1], const double (*xs)[D], int lane,
-                                          double (&a0)[NT], double (&a1)[NT]) {
+__device__ __forceinline__ void rotate_regs(const double2 *Rl, const double (&X)[NT][8], double (&a0)[NT],
+                                            double (&a1)[NT]) {
+    constexpr int PF = 3;  // columns of R in flight
+    static_assert(NT == 8, "fences cover 8 accumulators each");
 #pragma unroll
     for (int t = 0; t < NT; ++t) a0[t] = a1[t] = 0.0;
-    // two register sets in turn: one is read from LDS while the other is used
-    RotCols<NT> A, B;
-    rot_load<NT>(Rs, xs, lane, 0, A);
-#pragma unroll 1
-    for (int j = 0; j < D; j += 4) {
-        rot_load<NT>(Rs, xs, lane, j + 2, B);
-        rot_fma<NT>(A, a0, a1);
-        rot_load<NT>(Rs, xs, lane, min(j + 4, D - 2), A);  // the last pass rereads a pair (unused)
-        rot_fma<NT>(B, a0, a1);
-    }
+    dpp_fence(a0);
+    dpp_fence(a1);
+    double2 ring[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) ring[k] = Rl[k * 64];
+    rotate_cols8<NT, 0, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 1, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 2, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 3, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 4, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 5, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 6, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 7, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 8, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 9, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 10, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 11, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 12, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 13, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 14, PF>(Rl, ring, X, a0, a1);
+    rotate_cols8<NT, 15, PF>(Rl, ring, X, a0, a1);
 }
 
-// Keep the r channels of largest magnitude (ties to the lower channel).
 // Keys are the magnitude bit patterns (63 bits; order = magnitude order).
 // The threshold is found bit by bit with ballot counts, from the leading bit
 // of the largest key down (higher bits are zero in every key). It keeps the
@@ -468,10 +516,10 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
 
 // Bulk appends (prefill): one workgroup of 8 waves per (chunk of
 // COMPRESS_CHUNK blocks, matrix) of an (entry, KV head). R is copied into LDS
-// once per chunk; wave w takes blocks w, w + 8, ... of the chunk and rotates
-// their tokens BULK_NT at a time, so each R element read from LDS serves
-// 2 BULK_NT multiply-adds; the rows of a wave's next pass (in the same or its
-// next block) load while the current pass is rotated.
+// once per chunk, as binary64; wave w takes blocks w, w + 8, ... of the chunk
+// and rotates their tokens BULK_NT at a time with inputs in registers; the
+// rows of a wave's next pass (in the same or its next block) load while the
+// current pass is ranked and stored.
 constexpr int BULK_NT = 8;
 constexpr int BULK_WAVES = 8;
 
@@ -487,42 +535,43 @@ __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const Compres
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const size_t unit = (size_t)E.b * A.n_kv + g;
-    __shared__ __align__(16) double xs[BULK_WAVES][BULK_NT][D];
-    __shared__ float Rst[D][D + 1];
+    __shared__ __align__(16) double2 Rl[D * 64];  // [j][c]: (R[c][j], R[c + 64][j])
     {
-        const float4 *Rg = reinterpret_cast<const float4 *>(E.rot + ((size_t)g * 2 + mat) * D * D);
-        constexpr int PER = D * D / 4 / (64 * BULK_WAVES);
-        float4 v[PER];
+        // thread: channel pair c, columns 16 jb .. 16 jb + 15
+        const float *Rg = E.rot + ((size_t)g * 2 + mat) * D * D;
+        const int c = (int)threadIdx.x & 63, jb = (int)threadIdx.x >> 6;
+        const float4 *r0 = reinterpret_cast<const float4 *>(Rg + (size_t)c * D + 16 * jb);
+        const float4 *r1 = reinterpret_cast<const float4 *>(Rg + (size_t)(c + 64) * D + 16 * jb);
+        float4 u[4], v[4];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) v[k] = Rg[threadIdx.x + 64 * BULK_WAVES * k];
+        for (int k = 0; k < 4; ++k) {
+            u[k] = r0[k];
+            v[k] = r1[k];
+        }
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = (int)threadIdx.x + 64 * BULK_WAVES * k;
-            const int c = i / (D / 4), j = (i % (D / 4)) * 4;
-            Rst[c][j] = v[k].x;
-            Rst[c][j + 1] = v[k].y;
-            Rst[c][j + 2] = v[k].z;
-            Rst[c][j + 3] = v[k].w;
+        for (int k = 0; k < 4; ++k) {
+            const int j = 16 * jb + 4 * k;
+            Rl[(j + 0) * 64 + c] = make_double2(u[k].x, v[k].x);
+            Rl[(j + 1) * 64 + c] = make_double2(u[k].y, v[k].y);
+            Rl[(j + 2) * 64 + c] = make_double2(u[k].z, v[k].z);
+            Rl[(j + 3) * 64 + c] = make_double2(u[k].w, v[k].w);
         }
     }
     __syncthreads();
-    // this wave's blocks: c0 + w, c0 + w + BULK_WAVES, ... (E.blk0-relative)
+    const double2 *Rlane = Rl + lane;
+    const int n = lane & 15;
     const bits_t *xin = reinterpret_cast<const bits_t *>(mat ? A.v_new : A.k_new) + unit * A.n_max * D;
     auto row_of = [&](int blk, int slot) { return xin + (size_t)(E.row0 + (blk * BT + slot - E.a)) * D; };
     auto slots_of = [&](int blk, int &sa, int &se) {
         sa = max(E.a, blk * BT) - blk * BT;
         se = min(E.e, blk * BT + BT) - blk * BT;
     };
-    // rows of the next pass: block nb_blk, slots [n_slot, n_slot + BULK_NT)
-    bits_t nx0[BULK_NT], nx1[BULK_NT];
+    // rows of the next pass: block blk, slots [slot, slot + BULK_NT)
+    Row8<ST> raw[BULK_NT];
     auto load_pass = [&](int blk, int slot, int se) {
 #pragma unroll
         for (int t = 0; t < BULK_NT; ++t)
-            if (slot + t < se) {
-                const bits_t *xr = row_of(blk, slot + t);
-                nx0[t] = xr[lane];
-                nx1[t] = xr[lane + 64];
-            }
+            if (slot + t < se) row8_load<ST>(raw[t], row_of(blk, slot + t), n);
     };
     int bx = c0 + w;
     if (bx >= c1) return;
@@ -537,12 +586,19 @@ __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const Compres
         block_begin<ST, true>(J, A, E, unit, g, blk, mat, lane);
         for (int slot = J.sa; slot < J.se; slot += BULK_NT) {
             const int nt = min(BULK_NT, J.se - slot);
+            double X[BULK_NT][8];
 #pragma unroll
             for (int t = 0; t < BULK_NT; ++t) {
-                xs[w][t][lane] = t < nt ? (double)bits_to_float<ST>(nx0[t]) : 0.0;
-                xs[w][t][lane + 64] = t < nt ? (double)bits_to_float<ST>(nx1[t]) : 0.0;
+                if (t < nt) {
+                    row8_f64(raw[t], X[t]);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) X[t][m] = 0.0;
+                }
+                dpp_fence(X[t]);
             }
-            wave_lds_sync();
+            double a0[BULK_NT], a1[BULK_NT];
+            rotate_regs<BULK_NT>(Rlane, X, a0, a1);
             // the next pass's rows: this block's next slots, else the next block's first
             if (slot + BULK_NT < J.se) {
                 load_pass(blk, slot + BULK_NT, J.se);
@@ -551,9 +607,6 @@ __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const Compres
                 slots_of(blk + BULK_WAVES, sa2, se2);
                 load_pass(blk + BULK_WAVES, sa2, se2);
             }
-            double a0[BULK_NT], a1[BULK_NT];
-            rotate_nt<BULK_NT>(Rst, xs[w], lane, a0, a1);
-            wave_lds_sync();
             bool keep0[BULK_NT], keep1[BULK_NT];
             if (J.packed) {
                 topr_keep_nt<BULK_NT>(a0, a1, nt, J.r, lane, keep0, keep1);

@@ -260,6 +260,14 @@ __device__ __forceinline__ void topr_keep_nt(const double (&v0)[NT], const doubl
             excess += cnt[t] - r;
         }
     }
+    if (excess == 0) {  // every token has exactly r keys >= its threshold
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            keep0[t] = k0[t] >= thr[t];
+            keep1[t] = k1[t] >= thr[t];
+        }
+        return;
+    }
     const uint64_t below = lanes_below(lane);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {

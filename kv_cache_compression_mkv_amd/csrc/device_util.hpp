@@ -31,6 +31,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     const uint64_t b = (uint64_t)__double_as_longlong(x);
     const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    const uint32_t ah = (uint32_t)(b >> 32) & 0x7FFFFFFFu, lo = (uint32_t)b;
+    if (ah - 0x38100000u < 0x47F00000u - 0x38100000u) {
+        // 2^-126 <= |x| < 2^128 (binary32 normal range): rebias the exponent,
+        // keep the top 23 fraction bits and OR in the sticky bit of the rest
+        const uint32_t f = ((ah - 0x38000000u) << 3) | (lo >> 29) | ((lo & 0x1FFFFFFFu) != 0u ? 1u : 0u);
+        return (uint16_t)(sign | ((f + 0x7FFFu + ((f >> 16) & 1u)) >> 16));
+    }
     const int ex = (int)((b >> 52) & 0x7ff);
     const uint64_t m = b & 0xFFFFFFFFFFFFFull;
     if (ex == 0x7ff) return (uint16_t)(sign | (m ? 0x7FC0u : 0x7F80u));

@@ -534,7 +534,8 @@ constexpr int BULK_WAVES = 8;
 template <typename ST>
 __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const CompressArgs A) {
     using bits_t = typename ST::bits_t;
-    const CompressEntry &E = A.ent[blockIdx.z];
+    // a copy: the stores below would otherwise make the compiler reload entry fields
+    const CompressEntry E = A.ent[blockIdx.z];
     const int c0 = ((int)blockIdx.x >> 1) * A.chunk_blocks;
     if (c0 >= E.nblk) return;
     const int c1 = min(c0 + A.chunk_blocks, E.nblk);
@@ -576,10 +577,10 @@ __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const Compres
     };
     // rows of the next pass: block blk, slots [slot, slot + BULK_NT)
     Row8<ST> raw[BULK_NT];
+    // (slot < se; rows past the block's last new token repeat it and are not used)
     auto load_pass = [&](int blk, int slot, int se) {
 #pragma unroll
-        for (int t = 0; t < BULK_NT; ++t)
-            if (slot + t < se) row8_load<ST>(raw[t], row_of(blk, slot + t), n);
+        for (int t = 0; t < BULK_NT; ++t) row8_load<ST>(raw[t], row_of(blk, min(slot + t, se - 1)), n);
     };
     int bx = c0 + w;
     if (bx >= c1) return;

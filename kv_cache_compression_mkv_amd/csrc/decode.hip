@@ -31,6 +31,11 @@ __device__ __forceinline__ const DSeg &seg_of(const DecodeArgs &A, int bl, int s
     return A.seg[bl * A.nseg + si];
 }
 
+// packed j of a request takes the sliced select (nb > BIG_SEL_MIN)
+__device__ __forceinline__ bool sliced(const DecodeArgs &A, int j, const DSeg &S) {
+    return A.big_row[j] >= 0 && S.nb > BIG_SEL_MIN;
+}
+
 // ----------------------------------------------------------------------------
 // q_rotate: four workgroups per (request, KV head), 32 channels each.
 // ----------------------------------------------------------------------------
@@ -56,6 +61,41 @@ __global__ __launch_bounds__(256) void k_qrot(const DecodeArgs A) {
     const int b = A.b0 + bl;
     qrot_block<G>(slot_rot(A, bl, slot), A.q + (size_t)b * A.hq * D, A.qa + ((size_t)b * A.nslot + slot) * A.hq * D,
                   A.qs + ((size_t)b * A.nslot + slot) * A.hkv * D * 2 * G, (int)blockIdx.y, (int)blockIdx.x, qsh);
+}
+
+// DPP row (16-lane) reductions on integers; every lane of the row gets the result
+#define MKV_RORI(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), ctrl, 0xf, 0xf, false)
+__device__ __forceinline__ int row_sum16_i(int v) {
+    v += MKV_RORI(v, 0x121);
+    v += MKV_RORI(v, 0x122);
+    v += MKV_RORI(v, 0x124);
+    v += MKV_RORI(v, 0x128);
+    return v;
+}
+__device__ __forceinline__ uint32_t row_min16_u(uint32_t v) {
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x121));
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x122));
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x124));
+    v = min(v, (uint32_t)MKV_RORI((int)v, 0x128));
+    return v;
+}
+__device__ __forceinline__ uint32_t row_max16_u(uint32_t v) {
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x121));
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x122));
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x124));
+    v = max(v, (uint32_t)MKV_RORI((int)v, 0x128));
+    return v;
+}
+#undef MKV_RORI
+__device__ __forceinline__ int lane_int(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// wave-uniform min / max of a per-lane value
+__device__ __forceinline__ void wave_minmax_u(uint32_t &mn, uint32_t &mx) {
+    const uint32_t a = row_min16_u(mn), b = row_max16_u(mx);
+    mn = min(min((uint32_t)lane_int((int)a, 0), (uint32_t)lane_int((int)a, 16)),
+             min((uint32_t)lane_int((int)a, 32), (uint32_t)lane_int((int)a, 48)));
+    mx = max(max((uint32_t)lane_int((int)b, 0), (uint32_t)lane_int((int)b, 16)),
+             max((uint32_t)lane_int((int)b, 32), (uint32_t)lane_int((int)b, 48)));
 }
 
 // ----------------------------------------------------------------------------
@@ -111,44 +151,39 @@ __device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, i
             A.scores[A.sc_off[j] + ((size_t)b * A.hq + g * G + i) * nbc + l] = acc[i];
         A.mask[A.mk_off[j] + ((size_t)b * A.hkv + g) * nbc + l] = 0u;
     }
+    if (sliced(A, j, S)) {
+        // the sliced select's inputs: each tile's key range per head, and
+        // (tile 0) cleared histogram and candidate state of the group's heads
+        const int ntc = (A.nbcap[j] + META_TILE - 1) / META_TILE;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const bool valid = l < S.nb;
+            uint32_t mn = valid ? score_key(acc[i]) : 0xFFFFFFFFu, mx = valid ? score_key(acc[i]) : 0u;
+            wave_minmax_u(mn, mx);
+            uint32_t *tm = A.tmm + A.tm_off[j] + (((size_t)b * A.hq + g * G + i) * ntc + tile) * 2;
+            if (lane == 0) {
+                tm[0] = mn;
+                tm[1] = mx;
+            }
+        }
+        if (tile == 0) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                BigRow &R = A.big[A.big_row[j] + (size_t)b * A.hq + g * G + i];
+                uint4 *hv = reinterpret_cast<uint4 *>(R.hist);
+                for (int q = lane; q < BSEL_BINS / 4; q += 64) hv[q] = make_uint4(0u, 0u, 0u, 0u);
+                if (lane == 0) {
+                    R.bmn = 0xFFFFFFFFu;
+                    R.bmx = 0u;
+                    R.ncand = 0u;
+                }
+            }
+        }
+    }
 }
 
 constexpr int SEL_MAX_WAVES = 16;
 
-// DPP row (16-lane) reductions on integers; every lane of the row gets the result
-#define MKV_RORI(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), ctrl, 0xf, 0xf, false)
-__device__ __forceinline__ int row_sum16_i(int v) {
-    v += MKV_RORI(v, 0x121);
-    v += MKV_RORI(v, 0x122);
-    v += MKV_RORI(v, 0x124);
-    v += MKV_RORI(v, 0x128);
-    return v;
-}
-__device__ __forceinline__ uint32_t row_min16_u(uint32_t v) {
-    v = min(v, (uint32_t)MKV_RORI((int)v, 0x121));
-    v = min(v, (uint32_t)MKV_RORI((int)v, 0x122));
-    v = min(v, (uint32_t)MKV_RORI((int)v, 0x124));
-    v = min(v, (uint32_t)MKV_RORI((int)v, 0x128));
-    return v;
-}
-__device__ __forceinline__ uint32_t row_max16_u(uint32_t v) {
-    v = max(v, (uint32_t)MKV_RORI((int)v, 0x121));
-    v = max(v, (uint32_t)MKV_RORI((int)v, 0x122));
-    v = max(v, (uint32_t)MKV_RORI((int)v, 0x124));
-    v = max(v, (uint32_t)MKV_RORI((int)v, 0x128));
-    return v;
-}
-#undef MKV_RORI
-__device__ __forceinline__ int lane_int(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-
-// wave-uniform min / max of a per-lane value
-__device__ __forceinline__ void wave_minmax_u(uint32_t &mn, uint32_t &mx) {
-    const uint32_t a = row_min16_u(mn), b = row_max16_u(mx);
-    mn = min(min((uint32_t)lane_int((int)a, 0), (uint32_t)lane_int((int)a, 16)),
-             min((uint32_t)lane_int((int)a, 32), (uint32_t)lane_int((int)a, 48)));
-    mx = max(max((uint32_t)lane_int((int)b, 0), (uint32_t)lane_int((int)b, 16)),
-             max((uint32_t)lane_int((int)b, 32), (uint32_t)lane_int((int)b, 48)));
-}
 
 // Cross-wave helpers (nw <= 16 waves): after the barrier, lane i of every
 // wave reads wave i's entry and a DPP row reduction combines them.
@@ -352,6 +387,7 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
     const int b = A.b0 + bl, g = (int)blockIdx.y, hi = (int)blockIdx.x;
     const int h = g * G + hi;
     const DSeg &S = seg_of(A, bl, A.pseg[j]);
+    if (sliced(A, j, S)) return;
     const int n = S.nb, k = S.k;
     const int nbc = A.nbcap[j];
     const int nw = (int)(blockDim.x >> 6), lane = lane_id();
@@ -530,6 +566,390 @@ __global__ __launch_bounds__(1024) void k_select(const DecodeArgs A) {
             }
         }
         base += popc64(m);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Sliced select of a large packed segment (more than BIG_SEL_MIN blocks): one
+// workgroup of 4 waves per (slice of BSL blocks, request, query head). Lane l
+// of wave w holds the keys of blocks s BSL + (16 w + i) 64 + l, so block order
+// is (slice, wave, i, lane) order.
+//   1. histogram: the segment's key range [kmin, kmax] comes from the score
+//      pass's per-tile ranges; keys fall into BSEL_BINS bins of width
+//      2^sft in key space (monotone in the score); each slice adds its
+//      counts to the row's histogram.
+//   2. candidates: every slice finds the same threshold bin (the highest bin
+//      whose keys and those above it reach k), records its own counts above
+//      and in that bin, and appends its keys of the bin to the candidates.
+//   3. output: every slice derives the same exact threshold (the k-th largest
+//      key) from the candidates, the counts of the slices before it give its
+//      first output position, and ties at the threshold go to the lowest
+//      blocks; kept blocks are written in ascending order.
+// ----------------------------------------------------------------------------
+constexpr int BSEL_KPT = BSL / 256;
+
+// shift of the key-space bins: (kmax - kmin) >> sft < BSEL_BINS
+__device__ __forceinline__ int bsel_shift(uint32_t span) {
+    const int bits = span ? 32 - __clz(span) : 0;
+    return max(0, bits - 11);
+}
+
+struct BselRow {
+    int z, bl, j, b, h, s, n, k;
+    const DSeg *S;
+};
+
+// the launch's (slice, request, head, segment) of this workgroup; false when
+// the segment does not take the sliced select
+__device__ __forceinline__ bool bsel_row(const DecodeArgs &A, BselRow &r) {
+    r.z = (int)blockIdx.z;
+    r.bl = r.z / A.npk;
+    r.j = r.z % A.npk;
+    r.b = A.b0 + r.bl;
+    r.h = (int)blockIdx.y;
+    r.s = (int)blockIdx.x;
+    r.S = &seg_of(A, r.bl, A.pseg[r.j]);
+    r.n = r.S->nb;
+    r.k = r.S->k;
+    return sliced(A, r.j, *r.S);
+}
+
+// this slice's keys (0 for blocks past the segment's end); every load is
+// issued before any is used
+__device__ __forceinline__ void bsel_keys(const DecodeArgs &A, const BselRow &r, uint32_t (&key)[BSEL_KPT]) {
+    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+    const float *sc = A.scores + A.sc_off[r.j] + ((size_t)r.b * A.hq + r.h) * A.nbcap[r.j];
+    const int base = r.s * BSL + w * BSEL_KPT * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < BSEL_KPT; ++i) key[i] = __float_as_uint(sc[min(base + i * 64, r.n - 1)]);
+#pragma unroll
+    for (int i = 0; i < BSEL_KPT; ++i) key[i] = base + i * 64 < r.n ? score_key(__uint_as_float(key[i])) : 0u;
+}
+
+struct BselHistShared {
+    int v[2][SEL_MAX_WAVES][3];
+    uint32_t hist[BSEL_BINS];
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void k_bsel_hist(const DecodeArgs A) {
+    BselRow r;
+    if (!bsel_row(A, r) || r.k >= r.n || r.s * BSL >= r.n) return;
+    BigRow &R = A.big[A.big_row[r.j] + (size_t)r.b * A.hq + r.h];
+    __shared__ BselHistShared sh;
+    int ph = 0;
+    const int tid = (int)threadIdx.x;
+    uint32_t key[BSEL_KPT];
+    bsel_keys(A, r, key);
+    // key range of the whole segment from its tiles' ranges
+    const int ntile = (r.n + META_TILE - 1) / META_TILE, ntc = (A.nbcap[r.j] + META_TILE - 1) / META_TILE;
+    const uint32_t *tm = A.tmm + A.tm_off[r.j] + ((size_t)r.b * A.hq + r.h) * ntc * 2;
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    for (int t = tid; t < ntile; t += 256) {
+        kmn = min(kmn, tm[2 * t]);
+        kmx = max(kmx, tm[2 * t + 1]);
+    }
+    xwave_minmax(sh, ph, 4, kmn, kmx);
+    if (r.s == 0 && tid == 0) {
+        R.kmin = kmn;
+        R.kmax = kmx;
+    }
+    if (kmn == kmx) return;  // every key equal: the output pass needs no histogram
+    const int sft = bsel_shift(kmx - kmn);
+    for (int i = tid; i < BSEL_BINS; i += 256) sh.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BSEL_KPT; ++i)
+        if (key[i] != 0u) atomicAdd(&sh.hist[(key[i] - kmn) >> sft], 1u);
+    __syncthreads();
+    for (int i = tid; i < BSEL_BINS; i += 256) {
+        const uint32_t c = sh.hist[i];
+        if (c) atomicAdd(&R.hist[i], c);
+    }
+}
+
+struct BselCandShared {
+    int v[2][SEL_MAX_WAVES][3];
+    int res[3];
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void k_bsel_cand(const DecodeArgs A) {
+    BselRow r;
+    if (!bsel_row(A, r) || r.k >= r.n || r.s * BSL >= r.n) return;
+    BigRow &R = A.big[A.big_row[r.j] + (size_t)r.b * A.hq + r.h];
+    const uint32_t kmn = R.kmin, kmx = R.kmax;
+    if (kmn == kmx) return;
+    __shared__ BselCandShared sh;
+    int ph = 0;
+    const int tid = (int)threadIdx.x, lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    uint32_t key[BSEL_KPT];
+    bsel_keys(A, r, key);
+    // threshold bin: thread t holds bins 8t .. 8t + 7; suffix sums from the top
+    uint32_t hb[8];
+    {
+        const uint4 *hv = reinterpret_cast<const uint4 *>(R.hist) + 2 * tid;
+        const uint4 x0 = hv[0], x1 = hv[1];
+        hb[0] = x0.x; hb[1] = x0.y; hb[2] = x0.z; hb[3] = x0.w;
+        hb[4] = x1.x; hb[5] = x1.y; hb[6] = x1.z; hb[7] = x1.w;
+    }
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tsum += (int)hb[q];
+    int suf = tsum;  // inclusive suffix within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
+    }
+    if (lane == 0) sh.v[ph][w][0] = suf;  // the wave's total
+    __syncthreads();
+    int above_w = 0;
+    for (int v = w + 1; v < 4; ++v) above_w += sh.v[ph][v][0];
+    int run = suf - tsum + above_w;  // keys in the bins of higher threads
+#pragma unroll
+    for (int q = 7; q >= 0; --q) {
+        const int c = (int)hb[q];
+        if (run < r.k && run + c >= r.k) {
+            sh.res[0] = 8 * tid + q;
+            sh.res[1] = run;
+            sh.res[2] = c;
+        }
+        run += c;
+    }
+    __syncthreads();
+    ph ^= 1;
+    const int bstar = sh.res[0];
+    const int sft = bsel_shift(kmx - kmn);
+    const uint64_t below = lanes_below(lane);
+    int above_s = 0, in_s = 0;
+    uint32_t cmn = 0xFFFFFFFFu, cmx = 0u;
+#pragma unroll
+    for (int i = 0; i < BSEL_KPT; ++i) {
+        const bool valid = key[i] != 0u;
+        const int bin = (int)((key[i] - kmn) >> sft);
+        above_s += popc64(ballot(valid && bin > bstar));
+        const bool inb = valid && bin == bstar;
+        const uint64_t m = ballot(inb);
+        if (m) {
+            const int first = __builtin_ctzll(m);
+            uint32_t base = 0u;
+            if (lane == first) base = atomicAdd(&R.ncand, (uint32_t)popc64(m));
+            base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+            const uint32_t pos = base + (uint32_t)popc64(m & below);
+            if (inb && pos < (uint32_t)BSEL_CAP) {
+                R.cand[pos][0] = key[i];
+                R.cand[pos][1] = (uint32_t)r.s;
+            }
+            in_s += popc64(m);
+        }
+        if (inb) {
+            cmn = min(cmn, key[i]);
+            cmx = max(cmx, key[i]);
+        }
+    }
+    wave_minmax_u(cmn, cmx);
+    if (lane == 0 && cmx != 0u) {
+        atomicMin(&R.bmn, cmn);
+        atomicMax(&R.bmx, cmx);
+    }
+    int unused = 0;
+    xwave_sum3(sh, ph, 4, above_s, in_s, unused);
+    if (tid == 0) {
+        R.slc[r.s][0] = above_s;
+        R.slc[r.s][1] = in_s;
+        if (r.s == 0) {
+            R.bstar = bstar;
+            R.above = sh.res[1];
+            R.inbin = sh.res[2];
+        }
+    }
+}
+
+struct BselOutShared {
+    int v[2][SEL_MAX_WAVES][3];
+    uint32_t act[64];
+    uint32_t thr;
+    int gtc[BSEL_MAX_SLICES], eqc[BSEL_MAX_SLICES];
+    int res[2];  // this slice's first output position, its quota of keys equal to the threshold
+};
+
+// Keys counted over the whole segment (scores re-read from memory), for the
+// rare threshold bins with more than BSEL_CAP keys: number of keys >= cand.
+__device__ __forceinline__ int bsel_count_all(const DecodeArgs &A, const BselRow &r, BselOutShared &sh, int &ph,
+                                              uint32_t cand) {
+    const float *sc = A.scores + A.sc_off[r.j] + ((size_t)r.b * A.hq + r.h) * A.nbcap[r.j];
+    int c = 0;
+    for (int blk = (int)threadIdx.x; blk < r.n; blk += 256) c += score_key(sc[blk]) >= cand ? 1 : 0;
+    const int rs = row_sum16_i(c);
+    c = (lane_int(rs, 0) + lane_int(rs, 16)) + (lane_int(rs, 32) + lane_int(rs, 48));
+    int u1 = 0, u2 = 0;
+    xwave_sum3(sh, ph, 4, c, u1, u2);
+    return c;
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_bsel_out(const DecodeArgs A) {
+    BselRow r;
+    if (!bsel_row(A, r)) return;
+    const int n = r.n, k = r.k, j = r.j, b = r.b, h = r.h, s = r.s;
+    const int g = h / G, hi = h % G;
+    const int tid = (int)threadIdx.x, lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    int coloff = 0;
+    for (int jj = 0; jj < j; ++jj) coloff += seg_of(A, r.bl, A.pseg[jj]).k;
+    int32_t *so = A.sel_out ? A.sel_out + ((size_t)b * A.hq + h) * A.sel_cols : nullptr;
+    if (so && j == A.npk - 1 && s == 0)
+        for (int64_t c = coloff + k + tid; c < A.sel_cols; c += 256) so[c] = -1;
+    if (k <= 0 || s * BSL >= n) return;
+    __shared__ BselOutShared sh;
+    int ph = 0;
+    uint32_t key[BSEL_KPT];
+    bsel_keys(A, r, key);
+    const BigRow &R = A.big[A.big_row[j] + (size_t)b * A.hq + h];
+    const int nsl = (n + BSL - 1) / BSL;
+    // Kept: every valid key when k >= n; the first k blocks when every key is
+    // equal; else keys above thr, and keys equal to thr while the slice's
+    // quota lasts (by_bin: every key of bin bstar or above).
+    int mode = 0;  // 0: all, 1: first k blocks, 2: by bin, 3: threshold
+    uint32_t thr = 0u, kmn = 0u;
+    int sft = 0, bstar = 0, base = 0, quota = 0;
+    if (k < n) {
+        kmn = R.kmin;
+        const uint32_t kmx = R.kmax;
+        if (kmn == kmx) {
+            mode = 1;
+        } else {
+            sft = bsel_shift(kmx - kmn);
+            bstar = R.bstar;
+            const int need = k - R.above, inbin = R.inbin;
+            if (inbin == need) {
+                mode = 2;
+                if (tid == 0) {
+                    int bs = 0;
+                    for (int q = 0; q < s; ++q) bs += R.slc[q][0] + R.slc[q][1];
+                    sh.res[0] = bs;
+                }
+            } else {
+                mode = 3;
+                for (int q = tid; q < nsl; q += 256) sh.gtc[q] = sh.eqc[q] = 0;
+                const uint32_t bmn = R.bmn, bmx = R.bmx;
+                if (bmn == bmx) {
+                    // every key of the bin ties at the threshold
+                    thr = bmn;
+                    for (int q = tid; q < nsl; q += 256) sh.eqc[q] = R.slc[q][1];
+                } else if (inbin <= BSEL_CAP) {
+                    // exact threshold among the candidates (padding keys 0 lie below them)
+                    uint32_t ck[BSEL_CAP / 256];
+#pragma unroll
+                    for (int i = 0; i < BSEL_CAP / 256; ++i) {
+                        const int at = tid + 256 * i;
+                        ck[i] = at < inbin ? R.cand[at][0] : 0u;
+                    }
+                    thr = radix_threshold<BSEL_CAP / 256>(sh, ph, 4, ck, bmn, bmx, need);
+                    __syncthreads();
+#pragma unroll
+                    for (int i = 0; i < BSEL_CAP / 256; ++i) {
+                        const int at = tid + 256 * i;
+                        if (at < inbin) {
+                            const int q = min((int)R.cand[at][1], nsl - 1);
+                            if (ck[i] > thr) atomicAdd(&sh.gtc[q], 1);
+                            else if (ck[i] == thr) atomicAdd(&sh.eqc[q], 1);
+                        }
+                    }
+                } else {
+                    // more candidates than stored: bit search over every key of the segment
+                    const uint32_t diff = bmn ^ bmx;
+                    int bit = 31 - __clz(diff);
+                    uint32_t t = bmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u));
+                    const int above = R.above;
+                    int cnt = above + inbin;  // keys >= t (every key of the bin is >= bmn >= t)
+                    for (; bit >= 0 && cnt != k; --bit) {
+                        const uint32_t cand = t | (1u << bit);
+                        const int c = bsel_count_all(A, r, sh, ph, cand);
+                        if (c >= k) {
+                            t = cand;
+                            cnt = c;
+                        }
+                    }
+                    thr = t;
+                    __syncthreads();
+                    const float *sc = A.scores + A.sc_off[j] + ((size_t)b * A.hq + h) * A.nbcap[j];
+                    for (int blk = tid; blk < n; blk += 256) {
+                        const uint32_t kk = score_key(sc[blk]);
+                        const int q = blk / BSL;
+                        if (((kk - kmn) >> sft) == (uint32_t)bstar && kk > thr) atomicAdd(&sh.gtc[q], 1);
+                        else if (kk == thr) atomicAdd(&sh.eqc[q], 1);
+                    }
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    int gt_all = 0;
+                    for (int q = 0; q < nsl; ++q) gt_all += sh.gtc[q];
+                    int left = need - gt_all;  // keys equal to thr still to take, lowest blocks first
+                    int bs = 0, mine = 0;
+                    for (int q = 0; q <= s; ++q) {
+                        const int tq = min(sh.eqc[q], max(left, 0));
+                        if (q < s) bs += R.slc[q][0] + sh.gtc[q] + tq;
+                        else mine = tq;
+                        left -= tq;
+                    }
+                    sh.res[0] = bs;
+                    sh.res[1] = mine;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (mode == 0) base = s * BSL;
+    else if (mode == 2 || mode == 3) base = sh.res[0];
+    if (mode == 3) quota = sh.res[1];
+    const uint64_t below = lanes_below(lane);
+    const int blk0 = s * BSL + w * BSEL_KPT * 64 + lane;
+    uint32_t selm = 0u;
+    if (mode == 3) {
+        int eqw = 0;
+#pragma unroll
+        for (int i = 0; i < BSEL_KPT; ++i) eqw += popc64(ballot(key[i] != 0u && key[i] == thr));
+        int erun = xwave_excl(sh, ph, 4, eqw);
+#pragma unroll
+        for (int i = 0; i < BSEL_KPT; ++i) {
+            const bool eq = key[i] != 0u && key[i] == thr;
+            const uint64_t em = ballot(eq);
+            const int rank = erun + popc64(em & below);
+            if (key[i] != 0u && (key[i] > thr || (eq && rank < quota))) selm |= 1u << i;
+            erun += popc64(em);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BSEL_KPT; ++i) {
+            const bool valid = key[i] != 0u;
+            bool kept = valid;
+            if (mode == 1) kept = valid && blk0 + i * 64 < k;
+            else if (mode == 2) kept = valid && (int)((key[i] - kmn) >> sft) >= bstar;
+            if (kept) selm |= 1u << i;
+        }
+    }
+    int cw = 0;
+#pragma unroll
+    for (int i = 0; i < BSEL_KPT; ++i) cw += popc64(ballot((selm >> i) & 1u));
+    if (mode == 1) base = s * BSL;  // the first k blocks: position = block
+    int pos0 = base + xwave_excl(sh, ph, 4, cw);
+    int32_t *sl = A.sel + A.sl_off[j] + ((size_t)b * A.hq + h) * A.kcap[j];
+    uint32_t *mk = A.mask + A.mk_off[j] + ((size_t)b * A.hkv + g) * A.nbcap[j];
+#pragma unroll
+    for (int i = 0; i < BSEL_KPT; ++i) {
+        const bool sel = (selm >> i) & 1u;
+        const uint64_t m = ballot(sel);
+        if (sel) {
+            const int pos = pos0 + popc64(m & below);
+            if (pos < k) {
+                const int blk = blk0 + i * 64;
+                sl[pos] = blk;
+                if (so) so[coloff + pos] = blk;
+                reinterpret_cast<uint8_t *>(mk + blk)[hi] = 1;
+            }
+        }
+        pos0 += popc64(m);
     }
 }
 
@@ -1572,12 +1992,19 @@ hipError_t select_launch_kpt(const DecodeArgs &a, hipStream_t s) {
 
 template <int G>
 hipError_t select_launch(const DecodeArgs &a, hipStream_t s) {
+    hipError_t e = hipSuccess;
     switch (a.sel_kpt) {
-    case 4: return select_launch_kpt<G, 4>(a, s);
-    case 16: return select_launch_kpt<G, 16>(a, s);
-    case 64: return select_launch_kpt<G, 64>(a, s);
+    case 0: break;  // every packed segment takes the sliced select
+    case 4: e = select_launch_kpt<G, 4>(a, s); break;
+    case 16: e = select_launch_kpt<G, 16>(a, s); break;
     default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess || a.bsel_slices <= 0) return e;
+    const dim3 grid((unsigned)a.bsel_slices, (unsigned)a.hq, (unsigned)(a.n_req * a.npk));
+    hipLaunchKernelGGL((k_bsel_hist<G>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bsel_cand<G>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bsel_out<G>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -153,8 +153,10 @@ int rot_slots(const mkv_cache *c, int (&slot_of)[MKV_MAX_SEGMENTS]) {
 
 // ---------------------------------------------------------- workspace map --
 struct WsMap {
-    size_t qa, qs, scores, mask, sel, part, total;
+    size_t qa, qs, scores, mask, sel, part, big, tmm, total;
     int64_t sc_off[MKV_MAX_SEGMENTS], mk_off[MKV_MAX_SEGMENTS], sl_off[MKV_MAX_SEGMENTS];
+    int64_t tm_off[MKV_MAX_SEGMENTS];
+    int32_t big_row[MKV_MAX_SEGMENTS];
     int32_t nbcap[MKV_MAX_SEGMENTS], kcap[MKV_MAX_SEGMENTS], pseg[MKV_MAX_SEGMENTS];
     int npk;
     int nslot;
@@ -167,7 +169,7 @@ WsMap ws_map(const mkv_cache *c) {
     WsMap m{};
     const size_t B = c->batch, Hq = c->n_q_heads, Hkv = c->n_kv_heads;
     const int G = (int)(Hq / Hkv);
-    int64_t sc = 0, mk = 0, sl = 0;
+    int64_t sc = 0, mk = 0, sl = 0, rows = 0, tm = 0;
     m.npk = 0;
     m.nslot = rot_slots(c, m.slot_of);
     const size_t NS = (size_t)m.nslot;
@@ -186,6 +188,15 @@ WsMap ws_map(const mkv_cache *c) {
         sc += (int64_t)(B * Hq) * nbc;
         mk += (int64_t)(B * Hkv) * nbc;
         sl += (int64_t)(B * Hq) * m.kcap[p];
+        // segments that can outgrow BIG_SEL_MIN blocks: state of the sliced select
+        m.big_row[p] = -1;
+        m.tm_off[p] = 0;
+        if (nbc > BIG_SEL_MIN) {
+            m.big_row[p] = (int32_t)rows;
+            m.tm_off[p] = tm;
+            rows += (int64_t)(B * Hq);
+            tm += (int64_t)(B * Hq) * ceil_div(nbc, META_TILE) * 2;
+        }
     }
     size_t off = 0;
     m.qa = off;
@@ -200,6 +211,10 @@ WsMap ws_map(const mkv_cache *c) {
     off = align256(off + (size_t)sl * 4);
     m.part = off;
     off = align256(off + B * Hq * NS * MAX_PARTS * PART * 4);
+    m.big = off;
+    off = align256(off + (size_t)rows * sizeof(BigRow));
+    m.tmm = off;
+    off = align256(off + (size_t)tm * 4);
     m.total = off;
     return m;
 }
@@ -409,7 +424,11 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
             A.nbcap[p] = m.nbcap[p];
             A.kcap[p] = m.kcap[p];
             A.pseg[p] = m.pseg[p];
+            A.big_row[p] = m.big_row[p];
+            A.tm_off[p] = m.tm_off[p];
         }
+        A.big = reinterpret_cast<BigRow *>(ws + m.big);
+        A.tmm = reinterpret_cast<uint32_t *>(ws + m.tmm);
         A.b0 = b0;
         A.n_req = n_req;
         A.nseg = c->n_segments;
@@ -418,6 +437,7 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
         A.hkv = c->n_kv_heads;
         A.nslot = m.nslot;
         int max_tiles = 0, max_nb = 0, max_r = 1;
+        bool unsliced = false;  // some request's packed segment takes the one-workgroup select
         for (int i = 0; i < n_req; ++i) {
             for (int j = 0; j < c->n_segments; ++j) {
                 const mkv_segment &sg = segof(c, b0 + i, j);
@@ -437,15 +457,24 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                 if (sg.kind == MKV_SEG_PACKED) {
                     D_.k = (int32_t)keep_blocks(D_.nb, sg.keep_ppm, sg.k_abs);
                     max_tiles = std::max(max_tiles, (int)ceil_div(D_.nb, META_TILE));
-                    max_nb = std::max(max_nb, D_.nb);
                     max_r = std::max(max_r, (int)sg.r);
+                    // the same rule as the device's: sliced select past BIG_SEL_MIN blocks
+                    int p = 0;
+                    while (m.pseg[p] != j) ++p;
+                    if (m.big_row[p] >= 0 && D_.nb > BIG_SEL_MIN)
+                        A.bsel_slices = std::max(A.bsel_slices, (int32_t)ceil_div(D_.nb, BSL));
+                    else {
+                        max_nb = std::max(max_nb, D_.nb);
+                        unsliced = true;
+                    }
                 }
             }
         }
-        // select: 4 keys per lane up to 1024 blocks, 16 up to 16384 (at most
-        // 16 waves), 64 beyond
-        const int kpt = max_nb <= 1024 ? 4 : max_nb <= 16384 ? 16 : 64;
-        A.sel_kpt = kpt;
+        // select: 4 keys per lane up to 1024 blocks, 16 up to BIG_SEL_MIN
+        // (at most 16 waves); larger segments take the sliced select
+        static_assert(BIG_SEL_MIN <= 16 * 64 * 16, "one select workgroup covers every unsliced segment");
+        const int kpt = max_nb <= 1024 ? 4 : 16;
+        A.sel_kpt = unsliced ? kpt : 0;  // 0: no one-workgroup select launch
         A.sel_waves = (int32_t)std::max<int64_t>(1, ceil_div(max_nb, 64 * kpt));
 
         mkv_status st = MKV_OK;

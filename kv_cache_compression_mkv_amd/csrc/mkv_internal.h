@@ -89,6 +89,27 @@ struct DSeg {
     int32_t nbcap;    // block capacity (layout stride)
 };  // 48 bytes
 
+// ---- sliced select of large packed segments -----------------------------------
+// A packed segment of more than BIG_SEL_MIN blocks (in one request, at decode
+// time) is selected by slices of BSL blocks, one workgroup each, in three
+// launches that share one BigRow per (request, query head, segment).
+constexpr int BIG_SEL_MIN = 16384;
+constexpr int BSL = 4096;               // blocks per slice: 4 waves x 16 keys per lane
+constexpr int BSEL_BINS = 2048;         // key-space bins of the histogram pass
+constexpr int BSEL_CAP = 2048;          // candidate keys kept for the exact threshold
+constexpr int BSEL_MAX_SLICES = MKV_MAX_PACKED_BLOCKS / BSL;
+static_assert(BSEL_MAX_SLICES * BSL == MKV_MAX_PACKED_BLOCKS, "slices cover the largest packed segment");
+struct BigRow {
+    uint32_t kmin, kmax;       // key range of the segment's scores
+    uint32_t bmn, bmx;         // key range of the keys in the threshold bin
+    uint32_t ncand;            // keys in the threshold bin (candidates past BSEL_CAP are not stored)
+    int32_t bstar, above, inbin;  // threshold bin, keys in higher bins, keys in it
+    uint32_t hist[BSEL_BINS];
+    int32_t slc[BSEL_MAX_SLICES][2];  // per slice: keys in higher bins, keys in the threshold bin
+    uint32_t cand[BSEL_CAP][2];       // (key, slice) of the threshold bin's keys
+};
+static_assert(sizeof(BigRow) % 16 == 0, "rows stay 16-byte aligned");
+
 struct DecodeArgs {
     DSeg seg[TABLE];  // [n_req][nseg]
     const float *rot;
@@ -119,6 +140,11 @@ struct DecodeArgs {
     int32_t cur_slot;   // attend: the slot whose segments this launch attends
     int32_t qrot_from;  // q_rotate: first slot to rotate (1 when the append's launch did slot 0)
     int32_t nparts[MKV_MAX_SEGMENTS + 1];  // merge: partials per slot
+    BigRow *big;      // sliced select: per packed j with big_row[j] >= 0, rows [B][Hq] from big_row[j]
+    uint32_t *tmm;    // per such j: [B][Hq][ceil(nbcap_j / 64)][2] min and max score key of each 64-block tile
+    int64_t tm_off[MKV_MAX_SEGMENTS];
+    int32_t big_row[MKV_MAX_SEGMENTS];  // -1: packed j never takes the sliced select (nbcap <= BIG_SEL_MIN)
+    int32_t bsel_slices;                // slices of the launch's largest sliced segment (0: none)
 };
 
 static_assert(sizeof(DSeg) == 48, "decode segment layout");

@@ -7,8 +7,10 @@ score is a_l * sum(q') / sqrt(d), and the score order is the order of a_l
 (or its reverse). Cases: many exact ties at the k-th score (ties go to the
 lower block), one outlier far above the rest (every other score falls into
 one bin of a value histogram, so the exact bit search decides), mixed signs,
-and a segment where every block ties. Selections must equal the oracle's
-exactly; outputs match the oracle on the GPU's selection.
+a segment where every block ties, and many distinct scores crowded into one
+bin between two far outliers. Segments of 20000 blocks take the sliced
+select. Selections must equal the oracle's exactly; outputs match the oracle
+on the GPU's selection.
 """
 import numpy as np
 import pytest
@@ -67,15 +69,19 @@ def _set_block_values(c, w, comp, b, g, j, a):
     comp["meta_flat"][off:off + nb] = vals
 
 
-@pytest.mark.parametrize("case", ["ties", "outlier", "mixed_sign", "all_equal"])
-def test_select_adversarial_scores(case):
-    segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * 3000, 38, 100000, 0),
-            synth.seg(synth.DENSE, 32 + 16 * 3000, 64)]
-    T = 32 + 16 * 3000 + 40
-    w = dict(cfg=2, batch=1, n_q_heads=8, n_kv_heads=2, d=128, dtype="bf16", lengths=np.array([T]), segs=[segs])
+@pytest.mark.parametrize("nb", [3000, 20000])
+@pytest.mark.parametrize("case", ["ties", "outlier", "mixed_sign", "all_equal", "crowded"])
+def test_select_adversarial_scores(case, nb):
+    """nb = 3000 blocks: one workgroup per head; nb = 20000 (more than
+    16384): the sliced select over 4096-block slices."""
+    hkv = 2 if nb <= 4096 else 1
+    segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * nb, 38, 100000, 0),
+            synth.seg(synth.DENSE, 32 + 16 * nb, 64)]
+    T = 32 + 16 * nb + 40
+    w = dict(cfg=2, batch=1, n_q_heads=4 * hkv, n_kv_heads=hkv, d=128, dtype="bf16", lengths=np.array([T]),
+             segs=[segs])
     c, raw, R = build(torch, w)
-    nb = 3000
-    rng = np.random.default_rng({"ties": 1, "outlier": 2, "mixed_sign": 3, "all_equal": 4}[case])
+    rng = np.random.default_rng({"ties": 1, "outlier": 2, "mixed_sign": 3, "all_equal": 4, "crowded": 5}[case])
     if case == "ties":
         a = np.round(rng.uniform(1.0, 2.0, nb) * 8) / 8          # 9 distinct values, ~330 blocks each
     elif case == "outlier":
@@ -83,11 +89,17 @@ def test_select_adversarial_scores(case):
         a[1234] = 2.0 ** 60                                       # far above: the rest share one bin
     elif case == "mixed_sign":
         a = rng.choice([-1, 1], nb) * 2.0 ** rng.integers(-20, 20, nb) * (1 + rng.integers(0, 8, nb) / 8)
+    elif case == "crowded":
+        # 16 values in [1, 1.125) between two far outliers: with the key range
+        # this wide, almost every block lands in one histogram bin of distinct keys
+        a = 1.0 + rng.integers(0, 16, nb) / 128.0
+        a[7] = 2.0 ** -60
+        a[nb - 5] = 2.0 ** 60
     else:
         a = np.full(nb, 0.75)
-    q = synth.gen_q(2, 11, 1, 8, "bf16")
+    q = synth.gen_q(2, 11, 1, 4 * hkv, "bf16")
     ex = 0
-    for g in range(2):
+    for g in range(hkv):
         comp, Rk, Rv = oracle_unit(w, raw, R, 0, g, T)
         _set_block_values(c, w, comp, 0, g, 1, a)
         out, sel = c.decode(torch.from_numpy(q).cuda(), want_sel=True)
@@ -99,4 +111,4 @@ def test_select_adversarial_scores(case):
             assert sel[0, 4 * g + h, :own["sel"][0].shape[1]].tolist() == own["sel"][0][h].tolist(), \
                 "%s: g=%d h=%d selection differs" % (case, g, h)
         ex += check_decode_unit(w, comp, Rk, Rv, q[0, hs].astype(np.float64), out[0, hs], sel[0, hs], 5e-3, T, 0, g)
-    log("adversarial select (%s): selections equal the oracle's" % case)
+    log("adversarial select (%s, %d blocks): selections equal the oracle's" % (case, nb))

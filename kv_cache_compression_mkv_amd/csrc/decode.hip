@@ -644,10 +644,15 @@ __global__ __launch_bounds__(256) void k_bsel_hist(const DecodeArgs A) {
     // key range of the whole segment from its tiles' ranges
     const int ntile = (r.n + META_TILE - 1) / META_TILE, ntc = (A.nbcap[r.j] + META_TILE - 1) / META_TILE;
     const uint32_t *tm = A.tmm + A.tm_off[r.j] + ((size_t)r.b * A.hq + r.h) * ntc * 2;
+    static_assert(MKV_MAX_PACKED_BLOCKS / META_TILE <= 4 * 256, "four tiles per thread at most");
+    uint2 tv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tv[q] = reinterpret_cast<const uint2 *>(tm)[min(tid + 256 * q, ntile - 1)];
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    for (int t = tid; t < ntile; t += 256) {
-        kmn = min(kmn, tm[2 * t]);
-        kmx = max(kmx, tm[2 * t + 1]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        kmn = min(kmn, tv[q].x);  // (repeated tiles change nothing)
+        kmx = max(kmx, tv[q].y);
     }
     xwave_minmax(sh, ph, 4, kmn, kmx);
     if (r.s == 0 && tid == 0) {
@@ -678,21 +683,21 @@ __global__ __launch_bounds__(256) void k_bsel_cand(const DecodeArgs A) {
     BselRow r;
     if (!bsel_row(A, r) || r.k >= r.n || r.s * BSL >= r.n) return;
     BigRow &R = A.big[A.big_row[r.j] + (size_t)r.b * A.hq + r.h];
-    const uint32_t kmn = R.kmin, kmx = R.kmax;
-    if (kmn == kmx) return;
     __shared__ BselCandShared sh;
     int ph = 0;
     const int tid = (int)threadIdx.x, lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    // keys, key range and histogram are requested together
     uint32_t key[BSEL_KPT];
     bsel_keys(A, r, key);
+    const uint2 kr = *reinterpret_cast<const uint2 *>(&R.kmin);
+    const uint4 *hv = reinterpret_cast<const uint4 *>(R.hist) + 2 * tid;
+    const uint4 x0 = hv[0], x1 = hv[1];
+    const uint32_t kmn = kr.x, kmx = kr.y;
+    if (kmn == kmx) return;
     // threshold bin: thread t holds bins 8t .. 8t + 7; suffix sums from the top
     uint32_t hb[8];
-    {
-        const uint4 *hv = reinterpret_cast<const uint4 *>(R.hist) + 2 * tid;
-        const uint4 x0 = hv[0], x1 = hv[1];
-        hb[0] = x0.x; hb[1] = x0.y; hb[2] = x0.z; hb[3] = x0.w;
-        hb[4] = x1.x; hb[5] = x1.y; hb[6] = x1.z; hb[7] = x1.w;
-    }
+    hb[0] = x0.x; hb[1] = x0.y; hb[2] = x0.z; hb[3] = x0.w;
+    hb[4] = x1.x; hb[5] = x1.y; hb[6] = x1.z; hb[7] = x1.w;
     int tsum = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) tsum += (int)hb[q];
@@ -768,11 +773,73 @@ __global__ __launch_bounds__(256) void k_bsel_cand(const DecodeArgs A) {
 
 struct BselOutShared {
     int v[2][SEL_MAX_WAVES][3];
+    int slc[BSEL_MAX_SLICES][2];
     uint32_t act[64];
     uint32_t thr;
     int gtc[BSEL_MAX_SLICES], eqc[BSEL_MAX_SLICES];
-    int res[2];  // this slice's first output position, its quota of keys equal to the threshold
+    int res[2];   // this slice's first output position, its quota of keys equal to the threshold
+    uint32_t sub[256];  // candidates per sub-bin of the threshold bin
+    int sres[3];        // sub-bin holding the need-th largest candidate, candidates above it, in it
+    int nact;
 };
+
+// The need-th largest of the n candidate keys ck (thread t holds candidates
+// t + 256 i; 0 pads), all in [bmn, bmx]: a 256-bin histogram of the
+// candidates locates it; when at most 64 candidates share its sub-bin one
+// wave finishes with ballots, else the exact 2-bit search runs.
+__device__ __forceinline__ uint32_t bsel_cand_threshold(BselOutShared &sh, int &ph, const uint32_t (&ck)[BSEL_CAP / 256],
+                                                        uint32_t bmn, uint32_t bmx, int need) {
+    const int tid = (int)threadIdx.x, lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    const uint32_t span = bmx - bmn;
+    const int bits = span ? 32 - __clz(span) : 0;
+    const int sft = max(0, bits - 8);  // span >> sft < 256
+    sh.sub[tid] = 0u;
+    if (tid == 0) sh.nact = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BSEL_CAP / 256; ++i)
+        if (ck[i] != 0u) atomicAdd(&sh.sub[(ck[i] - bmn) >> sft], 1u);
+    __syncthreads();
+    if (w == 0) {
+        // lane holds sub-bins 4 lane .. 4 lane + 3; suffix counts from the top
+        const uint4 hv = reinterpret_cast<const uint4 *>(sh.sub)[lane];
+        const uint32_t tot = hv.x + hv.y + hv.z + hv.w;
+        uint32_t suf = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_down(suf, o, 64);
+            if (lane + o < 64) suf += y;
+        }
+        const uint32_t a3 = suf - tot, s3 = a3 + hv.w, s2 = s3 + hv.z, s1 = s2 + hv.y, s0 = s1 + hv.x;
+        const uint64_t m = ballot(s0 >= (uint32_t)need);
+        const int L = 63 - __clzll(m);
+        if (lane == L) {
+            if (s3 >= (uint32_t)need) { sh.sres[0] = 4 * L + 3; sh.sres[1] = (int)a3; sh.sres[2] = (int)hv.w; }
+            else if (s2 >= (uint32_t)need) { sh.sres[0] = 4 * L + 2; sh.sres[1] = (int)s3; sh.sres[2] = (int)hv.z; }
+            else if (s1 >= (uint32_t)need) { sh.sres[0] = 4 * L + 1; sh.sres[1] = (int)s2; sh.sres[2] = (int)hv.y; }
+            else { sh.sres[0] = 4 * L; sh.sres[1] = (int)s1; sh.sres[2] = (int)hv.x; }
+        }
+    }
+    __syncthreads();
+    const int sb = sh.sres[0], above = sh.sres[1], cnt = sh.sres[2];
+    if (cnt > 64) return radix_threshold<BSEL_CAP / 256>(sh, ph, 4, ck, bmn, bmx, need);
+    const int nd = need - above;  // 1 .. cnt
+#pragma unroll
+    for (int i = 0; i < BSEL_CAP / 256; ++i)
+        if (ck[i] != 0u && (int)((ck[i] - bmn) >> sft) == sb) sh.act[atomicAdd(&sh.nact, 1)] = ck[i];
+    __syncthreads();
+    if (w == 0) {
+        const uint32_t x = lane < cnt ? sh.act[lane] : 0u;  // candidates are > 0
+        uint32_t t = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            if (popc64(ballot(x >= c)) >= nd) t = c;
+        }
+        if (lane == 0) sh.thr = t;
+    }
+    __syncthreads();
+    return sh.thr;
+}
 
 // Keys counted over the whole segment (scores re-read from memory), for the
 // rare threshold bins with more than BSEL_CAP keys: number of keys >= cand.
@@ -807,36 +874,45 @@ __global__ __launch_bounds__(256) void k_bsel_out(const DecodeArgs A) {
     bsel_keys(A, r, key);
     const BigRow &R = A.big[A.big_row[j] + (size_t)b * A.hq + h];
     const int nsl = (n + BSL - 1) / BSL;
+    // the row's header and per-slice counts, requested together
+    const uint4 h0 = *reinterpret_cast<const uint4 *>(&R.kmin);   // kmin, kmax, bmn, bmx
+    const uint4 h1 = *reinterpret_cast<const uint4 *>(&R.ncand);  // ncand, bstar, above, inbin
+    if (tid < nsl && k < n) {
+        const int2 c = *reinterpret_cast<const int2 *>(&R.slc[tid][0]);
+        sh.slc[tid][0] = c.x;
+        sh.slc[tid][1] = c.y;
+    }
     // Kept: every valid key when k >= n; the first k blocks when every key is
     // equal; else keys above thr, and keys equal to thr while the slice's
     // quota lasts (by_bin: every key of bin bstar or above).
     int mode = 0;  // 0: all, 1: first k blocks, 2: by bin, 3: threshold
     uint32_t thr = 0u, kmn = 0u;
     int sft = 0, bstar = 0, base = 0, quota = 0;
+    __syncthreads();
     if (k < n) {
-        kmn = R.kmin;
-        const uint32_t kmx = R.kmax;
+        kmn = h0.x;
+        const uint32_t kmx = h0.y;
         if (kmn == kmx) {
             mode = 1;
         } else {
             sft = bsel_shift(kmx - kmn);
-            bstar = R.bstar;
-            const int need = k - R.above, inbin = R.inbin;
+            bstar = (int)h1.y;
+            const int need = k - (int)h1.z, inbin = (int)h1.w;
             if (inbin == need) {
                 mode = 2;
                 if (tid == 0) {
                     int bs = 0;
-                    for (int q = 0; q < s; ++q) bs += R.slc[q][0] + R.slc[q][1];
+                    for (int q = 0; q < s; ++q) bs += sh.slc[q][0] + sh.slc[q][1];
                     sh.res[0] = bs;
                 }
             } else {
                 mode = 3;
                 for (int q = tid; q < nsl; q += 256) sh.gtc[q] = sh.eqc[q] = 0;
-                const uint32_t bmn = R.bmn, bmx = R.bmx;
+                const uint32_t bmn = h0.z, bmx = h0.w;
                 if (bmn == bmx) {
                     // every key of the bin ties at the threshold
                     thr = bmn;
-                    for (int q = tid; q < nsl; q += 256) sh.eqc[q] = R.slc[q][1];
+                    for (int q = tid; q < nsl; q += 256) sh.eqc[q] = sh.slc[q][1];
                 } else if (inbin <= BSEL_CAP) {
                     // exact threshold among the candidates (padding keys 0 lie below them)
                     uint32_t ck[BSEL_CAP / 256];
@@ -845,7 +921,7 @@ __global__ __launch_bounds__(256) void k_bsel_out(const DecodeArgs A) {
                         const int at = tid + 256 * i;
                         ck[i] = at < inbin ? R.cand[at][0] : 0u;
                     }
-                    thr = radix_threshold<BSEL_CAP / 256>(sh, ph, 4, ck, bmn, bmx, need);
+                    thr = bsel_cand_threshold(sh, ph, ck, bmn, bmx, need);
                     __syncthreads();
 #pragma unroll
                     for (int i = 0; i < BSEL_CAP / 256; ++i) {
@@ -861,8 +937,7 @@ __global__ __launch_bounds__(256) void k_bsel_out(const DecodeArgs A) {
                     const uint32_t diff = bmn ^ bmx;
                     int bit = 31 - __clz(diff);
                     uint32_t t = bmx & ~((bit == 31) ? 0xFFFFFFFFu : ((2u << bit) - 1u));
-                    const int above = R.above;
-                    int cnt = above + inbin;  // keys >= t (every key of the bin is >= bmn >= t)
+                    int cnt = (int)h1.z + inbin;  // keys >= t (every key of the bin is >= bmn >= t)
                     for (; bit >= 0 && cnt != k; --bit) {
                         const uint32_t cand = t | (1u << bit);
                         const int c = bsel_count_all(A, r, sh, ph, cand);
@@ -889,7 +964,7 @@ __global__ __launch_bounds__(256) void k_bsel_out(const DecodeArgs A) {
                     int bs = 0, mine = 0;
                     for (int q = 0; q <= s; ++q) {
                         const int tq = min(sh.eqc[q], max(left, 0));
-                        if (q < s) bs += R.slc[q][0] + sh.gtc[q] + tq;
+                        if (q < s) bs += sh.slc[q][0] + sh.gtc[q] + tq;
                         else mine = tq;
                         left -= tq;
                     }

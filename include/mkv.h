@@ -250,6 +250,55 @@ mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_
                                   int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t r, void *data_out,
                                   void *meta_out, float *rot_out);
 
+/* Segment strategy generation ([S] 4.3 and 5.5: output caches start a new
+ * segment when the accumulated compression loss exceeds a threshold or at the
+ * maximum length; each segment's strategy holds its rotation and retention;
+ * the loss and the covariance are updated incrementally on the host).
+ * Host-only, synchronous (OpenMP); meant to run beside decode, like the
+ * recompression it feeds.
+ *
+ * Loss of a set of tokens under a strategy (R, r): the energy of the rotated
+ * vectors x' = R x outside each vector's own r largest magnitudes (what the
+ * top-r of [N] Eq. 9 drops), over their total rotated energy, summed over the
+ * KV heads and over keys and values.
+ *
+ * k_host, v_host: host [n_kv_heads][row_stride][d] in `dtype` (f32, or bf16 bit
+ * patterns as uint16); tokens 0 .. n_tokens-1 of each head (row_stride >= n_tokens).
+ * rot, rot0, seg_rot: float32 [n_kv_heads][2][d][d] per strategy (R_k, R_v per
+ * head, rows as mkv_rotation_from_prefill's), applied as stored.
+ *
+ * mkv_strategy_loss_curve: loss_out [d + 1] = the loss for r = 0 .. d of
+ * every token under `rot`. */
+mkv_status mkv_strategy_loss_curve(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
+                                   int32_t n_kv_heads, int64_t n_tokens, int64_t row_stride, const float *rot,
+                                   double *loss_out);
+
+/* mkv_strategy_segments: cut one request's token stream into segments and
+ * give each its strategy. (rot0, r0) is the strategy in force at token 0
+ * (e.g. the previous segment's). A segment ends at a 16-token block boundary
+ * once it holds at least min_len tokens and its loss under the strategy in
+ * force exceeds cut_loss, or when it holds max_len tokens (a positive
+ * multiple of 16; [S] 4.3 uses 64K); the last segment ends with the data.
+ * Each segment then gets, per KV head, R_k and R_v from the Gram matrices of
+ * its own tokens (accumulated while they are scanned; eigenvectors ordered and
+ * signed as in mkv_rotation_from_prefill), and the smallest r in
+ * [r_min, r_max] whose loss under them is at most keep_loss (r_max if none);
+ * that strategy is in force for the next segment ([S] 5.4: the current
+ * segment is compressed with the previous strategy until it is finished).
+ * Outputs (host): seg_end [seg_cap] exclusive end token, seg_r [seg_cap],
+ * seg_rot [seg_cap][n_kv_heads][2][d][d] (nullable), *n_seg. Sums run in
+ * token order per (head, matrix) and combine in a fixed order, so results do
+ * not depend on the thread count.
+ * Errors: MKV_ERR_ARG (sizes, 0 <= r_min <= r_max <= d, 0 <= r0 <= d,
+ * max_len not a positive multiple of 16, NaN thresholds), MKV_ERR_CAPACITY
+ * (more than seg_cap segments: the first seg_cap are written and *n_seg =
+ * seg_cap), MKV_ERR_NOCONVERGE. */
+mkv_status mkv_strategy_segments(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
+                                 int32_t n_kv_heads, int64_t n_tokens, int64_t row_stride, const float *rot0,
+                                 int32_t r0, double cut_loss, double keep_loss, int32_t r_min, int32_t r_max,
+                                 int64_t min_len, int64_t max_len, int64_t seg_cap, int64_t *seg_end,
+                                 int32_t *seg_r, float *seg_rot, int64_t *n_seg);
+
 /* Stream-ordered swap of packed segment `seg` of request b to new device
  * buffers (data, meta, rot: as mkv_segment's, e.g. mkv_recompress_segment's
  * outputs copied to the device), without any host wait: if ready_event (a

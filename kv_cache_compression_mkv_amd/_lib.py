@@ -29,6 +29,7 @@ MKV_SCRATCH_BYTES = 128 << 20
 EXPORTS = ["mkv_status_str", "mkv_rotation_from_prefill", "mkv_segment_bytes", "mkv_compress_append",
            "mkv_block_meta", "mkv_decode_workspace_bytes", "mkv_decode_sel_cols", "mkv_decode_attn",
            "mkv_append_decode", "mkv_decode_attn_noalloc", "mkv_recompress_segment", "mkv_swap_segment",
+           "mkv_strategy_loss_curve", "mkv_strategy_segments",
            "mkv_timing_enable", "mkv_timing_read", "mkv_stage_name"]
 
 
@@ -76,6 +77,11 @@ def _load():
     L.mkv_append_decode.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P, P, P, I64, P, SZ, P]
     L.mkv_recompress_segment.restype = ctypes.c_int
     L.mkv_recompress_segment.argtypes = [P, P, I32, I32, I32, I64, I64, I32, P, P, P]
+    L.mkv_strategy_loss_curve.restype = ctypes.c_int
+    L.mkv_strategy_loss_curve.argtypes = [P, P, I32, I32, I32, I64, I64, P, P]
+    L.mkv_strategy_segments.restype = ctypes.c_int
+    L.mkv_strategy_segments.argtypes = [P, P, I32, I32, I32, I64, I64, P, I32, ctypes.c_double, ctypes.c_double,
+                                        I32, I32, I64, I64, I64, P, P, P, P]
     L.mkv_swap_segment.restype = ctypes.c_int
     L.mkv_swap_segment.argtypes = [ctypes.POINTER(mkv_cache), I32, I32, P, P, P, P, P]
     L.mkv_decode_attn_noalloc.restype = ctypes.c_int
@@ -145,6 +151,47 @@ def mkv_recompress_segment(k_ptr: int, v_ptr: int, dtype: int, d: int, n_kv_head
                            r: int, data_ptr: int, meta_ptr: int, rot_ptr: int):
     _check(LIB.mkv_recompress_segment(k_ptr, v_ptr, dtype, d, n_kv_heads, n_tokens, t_cap, r, data_ptr, meta_ptr,
                                       rot_ptr), "mkv_recompress_segment")
+
+
+def _host_stream(K, V):
+    """(k, v, dtype code, d, n_kv_heads, n_tokens, row_stride) of host arrays [H][n][d]
+    (float32 values, or uint16 bf16 bit patterns)."""
+    import numpy as np
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    if K.shape != V.shape or K.ndim != 3 or K.dtype != V.dtype or K.dtype not in (np.float32, np.uint16):
+        raise ValueError("K and V: equal shapes [H][n][d], float32 or uint16 (bf16 bits)")
+    code = MKV_F32 if K.dtype == np.float32 else MKV_BF16
+    H, n, d = K.shape
+    return K, V, code, d, H, n, n
+
+
+def mkv_strategy_loss_curve(K, V, rot):
+    """Loss for r = 0 .. d of every token under rot [H][2][d][d] (float32)."""
+    import numpy as np
+    K, V, code, d, H, n, stride = _host_stream(K, V)
+    rot = np.ascontiguousarray(rot, dtype=np.float32)
+    out = np.empty(d + 1, np.float64)
+    _check(LIB.mkv_strategy_loss_curve(K.ctypes.data, V.ctypes.data, code, d, H, n, stride, rot.ctypes.data,
+                                       out.ctypes.data), "mkv_strategy_loss_curve")
+    return out
+
+
+def mkv_strategy_segments(K, V, rot0, r0: int, cut_loss: float, keep_loss: float, r_min: int, r_max: int,
+                          min_len: int, max_len: int, seg_cap: int = 1024):
+    """[(end, r, rot [H][2][d][d] float32)] of one request's token stream."""
+    import numpy as np
+    K, V, code, d, H, n, stride = _host_stream(K, V)
+    rot0 = np.ascontiguousarray(rot0, dtype=np.float32)
+    ends = np.zeros(seg_cap, np.int64)
+    rs = np.zeros(seg_cap, np.int32)
+    rots = np.zeros((seg_cap, H, 2, d, d), np.float32)
+    ns = ctypes.c_int64(0)
+    _check(LIB.mkv_strategy_segments(K.ctypes.data, V.ctypes.data, code, d, H, n, stride, rot0.ctypes.data, r0,
+                                     float(cut_loss), float(keep_loss), r_min, r_max, min_len, max_len, seg_cap,
+                                     ends.ctypes.data, rs.ctypes.data, rots.ctypes.data, ctypes.byref(ns)),
+           "mkv_strategy_segments")
+    return [(int(ends[i]), int(rs[i]), rots[i]) for i in range(ns.value)]
 
 
 def mkv_swap_segment(cache: mkv_cache, b: int, seg: int, data_ptr: int, meta_ptr: int, rot_ptr: int, event,

@@ -13,7 +13,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 HIP_SOURCES = ["compress.hip", "decode.hip", "noalloc.hip"]
-HOST_SOURCES = ["mkv_host.cpp", "rotation.cpp", "recompress.cpp"]
+HOST_SOURCES = ["mkv_host.cpp", "rotation.cpp", "recompress.cpp", "strategy.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # no packed-fp32 instructions anywhere in the device code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -15,16 +15,23 @@
 #include <vector>
 
 #include "../../include/mkv.h"
+#include "host_la.h"
 
-namespace {
+namespace mkv {
 
-double elem(const void *x, int32_t dtype, int64_t i) {
+double host_elem(const void *x, int32_t dtype, int64_t i) {
     if (dtype == MKV_F32) return (double)static_cast<const float *>(x)[i];
     uint32_t u = (uint32_t) static_cast<const uint16_t *>(x)[i] << 16;
     float f;
     memcpy(&f, &u, 4);
     return (double)f;
 }
+
+}  // namespace mkv
+
+namespace {
+
+using mkv::host_elem;
 
 // Upper triangle of X^T X, X given row-major [T][d] in the storage dtype.
 // The tokens are cut into GRAM_PARTS contiguous ranges of whole 64-token
@@ -51,7 +58,7 @@ void gram(const void *x, int32_t dtype, int64_t T, int d, std::vector<double> &G
                 const int64_t t0 = ci * chunk;
                 const int64_t n = std::min<int64_t>(chunk, T - t0);
                 for (int64_t t = 0; t < n; ++t)
-                    for (int c = 0; c < d; ++c) xt[(size_t)c * chunk + t] = elem(x, dtype, (t0 + t) * d + c);
+                    for (int c = 0; c < d; ++c) xt[(size_t)c * chunk + t] = host_elem(x, dtype, (t0 + t) * d + c);
                 for (int i = 0; i < d; ++i) {
                     const double *xi = &xt[(size_t)i * chunk];
                     for (int j = i; j < d; ++j) {
@@ -165,16 +172,8 @@ bool tridiag_qr(int n, std::vector<double> &a, std::vector<double> &b, std::vect
 
 }  // namespace
 
-extern "C" mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtype, int64_t T, int32_t d,
-                                                float *R_out, double *sigma_out) {
-    if (!R_out || d < 1 || d > 256 || T < 0 || (T > 0 && !x_host)) return MKV_ERR_ARG;
-    if (dtype != MKV_F32 && dtype != MKV_BF16) return MKV_ERR_ARG;
-    std::vector<double> G, a, b, Q;
-    if (T > 0) {
-        gram(x_host, dtype, T, d, G);
-    } else {
-        G.assign((size_t)d * d, 0.0);
-    }
+mkv_status mkv::rotation_from_gram(std::vector<double> &G, int d, float *R_out, double *sigma_out) {
+    std::vector<double> a, b, Q;
     tridiagonalize(d, G, a, b, Q);
     if (!tridiag_qr(d, a, b, Q)) return MKV_ERR_NOCONVERGE;
     std::vector<int> order(d);
@@ -190,4 +189,17 @@ extern "C" mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtyp
         if (sigma_out) sigma_out[c] = sqrt(a[col] > 0.0 ? a[col] : 0.0);
     }
     return MKV_OK;
+}
+
+extern "C" mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtype, int64_t T, int32_t d,
+                                                float *R_out, double *sigma_out) {
+    if (!R_out || d < 1 || d > 256 || T < 0 || (T > 0 && !x_host)) return MKV_ERR_ARG;
+    if (dtype != MKV_F32 && dtype != MKV_BF16) return MKV_ERR_ARG;
+    std::vector<double> G;
+    if (T > 0) {
+        gram(x_host, dtype, T, d, G);
+    } else {
+        G.assign((size_t)d * d, 0.0);
+    }
+    return mkv::rotation_from_gram(G, d, R_out, sigma_out);
 }

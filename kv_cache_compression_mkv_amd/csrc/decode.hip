@@ -1871,8 +1871,13 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
 }
 
 // QA < QB: packed segments with ceil(r / 4) <= QA run the QA code, the others QB
+// Occupancy floor: 4 waves per SIMD for bf16 records; fp32 windows are twice
+// as wide and fit 3 (2 at r > 64).
+template <typename ST, int QB>
+constexpr int attend_min_waves() { return ST::bytes == 2 ? 4 : (QB > 16 ? 2 : 3); }
+
 template <typename ST, int G, int QA, int QB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_attend(const DecodeArgs A) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_min_waves<ST, QB>(), 8))) void k_attend(const DecodeArgs A) {
     const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
     const int b = A.b0 + bl;
     // wave-uniform: the split bounds and their 64-bit arithmetic stay scalar

@@ -107,7 +107,8 @@ def union_summary(w, lengths, sel):
                 blocks = sel[b, g * G:(g + 1) * G, col:col + k]
                 uni += len(np.unique(blocks))
             col += k
-            rows.append(dict(kind="packed", filled=filled, r=s["r"], n_blocks=nb, union=uni))
+            rows.append(dict(kind="packed", filled=filled, r=s["r"], n_blocks=nb, union=uni,
+                             bitmap=s["kind"] == synth.BITMAP))
         out.append(rows)
     return out
 
@@ -242,6 +243,8 @@ def main():
                                                                  "(-1: half of --cpu-steps)")
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct layer caches visited round-robin (keeps every call cache-cold)")
+    ap.add_argument("--layout", choices=["u8", "bitmap"], default="u8",
+                    help="position format of the packed records: u8 channel indices (default) or bitmaps")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a streaming scale kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -253,6 +256,8 @@ def main():
     K_steps, W_steps = args.steps, args.warmup
     cap_extra = W_steps + 2 * K_steps + 64
     w = workload(args.config, args.scale, cap_extra)
+    if args.layout == "bitmap":
+        w["segs"] = synth.as_bitmap(w["segs"])
     T0 = np.asarray(w["lengths"], np.int64)
     B, hq, hkv, d, dt = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["d"], w["dtype"]
     n_step_total = W_steps + 2 * K_steps + 1
@@ -355,8 +360,8 @@ def main():
     summ = union_summary(w, lens_now, sel.cpu().numpy())
     sb = 2 if dt == "bf16" else 4
     call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
-    r_new = [s["r"] for s in w["segs"][0] if s["kind"] == synth.PACKED][-1]
-    append = bm.append_bytes(d, sb, hkv, B, r_new)
+    r_new = [s["r"] for s in w["segs"][0] if synth.is_packed(s["kind"])][-1]
+    append = bm.append_bytes(d, sb, hkv, B, r_new, args.layout == "bitmap")
     step_bytes = call["total"] + append
     # algorithmic bytes each kernel of the step must move (the query rotation
     # runs in the append's launch: it reads R_k and the queries, writes q')
@@ -442,6 +447,7 @@ def main():
             "seq_len": int(T0.max()),
             "segments": seg_desc,
             "storage": dt,
+            "record_positions": "bitmap" if args.layout == "bitmap" else "u8 indices",
             "parallelism": "single GPU",
             "layer_caches": n_layers,
         },

@@ -57,7 +57,7 @@ typedef enum {
 } mkv_status;
 
 typedef enum { MKV_F32 = 0, MKV_BF16 = 1 } mkv_dtype;
-typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1 } mkv_seg_kind;
+typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1, MKV_SEG_BITMAP = 2 } mkv_seg_kind;
 
 /* One segment of one request ([S] 4.1, 4.3: the cache is split into segments,
  * each with its own channel retention and block retention).
@@ -65,7 +65,12 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1 } mkv_seg_kind;
  * kind      MKV_SEG_DENSE: tokens are rotated and stored at full width and are
  *           always attended (attention-sink and recent-window segments).
  *           MKV_SEG_PACKED: tokens keep their own r largest rotated elements
- *           ([N] Eq. 9) and blocks are chosen per query head by top-k.
+ *           ([N] Eq. 9) and blocks are chosen per query head by top-k; each
+ *           kept element's position is a u8 channel index.
+ *           MKV_SEG_BITMAP: the same, with each vector's kept positions held
+ *           as a d-bit bitmap ([S] 5.1: a position bitmap instead of per-element
+ *           indices; one bit per channel). "Packed" below means either kind;
+ *           the packed segments of one cache all use the same one.
  * r         kept elements per vector, 1..head_dim (packed only).
  * keep_ppm  block keep ratio in parts per million, 1..1000000 (packed only);
  *           k = ceil(keep_ppm * n_blocks / 1e6) in integers, clamped to [1, n].
@@ -94,6 +99,11 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1 } mkv_seg_kind;
  *                K values [16][r] | V values [16][r] | K indices [16][r] u8 |
  *                V indices [16][r] u8; each vector's kept channels in ascending
  *                channel order. Slots of a block past its last token are zero.
+ *   bitmap data: [n_kv_heads][nb][record], record of 16 * r * 2 * s + 2 * 16 * d / 8
+ *                bytes = K values [16][r] | V values [16][r] | K bitmaps [16][d / 8] |
+ *                V bitmaps [16][d / 8]; bit c % 8 of byte c / 8 of a vector's
+ *                bitmap is set iff channel c is kept; values in ascending channel
+ *                order, as above.
  *                MKV_PACKED_TAIL_BYTES follow the last record: decode reads
  *                whole dwords around each record's fields and may touch them
  *                (their contents are never used, nothing writes them).
@@ -239,7 +249,8 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
  * k_host, v_host: [n_kv_heads][n_tokens][d] in `dtype` (f32 values or bf16
  *   bit patterns), n_tokens in 1..t_cap.
  * Outputs in the documented device layouts, in host memory the caller owns:
- *   data_out [mkv_segment_bytes(dtype, MKV_SEG_PACKED, r, d, n_kv_heads, t_cap)]
+ * kind: the segment's record format, MKV_SEG_PACKED or MKV_SEG_BITMAP.
+ *   data_out [mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap)]
  *     (slots after the last token zero; the tail bytes are left as they are),
  *   meta_out [that call's meta bytes] (blocks past the last one zero),
  *   rot_out float32 [n_kv_heads][2][d][d].
@@ -247,8 +258,8 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
  * MKV_BF16, r in 1..d. Errors: MKV_ERR_ARG, MKV_ERR_UNSUPPORTED,
  * MKV_ERR_NOCONVERGE. */
 mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
-                                  int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t r, void *data_out,
-                                  void *meta_out, float *rot_out);
+                                  int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t kind, int32_t r,
+                                  void *data_out, void *meta_out, float *rot_out);
 
 /* Segment strategy generation ([S] 4.3 and 5.5: output caches start a new
  * segment when the accumulated compression loss exceeds a threshold or at the

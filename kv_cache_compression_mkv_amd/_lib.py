@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmkv.so")
 MKV_OK, MKV_ERR_ARG, MKV_ERR_UNSUPPORTED, MKV_ERR_CAPACITY, MKV_ERR_WORKSPACE, MKV_ERR_NOCONVERGE, \
     MKV_ERR_HIP = range(7)
 MKV_F32, MKV_BF16 = 0, 1
-MKV_SEG_DENSE, MKV_SEG_PACKED = 0, 1
+MKV_SEG_DENSE, MKV_SEG_PACKED, MKV_SEG_BITMAP = 0, 1, 2
 MKV_BLOCK_TOKENS = 16
 MKV_HEAD_DIM = 128
 MKV_MAX_GROUP = 4
@@ -76,7 +76,7 @@ def _load():
     L.mkv_append_decode.restype = ctypes.c_int
     L.mkv_append_decode.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P, P, P, I64, P, SZ, P]
     L.mkv_recompress_segment.restype = ctypes.c_int
-    L.mkv_recompress_segment.argtypes = [P, P, I32, I32, I32, I64, I64, I32, P, P, P]
+    L.mkv_recompress_segment.argtypes = [P, P, I32, I32, I32, I64, I64, I32, I32, P, P, P]
     L.mkv_strategy_loss_curve.restype = ctypes.c_int
     L.mkv_strategy_loss_curve.argtypes = [P, P, I32, I32, I32, I64, I64, P, P]
     L.mkv_strategy_segments.restype = ctypes.c_int
@@ -148,9 +148,9 @@ def mkv_append_decode(cache: mkv_cache, k_ptr: int, v_ptr: int, n_new_ptr: int, 
 
 
 def mkv_recompress_segment(k_ptr: int, v_ptr: int, dtype: int, d: int, n_kv_heads: int, n_tokens: int, t_cap: int,
-                           r: int, data_ptr: int, meta_ptr: int, rot_ptr: int):
-    _check(LIB.mkv_recompress_segment(k_ptr, v_ptr, dtype, d, n_kv_heads, n_tokens, t_cap, r, data_ptr, meta_ptr,
-                                      rot_ptr), "mkv_recompress_segment")
+                           kind: int, r: int, data_ptr: int, meta_ptr: int, rot_ptr: int):
+    _check(LIB.mkv_recompress_segment(k_ptr, v_ptr, dtype, d, n_kv_heads, n_tokens, t_cap, kind, r, data_ptr,
+                                      meta_ptr, rot_ptr), "mkv_recompress_segment")
 
 
 def _host_stream(K, V):

@@ -87,7 +87,7 @@ class Cache:
         k = np.ascontiguousarray(k_host)
         v = np.ascontiguousarray(v_host)
         L.mkv_recompress_segment(k.ctypes.data, v.ctypes.data, self.code, self.d, self.hkv, int(k.shape[1]),
-                                 s["t_cap"], s["r"], data.ctypes.data, meta.ctypes.data, rot.ctypes.data)
+                                 s["t_cap"], s["kind"], s["r"], data.ctypes.data, meta.ctypes.data, rot.ctypes.data)
         return data, meta, rot
 
     def swap_segment(self, b: int, j: int, data, meta, rot, copy_stream=None):

@@ -291,7 +291,7 @@ struct BlockJob {
     char *meta_tile;
     const typename ST::bits_t *xin;
     int p0, sa, se, r, G16, cpg;
-    bool packed, do_meta;
+    bool packed, bitmap, do_meta;
     uint32_t mn0, mx0, mn1, mx1;
     typename ST::bits_t x0, x1;  // row of the first new token (lane's channels; one-token appends)
 };
@@ -306,19 +306,21 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     const int sa = max(E.a, p0) - p0;
     const int se = min(E.e, p0 + BT) - p0;
     const bits_t *xin = reinterpret_cast<const bits_t *>(wave ? A.v_new : A.k_new) + unit * A.n_max * D;
-    const bool packed = E.kind == MKV_SEG_PACKED;
+    const bool packed = packed_kind(E.kind);
+    const bool bitmap = E.kind == MKV_SEG_BITMAP;
     const int r = E.r;
     char *blkbase;
     if (packed) {
-        const size_t rec = (size_t)BT * r * 2 * (ST::bytes + 1);
+        const size_t rec = (size_t)record_bytes(E.kind, r, ST::bytes);
         blkbase = static_cast<char *>(E.data) + ((size_t)g * E.nbcap + blk) * rec;
     } else {
         blkbase = static_cast<char *>(E.data) + ((size_t)g * E.nbcap + blk) * 2 * BT * D * ST::bytes;
     }
     bits_t *vals = packed ? reinterpret_cast<bits_t *>(blkbase + (size_t)wave * BT * r * ST::bytes)
                           : reinterpret_cast<bits_t *>(blkbase + (size_t)wave * BT * D * ST::bytes);
+    // u8 indices [16][r], or bitmaps [16][D / 8], of this matrix
     uint8_t *idxs = packed ? reinterpret_cast<uint8_t *>(blkbase + (size_t)2 * BT * r * ST::bytes +
-                                                         (size_t)wave * BT * r)
+                                                         (size_t)wave * BT * (bitmap ? D / 8 : r))
                            : nullptr;
 
     // per-block keys (keys wave, packed segments): running totalOrder min/max
@@ -362,6 +364,7 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     J.G16 = G16;
     J.cpg = cpg;
     J.packed = packed;
+    J.bitmap = bitmap;
     J.do_meta = do_meta;
     J.mn0 = mn0; J.mx0 = mx0; J.mn1 = mn1; J.mx1 = mx1;
     J.x0 = x0;
@@ -381,16 +384,19 @@ __device__ __forceinline__ void store_kept(BlockJob<ST> &J, int slot, double v0,
         const uint64_t m0 = ballot(keep0), m1 = ballot(keep1);
         const uint64_t below = lanes_below(lane);
         bits_t *vrow = J.vals + (size_t)slot * J.r;
-        uint8_t *irow = J.idxs + (size_t)slot * J.r;
-        if (keep0) {
-            const int pos = popc64(m0 & below);
-            vrow[pos] = s0;
-            irow[pos] = (uint8_t)lane;
-        }
-        if (keep1) {
-            const int pos = popc64(m0) + popc64(m1 & below);
-            vrow[pos] = s1;
-            irow[pos] = (uint8_t)(lane + 64);
+        if (keep0) vrow[popc64(m0 & below)] = s0;
+        if (keep1) vrow[popc64(m0) + popc64(m1 & below)] = s1;
+        if (J.bitmap) {
+            // bit c of the vector's bitmap: channel c kept (channels lane and lane + 64 of the ballots)
+            if (lane == 0) {
+                uint64_t *brow = reinterpret_cast<uint64_t *>(J.idxs + (size_t)slot * (D / 8));
+                brow[0] = m0;
+                brow[1] = m1;
+            }
+        } else {
+            uint8_t *irow = J.idxs + (size_t)slot * J.r;
+            if (keep0) irow[popc64(m0 & below)] = (uint8_t)lane;
+            if (keep1) irow[popc64(m0) + popc64(m1 & below)] = (uint8_t)(lane + 64);
         }
         if (J.do_meta) {
             const uint32_t q0 = order_key<ST>(keep0 ? s0 : (bits_t)0);
@@ -420,10 +426,9 @@ __device__ __forceinline__ void block_finish(const BlockJob<ST> &J, int blk, int
     using bits_t = typename ST::bits_t;
     if (J.sa == 0 && J.se < BT) {
         if (J.packed) {
-            for (int i = J.se * J.r + lane; i < BT * J.r; i += 64) {
-                J.vals[i] = (bits_t)0;
-                J.idxs[i] = 0;
-            }
+            for (int i = J.se * J.r + lane; i < BT * J.r; i += 64) J.vals[i] = (bits_t)0;
+            const int ib = J.bitmap ? D / 8 : J.r;  // position bytes per vector
+            for (int i = J.se * ib + lane; i < BT * ib; i += 64) J.idxs[i] = 0;
         } else {
             for (int i = J.se * D + lane; i < BT * D; i += 64) J.vals[i] = (bits_t)0;
         }
@@ -643,7 +648,8 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
     const int g = (int)blockIdx.y;
     const int lane = lane_id();
     const int r = E.r;
-    const size_t rec = (size_t)BT * r * 2 * (ST::bytes + 1);
+    const bool bitmap = E.kind == MKV_SEG_BITMAP;
+    const size_t rec = (size_t)record_bytes(E.kind, r, ST::bytes);
     const char *base = static_cast<const char *>(E.data) + ((size_t)g * E.nbcap + blk) * rec;
     const bits_t *kv = reinterpret_cast<const bits_t *>(base);
     const uint8_t *ki = reinterpret_cast<const uint8_t *>(base + (size_t)2 * BT * r * ST::bytes);
@@ -651,15 +657,27 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
     __shared__ bits_t row[D];
     uint32_t mn0 = 0xFFFFFFFFu, mx0 = 0u, mn1 = 0xFFFFFFFFu, mx1 = 0u;
     for (int t = 0; t < nvalid; ++t) {
-        row[lane] = 0;
-        row[lane + 64] = 0;
-        wave_lds_sync();
-        for (int m = lane; m < r; m += 64) row[ki[t * r + m] & (D - 1)] = kv[t * r + m];
-        wave_lds_sync();
-        const uint32_t q0 = order_key<ST>(row[lane]), q1 = order_key<ST>(row[lane + 64]);
+        bits_t v0, v1;
+        if (bitmap) {
+            // channel c is the rank(c)-th kept element of the token
+            const uint64_t *bm = reinterpret_cast<const uint64_t *>(ki + (size_t)t * (D / 8));
+            const uint64_t m0 = bm[0], m1 = bm[1];
+            const uint64_t below = lanes_below(lane);
+            v0 = ((m0 >> lane) & 1ull) ? kv[t * r + popc64(m0 & below)] : (bits_t)0;
+            v1 = ((m1 >> lane) & 1ull) ? kv[t * r + popc64(m0) + popc64(m1 & below)] : (bits_t)0;
+        } else {
+            row[lane] = 0;
+            row[lane + 64] = 0;
+            wave_lds_sync();
+            for (int m = lane; m < r; m += 64) row[ki[t * r + m] & (D - 1)] = kv[t * r + m];
+            wave_lds_sync();
+            v0 = row[lane];
+            v1 = row[lane + 64];
+            wave_lds_sync();
+        }
+        const uint32_t q0 = order_key<ST>(v0), q1 = order_key<ST>(v1);
         mn0 = min(mn0, q0); mx0 = max(mx0, q0);
         mn1 = min(mn1, q1); mx1 = max(mx1, q1);
-        wave_lds_sync();
     }
     const int G16 = 2 * D * ST::bytes / 16;
     const int cpg = 16 / (2 * ST::bytes);

@@ -1211,15 +1211,17 @@ __device__ __forceinline__ void load_words(const char *p, uint32_t (&w)[N]) {
 template <int N>
 constexpr int load_instrs() { return N / 4 + (N % 4 ? 1 : 0); }
 
-// One record's windows for one lane.
-template <typename ST, int QM>
+// One record's windows for one lane. Bitmap records (BM) carry the token's
+// K and V position bitmaps instead of the u8 index windows.
+template <typename ST, int QM, bool BM>
 struct PkWin {
     // values: a bf16 window may start 2 bytes before the lane's first element
     static constexpr int NV = ST::bytes == 2 ? (2 * QM + 5) / 4 : QM;
     // indices: the window may start up to 3 bytes early
     static constexpr int NI = (QM + 6) / 4;
-    static constexpr int LOADS = 2 * load_instrs<NV>() + 2 * load_instrs<NI>();
+    static constexpr int LOADS = 2 * load_instrs<NV>() + (BM ? 2 : 2 * load_instrs<NI>());
     uint32_t kv[NV], vv[NV], ki[NI], vi[NI];
+    uint4 bk, bv;
 };
 
 // Per-lane constants of one packed segment.
@@ -1227,6 +1229,8 @@ template <typename ST, int QM>
 struct PkGeom {
     uint32_t o_kv, o_vv, o_ki, o_vi;  // window offsets in the record
     uint32_t sv, si;                  // byte shifts of the value / index windows
+    uint32_t o_bk, o_bv;              // bitmap records: the token's K and V bitmaps
+    uint32_t l_ki, l_vi;              // bitmap records: index windows in the wave's LDS index buffer
     int cnt;                          // elements of this lane's part
     int row;                          // t * 128: this token's tile row
     __device__ __forceinline__ void init(int r) {
@@ -1243,16 +1247,47 @@ struct PkGeom {
         o_vv = reg + o_kv;
         o_ki = 2 * reg + (e0 & ~3u);
         o_vi = o_ki + (uint32_t)BT * r;
+        o_bk = 2 * reg + (uint32_t)t * (D / 8);
+        o_bv = o_bk + (uint32_t)BT * (D / 8);
+        l_ki = e0 & ~3u;
+        l_vi = l_ki + (uint32_t)BT * r;
         row = t * D;
     }
 };
 
-template <typename ST, int QM>
-__device__ __forceinline__ void load_win(const char *rec, const PkGeom<ST, QM> &gm, PkWin<ST, QM> &W) {
+template <typename ST, int QM, bool BM>
+__device__ __forceinline__ void load_win(const char *rec, const PkGeom<ST, QM> &gm, PkWin<ST, QM, BM> &W) {
     load_words(rec + gm.o_kv, W.kv);
     load_words(rec + gm.o_vv, W.vv);
-    load_words(rec + gm.o_ki, W.ki);
-    load_words(rec + gm.o_vi, W.vi);
+    if constexpr (BM) {
+        W.bk = *reinterpret_cast<const uint4 *>(rec + gm.o_bk);
+        W.bv = *reinterpret_cast<const uint4 *>(rec + gm.o_bv);
+    } else {
+        load_words(rec + gm.o_ki, W.ki);
+        load_words(rec + gm.o_vi, W.vi);
+    }
+}
+
+// Bitmap records: lane p of a token writes the channels of the set bits of
+// word p of the token's bitmap b (channels 32 p .. 32 p + 31) to dst, at their
+// ranks among the token's kept elements, so dst holds the token's u8 indices
+// in ascending channel order.
+__device__ __forceinline__ void bitmap_positions(const uint4 b, int p, uint8_t *dst) {
+    const int c0 = __popc(b.x), c1 = __popc(b.y), c2 = __popc(b.z);
+    uint32_t w = p == 0 ? b.x : p == 1 ? b.y : p == 2 ? b.z : b.w;
+    int pos = (p > 0 ? c0 : 0) + (p > 1 ? c1 : 0) + (p > 2 ? c2 : 0);
+    while (w) {
+        dst[pos++] = (uint8_t)(32 * p + __builtin_ctz(w));
+        w &= w - 1u;
+    }
+}
+
+// N dwords from the wave's LDS index buffer (4-byte aligned)
+template <int N>
+__device__ __forceinline__ void lds_words(const uint8_t *p, uint32_t (&w)[N]) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = q[i];
 }
 
 // Per-wave LDS of the packed path: the dense V tile; row 16 absorbs masked writes.
@@ -1348,25 +1383,45 @@ __device__ __forceinline__ uint32_t win_word(const uint32_t (&w)[NV], int k, uin
     else return w[k];
 }
 
-template <typename ST, int G, int QM, int WAITN>
-__device__ __forceinline__ void pk_proc(const PkWin<ST, QM> &W, const PkGeom<ST, QM> &gm, int hm, int nv,
-                                        const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S) {
+template <typename ST, int G, int QM, int WAITN, bool BM>
+__device__ __forceinline__ void pk_proc(const PkWin<ST, QM, BM> &W, const PkGeom<ST, QM> &gm, int hm, int nv,
+                                        const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S, uint8_t *ib,
+                                        int r) {
     const int lane = lane_id();
     vm_wait<WAITN>();
+    constexpr int NI = PkWin<ST, QM, BM>::NI;
+    uint32_t wki[NI], wvi[NI];
+    if constexpr (BM) {
+        // the record's u8 indices, decoded from its bitmaps into the wave's
+        // LDS buffer ([16][r] K then [16][r] V), then read as index windows
+        const int t = lane >> 2, p = lane & 3;
+        bitmap_positions(W.bk, p, ib + t * r);
+        bitmap_positions(W.bv, p, ib + BT * r + t * r);
+        wave_lds_sync();
+        lds_words(ib + gm.l_ki, wki);
+        lds_words(ib + gm.l_vi, wvi);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+            wki[k] = W.ki[k];
+            wvi[k] = W.vi[k];
+        }
+    }
     // indices: element j = byte j of the aligned index words
     constexpr int NIW = (QM + 3) / 4;
     uint32_t ki[NIW], vi[NIW];
 #pragma unroll
     for (int k = 0; k < NIW; ++k) {
-        ki[k] = __builtin_amdgcn_alignbyte(W.ki[k + 1], W.ki[k], gm.si);
-        vi[k] = __builtin_amdgcn_alignbyte(W.vi[k + 1], W.vi[k], gm.si);
+        ki[k] = __builtin_amdgcn_alignbyte(wki[k + 1], wki[k], gm.si);
+        vi[k] = __builtin_amdgcn_alignbyte(wvi[k + 1], wvi[k], gm.si);
     }
     // ---- V scatter first: its LDS writes drain while K is computed
 #pragma unroll
     for (int j = 0; j < QM; ++j) {
         // past the lane's part the index byte belongs to other data: such
         // writes go to the lane's own slot of the dummy row
-        const int c = (int)((vi[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+        // (bitmap records: bytes of tokens past the block's last one are stale, so masked to a channel)
+        const int c = (int)((vi[j >> 2] >> (8 * (j & 3))) & (BM ? (uint32_t)(D - 1) : 0xFFu));
         const int at = j < gm.cnt ? gm.row + c : BT * D + lane;
         if constexpr (ST::bytes == 2) {
             const uint32_t w = win_word<ST>(W.vv, j >> 1, gm.sv);
@@ -1419,13 +1474,14 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM> &W, const PkGeom<ST,
 // record load is a scalar base plus loop-invariant per-lane offsets
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <typename ST, int G, int QM>
+template <typename ST, int G, int QM, bool BM>
 __device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_base, size_t rec, int r,
-                                       int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S) {
+                                       int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S,
+                                       uint8_t *ib) {
     PkGeom<ST, QM> gm;
     gm.init(r);
-    constexpr int WN = PkWin<ST, QM>::LOADS;
-    PkWin<ST, QM> B0, B1;
+    constexpr int WN = PkWin<ST, QM, BM>::LOADS;
+    PkWin<ST, QM, BM> B0, B1;
     // a load past the end of the list repeats its last record, so every step
     // has exactly one record in flight behind the one it computes
     auto at = [&](int i) {
@@ -1435,24 +1491,26 @@ __device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_
     load_win(at(0), gm, B0);
     for (int i = 0; i < n; i += 2) {
         load_win(at(i + 1), gm, B1);
-        pk_proc<ST, G, QM, WN>(B0, gm, uniform_int(list[i].y), nv_of(i), qsh, L, S);
+        pk_proc<ST, G, QM, WN, BM>(B0, gm, uniform_int(list[i].y), nv_of(i), qsh, L, S, ib, r);
         if (i + 1 >= n) break;
         load_win(at(i + 2), gm, B0);
-        pk_proc<ST, G, QM, WN>(B1, gm, uniform_int(list[i + 1].y), nv_of(i + 1), qsh, L, S);
+        pk_proc<ST, G, QM, WN, BM>(B1, gm, uniform_int(list[i + 1].y), nv_of(i + 1), qsh, L, S, ib, r);
     }
 }
 
 // the records of one packed segment, with the windows code of their r
-template <typename ST, int G, int QA, int QB>
+// (BM: the cache's packed segments hold bitmap records; ib is the wave's LDS
+// index buffer for them)
+template <typename ST, int G, int QA, int QB, bool BM>
 __device__ __forceinline__ void run_records(const int2 *list, int n, const char *seg_base, size_t rec, int r,
                                             int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L,
-                                            PkState<G> &S) {
-    if (((r + 3) >> 2) <= QA) pk_run<ST, G, QA>(list, n, seg_base, rec, r, filled, qsh, L, S);
-    else pk_run<ST, G, QB>(list, n, seg_base, rec, r, filled, qsh, L, S);
+                                            PkState<G> &S, uint8_t *ib) {
+    if (((r + 3) >> 2) <= QA) pk_run<ST, G, QA, BM>(list, n, seg_base, rec, r, filled, qsh, L, S, ib);
+    else pk_run<ST, G, QB, BM>(list, n, seg_base, rec, r, filled, qsh, L, S, ib);
 }
 
-__device__ __forceinline__ int64_t packed_weight(int r, int sb, int G) {
-    const int64_t rec = (int64_t)BT * r * 2 * (sb + 1);
+__device__ __forceinline__ int64_t packed_weight(int kind, int r, int sb, int G) {
+    const int64_t rec = record_bytes(kind, r, sb);
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
 }
 
@@ -1618,10 +1676,10 @@ __device__ __forceinline__ void attend_dense_split(const DecodeArgs &A, int bl, 
 }
 
 // packed split s of S_p: an equal share (by bytes) of the unit's union records
-template <typename ST, int G, int QA, int QB>
+template <typename ST, int G, int QA, int QB, bool BM>
 __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl, int b, int g, int s,
                                                     const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list,
-                                                    float *dst) {
+                                                    float *dst, uint8_t *ib) {
     constexpr int sb = ST::bytes;
     const int lane = lane_id();
     for (int i = lane; i < BT * D; i += 64) (&L.vt[0][0])[i] = 0;
@@ -1630,17 +1688,18 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
     int64_t W = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &Sg = seg_of(A, bl, si);
-        if (Sg.kind == MKV_SEG_PACKED && Sg.slot == A.cur_slot) W += (int64_t)G * Sg.k * packed_weight(Sg.r, sb, G);
+        if (packed_kind(Sg.kind) && Sg.slot == A.cur_slot)
+            W += (int64_t)G * Sg.k * packed_weight(Sg.kind, Sg.r, sb, G);
     }
     const int64_t lo = W * s / A.S_p, hi = W * (s + 1) / A.S_p;
     int64_t Wb = 0;
     int pj = 0;
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &Sg = seg_of(A, bl, si);
-        if (Sg.kind != MKV_SEG_PACKED) continue;
+        if (!packed_kind(Sg.kind)) continue;
         const int myj = pj++;
         if (Sg.slot != A.cur_slot) continue;
-        const int64_t w = packed_weight(Sg.r, sb, G);
+        const int64_t w = packed_weight(Sg.kind, Sg.r, sb, G);
         const int64_t items = (int64_t)G * Sg.k;
         int64_t i0 = lo - Wb, i1 = hi - Wb;
         i0 = i0 <= 0 ? 0 : (i0 + w - 1) / w;
@@ -1650,7 +1709,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
         Wb += items * w;
         if (i0 >= i1) continue;
         const int r = Sg.r;
-        const size_t rec = (size_t)BT * r * 2 * (sb + 1);
+        const size_t rec = (size_t)record_bytes(Sg.kind, r, sb);
         const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
         const int kc = A.kcap[myj];
         const int32_t *sel = A.sel + A.sl_off[myj] + ((size_t)b * A.hq + g * G) * kc;
@@ -1674,7 +1733,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
             if (keep) list[popc64(km & lanes_below(lane))] = make_int2(blk, hm);
             const int n = popc64(km);
             wave_lds_sync();
-            if (n > 0) run_records<ST, G, QA, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+            if (n > 0) run_records<ST, G, QA, QB, BM>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S, ib);
             wave_lds_sync();
         }
     }
@@ -1755,11 +1814,12 @@ __device__ __forceinline__ int union_entry(uint32_t pos, uint32_t Wb, uint32_t w
 }
 
 // Weighted positions stay below 2^32 / 4: at most 4 segments x 4096 records
-// x (16 r 2 (s + 1) + UNION_RECORD_FIXED <= 20480 + 16384) bytes.
-template <typename ST, int G, int QA, int QB>
+// x (record bytes + UNION_RECORD_FIXED <= 20480 + 16384) bytes (bitmap records
+// are at most 16896 bytes).
+template <typename ST, int G, int QA, int QB, bool BM>
 __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl, int b, int g, int xs, int wave,
                                                     const float (*qsh)[2 * D], PkLds<ST, G> &L, int2 *list,
-                                                    float *dst, UnionLds &U) {
+                                                    float *dst, UnionLds &U, uint8_t *ib) {
     constexpr int sb = ST::bytes;
     const int lane = lane_id();
     const int npk = A.npk;
@@ -1771,7 +1831,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
         const DSeg &Sg = seg_of(A, bl, A.pseg[min(j, npk - 1)]);
         nbj[j] = (j < npk && Sg.slot == A.cur_slot) ? Sg.nb : 0;
         rj[j] = Sg.r;
-        wj[j] = (uint32_t)(BT * Sg.r * 2 * (sb + 1) + UNION_RECORD_FIXED);
+        wj[j] = (uint32_t)(record_bytes(Sg.kind, Sg.r, sb) + UNION_RECORD_FIXED);
     }
     uint32_t w[UNION_MAX_SEGS][16];
 #pragma unroll
@@ -1851,7 +1911,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
         if (v0 >= v1) continue;
         const DSeg &Sg = seg_of(A, bl, A.pseg[j]);
         const int r = rj[j];
-        const size_t rec = (size_t)BT * r * 2 * (sb + 1);
+        const size_t rec = (size_t)record_bytes(Sg.kind, r, sb);
         const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
         for (int base = v0; base < v1; base += 64) {
             // (the host bounds the workgroup's entries by UNION_CAP; the clamp
@@ -1863,7 +1923,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
                 list[lane] = make_int2((int)(e & 0xFFFFu), (int)(e >> 16));
             }
             wave_lds_sync();
-            run_records<ST, G, QA, QB>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S);
+            run_records<ST, G, QA, QB, BM>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S, ib);
             wave_lds_sync();
         }
     }
@@ -1872,12 +1932,19 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
 
 // QA < QB: packed segments with ceil(r / 4) <= QA run the QA code, the others QB
 // Occupancy floor: 4 waves per SIMD for bf16 records; fp32 windows are twice
-// as wide and fit 3 (2 at r > 64).
-template <typename ST, int QB>
-constexpr int attend_min_waves() { return ST::bytes == 2 ? 4 : (QB > 16 ? 2 : 3); }
+// as wide and fit 3 (2 at r > 64). Bitmap launches hold 4 KB more LDS per
+// wave: 3 workgroups per CU (bf16), 2 (fp32).
+template <typename ST, int QB, bool BM>
+constexpr int attend_min_waves() {
+    return BM ? (ST::bytes == 2 ? 3 : 2) : (ST::bytes == 2 ? 4 : (QB > 16 ? 2 : 3));
+}
 
-template <typename ST, int G, int QA, int QB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_min_waves<ST, QB>(), 8))) void k_attend(const DecodeArgs A) {
+// BM: the cache's packed segments hold bitmap records (each wave then has a
+// 4 KB LDS index buffer)
+constexpr int BM_IDX_BYTES = 2 * BT * D + 64;
+
+template <typename ST, int G, int QA, int QB, bool BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_min_waves<ST, QB, BM>(), 8))) void k_attend(const DecodeArgs A) {
     const int bl = (int)blockIdx.z, g = (int)blockIdx.y;
     const int b = A.b0 + bl;
     // wave-uniform: the split bounds and their 64-bit arithmetic stay scalar
@@ -1888,6 +1955,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_min_
     __shared__ __align__(16) float qsh[G][2 * D];
     __shared__ __align__(16) PkLds<ST, G> lds[4];
     __shared__ int2 lists[4][64];
+    __shared__ __align__(16) uint8_t bmi[BM ? 4 : 1][BM ? BM_IDX_BYTES : 16];
     for (int i = (int)threadIdx.x; i < G * 2 * D; i += 256) {
         const int h = i / (2 * D), c = i % (2 * D);
         qsh[h][c] = c < D ? A.qa[(((size_t)b * A.nslot + A.cur_slot) * A.hq + g * G + h) * D + c] : 0.f;
@@ -1902,9 +1970,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_min_
     const int s = xs * 4 + wave;
     if (packed && A.union_mode) {
         __shared__ UnionLds U;
-        attend_packed_union<ST, G, QA, QB>(A, bl, b, g, xs, wave, qsh, lds[wave], lists[wave], mine, U);
+        attend_packed_union<ST, G, QA, QB, BM>(A, bl, b, g, xs, wave, qsh, lds[wave], lists[wave], mine, U,
+                                               BM ? bmi[wave] : nullptr);
     } else if (s < S) {
-        if (packed) attend_packed_split<ST, G, QA, QB>(A, bl, b, g, s, qsh, lds[wave], lists[wave], mine);
+        if (packed)
+            attend_packed_split<ST, G, QA, QB, BM>(A, bl, b, g, s, qsh, lds[wave], lists[wave], mine,
+                                                   BM ? bmi[wave] : nullptr);
         else attend_dense_split<ST, G>(A, bl, g, s, qsh, lds[wave].zb[0], mine);
     }
     __syncthreads();
@@ -2132,12 +2203,17 @@ hipError_t launch_merge(const DecodeArgs &a, int G, hipStream_t s) {
 
 template <typename ST, int G>
 void attend_launch(const DecodeArgs &a, int qmax, dim3 grid, hipStream_t s) {
-#define MKV_PK(QA, QB) hipLaunchKernelGGL((k_attend<ST, G, QA, QB>), grid, dim3(256), 0, s, a)
-    if (qmax <= 4) MKV_PK(4, 4);
-    else if (qmax <= 8) MKV_PK(4, 8);
-    else if (qmax <= 10) MKV_PK(8, 10);
-    else if (qmax <= 16) MKV_PK(10, 16);
-    else MKV_PK(16, 32);
+#define MKV_PK(QA, QB, BM) hipLaunchKernelGGL((k_attend<ST, G, QA, QB, BM>), grid, dim3(256), 0, s, a)
+    if (a.has_bitmap) {  // bitmap records: two window shapes
+        if (qmax <= 10) MKV_PK(8, 10, true);
+        else MKV_PK(16, 32, true);
+        return;
+    }
+    if (qmax <= 4) MKV_PK(4, 4, false);
+    else if (qmax <= 8) MKV_PK(4, 8, false);
+    else if (qmax <= 10) MKV_PK(8, 10, false);
+    else if (qmax <= 16) MKV_PK(10, 16, false);
+    else MKV_PK(16, 32, false);
 #undef MKV_PK
 }
 

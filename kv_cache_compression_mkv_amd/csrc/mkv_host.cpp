@@ -115,11 +115,15 @@ mkv_status check_cache(const mkv_cache *c) {
         for (int j = 0; j < c->n_segments; ++j) {
             const mkv_segment &s = segof(c, b, j);
             const mkv_segment &s0 = segof(c, 0, j);
-            if (s.kind != MKV_SEG_DENSE && s.kind != MKV_SEG_PACKED) return MKV_ERR_ARG;
+            if (s.kind != MKV_SEG_DENSE && !packed_kind(s.kind)) return MKV_ERR_ARG;
             if (s.t_begin != t || s.t_cap < 1 || !s.data) return MKV_ERR_ARG;
             if (s.kind != s0.kind || s.r != s0.r || s.keep_ppm != s0.keep_ppm || s.k_abs != s0.k_abs)
                 return MKV_ERR_ARG;
-            if (s.kind == MKV_SEG_PACKED) {
+            if (packed_kind(s.kind)) {
+                // one position format per cache (u8 indices or bitmaps)
+                for (int jj = 0; jj < j; ++jj)
+                    if (packed_kind(segof(c, 0, jj).kind) && segof(c, 0, jj).kind != s.kind) return MKV_ERR_ARG;
+                if (s.kind == MKV_SEG_BITMAP && c->head_dim != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
                 if (s.r < 1 || s.r > c->head_dim || !s.meta || s.k_abs < 0) return MKV_ERR_ARG;
                 if (s.k_abs == 0 && (s.keep_ppm < 1 || s.keep_ppm > 1000000)) return MKV_ERR_ARG;
                 if (ceil_div(s.t_cap, BT) > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
@@ -174,7 +178,7 @@ WsMap ws_map(const mkv_cache *c) {
     m.nslot = rot_slots(c, m.slot_of);
     const size_t NS = (size_t)m.nslot;
     for (int j = 0; j < c->n_segments; ++j) {
-        if (segof(c, 0, j).kind != MKV_SEG_PACKED) continue;
+        if (!packed_kind(segof(c, 0, j).kind)) continue;
         int64_t nbc = 0;
         for (int b = 0; b < c->batch; ++b) nbc = std::max<int64_t>(nbc, ceil_div(segof(c, b, j).t_cap, BT));
         const mkv_segment &s = segof(c, 0, j);
@@ -225,7 +229,7 @@ int64_t sel_cols_now(const mkv_cache *c) {
         int64_t s = 0;
         for (int j = 0; j < c->n_segments; ++j) {
             const mkv_segment &sg = segof(c, b, j);
-            if (sg.kind != MKV_SEG_PACKED) continue;
+            if (!packed_kind(sg.kind)) continue;
             s += keep_blocks(ceil_div(seg_filled(c, b, j), BT), sg.keep_ppm, sg.k_abs);
         }
         best = std::max(best, s);
@@ -345,8 +349,8 @@ void plan_splits(DecodeArgs &A, const mkv_cache *c, int slot, int G, int sb, int
         for (int j = 0; j < c->n_segments; ++j) {
             const DSeg &D_ = A.seg[i * c->n_segments + j];
             if (D_.slot != slot) continue;
-            if (D_.kind == MKV_SEG_PACKED) {
-                const int64_t rec = (int64_t)BT * D_.r * 2 * (sb + 1);
+            if (packed_kind(D_.kind)) {
+                const int64_t rec = record_bytes(D_.kind, D_.r, sb);
                 W += (int64_t)G * D_.k * ((G > 1 ? rec * 4 / 5 : rec) + 256);
                 max_nb = std::max(max_nb, D_.nb);
             } else {
@@ -357,7 +361,7 @@ void plan_splits(DecodeArgs &A, const mkv_cache *c, int slot, int G, int sb, int
         Dmax = std::max(Dmax, Dn);
     }
     for (int j = 0; j < c->n_segments; ++j)
-        if (A.seg[j].kind == MKV_SEG_PACKED && A.seg[j].slot == slot) ++npk_slot;
+        if (packed_kind(A.seg[j].kind) && A.seg[j].slot == slot) ++npk_slot;
     // splits of about 96 KB of packed and 128 KB of dense reads each: both
     // kinds fit one round of resident waves with room to spare (measured
     // on the 128K workload: 88-104 KB packed splits are the fastest; 64 KB
@@ -377,9 +381,9 @@ void plan_splits(DecodeArgs &A, const mkv_cache *c, int slot, int G, int sb, int
             int64_t u = 0;
             for (int j = 0; j < c->n_segments; ++j) {
                 const DSeg &D_ = A.seg[i * c->n_segments + j];
-                if (D_.kind != MKV_SEG_PACKED || D_.slot != slot) continue;
+                if (!packed_kind(D_.kind) || D_.slot != slot) continue;
                 u += std::min<int64_t>((int64_t)G * D_.k, D_.nb);
-                const int64_t w = (int64_t)BT * D_.r * 2 * (sb + 1) + UNION_RECORD_FIXED;
+                const int64_t w = record_bytes(D_.kind, D_.r, sb) + UNION_RECORD_FIXED;
                 wmin = std::min(wmin, w);
                 wmax = std::max(wmax, w);
             }
@@ -454,7 +458,7 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                 D_.filled = (int32_t)seg_filled(c, b0 + i, j);
                 D_.nb = (int32_t)ceil_div(D_.filled, BT);
                 D_.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
-                if (sg.kind == MKV_SEG_PACKED) {
+                if (packed_kind(sg.kind)) {
                     D_.k = (int32_t)keep_blocks(D_.nb, sg.keep_ppm, sg.k_abs);
                     max_tiles = std::max(max_tiles, (int)ceil_div(D_.nb, META_TILE));
                     max_r = std::max(max_r, (int)sg.r);
@@ -494,6 +498,9 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
         for (int slot = 0; slot < m.nslot; ++slot) {
             DecodeArgs As = A;
             As.cur_slot = slot;
+            As.has_bitmap = 0;
+            for (int j = 0; j < c->n_segments; ++j)
+                if (segof(c, 0, j).kind == MKV_SEG_BITMAP) As.has_bitmap = 1;
             plan_splits(As, c, slot, G, sb, m.npk);
             if ((As.S_d + 3) / 4 + (As.S_p + 3) / 4 > MAX_PARTS) return MKV_ERR_UNSUPPORTED;  // (never: S_d + S_p <= 256)
             A.nparts[slot] = (As.S_d + 3) / 4 + (As.S_p + 3) / 4;
@@ -530,12 +537,12 @@ size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int3
     const size_t s = elem_bytes(dtype);
     const size_t nb = (size_t)ceil_div(t_cap, BT);
     if (kind == MKV_SEG_DENSE) return (size_t)n_kv_heads * nb * 2 * BT * d * s;
-    if (kind != MKV_SEG_PACKED || r < 1 || r > d) return 0;
+    if (!packed_kind(kind) || r < 1 || r > d || (kind == MKV_SEG_BITMAP && d != D)) return 0;
     if (meta_bytes_out) {
         const size_t ntile = ceil_div((int64_t)nb, META_TILE);
         *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * d * s;
     }
-    return (size_t)n_kv_heads * nb * BT * r * 2 * (s + 1) + MKV_PACKED_TAIL_BYTES;
+    return (size_t)n_kv_heads * nb * record_bytes(kind, r, s) + MKV_PACKED_TAIL_BYTES;
 }
 
 mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
@@ -551,7 +558,7 @@ mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_ne
 mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
     mkv_status st = check_cache(c);
     if (st != MKV_OK) return st;
-    if (seg < 0 || seg >= c->n_segments || segof(c, 0, seg).kind != MKV_SEG_PACKED) return MKV_ERR_ARG;
+    if (seg < 0 || seg >= c->n_segments || !packed_kind(segof(c, 0, seg).kind)) return MKV_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int b0 = 0; b0 < c->batch; b0 += TABLE) {
         MetaArgs A;
@@ -568,6 +575,7 @@ mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
             E.r = sg.r;
             E.b = b0 + i;
             E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
+            E.kind = sg.kind;
             max_nb = std::max(max_nb, E.nb);
         }
         A.n_ent = n;
@@ -584,7 +592,7 @@ mkv_status mkv_swap_segment(mkv_cache *c, int32_t b, int32_t seg, void *data, vo
     if (st != MKV_OK) return st;
     if (b < 0 || b >= c->batch || seg < 0 || seg >= c->n_segments) return MKV_ERR_ARG;
     mkv_segment &sg = c->segs[(size_t)b * c->n_segments + seg];
-    if (sg.kind != MKV_SEG_PACKED || !data || !meta || !rot) return MKV_ERR_ARG;
+    if (!packed_kind(sg.kind) || !data || !meta || !rot) return MKV_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(data) & 15) || (reinterpret_cast<uintptr_t>(meta) & 15) ||
         (reinterpret_cast<uintptr_t>(rot) & 15))
         return MKV_ERR_ARG;

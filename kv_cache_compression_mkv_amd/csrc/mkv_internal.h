@@ -16,6 +16,13 @@ constexpr int D = MKV_HEAD_DIM;
 constexpr int BT = MKV_BLOCK_TOKENS;
 constexpr int TABLE = 64;       // (request, segment) entries per launch
 constexpr int META_TILE = 64;   // blocks per meta tile
+
+// packed segments of either position format
+__host__ __device__ constexpr bool packed_kind(int kind) { return kind == MKV_SEG_PACKED || kind == MKV_SEG_BITMAP; }
+// bytes of one packed block record (values, then u8 indices or bitmaps)
+__host__ __device__ constexpr int64_t record_bytes(int kind, int r, int sb) {
+    return (int64_t)BT * r * 2 * sb + (kind == MKV_SEG_BITMAP ? (int64_t)2 * BT * (D / 8) : (int64_t)2 * BT * r);
+}
 constexpr int MAX_SPLITS = 256; // attention splits per (request, KV head)
 // Partials per (request, query head): one per attend workgroup of 4 splits.
 // With S_d + S_p <= MAX_SPLITS there are ceil(S_d / 4) + ceil(S_p / 4) <= 65.
@@ -67,7 +74,7 @@ static_assert(sizeof(CompressArgs) <= 4096, "kernel arguments stay below 4 KB");
 struct MetaEntry {
     const void *data;
     void *meta;
-    int32_t filled, nb, r, b, nbcap, pad;
+    int32_t filled, nb, r, b, nbcap, kind;
 };  // 40 bytes
 
 struct MetaArgs {
@@ -145,6 +152,7 @@ struct DecodeArgs {
     int64_t tm_off[MKV_MAX_SEGMENTS];
     int32_t big_row[MKV_MAX_SEGMENTS];  // -1: packed j never takes the sliced select (nbcap <= BIG_SEL_MIN)
     int32_t bsel_slices;                // slices of the launch's largest sliced segment (0: none)
+    int32_t has_bitmap;                 // attend: the cache's packed segments hold bitmap records
 };
 
 static_assert(sizeof(DSeg) == 48, "decode segment layout");

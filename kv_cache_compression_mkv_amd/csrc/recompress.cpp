@@ -76,17 +76,21 @@ uint32_t order_key(uint32_t v, int s) {
 }  // namespace
 
 extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
-                                             int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t r,
-                                             void *data_out, void *meta_out, float *rot_out) {
+                                             int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t kind,
+                                             int32_t r, void *data_out, void *meta_out, float *rot_out) {
     if (!k_host || !v_host || !data_out || !meta_out || !rot_out || n_kv_heads < 1 || t_cap < 1 || n_tokens < 1 ||
-        n_tokens > t_cap || r < 1 || r > d)
+        n_tokens > t_cap || r < 1 || r > d || (kind != MKV_SEG_PACKED && kind != MKV_SEG_BITMAP))
         return MKV_ERR_ARG;
     if (d != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
     if (dtype != MKV_F32 && dtype != MKV_BF16) return MKV_ERR_UNSUPPORTED;
     if ((t_cap + BT - 1) / BT > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
     const int s = dtype == MKV_BF16 ? 2 : 4;
     const int64_t nbcap = (t_cap + BT - 1) / BT, nb = (n_tokens + BT - 1) / BT;
-    const int64_t rec = (int64_t)BT * r * 2 * (s + 1);
+    const bool bitmap = kind == MKV_SEG_BITMAP;
+    // record: K values, V values, then K and V positions (u8 indices [16][r]
+    // each, or 16-byte bitmaps [16] each)
+    const int64_t pos_bytes = bitmap ? (int64_t)BT * (d / 8) : (int64_t)BT * r;
+    const int64_t rec = (int64_t)BT * r * 2 * s + 2 * pos_bytes;
     const int64_t ntile = (nbcap + 63) / 64;
     const int ng = 2 * d * s / 16, cpg = d / ng;  // meta 16-byte groups per block, channels per group
     const int64_t mhead = ntile * ng * 64 * 16;
@@ -140,8 +144,8 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
                         std::copy(order.begin(), order.begin() + r, kept.begin());
                         std::sort(kept.begin(), kept.end());
                         char *vals = blk + (size_t)kv * BT * r * s + (size_t)slot * r * s;
-                        uint8_t *idx = reinterpret_cast<uint8_t *>(blk + (size_t)2 * BT * r * s + (size_t)kv * BT * r +
-                                                                   (size_t)slot * r);
+                        uint8_t *pos = reinterpret_cast<uint8_t *>(blk + (size_t)2 * BT * r * s + kv * pos_bytes +
+                                                                   (size_t)slot * (bitmap ? d / 8 : r));
                         uint32_t stored[MKV_HEAD_DIM] = {0};
                         for (int m = 0; m < r; ++m) {
                             const int c = kept[m];
@@ -152,7 +156,8 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
                             } else {
                                 memcpy(vals + (size_t)m * 4, &bits, 4);
                             }
-                            idx[m] = (uint8_t)c;
+                            if (bitmap) pos[c / 8] |= (uint8_t)(1u << (c % 8));
+                            else pos[m] = (uint8_t)c;
                             stored[c] = bits;
                         }
                         if (kv == 0)

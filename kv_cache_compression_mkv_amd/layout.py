@@ -32,6 +32,46 @@ def unpack_packed(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str):
                 kidx=ki, vidx=vi)
 
 
+def record_bytes(kind: int, r: int, dtype: str, d: int = 128) -> int:
+    """Bytes of one packed block record (kind 1: u8 indices, kind 2: bitmaps)."""
+    s = 2 if dtype == "bf16" else 4
+    return BT * r * 2 * s + (2 * BT * (d // 8) if kind == 2 else 2 * BT * r)
+
+
+def unpack_bitmap(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, d: int = 128):
+    """Bitmap records -> the fields of unpack_packed (indices are the set bits in
+    ascending order, 0-padded after a vector's last set bit) plus the bitmaps
+    as booleans [hkv][nbcap][16][d] (kbm, vbm)."""
+    s = 2 if dtype == "bf16" else 4
+    rec = record_bytes(2, r, dtype, d)
+    a = np.ascontiguousarray(data, np.uint8)[:hkv * nbcap * rec].reshape(hkv, nbcap, rec)
+    kb, kv = _vals(np.ascontiguousarray(a[:, :, :BT * r * s]).reshape(-1), dtype)
+    vb, vv = _vals(np.ascontiguousarray(a[:, :, BT * r * s:2 * BT * r * s]).reshape(-1), dtype)
+    nbm = BT * (d // 8)
+    def bits(x):
+        return np.unpackbits(np.ascontiguousarray(x).reshape(hkv, nbcap, BT, d // 8), axis=-1,
+                             bitorder="little").astype(bool)
+    kbm = bits(a[:, :, 2 * BT * r * s:2 * BT * r * s + nbm])
+    vbm = bits(a[:, :, 2 * BT * r * s + nbm:2 * BT * r * s + 2 * nbm])
+    def idx(bm):
+        out = np.zeros(bm.shape[:3] + (r,), np.uint8)
+        ch = np.arange(d)
+        for pos in np.ndindex(*bm.shape[:3]):
+            sel = ch[bm[pos]][:r]
+            out[pos][:sel.size] = sel
+        return out
+    shp = (hkv, nbcap, BT, r)
+    return dict(kval=kv.reshape(shp), vval=vv.reshape(shp), kbits=kb.reshape(shp), vbits=vb.reshape(shp),
+                kidx=idx(kbm), vidx=idx(vbm), kbm=kbm, vbm=vbm)
+
+
+def unpack_records(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, kind: int, d: int = 128):
+    """unpack_packed or unpack_bitmap by segment kind."""
+    if kind == 2:
+        return unpack_bitmap(data, hkv, nbcap, r, dtype, d)
+    return unpack_packed(data, hkv, nbcap, r, dtype)
+
+
 def unpack_dense(data: np.ndarray, hkv: int, nbcap: int, dtype: str, d: int = 128):
     """-> (values float64, bits), each [hkv][nbcap][2][16][d]."""
     bits, vals = _vals(np.ascontiguousarray(data, np.uint8).reshape(-1), dtype)

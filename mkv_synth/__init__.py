@@ -36,7 +36,17 @@ N_SPIKES = 4
 SPIKE = 6.0
 
 DENSE = 0
-PACKED = 1
+PACKED = 1   # packed records with u8 channel indices
+BITMAP = 2   # packed records with per-vector position bitmaps
+
+
+def is_packed(kind) -> bool:
+    return kind in (PACKED, BITMAP)
+
+
+def as_bitmap(segs):
+    """The same segment table with every packed segment holding bitmap records."""
+    return [[dict(s, kind=BITMAP) if s["kind"] == PACKED else dict(s) for s in row] for row in segs]
 
 
 # ----------------------------------------------------------------------------

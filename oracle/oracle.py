@@ -20,7 +20,7 @@ _SO = os.path.join(_HERE, "liboracle.so")
 _LIB = None
 
 DTYPES = {"f32": 0, "bf16": 1, "f64": 2}
-DENSE, PACKED = 0, 1
+DENSE, PACKED, BITMAP = 0, 1, 2  # BITMAP: packed, positions stored as bitmaps (same kept set)
 BLOCK = 16
 
 
@@ -118,7 +118,7 @@ def block_keep(n: int, keep_ppm: int, k_abs: int) -> int:
 
 
 def _seg_arrays(segs):
-    kind = _c([s["kind"] for s in segs], np.int32)
+    kind = _c([DENSE if s["kind"] == DENSE else PACKED for s in segs], np.int32)
     tb = _c([s["t_begin"] for s in segs], np.int64)
     cap = _c([s["t_cap"] for s in segs], np.int64)
     r = _c([s["r"] for s in segs], np.int32)
@@ -131,7 +131,7 @@ def seg_blocks(segs, length: int, block: int = BLOCK):
     """Per packed segment: (n_blocks, k) at the given request length."""
     out = []
     for s in segs:
-        if s["kind"] != PACKED:
+        if s["kind"] == DENSE:
             continue
         filled = min(max(length - s["t_begin"], 0), s["t_cap"])
         nb = -(-filled // block)
@@ -165,7 +165,7 @@ def compress_unit(Kraw, Vraw, Rk, Rv, segs, length: int, dtype: str, block: int 
     d = Kraw.shape[1]
     Rk, Rv = _c(Rk, np.float64), _c(Rv, np.float64)
     kind, tb, cap, r, keep, kabs = _seg_arrays(segs)
-    nbcaps = [-(-s["t_cap"] // block) for s in segs if s["kind"] == PACKED]
+    nbcaps = [-(-s["t_cap"] // block) for s in segs if s["kind"] != DENSE]
     if state is None:
         rows = max(Kraw.shape[0], length, 1)
         st = dict(Khat=np.zeros((rows, d)), Vhat=np.zeros((rows, d)), Kidx=np.full((rows, d), -1, np.int16),

@@ -136,11 +136,19 @@ def compare_compress(cache, w, comp, b, g, length):
                 assert np.all(bits[0, nb - 1, :, filled % 16:] == 0)
             continue
         r = s["r"]
-        rec = 16 * r * 2 * (sb + 1)
-        P = layout.unpack_packed(_head_bytes(cache.data[b][j], g, nbcap * rec), 1, nbcap, r, dt)
+        rec = layout.record_bytes(s["kind"], r, dt, d)
+        P = layout.unpack_records(_head_bytes(cache.data[b][j], g, nbcap * rec), 1, nbcap, r, dt, s["kind"], d)
         for hat, idx, gbits, gidx, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
                                             (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
             ei = idx[tb:tb + filled, :r].astype(np.int64)
+            if s["kind"] == synth.BITMAP:
+                # the bitmap holds exactly the kept channels, and nothing past the last token
+                ebm = np.zeros((nbcap * 16, d), bool)
+                np.put_along_axis(ebm[:filled], ei, True, axis=1)
+                gbm = P[name.lower() + "bm"][0].reshape(nbcap * 16, d)
+                bad = _first_bad(np.all(gbm[:filled] == ebm[:filled], axis=1), tb)
+                assert bad is None, "%s bitmap b=%d g=%d seg=%d t=%d" % (name, b, g, j, bad)
+                assert not gbm[filled:nb * 16].any(), "%s bitmap padding b=%d g=%d seg=%d" % (name, b, g, j)
             gi = gidx[0].reshape(nbcap * 16, r)[:filled].astype(np.int64)
             bad = _first_bad(np.all(gi == ei, axis=1), tb)
             assert bad is None, "%s idx b=%d g=%d seg=%d t=%d: %s vs %s" % (
@@ -214,7 +222,7 @@ def check_decode_unit(w, comp, Rk, Rv, q_unit, out_gpu, sel_gpu_unit, tol, lengt
 
 def _pidx(segs, j):
     """Index of segment j among the packed segments."""
-    return sum(1 for s in segs[:j] if s["kind"] == synth.PACKED)
+    return sum(1 for s in segs[:j] if synth.is_packed(s["kind"]))
 
 
 def compare_packed_blocks(cache, w, comp, b, g, j, blocks, length):
@@ -227,12 +235,12 @@ def compare_packed_blocks(cache, w, comp, b, g, j, blocks, length):
     s = w["segs"][b][j]
     r, tb = s["r"], s["t_begin"]
     nbcap = -(-s["t_cap"] // 16)
-    rec = 16 * r * 2 * (sb + 1)
+    rec = layout.record_bytes(s["kind"], r, dt, d)
     filled = min(max(length - tb, 0), s["t_cap"])
     data = cache.data[b][j]
     for l in blocks:
         off = (g * nbcap + l) * rec
-        P = layout.unpack_packed(data[off:off + rec].cpu().numpy(), 1, 1, r, dt)
+        P = layout.unpack_records(data[off:off + rec].cpu().numpy(), 1, 1, r, dt, s["kind"], d)
         nv = min(16, filled - 16 * l)
         for hat, idx, gb, gi, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
                                        (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
@@ -271,14 +279,15 @@ class Snapshot:
         s = w["segs"][b][j]
         nbcap = -(-s["t_cap"] // 16)
         out = set()
-        if s["kind"] == synth.PACKED:
-            per = 16 * s["r"] * 2 * (sb + 1)
+        if synth.is_packed(s["kind"]):
+            from kv_cache_compression_mkv_amd import layout
+            per = layout.record_bytes(s["kind"], s["r"], dt, d)
         else:
             per = 2 * 16 * d * sb
         for off in self._diff(cache.data[b][j], self.data[b][j]):
             g, rem = divmod(int(off), nbcap * per)
             out.add((g, rem // per) if g < hkv else (-1, -1))
-        if s["kind"] == synth.PACKED:
+        if synth.is_packed(s["kind"]):
             ntile = -(-nbcap // 64)
             tile_bytes = (2 * d * sb // 16) * 64 * 16
             for off in self._diff(cache.meta[b][j], self.meta[b][j]):

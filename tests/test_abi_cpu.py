@@ -51,6 +51,14 @@ def test_segment_bytes(L):
     assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_PACKED, 129, 128, 8, 100)[0] == 0
     assert L.mkv_segment_bytes(7, L.MKV_SEG_DENSE, 0, 128, 8, 100)[0] == 0
     assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_DENSE, 0, 128, 8, 0)[0] == 0
+    # bitmap records: the values, then one 16-byte position bitmap per vector
+    data, meta = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_BITMAP, 38, 128, 8, 63456)
+    assert data == 8 * 3966 * (2 * 16 * 38 * 2 + 2 * 16 * 16) + L.MKV_PACKED_TAIL_BYTES
+    assert meta == 8 * 62 * 64 * 512
+    data, meta = L.mkv_segment_bytes(L.MKV_F32, L.MKV_SEG_BITMAP, 128, 128, 1, 17)
+    assert data == 2 * (2 * 16 * 128 * 4 + 2 * 16 * 16) + L.MKV_PACKED_TAIL_BYTES and meta == 64 * 1024
+    assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_BITMAP, 8, 64, 8, 100)[0] == 0  # 128 channels only
+    assert L.mkv_segment_bytes(L.MKV_BF16, 3, 8, 128, 8, 100)[0] == 0
 
 
 class FakeCache:
@@ -67,7 +75,7 @@ class FakeCache:
                 e.kind, e.r, e.keep_ppm, e.k_abs = s["kind"], s["r"], s["keep_ppm"], s["k_abs"]
                 e.t_begin, e.t_cap = s["t_begin"], s["t_cap"]
                 e.data = 0x10000 * (1 + b * n + j)
-                e.meta = 0x90000000 + 0x10000 * (b * n + j) if s["kind"] == 1 else None
+                e.meta = 0x90000000 + 0x10000 * (b * n + j) if s["kind"] in (1, 2) else None
         self.c = L.mkv_cache(batch, hq, hkv, d, L.MKV_BF16 if dtype is None else dtype, n,
                              ctypes.cast(self.arr, ctypes.POINTER(L.mkv_segment)),
                              ctypes.cast(self.len, ctypes.POINTER(ctypes.c_int64)), 0x5000000)
@@ -112,6 +120,26 @@ def test_invalid_descriptors_are_rejected(L):
     # too many blocks in one packed segment
     big = [synth.seg(1, 0, 16 * 65537, 32, 40000, 0)]
     assert L.mkv_decode_workspace_bytes(FakeCache(L, big).c) == 0
+
+
+def test_bitmap_descriptors(L):
+    """A cache may use either packed record format, but only one of them."""
+    segs = _segs_cfg2()
+    bm = synth.as_bitmap([segs])[0]
+    assert [s["kind"] for s in bm] == [L.MKV_SEG_DENSE, L.MKV_SEG_BITMAP, L.MKV_SEG_DENSE]
+    f = FakeCache(L, bm, lengths=[32768])
+    assert L.mkv_decode_workspace_bytes(f.c) > 0
+    assert L.mkv_decode_sel_cols(f.c) == 198  # the same blocks as the u8-index layout
+    # mixed packed formats in one cache are rejected
+    two = [synth.seg(synth.DENSE, 0, 64), synth.seg(synth.PACKED, 64, 1024, 32, 100000, 0),
+           synth.seg(synth.BITMAP, 1088, 1024, 32, 100000, 0)]
+    assert L.mkv_decode_workspace_bytes(FakeCache(L, two, lengths=[1500]).c) == 0
+    two[1]["kind"] = synth.BITMAP
+    assert L.mkv_decode_workspace_bytes(FakeCache(L, two, lengths=[1500]).c) > 0
+    # an unknown kind
+    bad = [dict(s) for s in segs]
+    bad[1]["kind"] = 3
+    assert L.mkv_decode_workspace_bytes(FakeCache(L, bad).c) == 0
 
 
 def test_calls_fail_before_any_launch(L):

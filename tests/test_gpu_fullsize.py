@@ -51,7 +51,7 @@ def check_index_properties(c, w):
     for b in range(w["batch"]):
         L = c.lengths[b]
         for j, s in enumerate(w["segs"][b]):
-            if s["kind"] != synth.PACKED:
+            if not synth.is_packed(s["kind"]):
                 continue
             filled = min(max(L - s["t_begin"], 0), s["t_cap"])
             if filled == 0:

@@ -2,7 +2,7 @@
 the oracle, on the CPU: the library computes each KV head's own rotation from
 the segment's vectors and re-packs the segment; the oracle, compressing the
 same raw vectors with that segment rotation, must store the same bits --
-indices, values, zero slots and blocks, and block keys."""
+indices (or position bitmaps), values, zero slots and blocks, and block keys."""
 import numpy as np
 import pytest
 
@@ -21,8 +21,10 @@ def _bits(v, dtype):
     return (f.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else f.view(np.uint32)
 
 
-@pytest.mark.parametrize("dtype,r,n,cap", [("bf16", 26, 500, 520), ("bf16", 38, 1024, 1024), ("f32", 32, 333, 400)])
-def test_recompress_matches_oracle(L, dtype, r, n, cap):
+@pytest.mark.parametrize("dtype,r,n,cap,kind", [("bf16", 26, 500, 520, 1), ("bf16", 38, 1024, 1024, 1),
+                                                ("f32", 32, 333, 400, 1), ("bf16", 38, 500, 520, 2),
+                                                ("f32", 17, 333, 400, 2)])
+def test_recompress_matches_oracle(L, dtype, r, n, cap, kind):
     from kv_cache_compression_mkv_amd import layout
     hkv, d = 2, 128
     code = L.MKV_BF16 if dtype == "bf16" else L.MKV_F32
@@ -32,15 +34,18 @@ def test_recompress_matches_oracle(L, dtype, r, n, cap):
     for g in range(hkv):
         synth.gen_kv_into(7, 0, g, 0, 1000, 1000 + n, dtype, K[g], d)
         synth.gen_kv_into(7, 0, g, 1, 1000, 1000 + n, dtype, V[g], d)
-    nbytes, mbytes = L.mkv_segment_bytes(code, L.MKV_SEG_PACKED, r, d, hkv, cap)
+    nbytes, mbytes = L.mkv_segment_bytes(code, kind, r, d, hkv, cap)
     data = np.full(nbytes, 0xAB, np.uint8)
     meta = np.full(mbytes, 0xCD, np.uint8)
     rot = np.empty((hkv, 2, d, d), np.float32)
-    L.mkv_recompress_segment(K.ctypes.data, V.ctypes.data, code, d, hkv, n, cap, r, data.ctypes.data,
+    L.mkv_recompress_segment(K.ctypes.data, V.ctypes.data, code, d, hkv, n, cap, kind, r, data.ctypes.data,
                              meta.ctypes.data, rot.ctypes.data)
     nbcap, nb = -(-cap // 16), -(-n // 16)
-    s = 2 if dtype == "bf16" else 4
-    P = layout.unpack_packed(data, hkv, nbcap, r, dtype)
+    P = layout.unpack_records(data, hkv, nbcap, r, dtype, kind, d)
+    if kind == L.MKV_SEG_BITMAP:  # exactly r positions per stored vector, none in empty slots
+        for bm in (P["kbm"], P["vbm"]):
+            cnt = bm.sum(axis=-1).reshape(hkv, -1)
+            assert np.all(cnt[:, :n] == r) and np.all(cnt[:, n:] == 0)
     _, mbits = layout.unpack_meta(meta, hkv, nbcap, dtype, d)
     to64 = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if dtype == "bf16" else \
         (lambda a: a.astype(np.float64))
@@ -62,18 +67,24 @@ def test_recompress_matches_oracle(L, dtype, r, n, cap):
         assert np.array_equal(mbits[g, :nb], _bits(comp["meta"][0], dtype))
         assert np.all(mbits[g, nb:] == 0)
     # the tail bytes after the last record are not written
-    assert np.all(data[hkv * nbcap * 16 * r * 2 * (s + 1):] == 0xAB)
+    assert np.all(data[hkv * nbcap * layout.record_bytes(kind, r, dtype, d):] == 0xAB)
 
 
 def test_recompress_rejects_bad_arguments(L):
     buf = np.zeros(16, np.uint8)
+    P = L.MKV_SEG_PACKED
     with pytest.raises(L.MkvError):
-        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 0, 16, 8, buf.ctypes.data,
+        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 0, 16, P, 8, buf.ctypes.data,
                                  buf.ctypes.data, buf.ctypes.data)
     with pytest.raises(L.MkvError):
-        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 17, 16, 8, buf.ctypes.data,
+        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 17, 16, P, 8, buf.ctypes.data,
                                  buf.ctypes.data, buf.ctypes.data)
+    for kind in (L.MKV_SEG_DENSE, 3):  # not a packed record format
+        with pytest.raises(L.MkvError) as e:
+            L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 128, 1, 4, 16, kind, 8,
+                                     buf.ctypes.data, buf.ctypes.data, buf.ctypes.data)
+        assert e.value.status == L.MKV_ERR_ARG
     with pytest.raises(L.MkvError) as e:
-        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 64, 1, 4, 16, 8, buf.ctypes.data,
+        L.mkv_recompress_segment(buf.ctypes.data, buf.ctypes.data, L.MKV_BF16, 64, 1, 4, 16, P, 8, buf.ctypes.data,
                                  buf.ctypes.data, buf.ctypes.data)
     assert e.value.status == L.MKV_ERR_UNSUPPORTED

@@ -186,9 +186,15 @@ def gen_q(cfg: int, it: int, batch: int, n_q_heads: int, dtype: str, d: int = HE
 # ----------------------------------------------------------------------------
 # workload layouts
 # ----------------------------------------------------------------------------
-def seg(kind, t_begin, t_cap, r=0, keep_ppm=0, k_abs=0):
+def seg(kind, t_begin, t_cap, r=0, keep_ppm=0, k_abs=0, key_ch=0):
+    """key_ch: leading rotated channels covered by a packed segment's block keys (0: all)."""
     return dict(kind=kind, t_begin=int(t_begin), t_cap=int(t_cap), r=int(r),
-                keep_ppm=int(keep_ppm), k_abs=int(k_abs))
+                keep_ppm=int(keep_ppm), k_abs=int(k_abs), key_ch=int(key_ch))
+
+
+def with_key_channels(segs, key_ch: int):
+    """The same segment table with every packed segment's block keys over key_ch channels."""
+    return [[dict(s, key_ch=int(key_ch)) if is_packed(s["kind"]) else dict(s) for s in row] for row in segs]
 
 
 def _stack(parts):

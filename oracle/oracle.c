@@ -29,7 +29,11 @@
  *   - top-r ranks unrounded |x'|, ties to the lower channel, stored ascending;
  *   - per-block min/max over the sparse-reconstructed stored keys (0 at dropped
  *     channels), min/max taken in IEEE totalOrder (-0 < +0);
- *   - block score (1/sqrt(d)) sum_c max(q'_c mx_c, q'_c mn_c);
+ *   - block score (1/sqrt(d)) sum_c max(q'_c mx_c, q'_c mn_c), over the
+ *     leading key_ch rotated channels of a segment whose block keys are
+ *     channel-compressed ([S] 5.2 channel-compresses the per-block keys; the
+ *     rotation orders channels by descending singular value, so the leading
+ *     ones carry the most energy), over all d channels otherwise;
  *   - k = ceil(keep_ppm * n / 1e6) in integers (or k_abs), clamped to [1, n];
  *   - top-k per query head and per packed segment, ties to the lower block;
  *   - dense segments are always attended.
@@ -384,7 +388,9 @@ static int ascending_i32(const void *a, const void *b) {
 
 /* For each of the G query heads of a unit:
  *   q' = R_k q                                   ([N] Eq. 12 text; [S] 5.3)
- *   score of block l = (1/sqrt d) sum_c max(q'_c mx_c, q'_c mn_c)
+ *   score of block l = (1/sqrt d) sum_{c < m_j} max(q'_c mx_c, q'_c mn_c),
+ *     m_j = key_ch[j] channels of packed segment j (d when key_ch is NULL,
+ *     or key_ch[j] <= 0 or > d)
  *   top-k blocks per packed segment (ties -> lower block), ascending
  *   z_i = (1/sqrt d) q'[I_i]^T k^_i over dense tokens and selected blocks
  *   o = softmax(z) V^                            ([N] Eq. 13)
@@ -401,8 +407,8 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
                     const int16_t *Kidx, const int16_t *Vidx, const double *meta, const double *const *segR,
                     int nseg,
                     const int32_t *kind, const int64_t *t_begin, const int64_t *t_cap,
-                    const int32_t *r, const int32_t *keep_ppm, const int32_t *k_abs, const double *q,
-                    const double *Rk, const double *Rv, const int32_t *forced_sel, double *qrot,
+                    const int32_t *r, const int32_t *keep_ppm, const int32_t *k_abs, const int32_t *key_ch,
+                    const double *q, const double *Rk, const double *Rv, const int32_t *forced_sel, double *qrot,
                     double *scores, int32_t *sel, double *tau, double *out, int nthreads) {
     (void)r;
     int64_t nsum = 0, ksum = 0;
@@ -446,10 +452,11 @@ int orc_decode_unit(int d, int64_t len, int G, int block, const double *Khat, co
             const int64_t nb = n_blocks_of(seg_filled(len, t_begin[j], t_cap[j]), block);
             const int64_t k = orc_block_keep(nb, keep_ppm[j], k_abs[j]);
             const double *qj = qseg + (int64_t)j * d;
+            const int m = (key_ch && key_ch[j] > 0 && key_ch[j] < d) ? key_ch[j] : d;
             for (int64_t l = 0; l < nb; ++l) {
                 const double *mn = meta + (moff + l) * 2 * d, *mx = mn + d;
                 double s = 0.0;
-                for (int c = 0; c < d; ++c) {
+                for (int c = 0; c < m; ++c) {
                     const double a = qj[c] * mx[c], b = qj[c] * mn[c];
                     s += a > b ? a : b;
                 }

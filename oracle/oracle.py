@@ -57,7 +57,7 @@ def _lib():
                                         ctypes.c_int, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         L.orc_decode_unit.restype = ctypes.c_int
         L.orc_decode_unit.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
-                                      ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                      ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                       ctypes.c_int]
         _LIB = L
     return _LIB
@@ -125,6 +125,11 @@ def _seg_arrays(segs):
     keep = _c([s["keep_ppm"] for s in segs], np.int32)
     kabs = _c([s["k_abs"] for s in segs], np.int32)
     return kind, tb, cap, r, keep, kabs
+
+
+def _key_channels(segs):
+    """Per segment: the leading rotated channels its block keys cover (0: all)."""
+    return _c([s.get("key_ch", 0) for s in segs], np.int32)
 
 
 def seg_blocks(segs, length: int, block: int = BLOCK):
@@ -208,6 +213,7 @@ def decode_unit(comp, q, Rk, Rv, forced_sel=None, nthreads: int | None = None):
     G, d = q.shape
     segs, length, block = comp["segs"], comp["length"], comp["block"]
     kind, tb, cap, r, keep, kabs = _seg_arrays(segs)
+    kch = _key_channels(segs)
     nk = seg_blocks(segs, length, block)
     nsum = sum(n for n, _ in nk)
     ksum = sum(k for _, k in nk)
@@ -226,7 +232,7 @@ def decode_unit(comp, q, Rk, Rv, forced_sel=None, nthreads: int | None = None):
                                 comp["Kidx"].ctypes.data, comp["Vidx"].ctypes.data,
                                 comp["meta_flat"].ctypes.data, tab, len(segs), kind.ctypes.data,
                                 tb.ctypes.data, cap.ctypes.data, r.ctypes.data, keep.ctypes.data,
-                                kabs.ctypes.data, q.ctypes.data, _c(Rk, np.float64).ctypes.data,
+                                kabs.ctypes.data, kch.ctypes.data, q.ctypes.data, _c(Rk, np.float64).ctypes.data,
                                 _c(Rv, np.float64).ctypes.data,
                                 fs.ctypes.data if fs is not None else None, qrot.ctypes.data,
                                 scores.ctypes.data, sel.ctypes.data, tau.ctypes.data, out.ctypes.data,

@@ -82,6 +82,12 @@ MUTANTS = [
      "const double *R = (segR && segR[j]) ? segR[j] + (int64_t)which * d * d : (which == 0 ? Rk : Rv);",
      "const double *R = which == 0 ? Rk : Rv;",
      [pins.test_P4_per_segment_rotations_equal_dense_attention]),
+    # channel-compressed block keys are ignored: every score sums all d channels
+    ("key_channels_ignored", "const int m = (key_ch && key_ch[j] > 0 && key_ch[j] < d) ? key_ch[j] : d;",
+     "const int m = d;", [pins.test_key_channels_score_equals_full_score_of_masked_query]),
+    # the scores sum the trailing channels instead of the leading ones
+    ("key_channels_trailing", "for (int c = 0; c < m; ++c) {", "for (int c = d - m; c < d; ++c) {",
+     [pins.test_key_channels_score_equals_full_score_of_masked_query]),
     # incremental appends skip the first new token
     ("incremental_skips_first_token", "for (int64_t t = t_from; t < len; ++t) {\n        const int j",
      "for (int64_t t = t_from + 1; t < len; ++t) {\n        const int j",

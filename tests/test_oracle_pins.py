@@ -548,3 +548,35 @@ def test_per_segment_rotation_matches_unrotated_reconstruction():
         att = _token_mask(segs, T, res["sel"], h)
         o = brute.attention_dense(Kor, Vor, q[h], att, d)
         assert np.abs(o - res["out"][h]).max() <= 1e-12 * max(1.0, np.abs(o).max())
+
+
+# ----------------------------------------------- channel-compressed keys --
+def test_key_channels_score_equals_full_score_of_masked_query():
+    """Block keys over the leading m rotated channels (the paper summary's 5.2
+    channel-compresses the per-block keys): with the identity rotation, the
+    m-channel score of q is bit for bit the full-key score of q with its
+    channels from m on set to zero, so it inherits the full score's pins (P5);
+    m = 0 and m = d give the full score. The keys change only which blocks are
+    chosen: forcing that choice on full keys gives the same outputs."""
+    rng = np.random.default_rng(71)
+    d, T = 16, 200
+    K = orc.round_to(rng.standard_normal((T, d)), "bf16")
+    V = orc.round_to(rng.standard_normal((T, d)), "bf16")
+    eye = np.eye(d)
+    q = rng.standard_normal((3, d))
+    full = synth.seg(1, 0, T, 5, 300000, 0)
+    comp = orc.compress_unit(K, V, eye, eye, [full], T, "bf16")
+    ref_full = orc.decode_unit(comp, q, eye, eye)
+    for m in (0, d):
+        res = orc.decode_unit(dict(comp, segs=[dict(full, key_ch=m)]), q, eye, eye)
+        assert np.array_equal(res["scores"][0], ref_full["scores"][0])
+    for m in (4, 8, 12):
+        res = orc.decode_unit(dict(comp, segs=[dict(full, key_ch=m)]), q, eye, eye)
+        qm = q.copy()
+        qm[:, m:] = 0.0
+        ref = orc.decode_unit(comp, qm, eye, eye)
+        assert np.array_equal(res["scores"][0].view(np.uint64), ref["scores"][0].view(np.uint64))
+        assert np.array_equal(res["sel"][0], ref["sel"][0])
+        assert not np.array_equal(res["scores"][0], ref_full["scores"][0])
+        forced = orc.decode_unit(comp, q, eye, eye, forced_sel=res["sel"])
+        assert np.array_equal(res["out"].view(np.uint64), forced["out"].view(np.uint64))

@@ -108,7 +108,7 @@ def union_summary(w, lengths, sel):
                 uni += len(np.unique(blocks))
             col += k
             rows.append(dict(kind="packed", filled=filled, r=s["r"], n_blocks=nb, union=uni,
-                             bitmap=s["kind"] == synth.BITMAP))
+                             bitmap=s["kind"] == synth.BITMAP, key_ch=s.get("key_ch", 0)))
         out.append(rows)
     return out
 
@@ -245,6 +245,8 @@ def main():
                     help="distinct layer caches visited round-robin (keeps every call cache-cold)")
     ap.add_argument("--layout", choices=["u8", "bitmap"], default="u8",
                     help="position format of the packed records: u8 channel indices (default) or bitmaps")
+    ap.add_argument("--key-ch", type=int, default=0,
+                    help="block keys over the leading N rotated channels of every packed segment (0: all)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a streaming scale kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -258,6 +260,8 @@ def main():
     w = workload(args.config, args.scale, cap_extra)
     if args.layout == "bitmap":
         w["segs"] = synth.as_bitmap(w["segs"])
+    if args.key_ch:
+        w["segs"] = synth.with_key_channels(w["segs"], args.key_ch)
     T0 = np.asarray(w["lengths"], np.int64)
     B, hq, hkv, d, dt = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["d"], w["dtype"]
     n_step_total = W_steps + 2 * K_steps + 1
@@ -361,7 +365,7 @@ def main():
     sb = 2 if dt == "bf16" else 4
     call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
     r_new = [s["r"] for s in w["segs"][0] if synth.is_packed(s["kind"])][-1]
-    append = bm.append_bytes(d, sb, hkv, B, r_new, args.layout == "bitmap")
+    append = bm.append_bytes(d, sb, hkv, B, r_new, args.layout == "bitmap", args.key_ch)
     step_bytes = call["total"] + append
     # algorithmic bytes each kernel of the step must move (the query rotation
     # runs in the append's launch: it reads R_k and the queries, writes q')
@@ -448,6 +452,7 @@ def main():
             "segments": seg_desc,
             "storage": dt,
             "record_positions": "bitmap" if args.layout == "bitmap" else "u8 indices",
+            "key_channels": args.key_ch or d,
             "parallelism": "single GPU",
             "layer_caches": n_layers,
         },

@@ -89,8 +89,13 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1, MKV_SEG_BITMAP = 2 } mkv_s
  *           rotates its share of the output back by its own R_v,seg ([S] 5.4:
  *           a finished segment recompressed with its own SVD rotation; see
  *           mkv_recompress_segment and mkv_swap_segment).
+ * key_ch    packed only: the block keys cover the leading key_ch rotated
+ *           channels ([S] 5.2 channel-compresses the per-block keys; the
+ *           rotation orders channels by descending singular value), and block
+ *           scores sum over those channels only. 0 means all head_dim
+ *           channels; otherwise a multiple of 8 in 8..head_dim.
  * Across the requests of one cache, segment j must have the same kind, r,
- * keep_ppm and k_abs; t_begin, t_cap and rot may differ per request.
+ * keep_ppm, k_abs and key_ch; t_begin, t_cap and rot may differ per request.
  *
  * Device layouts (s = bytes per stored element, nb = ceil(t_cap / 16),
  * block l holds positions t_begin + 16 l .. t_begin + 16 l + 15, slot = position - block start):
@@ -107,7 +112,8 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1, MKV_SEG_BITMAP = 2 } mkv_s
  *                MKV_PACKED_TAIL_BYTES follow the last record: decode reads
  *                whole dwords around each record's fields and may touch them
  *                (their contents are never used, nothing writes them).
- *   packed meta: [n_kv_heads][ceil(nb / 64)][2 d s / 16][64][16 bytes]: for the
+ *   packed meta: [n_kv_heads][ceil(nb / 64)][2 m s / 16][64][16 bytes] with
+ *                m = key_ch (head_dim when 0): for the
  *                block l, lane l % 64 of tile l / 64 holds, per 16-byte group,
  *                the (min, max) pairs of 16 / (2 s) consecutive channels
  *                (bf16: channels 4g..4g+3, f32: 2g..2g+1), min first. min/max are
@@ -124,6 +130,8 @@ typedef struct mkv_segment {
     void *data;
     void *meta;
     const float *rot;
+    int32_t key_ch;
+    int32_t reserved; /* 0 */
 } mkv_segment;
 
 /* A compressed cache for one attention layer of a batch of requests.
@@ -166,10 +174,10 @@ mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtype, int64_t 
                                      float *R_out, double *sigma_out);
 
 /* Bytes of the device buffers of one segment: returns the data bytes and
- * writes the meta bytes (0 for dense) to meta_bytes_out (nullable).
- * Returns 0 for invalid arguments. */
+ * writes the meta bytes (0 for dense) to meta_bytes_out (nullable). key_ch is
+ * that of mkv_segment.key_ch, ignored for dense. Returns 0 for invalid arguments. */
 size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads,
-                         int64_t t_cap, size_t *meta_bytes_out);
+                         int64_t t_cap, int32_t key_ch, size_t *meta_bytes_out);
 
 /* Compress and append new tokens ([N] Eq. 7-9, Algorithm 1; [S] 4.2, 5.2, 5.4:
  * new vectors are rotated by the head's R, keep their top-r elements and are
@@ -249,8 +257,9 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
  * k_host, v_host: [n_kv_heads][n_tokens][d] in `dtype` (f32 values or bf16
  *   bit patterns), n_tokens in 1..t_cap.
  * Outputs in the documented device layouts, in host memory the caller owns:
- * kind: the segment's record format, MKV_SEG_PACKED or MKV_SEG_BITMAP.
- *   data_out [mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap)]
+ * kind: the segment's record format, MKV_SEG_PACKED or MKV_SEG_BITMAP;
+ * key_ch: its block-key channels, as in mkv_segment.
+ *   data_out [mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap, key_ch)]
  *     (slots after the last token zero; the tail bytes are left as they are),
  *   meta_out [that call's meta bytes] (blocks past the last one zero),
  *   rot_out float32 [n_kv_heads][2][d][d].
@@ -259,7 +268,7 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
  * MKV_ERR_NOCONVERGE. */
 mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
                                   int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t kind, int32_t r,
-                                  void *data_out, void *meta_out, float *rot_out);
+                                  int32_t key_ch, void *data_out, void *meta_out, float *rot_out);
 
 /* Segment strategy generation ([S] 4.3 and 5.5: output caches start a new
  * segment when the accumulated compression loss exceeds a threshold or at the

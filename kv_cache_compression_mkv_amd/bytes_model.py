@@ -5,7 +5,8 @@ Host-side arithmetic used to report achieved bandwidth; no device work.
 Layout facts (the library's documented storage, see include/mkv.h):
   * packed record of one 16-token block: K values, V values, K indices (u8),
     V indices (u8), each [16][r]  ->  16 * r * 2 * (s + 1) bytes;
-  * per-block keys (min and max of every channel): 2 * d * s bytes;
+  * per-block keys (min and max of each of the m = key_ch leading channels,
+    all d when key_ch is 0): 2 * m * s bytes;
   * dense block of 16 tokens: 16 * 2 * d * s bytes.
 """
 from __future__ import annotations
@@ -23,8 +24,8 @@ def packed_record_bytes(r: int, s: int, bitmap: bool = False, d: int = 128) -> i
     return BLOCK * r * 2 * s + (2 * BLOCK * (d // 8) if bitmap else BLOCK * r * 2)
 
 
-def meta_block_bytes(d: int, s: int) -> int:
-    return 2 * d * s
+def meta_block_bytes(d: int, s: int, key_ch: int = 0) -> int:
+    return 2 * (key_ch or d) * s
 
 
 def quest_key_overhead(block: int = BLOCK) -> float:
@@ -69,7 +70,7 @@ def decode_call_bytes(d: int, s: int, hkv: int, batch: int, hq: int, seg_summary
     for req in seg_summary:
         for sg in req:
             if sg["kind"] == "packed":
-                meta += sg["n_blocks"] * hkv * meta_block_bytes(d, s)
+                meta += sg["n_blocks"] * hkv * meta_block_bytes(d, s, sg.get("key_ch", 0))
                 records += sg["union"] * packed_record_bytes(sg["r"], s, sg.get("bitmap", False), d)
             else:
                 dense += dense_kv_bytes(sg["filled"], d, s) * hkv
@@ -79,11 +80,11 @@ def decode_call_bytes(d: int, s: int, hkv: int, batch: int, hq: int, seg_summary
                 total=meta + records + dense + rot + qo)
 
 
-def append_bytes(d: int, s: int, hkv: int, batch: int, r: int, bitmap: bool = False) -> int:
+def append_bytes(d: int, s: int, hkv: int, batch: int, r: int, bitmap: bool = False, key_ch: int = 0) -> int:
     """Algorithmic bytes of appending one token per request to a packed
     segment: per (request, KV head) read R_k and R_v (float32) and the raw key
     and value, write the two packed vectors (r values and r u8 indices, or a
     d-bit bitmap, each) and read and write the block's min/max keys."""
     pos = d // 8 if bitmap else r
-    per_unit = 2 * d * d * 4 + 2 * d * s + 2 * (r * s + pos) + 2 * meta_block_bytes(d, s)
+    per_unit = 2 * d * d * 4 + 2 * d * s + 2 * (r * s + pos) + 2 * meta_block_bytes(d, s, key_ch)
     return batch * hkv * per_unit

@@ -290,7 +290,7 @@ struct BlockJob {
     uint8_t *idxs;
     char *meta_tile;
     const typename ST::bits_t *xin;
-    int p0, sa, se, r, G16, cpg;
+    int p0, sa, se, r, G16, cpg, kch;
     bool packed, bitmap, do_meta;
     uint32_t mn0, mx0, mn1, mx1;
     typename ST::bits_t x0, x1;  // row of the first new token (lane's channels; one-token appends)
@@ -323,10 +323,12 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
                                                          (size_t)wave * BT * (bitmap ? D / 8 : r))
                            : nullptr;
 
-    // per-block keys (keys wave, packed segments): running totalOrder min/max
+    // per-block keys (keys wave, packed segments) of the leading kch
+    // channels: running totalOrder min/max
     const bool do_meta = packed && wave == 0;
-    const int G16 = 2 * D * ST::bytes / 16;  // 16-byte groups per block
-    const int cpg = 16 / (2 * ST::bytes);    // channels per group
+    const int kch = E.kch;
+    const int G16 = 2 * kch * ST::bytes / 16;  // 16-byte groups per block
+    const int cpg = 16 / (2 * ST::bytes);      // channels per group
     char *meta_tile = nullptr;
     uint32_t mn0 = 0xFFFFFFFFu, mx0 = 0u, mn1 = 0xFFFFFFFFu, mx1 = 0u;
     if (do_meta) {
@@ -336,6 +338,7 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
             const int bl = blk % META_TILE;
             for (int h = 0; h < 2; ++h) {
                 const int c = lane + 64 * h;
+                if (c >= kch) continue;
                 const bits_t *pr = reinterpret_cast<const bits_t *>(
                     meta_tile + ((size_t)(c / cpg) * META_TILE + bl) * 16 + (c % cpg) * 2 * ST::bytes);
                 const uint32_t kmn = order_key<ST>(pr[0]), kmx = order_key<ST>(pr[1]);
@@ -363,6 +366,7 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     J.r = r;
     J.G16 = G16;
     J.cpg = cpg;
+    J.kch = kch;
     J.packed = packed;
     J.bitmap = bitmap;
     J.do_meta = do_meta;
@@ -437,6 +441,7 @@ __device__ __forceinline__ void block_finish(const BlockJob<ST> &J, int blk, int
         const int bl = blk % META_TILE;
         for (int h = 0; h < 2; ++h) {
             const int c = lane + 64 * h;
+            if (c >= J.kch) continue;
             bits_t *pr = reinterpret_cast<bits_t *>(J.meta_tile + ((size_t)(c / J.cpg) * META_TILE + bl) * 16 +
                                                     (c % J.cpg) * 2 * ST::bytes);
             pr[0] = key_to_bits<ST>(h == 0 ? J.mn0 : J.mn1);
@@ -679,13 +684,14 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
         mn0 = min(mn0, q0); mx0 = max(mx0, q0);
         mn1 = min(mn1, q1); mx1 = max(mx1, q1);
     }
-    const int G16 = 2 * D * ST::bytes / 16;
+    const int G16 = 2 * E.kch * ST::bytes / 16;
     const int cpg = 16 / (2 * ST::bytes);
     const int ntile = (E.nbcap + META_TILE - 1) / META_TILE;
     char *tile = static_cast<char *>(E.meta) + ((size_t)g * ntile + blk / META_TILE) * G16 * META_TILE * 16;
     const int bl = blk % META_TILE;
     for (int h = 0; h < 2; ++h) {
         const int c = lane + 64 * h;
+        if (c >= E.kch) continue;
         bits_t *pr = reinterpret_cast<bits_t *>(tile + ((size_t)(c / cpg) * META_TILE + bl) * 16 +
                                                 (c % cpg) * 2 * ST::bytes);
         pr[0] = key_to_bits<ST>(h == 0 ? mn0 : mn1);

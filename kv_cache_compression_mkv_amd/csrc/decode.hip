@@ -102,7 +102,9 @@ __device__ __forceinline__ void wave_minmax_u(uint32_t &mn, uint32_t &mx) {
 // score: one wave per tile of 64 blocks, one lane per block. The tile's keys
 // are stored channel-group-major, so each 16-byte load of the wave covers
 // 1 KB of contiguous meta. q' enters as wave-uniform (scalar) operands split
-// into positive and negative parts: max(q mx, q mn) = q+ mx + q- mn.
+// into positive and negative parts: max(q mx, q mn) = q+ mx + q- mn. A
+// segment whose keys cover its leading kch channels reads and sums only those
+// groups.
 // ----------------------------------------------------------------------------
 template <typename ST, int G>
 __device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, int g, int tile) {
@@ -112,17 +114,17 @@ __device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, i
     const int ntile = (S.nb + META_TILE - 1) / META_TILE;
     if (tile >= ntile) return;
     const int l = tile * META_TILE + lane;
-    constexpr int NG = 2 * D * ST::bytes / 16;  // 16-byte groups per block
-    constexpr int CPG = D / NG;                 // channels per group
+    constexpr int CPG = 16 / (2 * ST::bytes);   // channels per 16-byte group
+    const int ng = S.kch / CPG;                 // groups per block
     const int ntile_cap = (S.nbcap + META_TILE - 1) / META_TILE;
     const uint4 *mt = reinterpret_cast<const uint4 *>(static_cast<const char *>(S.meta) +
-                                                      ((size_t)g * ntile_cap + tile) * NG * META_TILE * 16);
+                                                      ((size_t)g * ntile_cap + tile) * ng * META_TILE * 16);
     const float *__restrict__ qs = A.qs + ((((size_t)b * A.nslot + S.slot) * A.hkv + g) * D) * 2 * G;
     float acc[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.f;
 #pragma unroll 8
-    for (int grp = 0; grp < NG; ++grp) {
+    for (int grp = 0; grp < ng; ++grp) {
         const uint4 w = mt[grp * META_TILE + lane];
         float mn[CPG], mx[CPG];
         if constexpr (ST::bytes == 2) {

@@ -117,7 +117,8 @@ mkv_status check_cache(const mkv_cache *c) {
             const mkv_segment &s0 = segof(c, 0, j);
             if (s.kind != MKV_SEG_DENSE && !packed_kind(s.kind)) return MKV_ERR_ARG;
             if (s.t_begin != t || s.t_cap < 1 || !s.data) return MKV_ERR_ARG;
-            if (s.kind != s0.kind || s.r != s0.r || s.keep_ppm != s0.keep_ppm || s.k_abs != s0.k_abs)
+            if (s.kind != s0.kind || s.r != s0.r || s.keep_ppm != s0.keep_ppm || s.k_abs != s0.k_abs ||
+                s.key_ch != s0.key_ch)
                 return MKV_ERR_ARG;
             if (packed_kind(s.kind)) {
                 // one position format per cache (u8 indices or bitmaps)
@@ -125,6 +126,8 @@ mkv_status check_cache(const mkv_cache *c) {
                     if (packed_kind(segof(c, 0, jj).kind) && segof(c, 0, jj).kind != s.kind) return MKV_ERR_ARG;
                 if (s.kind == MKV_SEG_BITMAP && c->head_dim != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
                 if (s.r < 1 || s.r > c->head_dim || !s.meta || s.k_abs < 0) return MKV_ERR_ARG;
+                if (s.key_ch < 0 || s.key_ch > c->head_dim || s.key_ch % 8) return MKV_ERR_ARG;
+                if (s.reserved != 0) return MKV_ERR_ARG;
                 if (s.k_abs == 0 && (s.keep_ppm < 1 || s.keep_ppm > 1000000)) return MKV_ERR_ARG;
                 if (ceil_div(s.t_cap, BT) > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
             }
@@ -289,7 +292,8 @@ mkv_status append_enqueue(mkv_cache *c, const void *k_new, const void *v_new, co
             E.row0 = (int32_t)(sg.t_begin + a - p0);
             E.b = b;
             E.r = (int16_t)sg.r;
-            E.kind = (int16_t)sg.kind;
+            E.kind = (int8_t)sg.kind;
+            E.kch = (uint8_t)key_channels(sg.key_ch);
             E.blk0 = (int32_t)(a / BT);
             E.nblk = (int32_t)((e - 1) / BT - a / BT + 1);
             E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
@@ -454,7 +458,8 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                 // every request; requests whose segment has no own rotation
                 // there use the cache's, through the slot's launch
                 D_.slot = (int16_t)m.slot_of[j];
-                D_.r = sg.r;
+                D_.r = (int16_t)sg.r;
+                D_.kch = (int16_t)key_channels(sg.key_ch);
                 D_.filled = (int32_t)seg_filled(c, b0 + i, j);
                 D_.nb = (int32_t)ceil_div(D_.filled, BT);
                 D_.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
@@ -531,16 +536,17 @@ const char *mkv_status_str(mkv_status s) {
 }
 
 size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads, int64_t t_cap,
-                         size_t *meta_bytes_out) {
+                         int32_t key_ch, size_t *meta_bytes_out) {
     if (meta_bytes_out) *meta_bytes_out = 0;
     if ((dtype != MKV_F32 && dtype != MKV_BF16) || d < 1 || n_kv_heads < 1 || t_cap < 1) return 0;
     const size_t s = elem_bytes(dtype);
     const size_t nb = (size_t)ceil_div(t_cap, BT);
     if (kind == MKV_SEG_DENSE) return (size_t)n_kv_heads * nb * 2 * BT * d * s;
     if (!packed_kind(kind) || r < 1 || r > d || (kind == MKV_SEG_BITMAP && d != D)) return 0;
+    if (key_ch < 0 || key_ch > d || key_ch % 8) return 0;
     if (meta_bytes_out) {
         const size_t ntile = ceil_div((int64_t)nb, META_TILE);
-        *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * d * s;
+        *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * (key_ch > 0 ? key_ch : d) * s;
     }
     return (size_t)n_kv_heads * nb * record_bytes(kind, r, s) + MKV_PACKED_TAIL_BYTES;
 }
@@ -576,6 +582,7 @@ mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
             E.b = b0 + i;
             E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
             E.kind = sg.kind;
+            E.kch = key_channels(sg.key_ch);
             max_nb = std::max(max_nb, E.nb);
         }
         A.n_ent = n;

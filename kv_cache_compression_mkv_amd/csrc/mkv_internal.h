@@ -19,6 +19,8 @@ constexpr int META_TILE = 64;   // blocks per meta tile
 
 // packed segments of either position format
 __host__ __device__ constexpr bool packed_kind(int kind) { return kind == MKV_SEG_PACKED || kind == MKV_SEG_BITMAP; }
+// channels covered by a packed segment's block keys (0 means all)
+__host__ __device__ constexpr int key_channels(int key_ch) { return key_ch > 0 ? key_ch : D; }
 // bytes of one packed block record (values, then u8 indices or bitmaps)
 __host__ __device__ constexpr int64_t record_bytes(int kind, int r, int sb) {
     return (int64_t)BT * r * 2 * sb + (kind == MKV_SEG_BITMAP ? (int64_t)2 * BT * (D / 8) : (int64_t)2 * BT * r);
@@ -50,7 +52,8 @@ struct CompressEntry {
     int32_t nblk;     // blocks touched
     int32_t nbcap;    // block capacity of the segment
     int16_t r;        // kept elements (packed)
-    int16_t kind;     // MKV_SEG_*
+    int8_t kind;      // MKV_SEG_*
+    uint8_t kch;      // channels of the block keys (packed)
 };  // 56 bytes
 
 struct CompressArgs {
@@ -75,7 +78,8 @@ struct MetaEntry {
     const void *data;
     void *meta;
     int32_t filled, nb, r, b, nbcap, kind;
-};  // 40 bytes
+    int32_t kch, pad;  // channels of the block keys
+};  // 48 bytes
 
 struct MetaArgs {
     MetaEntry ent[TABLE];
@@ -89,7 +93,8 @@ struct DSeg {
     const float *rot; // the segment's own rotations [n_kv][2][D][D], or nullptr (the cache's)
     int16_t kind;
     int16_t slot;     // rotation slot: 0 the cache's rotation, else that of the segment index
-    int32_t r;
+    int16_t r;
+    int16_t kch;      // channels of the block keys (packed)
     int32_t filled;   // tokens stored
     int32_t nb;       // blocks stored
     int32_t k;        // blocks kept (packed)

@@ -77,9 +77,11 @@ uint32_t order_key(uint32_t v, int s) {
 
 extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
                                              int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t kind,
-                                             int32_t r, void *data_out, void *meta_out, float *rot_out) {
+                                             int32_t r, int32_t key_ch, void *data_out, void *meta_out,
+                                             float *rot_out) {
     if (!k_host || !v_host || !data_out || !meta_out || !rot_out || n_kv_heads < 1 || t_cap < 1 || n_tokens < 1 ||
-        n_tokens > t_cap || r < 1 || r > d || (kind != MKV_SEG_PACKED && kind != MKV_SEG_BITMAP))
+        n_tokens > t_cap || r < 1 || r > d || (kind != MKV_SEG_PACKED && kind != MKV_SEG_BITMAP) || key_ch < 0 ||
+        key_ch > d || key_ch % 8)
         return MKV_ERR_ARG;
     if (d != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
     if (dtype != MKV_F32 && dtype != MKV_BF16) return MKV_ERR_UNSUPPORTED;
@@ -92,7 +94,8 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
     const int64_t pos_bytes = bitmap ? (int64_t)BT * (d / 8) : (int64_t)BT * r;
     const int64_t rec = (int64_t)BT * r * 2 * s + 2 * pos_bytes;
     const int64_t ntile = (nbcap + 63) / 64;
-    const int ng = 2 * d * s / 16, cpg = d / ng;  // meta 16-byte groups per block, channels per group
+    const int kch = key_ch > 0 ? key_ch : d;  // channels of the block keys
+    const int cpg = 16 / (2 * s), ng = kch / cpg;  // channels per meta 16-byte group, groups per block
     const int64_t mhead = ntile * ng * 64 * 16;
     const size_t xsz = (size_t)n_tokens * d;
 
@@ -168,9 +171,9 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
                             }
                     }
                 }
-                // block keys: lane l % 64 of tile l / 64, group c / cpg, (min, max) of channel c
+                // block keys: lane l % 64 of tile l / 64, group c / cpg, (min, max) of channel c < kch
                 char *tile = meta + (size_t)g * mhead + (size_t)(l / 64) * ng * 64 * 16;
-                for (int c = 0; c < d; ++c) {
+                for (int c = 0; c < kch; ++c) {
                     char *pr = tile + ((size_t)(c / cpg) * 64 + l % 64) * 16 + (size_t)(c % cpg) * 2 * s;
                     for (int w = 0; w < 2; ++w) {
                         const uint32_t key = w ? kmx[c] : kmn[c];

@@ -79,11 +79,17 @@ def unpack_dense(data: np.ndarray, hkv: int, nbcap: int, dtype: str, d: int = 12
     return vals.reshape(shp), bits.reshape(shp)
 
 
-def unpack_meta(meta: np.ndarray, hkv: int, nbcap: int, dtype: str, d: int = 128):
-    """-> (values float64 [hkv][nbcap][2][d] (min, max), bits same shape)."""
+def meta_groups(dtype: str, d: int = 128, key_ch: int = 0) -> int:
+    """16-byte key groups per block of a packed segment whose keys cover key_ch channels (0: d)."""
     s = 2 if dtype == "bf16" else 4
-    ng = 2 * d * s // 16
-    cpg = d // ng
+    return 2 * (key_ch or d) * s // 16
+
+
+def unpack_meta(meta: np.ndarray, hkv: int, nbcap: int, dtype: str, d: int = 128, key_ch: int = 0):
+    """-> (values float64 [hkv][nbcap][2][m] (min, max), bits same shape), m = key_ch or d."""
+    ng = meta_groups(dtype, d, key_ch)
+    m = key_ch or d
+    cpg = m // ng
     ntile = -(-nbcap // TILE)
     raw = np.ascontiguousarray(meta, np.uint8).reshape(hkv, ntile, ng, TILE, 16)
     bits, vals = _vals(np.ascontiguousarray(raw).reshape(-1), dtype)

@@ -59,6 +59,16 @@ def test_segment_bytes(L):
     assert data == 2 * (2 * 16 * 128 * 4 + 2 * 16 * 16) + L.MKV_PACKED_TAIL_BYTES and meta == 64 * 1024
     assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_BITMAP, 8, 64, 8, 100)[0] == 0  # 128 channels only
     assert L.mkv_segment_bytes(L.MKV_BF16, 3, 8, 128, 8, 100)[0] == 0
+    # block keys over the leading key_ch channels: the meta shrinks to key_ch / d, the records do not
+    for key_ch, ok in ((32, True), (96, True), (128, True), (8, True), (12, False), (136, False), (-8, False)):
+        data, meta = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_PACKED, 38, 128, 8, 63456, key_ch)
+        if ok:
+            assert data == 8 * 3966 * 3648 + L.MKV_PACKED_TAIL_BYTES and meta == 8 * 62 * 64 * 2 * key_ch * 2
+        else:
+            assert data == 0
+    data, meta = L.mkv_segment_bytes(L.MKV_F32, L.MKV_SEG_BITMAP, 16, 128, 2, 100, 24)
+    assert meta == 2 * 1 * 64 * 2 * 24 * 4
+    assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_DENSE, 0, 128, 8, 100, 12)[0] > 0  # ignored for dense
 
 
 class FakeCache:
@@ -74,6 +84,7 @@ class FakeCache:
                 e = self.arr[b * n + j]
                 e.kind, e.r, e.keep_ppm, e.k_abs = s["kind"], s["r"], s["keep_ppm"], s["k_abs"]
                 e.t_begin, e.t_cap = s["t_begin"], s["t_cap"]
+                e.key_ch = s.get("key_ch", 0)
                 e.data = 0x10000 * (1 + b * n + j)
                 e.meta = 0x90000000 + 0x10000 * (b * n + j) if s["kind"] in (1, 2) else None
         self.c = L.mkv_cache(batch, hq, hkv, d, L.MKV_BF16 if dtype is None else dtype, n,
@@ -140,6 +151,22 @@ def test_bitmap_descriptors(L):
     bad = [dict(s) for s in segs]
     bad[1]["kind"] = 3
     assert L.mkv_decode_workspace_bytes(FakeCache(L, bad).c) == 0
+
+
+def test_key_channel_descriptors(L):
+    """key_ch: 0 or a multiple of 8 up to head_dim, the same in every request."""
+    base = _segs_cfg2()
+    for key_ch, ok in ((0, True), (32, True), (128, True), (20, False), (136, False), (-8, False)):
+        segs = synth.with_key_channels([base], key_ch)[0]
+        assert (L.mkv_decode_workspace_bytes(FakeCache(L, segs, lengths=[32768]).c) > 0) == ok, key_ch
+    # per-request key_ch must agree
+    f = FakeCache(L, synth.with_key_channels([base], 32)[0], batch=2, lengths=[32768, 32768])
+    assert L.mkv_decode_workspace_bytes(f.c) > 0
+    f.arr[1 * len(base) + 1].key_ch = 64
+    assert L.mkv_decode_workspace_bytes(f.c) == 0
+    f.arr[1 * len(base) + 1].key_ch = 32
+    f.arr[1].reserved = 1
+    assert L.mkv_decode_workspace_bytes(f.c) == 0
 
 
 def test_calls_fail_before_any_launch(L):

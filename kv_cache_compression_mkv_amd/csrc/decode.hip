@@ -106,21 +106,13 @@ __device__ __forceinline__ void wave_minmax_u(uint32_t &mn, uint32_t &mx) {
 // segment whose keys cover its leading kch channels reads and sums only those
 // groups.
 // ----------------------------------------------------------------------------
-template <typename ST, int G>
-__device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, int g, int tile) {
-    const int b = A.b0 + bl;
-    const DSeg &S = seg_of(A, bl, A.pseg[j]);
-    const int lane = lane_id();
-    const int ntile = (S.nb + META_TILE - 1) / META_TILE;
-    if (tile >= ntile) return;
-    const int l = tile * META_TILE + lane;
-    constexpr int CPG = 16 / (2 * ST::bytes);   // channels per 16-byte group
-    const int ng = S.kch / CPG;                 // groups per block
-    const int ntile_cap = (S.nbcap + META_TILE - 1) / META_TILE;
-    const uint4 *mt = reinterpret_cast<const uint4 *>(static_cast<const char *>(S.meta) +
-                                                      ((size_t)g * ntile_cap + tile) * ng * META_TILE * 16);
-    const float *__restrict__ qs = A.qs + ((((size_t)b * A.nslot + S.slot) * A.hkv + g) * D) * 2 * G;
-    float acc[G];
+// acc[i] = sum over the ng key groups of head i's q'+ mx + q'- mn (NGC > 0:
+// ng == NGC, known at compile time)
+template <typename ST, int G, int NGC>
+__device__ __forceinline__ void score_groups(const uint4 *mt, const float *__restrict__ qs, int lane, float (&acc)[G],
+                                             int ng) {
+    constexpr int CPG = 16 / (2 * ST::bytes);
+    if constexpr (NGC > 0) ng = NGC;
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.f;
 #pragma unroll 8
@@ -146,6 +138,27 @@ __device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, i
             }
         }
     }
+}
+
+template <typename ST, int G>
+__device__ __forceinline__ void score_tile(const DecodeArgs &A, int bl, int j, int g, int tile) {
+    const int b = A.b0 + bl;
+    const DSeg &S = seg_of(A, bl, A.pseg[j]);
+    const int lane = lane_id();
+    const int ntile = (S.nb + META_TILE - 1) / META_TILE;
+    if (tile >= ntile) return;
+    const int l = tile * META_TILE + lane;
+    constexpr int CPG = 16 / (2 * ST::bytes);   // channels per 16-byte group
+    const int ng = S.kch / CPG;                 // groups per block
+    const int ntile_cap = (S.nbcap + META_TILE - 1) / META_TILE;
+    const uint4 *mt = reinterpret_cast<const uint4 *>(static_cast<const char *>(S.meta) +
+                                                      ((size_t)g * ntile_cap + tile) * ng * META_TILE * 16);
+    const float *__restrict__ qs = A.qs + ((((size_t)b * A.nslot + S.slot) * A.hkv + g) * D) * 2 * G;
+    float acc[G];
+    // full keys: a compile-time trip count, as the common case; compressed keys: a run-time one
+    constexpr int NG_FULL = D / CPG;
+    if (ng == NG_FULL) score_groups<ST, G, NG_FULL>(mt, qs, lane, acc, NG_FULL);
+    else score_groups<ST, G, 0>(mt, qs, lane, acc, ng);
     if (l < S.nb) {
         const int nbc = A.nbcap[j];
 #pragma unroll

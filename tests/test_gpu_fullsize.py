@@ -44,8 +44,12 @@ def check_sel_properties(w, lengths, sel):
         assert np.all(sel[b, :, o:] == -1), "b=%d: padding" % b
 
 
+_POPC8 = np.array([bin(i).count("1") for i in range(256)], np.uint8)
+
+
 def check_index_properties(c, w):
-    """Stored channel indices of every filled slot strictly ascending, < d."""
+    """Stored channel indices of every filled slot strictly ascending, < d
+    (bitmap records: exactly r positions per filled slot, none after)."""
     from kv_cache_compression_mkv_amd import layout
     sb = 2 if w["dtype"] == "bf16" else 4
     for b in range(w["batch"]):
@@ -57,6 +61,15 @@ def check_index_properties(c, w):
             if filled == 0:
                 continue
             r, nbcap = s["r"], -(-s["t_cap"] // 16)
+            if s["kind"] == synth.BITMAP:
+                rec = layout.record_bytes(s["kind"], r, w["dtype"], w["d"])
+                for g in range(w["n_kv_heads"]):
+                    raw = c.data[b][j][g * nbcap * rec:(g + 1) * nbcap * rec].view(nbcap, rec)
+                    bm = raw[:, 2 * 16 * r * sb:].cpu().numpy().reshape(nbcap, 2, 16, w["d"] // 8)
+                    cnt = _POPC8[bm].sum(axis=-1, dtype=np.int32).transpose(0, 2, 1).reshape(nbcap * 16, 2)
+                    assert np.all(cnt[:filled] == r), "b=%d seg=%d g=%d: bitmap counts" % (b, j, g)
+                    assert np.all(cnt[filled:] == 0), "b=%d seg=%d g=%d: bitmap padding" % (b, j, g)
+                continue
             rec = 16 * r * 2 * (sb + 1)
             # record tail: K indices [16][r] then V indices [16][r]
             raw = c.data[b][j][:w["n_kv_heads"] * nbcap * rec].view(w["n_kv_heads"], nbcap, rec)
@@ -190,11 +203,17 @@ def test_128k_batch4_benchmark_launch():
     log("128K batch-4 full: stored caches equal, compress parity on %d units" % len(units))
 
 
-def test_1m_token_layer_share():
+@pytest.mark.parametrize("bitmap,key_ch", [(False, 0), (True, 32)], ids=["u8", "bitmap_keych32"])
+def test_1m_token_layer_share(bitmap, key_ch):
     """One layer's share at 1M tokens (65020 packed blocks, near the per-segment
-    maximum of 65536)."""
+    maximum of 65536; the sliced select), in the default layout and with bitmap
+    records and block keys over 32 channels."""
     w = synth.workload(4)
-    log("1M-token layer full: generating")
+    if bitmap:
+        w["segs"] = synth.as_bitmap(w["segs"])
+    if key_ch:
+        w["segs"] = synth.with_key_channels(w["segs"], key_ch)
+    log("1M-token layer full (bitmap=%s key_ch=%d): generating" % (bitmap, key_ch))
     c, raw, R = build(torch, w)
     check_index_properties(c, w)
     units = [(0, 0), (0, 5)]

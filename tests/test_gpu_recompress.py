@@ -38,10 +38,17 @@ def _oracle(w, K, V, R, b, g, length, seg_rot):
     return orc.compress_unit(Kr, Vr, Rk, Rv, w["segs"][b], length, w["dtype"], seg_rot=seg_rot), Rk, Rv
 
 
-def test_swap_recompressed_segment():
+@pytest.mark.parametrize("bitmap,key_ch", [(False, 0), (True, 48)], ids=["u8", "bitmap_keych48"])
+def test_swap_recompressed_segment(bitmap, key_ch):
+    """Also with bitmap records and block keys over 48 channels: the host
+    recompression writes the segment's own record format and key channels."""
     segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * 120, 26, 100000, 0),
             synth.seg(synth.PACKED, 32 + 16 * 120, 16 * 100, 38, 100000, 0),
             synth.seg(synth.DENSE, 32 + 16 * 220, 128)]
+    if bitmap:
+        segs = synth.as_bitmap([segs])[0]
+    if key_ch:
+        segs = synth.with_key_channels([segs], key_ch)[0]
     T = 32 + 16 * 220 + 40
     B = 3
     w = dict(cfg=3, batch=B, n_q_heads=32, n_kv_heads=8, d=128, dtype="bf16", lengths=np.array([T] * B),

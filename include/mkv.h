@@ -187,7 +187,9 @@ size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int3
  * 0..n_max). Each vector is rotated in float64 with exact products (summed in
  * ascending input channel), ranked by the unrounded magnitudes (ties to the
  * lower channel) and rounded once, to nearest even, to the storage type.
- * Packed segments also update the min/max keys of the blocks they touch.
+ * Packed segments store each vector in their record format (u8 indices or a
+ * position bitmap) and update the min/max keys (channels < key_ch) of the
+ * blocks they touch.
  * Advances c->len on success.
  * Errors: MKV_ERR_ARG, MKV_ERR_UNSUPPORTED, MKV_ERR_CAPACITY, MKV_ERR_HIP. */
 mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new,
@@ -212,7 +214,8 @@ int64_t mkv_decode_sel_cols(const mkv_cache *c);
 /* Decode attention straight from the compressed cache ([N] Eq. 12-14; [S] 4.2,
  * 5.3). For every request b and query head h, with q' = R_k q:
  *   score of block l = (1/sqrt d) sum_c max(q'_c mx_c, q'_c mn_c) over the
- *     block's min/max keys, for every block of every packed segment;
+ *     block's min/max keys (channels c < key_ch of its segment, all when
+ *     key_ch is 0), for every block of every packed segment;
  *   per packed segment, the k blocks of highest score (ties to the lower block);
  *   o = softmax(q' K^T / sqrt d) V^ over every stored dense token and every
  *     token of a selected block, with K^, V^ the packed sparse vectors;

@@ -4,6 +4,9 @@ Independent code paths that pin the oracle:
   * top-r by enumerating every r-subset of channels and maximising the exact
     sum of magnitudes (ties: lexicographically smallest subset), the
     definition behind the reading notes' Eq. 9 / Algorithm 1;
+  * group-granular top-r (one position bit per group of g adjacent channels,
+    the paper's section 5.1) by enumerating every choice of r / g groups and
+    maximising their exact total energy (same tie rule);
   * top-k blocks by enumerating every k-subset of blocks (same rule), the
     definition behind the paper's top-k block selection (section 4.2);
   * attention by dense reconstruction (zero-filled K^, V^), a masked softmax
@@ -27,6 +30,19 @@ def topr_subsets(xr, r: int):
         if best_sum is None or s > best_sum:
             best, best_sum = sub, s
     return np.array(best, dtype=np.int32)
+
+
+def topr_group_subsets(xr, r: int, g: int):
+    """Channels (ascending) of the best choice of r / g groups of g adjacent channels."""
+    xr = [Fraction(float(v)) for v in np.asarray(xr, np.float64)]
+    ng = len(xr) // g
+    energy = [sum((xr[g * i + m] ** 2 for m in range(g)), Fraction(0)) for i in range(ng)]
+    best, best_sum = None, None
+    for sub in itertools.combinations(range(ng), r // g):
+        s = sum((energy[i] for i in sub), Fraction(0))
+        if best_sum is None or s > best_sum:
+            best, best_sum = sub, s
+    return np.array([g * i + m for i in best for m in range(g)], dtype=np.int32)
 
 
 def topk_subsets(scores, k: int):

@@ -260,6 +260,32 @@ void orc_topr(const double *xr, int d, int r, int *idx) {
     qsort(idx, (size_t)r, sizeof(int), ascending_int);
 }
 
+/* [S] 5.1 (and 4.3's element-group size): a position bitmap with one bit per
+ * group of g adjacent channels keeps whole groups. Reading taken: the r / g
+ * groups i (channels g i .. g i + g - 1) of largest energy
+ *   e_i = sum_{m < g} x'^2_{g i + m}
+ * (binary64, each square and each sum rounded, m ascending), ties to the
+ * lower group -- the choice that drops the least energy; kept channels
+ * returned in ascending order. g divides d and r. */
+void orc_topr_groups(const double *xr, int d, int r, int g, int *idx) {
+    ranked tmp[256];
+    const int ng = d / g;
+    for (int i = 0; i < ng; ++i) {
+        double e = 0.0;
+        for (int m = 0; m < g; ++m) {
+            const double v = xr[g * i + m];
+            e += v * v;
+        }
+        tmp[i].mag = e;
+        tmp[i].c = i;
+    }
+    qsort(tmp, (size_t)ng, sizeof(ranked), by_magnitude);
+    int n = 0;
+    for (int k = 0; k < r / g; ++k)
+        for (int m = 0; m < g; ++m) idx[n++] = g * tmp[k].c + m;
+    qsort(idx, (size_t)n, sizeof(int), ascending_int);
+}
+
 static int find_segment(int nseg, const int64_t *t_begin, const int64_t *t_cap, int64_t t) {
     for (int j = 0; j < nseg; ++j)
         if (t >= t_begin[j] && t < t_begin[j] + t_cap[j]) return j;
@@ -284,6 +310,8 @@ static int64_t n_blocks_of(int64_t filled, int block) { return (filled + block -
  *        R_v) that replaces Rk, Rv for the tokens of that segment (the paper's
  *        per-segment SVD of recompressed segments, section 5.4; the reading
  *        notes' heterogeneous double buffering)
+ *   group (nullable): per segment, the channels per kept group (0 or 1: single
+ *        channels, orc_topr; else orc_topr_groups)
  *   Khat, Vhat [len][d]: stored values, 0 at dropped channels
  *   Kidx, Vidx [len][d]: kept channels ascending, then -1 (dense tokens: 0..d-1)
  *   meta: packed segments one after the other, each [ceil(t_cap/block)][2][d] (mn, mx)
@@ -291,7 +319,8 @@ static int64_t n_blocks_of(int64_t filled, int block) { return (filled + block -
 int orc_compress_unit(int d, int64_t len, int64_t t_from, int dtype, int block,
                       const double *Kraw, const double *Vraw, const double *Rk, const double *Rv,
                       const double *const *segR, int nseg, const int32_t *kind, const int64_t *t_begin,
-                      const int64_t *t_cap, const int32_t *r, double *Khat, double *Vhat, int16_t *Kidx,
+                      const int64_t *t_cap, const int32_t *r, const int32_t *group, double *Khat, double *Vhat,
+                      int16_t *Kidx,
                       int16_t *Vidx, double *meta, int nthreads) {
     if (t_from < 0) t_from = 0;
     for (int64_t t = t_from; t < len; ++t)
@@ -310,7 +339,8 @@ int orc_compress_unit(int d, int64_t len, int64_t t_from, int dtype, int block,
             int nk;
             if (kind[j] == ORC_PACKED) {
                 nk = r[j];
-                orc_topr(xr, d, nk, keep);
+                if (group && group[j] > 1) orc_topr_groups(xr, d, nk, group[j], keep);
+                else orc_topr(xr, d, nk, keep);
             } else {
                 nk = d;
                 for (int c = 0; c < d; ++c) keep[c] = c;

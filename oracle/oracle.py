@@ -50,11 +50,13 @@ def _lib():
         L.orc_rotation.argtypes = [P, I64, ctypes.c_int, P, P, ctypes.c_int]
         L.orc_topr.restype = None
         L.orc_topr.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        L.orc_topr_groups.restype = None
+        L.orc_topr_groups.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
         L.orc_block_keep.restype = I64
         L.orc_block_keep.argtypes = [I64, I32, I32]
         L.orc_compress_unit.restype = ctypes.c_int
         L.orc_compress_unit.argtypes = [ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P,
-                                        ctypes.c_int, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+                                        ctypes.c_int, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         L.orc_decode_unit.restype = ctypes.c_int
         L.orc_decode_unit.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
                                       ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -111,6 +113,24 @@ def topr(xr, r: int):
     idx = np.empty(r, np.int32)
     _lib().orc_topr(xr.ctypes.data, xr.size, r, idx.ctypes.data)
     return idx
+
+
+def topr_groups(xr, r: int, g: int):
+    """Kept channels (ascending) of the r / g highest-energy groups of g adjacent channels."""
+    xr = _c(xr, np.float64)
+    assert xr.size % g == 0 and r % g == 0
+    idx = np.empty(r, np.int32)
+    _lib().orc_topr_groups(xr.ctypes.data, xr.size, r, g, idx.ctypes.data)
+    return idx
+
+
+def _groups(segs):
+    """Per segment: channels per kept group (1: single channels)."""
+    for s in segs:
+        g = s.get("group", 0) or 1
+        if g > 1 and s["kind"] != DENSE and s["r"] % g:
+            raise ValueError("group %d does not divide r = %d" % (g, s["r"]))
+    return _c([s.get("group", 0) or 1 for s in segs], np.int32)
 
 
 def block_keep(n: int, keep_ppm: int, k_abs: int) -> int:
@@ -184,11 +204,13 @@ def compress_unit(Kraw, Vraw, Rk, Rv, segs, length: int, dtype: str, block: int 
             st["seg_rot"] = seg_rot
     tab, _rot_arrays = _seg_rot_table(st.get("seg_rot"), len(segs), d)
     t_from = st["length"]
+    grp = _groups(segs)
     Kin = _c(Kraw[:length], np.float64)
     Vin = _c(Vraw[:length], np.float64)
     rc = _lib().orc_compress_unit(d, length, t_from, DTYPES[dtype], block, Kin.ctypes.data, Vin.ctypes.data,
                                   Rk.ctypes.data, Rv.ctypes.data, tab, len(segs), kind.ctypes.data,
-                                  tb.ctypes.data, cap.ctypes.data, r.ctypes.data, st["Khat"].ctypes.data,
+                                  tb.ctypes.data, cap.ctypes.data, r.ctypes.data, grp.ctypes.data,
+                                  st["Khat"].ctypes.data,
                                   st["Vhat"].ctypes.data, st["Kidx"].ctypes.data, st["Vidx"].ctypes.data,
                                   st["meta_flat"].ctypes.data, nthreads or threads())
     if rc != 0:

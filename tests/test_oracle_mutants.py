@@ -88,6 +88,17 @@ MUTANTS = [
     # the scores sum the trailing channels instead of the leading ones
     ("key_channels_trailing", "for (int c = 0; c < m; ++c) {", "for (int c = d - m; c < d; ++c) {",
      [pins.test_key_channels_score_equals_full_score_of_masked_query]),
+    # group energies leave out each group's last channel
+    ("group_energy_drops_last", "for (int m = 0; m < g; ++m) {\n            const double v = xr[g * i + m];",
+     "for (int m = 0; m < g - 1; ++m) {\n            const double v = xr[g * i + m];",
+     [pins.test_group_topr_matches_subset_enumeration, pins.test_group_topr_with_one_channel_per_group_is_per_element_topr]),
+    # groups of strided instead of adjacent channels
+    ("group_strided", "const double v = xr[g * i + m];", "const double v = xr[i + ng * m];",
+     [pins.test_group_topr_matches_subset_enumeration, pins.test_group_topr_with_one_channel_per_group_is_per_element_topr]),
+    # the kept groups are the lowest-energy ones
+    ("group_lowest_kept", "for (int m = 0; m < g; ++m) idx[n++] = g * tmp[k].c + m;",
+     "for (int m = 0; m < g; ++m) idx[n++] = g * tmp[ng - 1 - k].c + m;",
+     [pins.test_group_topr_matches_subset_enumeration]),
     # incremental appends skip the first new token
     ("incremental_skips_first_token", "for (int64_t t = t_from; t < len; ++t) {\n        const int j",
      "for (int64_t t = t_from + 1; t < len; ++t) {\n        const int j",

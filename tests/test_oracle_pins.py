@@ -580,3 +580,67 @@ def test_key_channels_score_equals_full_score_of_masked_query():
         assert not np.array_equal(res["scores"][0], ref_full["scores"][0])
         forced = orc.decode_unit(comp, q, eye, eye, forced_sel=res["sel"])
         assert np.array_equal(res["out"].view(np.uint64), forced["out"].view(np.uint64))
+
+
+# -------------------------------------------------------- element groups --
+def test_group_topr_matches_subset_enumeration():
+    """One position bit per group of g adjacent channels (the paper summary's
+    5.1): the kept channels are the union of the r / g groups of largest total
+    energy, found by enumerating every choice of groups with exact rational
+    energies (ties: the lexicographically smallest choice); small integer
+    inputs make exact ties."""
+    for d, g in ((8, 2), (8, 4), (12, 2), (12, 4), (16, 8)):
+        rng = np.random.default_rng(100 * d + g)
+        for trial in range(30):
+            if trial % 3 == 0:
+                x = rng.integers(-3, 4, d).astype(np.float64)
+            else:
+                x = rng.standard_normal(d) * 10.0 ** rng.integers(-3, 3, d)
+            for r in range(g, d + 1, g):
+                assert orc.topr_groups(x, r, g).tolist() == brute.topr_group_subsets(x, r, g).tolist(), (x, r, g)
+
+
+def test_group_topr_with_one_channel_per_group_is_per_element_topr():
+    """With one nonzero channel per group, a group's energy is that channel's
+    square, so the kept groups are those of the per-element top-(r / g) (P3,
+    P6); a group with its energy split over its channels still ranks by the
+    sum."""
+    rng = np.random.default_rng(5)
+    for g in (2, 4, 8):
+        d = 64
+        for trial in range(20):
+            x = np.zeros(d)
+            off = rng.integers(0, g, d // g)
+            x[np.arange(d // g) * g + off] = rng.standard_normal(d // g)
+            for r in (g, 4 * g, 8 * g):
+                top = orc.topr(x, r // g)
+                exp = sorted(g * (c // g) + m for c in top for m in range(g))
+                assert orc.topr_groups(x, r, g).tolist() == exp
+    # equal energies (9 + 16 = 0 + 25) tie to the lower group
+    x = np.array([3.0, 4.0, 0.0, 5.0, 1.0, 1.0])
+    assert orc.topr_groups(x, 2, 2).tolist() == [0, 1]
+    x = np.array([0.0, 5.0, 3.0, 4.0, 1.0, 1.0])
+    assert orc.topr_groups(x, 2, 2).tolist() == [0, 1]
+    x = np.array([1.0, 1.0, 1.0, 1.0, 0.0, 1.9])
+    assert orc.topr_groups(x, 2, 2).tolist() == [4, 5]
+
+
+def test_group_compression_keeps_whole_groups():
+    """A packed segment with element groups stores, per vector, whole groups in
+    ascending channel order -- exactly the channels of topr_groups of its
+    rotated vector -- and its block keys come from those stored values."""
+    K, V, Rk, Rv, _ = _small_unit(T=90, d=16, r=8)
+    segs = [synth.seg(1, 0, 90, 8, 1000000, 0)]
+    segs[0]["group"] = 4
+    comp = orc.compress_unit(K, V, Rk, Rv, segs, 90, "bf16")
+    for t in range(90):
+        for raw, R, idx in ((K, Rk, comp["Kidx"]), (V, Rv, comp["Vidx"])):
+            xr = [0.0] * 16
+            for c in range(16):  # the oracle's order: j ascending, each product and sum rounded
+                acc = 0.0
+                for j in range(16):
+                    acc += R[c, j] * raw[t, j]
+                xr[c] = acc
+            assert idx[t, :8].tolist() == orc.topr_groups(np.array(xr), 8, 4).tolist()
+            assert np.all(idx[t, 8:] == -1)
+            assert np.all(np.diff(idx[t, :8].reshape(2, 4), axis=1) == 1)

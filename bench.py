@@ -108,7 +108,7 @@ def union_summary(w, lengths, sel):
                 uni += len(np.unique(blocks))
             col += k
             rows.append(dict(kind="packed", filled=filled, r=s["r"], n_blocks=nb, union=uni,
-                             bitmap=s["kind"] == synth.BITMAP, key_ch=s.get("key_ch", 0)))
+                             bitmap=s["kind"] == synth.BITMAP, key_ch=s.get("key_ch", 0), group=s.get("group", 0)))
         out.append(rows)
     return out
 
@@ -247,6 +247,8 @@ def main():
                     help="position format of the packed records: u8 channel indices (default) or bitmaps")
     ap.add_argument("--key-ch", type=int, default=0,
                     help="block keys over the leading N rotated channels of every packed segment (0: all)")
+    ap.add_argument("--group", type=int, default=0, choices=[0, 1, 2, 4, 8],
+                    help="every packed segment keeps whole groups of N adjacent channels (0: single channels)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a streaming scale kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -262,6 +264,8 @@ def main():
         w["segs"] = synth.as_bitmap(w["segs"])
     if args.key_ch:
         w["segs"] = synth.with_key_channels(w["segs"], args.key_ch)
+    if args.group > 1:
+        w["segs"] = synth.with_groups(w["segs"], args.group)
     T0 = np.asarray(w["lengths"], np.int64)
     B, hq, hkv, d, dt = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["d"], w["dtype"]
     n_step_total = W_steps + 2 * K_steps + 1
@@ -365,7 +369,7 @@ def main():
     sb = 2 if dt == "bf16" else 4
     call = bm.decode_call_bytes(d, sb, hkv, B, hq, summ)
     r_new = [s["r"] for s in w["segs"][0] if synth.is_packed(s["kind"])][-1]
-    append = bm.append_bytes(d, sb, hkv, B, r_new, args.layout == "bitmap", args.key_ch)
+    append = bm.append_bytes(d, sb, hkv, B, r_new, args.layout == "bitmap", args.key_ch, args.group)
     step_bytes = call["total"] + append
     # algorithmic bytes each kernel of the step must move (the query rotation
     # runs in the append's launch: it reads R_k and the queries, writes q')
@@ -453,6 +457,7 @@ def main():
             "storage": dt,
             "record_positions": "bitmap" if args.layout == "bitmap" else "u8 indices",
             "key_channels": args.key_ch or d,
+            "element_group": max(args.group, 1),
             "parallelism": "single GPU",
             "layer_caches": n_layers,
         },

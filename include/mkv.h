@@ -94,8 +94,15 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1, MKV_SEG_BITMAP = 2 } mkv_s
  *           rotation orders channels by descending singular value), and block
  *           scores sum over those channels only. 0 means all head_dim
  *           channels; otherwise a multiple of 8 in 8..head_dim.
+ * group     packed only: 0 or 1, each vector keeps its own r largest elements;
+ *           2, 4 or 8 (dividing r), it keeps whole groups of `group` adjacent
+ *           channels ([S] 5.1: one position bit per group of adjacent
+ *           elements; [S] 4.3: the element-group size): the r / group groups
+ *           i (channels group*i ...) of largest energy sum_m x'^2 (binary64,
+ *           each square and sum rounded, m ascending), ties to the lower
+ *           group. Bitmap records then hold one bit per group.
  * Across the requests of one cache, segment j must have the same kind, r,
- * keep_ppm, k_abs and key_ch; t_begin, t_cap and rot may differ per request.
+ * keep_ppm, k_abs, key_ch and group; t_begin, t_cap and rot may differ per request.
  *
  * Device layouts (s = bytes per stored element, nb = ceil(t_cap / 16),
  * block l holds positions t_begin + 16 l .. t_begin + 16 l + 15, slot = position - block start):
@@ -104,11 +111,11 @@ typedef enum { MKV_SEG_DENSE = 0, MKV_SEG_PACKED = 1, MKV_SEG_BITMAP = 2 } mkv_s
  *                K values [16][r] | V values [16][r] | K indices [16][r] u8 |
  *                V indices [16][r] u8; each vector's kept channels in ascending
  *                channel order. Slots of a block past its last token are zero.
- *   bitmap data: [n_kv_heads][nb][record], record of 16 * r * 2 * s + 2 * 16 * d / 8
- *                bytes = K values [16][r] | V values [16][r] | K bitmaps [16][d / 8] |
- *                V bitmaps [16][d / 8]; bit c % 8 of byte c / 8 of a vector's
- *                bitmap is set iff channel c is kept; values in ascending channel
- *                order, as above.
+ *   bitmap data: [n_kv_heads][nb][record], record of 16 * r * 2 * s + 2 * 16 * n / 8
+ *                bytes, n = d / max(group, 1) bits per vector = K values [16][r] |
+ *                V values [16][r] | K bitmaps [16][n / 8] | V bitmaps [16][n / 8];
+ *                bit i % 8 of byte i / 8 of a vector's bitmap is set iff channel i
+ *                (group i) is kept; values in ascending channel order, as above.
  *                MKV_PACKED_TAIL_BYTES follow the last record: decode reads
  *                whole dwords around each record's fields and may touch them
  *                (their contents are never used, nothing writes them).
@@ -131,7 +138,7 @@ typedef struct mkv_segment {
     void *meta;
     const float *rot;
     int32_t key_ch;
-    int32_t reserved; /* 0 */
+    int32_t group;
 } mkv_segment;
 
 /* A compressed cache for one attention layer of a batch of requests.
@@ -174,10 +181,11 @@ mkv_status mkv_rotation_from_prefill(const void *x_host, int32_t dtype, int64_t 
                                      float *R_out, double *sigma_out);
 
 /* Bytes of the device buffers of one segment: returns the data bytes and
- * writes the meta bytes (0 for dense) to meta_bytes_out (nullable). key_ch is
- * that of mkv_segment.key_ch, ignored for dense. Returns 0 for invalid arguments. */
+ * writes the meta bytes (0 for dense) to meta_bytes_out (nullable). key_ch and
+ * group are those of mkv_segment, ignored for dense. Returns 0 for invalid
+ * arguments. */
 size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads,
-                         int64_t t_cap, int32_t key_ch, size_t *meta_bytes_out);
+                         int64_t t_cap, int32_t key_ch, int32_t group, size_t *meta_bytes_out);
 
 /* Compress and append new tokens ([N] Eq. 7-9, Algorithm 1; [S] 4.2, 5.2, 5.4:
  * new vectors are rotated by the head's R, keep their top-r elements and are
@@ -261,8 +269,9 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
  *   bit patterns), n_tokens in 1..t_cap.
  * Outputs in the documented device layouts, in host memory the caller owns:
  * kind: the segment's record format, MKV_SEG_PACKED or MKV_SEG_BITMAP;
- * key_ch: its block-key channels, as in mkv_segment.
- *   data_out [mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap, key_ch)]
+ * key_ch, group: its block-key channels and element-group size, as in
+ * mkv_segment.
+ *   data_out [mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap, key_ch, group)]
  *     (slots after the last token zero; the tail bytes are left as they are),
  *   meta_out [that call's meta bytes] (blocks past the last one zero),
  *   rot_out float32 [n_kv_heads][2][d][d].
@@ -271,7 +280,7 @@ mkv_status mkv_append_decode(mkv_cache *c, const void *k_new, const void *v_new,
  * MKV_ERR_NOCONVERGE. */
 mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
                                   int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t kind, int32_t r,
-                                  int32_t key_ch, void *data_out, void *meta_out, float *rot_out);
+                                  int32_t key_ch, int32_t group, void *data_out, void *meta_out, float *rot_out);
 
 /* Segment strategy generation ([S] 4.3 and 5.5: output caches start a new
  * segment when the accumulated compression loss exceeds a threshold or at the

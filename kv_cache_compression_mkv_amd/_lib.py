@@ -37,7 +37,7 @@ class mkv_segment(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("keep_ppm", ctypes.c_int32),
                 ("k_abs", ctypes.c_int32), ("t_begin", ctypes.c_int64), ("t_cap", ctypes.c_int64),
                 ("data", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("rot", ctypes.c_void_p),
-                ("key_ch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("key_ch", ctypes.c_int32), ("group", ctypes.c_int32)]
 
 
 class mkv_cache(ctypes.Structure):
@@ -63,7 +63,7 @@ def _load():
     L.mkv_rotation_from_prefill.restype = ctypes.c_int
     L.mkv_rotation_from_prefill.argtypes = [P, I32, I64, I32, P, P]
     L.mkv_segment_bytes.restype = SZ
-    L.mkv_segment_bytes.argtypes = [I32, I32, I32, I32, I32, I64, I32, ctypes.POINTER(SZ)]
+    L.mkv_segment_bytes.argtypes = [I32, I32, I32, I32, I32, I64, I32, I32, ctypes.POINTER(SZ)]
     L.mkv_compress_append.restype = ctypes.c_int
     L.mkv_compress_append.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P]
     L.mkv_block_meta.restype = ctypes.c_int
@@ -77,7 +77,7 @@ def _load():
     L.mkv_append_decode.restype = ctypes.c_int
     L.mkv_append_decode.argtypes = [ctypes.POINTER(mkv_cache), P, P, P, I32, P, P, P, I64, P, SZ, P]
     L.mkv_recompress_segment.restype = ctypes.c_int
-    L.mkv_recompress_segment.argtypes = [P, P, I32, I32, I32, I64, I64, I32, I32, I32, P, P, P]
+    L.mkv_recompress_segment.argtypes = [P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32, P, P, P]
     L.mkv_strategy_loss_curve.restype = ctypes.c_int
     L.mkv_strategy_loss_curve.argtypes = [P, P, I32, I32, I32, I64, I64, P, P]
     L.mkv_strategy_segments.restype = ctypes.c_int
@@ -113,9 +113,10 @@ def mkv_rotation_from_prefill(x_ptr: int, dtype: int, T: int, d: int, R_out_ptr:
            "mkv_rotation_from_prefill")
 
 
-def mkv_segment_bytes(dtype: int, kind: int, r: int, d: int, n_kv_heads: int, t_cap: int, key_ch: int = 0):
+def mkv_segment_bytes(dtype: int, kind: int, r: int, d: int, n_kv_heads: int, t_cap: int, key_ch: int = 0,
+                      group: int = 0):
     meta = ctypes.c_size_t(0)
-    data = LIB.mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap, key_ch, ctypes.byref(meta))
+    data = LIB.mkv_segment_bytes(dtype, kind, r, d, n_kv_heads, t_cap, key_ch, group, ctypes.byref(meta))
     return int(data), int(meta.value)
 
 
@@ -149,8 +150,9 @@ def mkv_append_decode(cache: mkv_cache, k_ptr: int, v_ptr: int, n_new_ptr: int, 
 
 
 def mkv_recompress_segment(k_ptr: int, v_ptr: int, dtype: int, d: int, n_kv_heads: int, n_tokens: int, t_cap: int,
-                           kind: int, r: int, data_ptr: int, meta_ptr: int, rot_ptr: int, key_ch: int = 0):
-    _check(LIB.mkv_recompress_segment(k_ptr, v_ptr, dtype, d, n_kv_heads, n_tokens, t_cap, kind, r, key_ch,
+                           kind: int, r: int, data_ptr: int, meta_ptr: int, rot_ptr: int, key_ch: int = 0,
+                           group: int = 0):
+    _check(LIB.mkv_recompress_segment(k_ptr, v_ptr, dtype, d, n_kv_heads, n_tokens, t_cap, kind, r, key_ch, group,
                                       data_ptr, meta_ptr, rot_ptr), "mkv_recompress_segment")
 
 

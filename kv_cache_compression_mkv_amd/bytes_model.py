@@ -19,9 +19,10 @@ def dense_kv_bytes(tokens: int, d: int, s: int) -> int:
     return 2 * tokens * d * s
 
 
-def packed_record_bytes(r: int, s: int, bitmap: bool = False, d: int = 128) -> int:
-    """One block record: K and V values, then u8 indices or (bitmap) d-bit position bitmaps."""
-    return BLOCK * r * 2 * s + (2 * BLOCK * (d // 8) if bitmap else BLOCK * r * 2)
+def packed_record_bytes(r: int, s: int, bitmap: bool = False, d: int = 128, group: int = 0) -> int:
+    """One block record: K and V values, then u8 indices or (bitmap) position bitmaps of one
+    bit per channel, or per group of `group` channels."""
+    return BLOCK * r * 2 * s + (2 * BLOCK * (d // 8 // max(group, 1)) if bitmap else BLOCK * r * 2)
 
 
 def meta_block_bytes(d: int, s: int, key_ch: int = 0) -> int:
@@ -71,7 +72,8 @@ def decode_call_bytes(d: int, s: int, hkv: int, batch: int, hq: int, seg_summary
         for sg in req:
             if sg["kind"] == "packed":
                 meta += sg["n_blocks"] * hkv * meta_block_bytes(d, s, sg.get("key_ch", 0))
-                records += sg["union"] * packed_record_bytes(sg["r"], s, sg.get("bitmap", False), d)
+                records += sg["union"] * packed_record_bytes(sg["r"], s, sg.get("bitmap", False), d,
+                                                             sg.get("group", 0))
             else:
                 dense += dense_kv_bytes(sg["filled"], d, s) * hkv
     rot = batch * hkv * 2 * d * d * 4
@@ -80,11 +82,12 @@ def decode_call_bytes(d: int, s: int, hkv: int, batch: int, hq: int, seg_summary
                 total=meta + records + dense + rot + qo)
 
 
-def append_bytes(d: int, s: int, hkv: int, batch: int, r: int, bitmap: bool = False, key_ch: int = 0) -> int:
+def append_bytes(d: int, s: int, hkv: int, batch: int, r: int, bitmap: bool = False, key_ch: int = 0,
+                 group: int = 0) -> int:
     """Algorithmic bytes of appending one token per request to a packed
     segment: per (request, KV head) read R_k and R_v (float32) and the raw key
     and value, write the two packed vectors (r values and r u8 indices, or a
     d-bit bitmap, each) and read and write the block's min/max keys."""
-    pos = d // 8 if bitmap else r
+    pos = d // 8 // max(group, 1) if bitmap else r
     per_unit = 2 * d * d * 4 + 2 * d * s + 2 * (r * s + pos) + 2 * meta_block_bytes(d, s, key_ch)
     return batch * hkv * per_unit

@@ -38,7 +38,7 @@ class Cache:
             drow, mrow = [], []
             for j, s in enumerate(segs[b]):
                 nbytes, mbytes = L.mkv_segment_bytes(self.code, s["kind"], s["r"] or 1, head_dim,
-                                                      n_kv_heads, s["t_cap"], s.get("key_ch", 0))
+                                                      n_kv_heads, s["t_cap"], s.get("key_ch", 0), s.get("group", 0))
                 if nbytes == 0:
                     raise ValueError("invalid segment %r" % (s,))
                 dt = torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -49,6 +49,7 @@ class Cache:
                 e.kind, e.r, e.keep_ppm, e.k_abs = s["kind"], s["r"], s["keep_ppm"], s["k_abs"]
                 e.t_begin, e.t_cap = s["t_begin"], s["t_cap"]
                 e.key_ch = s.get("key_ch", 0)
+                e.group = s.get("group", 0)
                 e.data = dt.data_ptr()
                 e.meta = mt.data_ptr() if mt is not None else None
             self.data.append(drow)
@@ -82,7 +83,7 @@ class Cache:
         uint16). Returns host (data, meta, rot) in the device layouts."""
         s = self.seg_list[b][j]
         nbytes, mbytes = L.mkv_segment_bytes(self.code, s["kind"], s["r"], self.d, self.hkv, s["t_cap"],
-                                             s.get("key_ch", 0))
+                                             s.get("key_ch", 0), s.get("group", 0))
         data = np.zeros(nbytes, np.uint8)
         meta = np.zeros(mbytes, np.uint8)
         rot = np.zeros((self.hkv, 2, self.d, self.d), np.float32)
@@ -90,7 +91,7 @@ class Cache:
         v = np.ascontiguousarray(v_host)
         L.mkv_recompress_segment(k.ctypes.data, v.ctypes.data, self.code, self.d, self.hkv, int(k.shape[1]),
                                  s["t_cap"], s["kind"], s["r"], data.ctypes.data, meta.ctypes.data, rot.ctypes.data,
-                                 s.get("key_ch", 0))
+                                 s.get("key_ch", 0), s.get("group", 0))
         return data, meta, rot
 
     def swap_segment(self, b: int, j: int, data, meta, rot, copy_stream=None):

@@ -281,6 +281,62 @@ __device__ __forceinline__ void topr_keep_nt(const double (&v0)[NT], const doubl
     }
 }
 
+// Element groups (g > 1 adjacent channels kept or dropped together). The
+// energy of group `lane` (channels g lane .. g lane + g - 1) from the rotated
+// channels held as v0 (channel lane) and v1 (channel lane + 64) of every lane:
+// binary64, each square and each sum rounded, channels ascending; 0 on lanes
+// >= D / g. Those zero keys sit above every group's slot, so the top-r search's
+// tie rule (lower slot first) never prefers them to a group of energy 0.
+__device__ __forceinline__ double group_energy(double v0, double v1, int g, int lane) {
+#pragma clang fp contract(off)
+    double e = 0.0;
+    for (int m = 0; m < g; ++m) {
+        const int c = g * lane + m;
+        const double a = __shfl(v0, c & 63, 64), b = __shfl(v1, c & 63, 64);
+        const double x = c < 64 ? a : b;
+        e = e + x * x;
+    }
+    return lane < D / g ? e : 0.0;
+}
+
+// kept flags of channels lane and lane + 64 from the per-group flags (group i on lane i)
+__device__ __forceinline__ void group_expand(bool kg, int g, int lane, bool &keep0, bool &keep1) {
+    const int f = kg ? 1 : 0;
+    keep0 = __shfl(f, lane / g, 64) != 0;
+    keep1 = __shfl(f, (lane + 64) / g, 64) != 0;
+}
+
+// top-r of one token with element groups of g channels (g = 1: single channels)
+__device__ __forceinline__ void topr_keep_g(double v0, double v1, int r, int g, int lane, bool &keep0,
+                                            bool &keep1) {
+    if (g <= 1) {
+        topr_keep(v0, v1, r, lane, keep0, keep1);
+        return;
+    }
+    bool kg, unused;
+    topr_keep(group_energy(v0, v1, g, lane), 0.0, r / g, lane, kg, unused);
+    group_expand(kg, g, lane, keep0, keep1);
+}
+
+template <int NT>
+__device__ __forceinline__ void topr_keep_nt_g(const double (&v0)[NT], const double (&v1)[NT], int nt, int r, int g,
+                                               int lane, bool (&keep0)[NT], bool (&keep1)[NT]) {
+    if (g <= 1) {
+        topr_keep_nt<NT>(v0, v1, nt, r, lane, keep0, keep1);
+        return;
+    }
+    double e[NT], z[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        e[t] = group_energy(v0[t], v1[t], g, lane);
+        z[t] = 0.0;
+    }
+    bool kg[NT], unused[NT];
+    topr_keep_nt<NT>(e, z, nt, r / g, lane, kg, unused);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) group_expand(kg[t], g, lane, keep0[t], keep1[t]);
+}
+
 // Per-block state of one wave's append into block blk of one (entry, KV head,
 // matrix): destination pointers, the new slots [sa, se), the running keys of
 // a packed segment's block (keys matrix only) and the first new row.
@@ -290,7 +346,7 @@ struct BlockJob {
     uint8_t *idxs;
     char *meta_tile;
     const typename ST::bits_t *xin;
-    int p0, sa, se, r, G16, cpg, kch;
+    int p0, sa, se, r, G16, cpg, kch, g;
     bool packed, bitmap, do_meta;
     uint32_t mn0, mx0, mn1, mx1;
     typename ST::bits_t x0, x1;  // row of the first new token (lane's channels; one-token appends)
@@ -311,16 +367,16 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     const int r = E.r;
     char *blkbase;
     if (packed) {
-        const size_t rec = (size_t)record_bytes(E.kind, r, ST::bytes);
+        const size_t rec = (size_t)record_bytes(E.kind, r, ST::bytes, E.group);
         blkbase = static_cast<char *>(E.data) + ((size_t)g * E.nbcap + blk) * rec;
     } else {
         blkbase = static_cast<char *>(E.data) + ((size_t)g * E.nbcap + blk) * 2 * BT * D * ST::bytes;
     }
     bits_t *vals = packed ? reinterpret_cast<bits_t *>(blkbase + (size_t)wave * BT * r * ST::bytes)
                           : reinterpret_cast<bits_t *>(blkbase + (size_t)wave * BT * D * ST::bytes);
-    // u8 indices [16][r], or bitmaps [16][D / 8], of this matrix
+    // u8 indices [16][r], or bitmaps [16][D / 8 / group], of this matrix
     uint8_t *idxs = packed ? reinterpret_cast<uint8_t *>(blkbase + (size_t)2 * BT * r * ST::bytes +
-                                                         (size_t)wave * BT * (bitmap ? D / 8 : r))
+                                                         (size_t)wave * BT * pos_bytes(E.kind, r, E.group))
                            : nullptr;
 
     // per-block keys (keys wave, packed segments) of the leading kch
@@ -367,6 +423,7 @@ __device__ __forceinline__ void block_begin(BlockJob<ST> &J, const CompressArgs 
     J.G16 = G16;
     J.cpg = cpg;
     J.kch = kch;
+    J.g = E.group;
     J.packed = packed;
     J.bitmap = bitmap;
     J.do_meta = do_meta;
@@ -390,12 +447,23 @@ __device__ __forceinline__ void store_kept(BlockJob<ST> &J, int slot, double v0,
         bits_t *vrow = J.vals + (size_t)slot * J.r;
         if (keep0) vrow[popc64(m0 & below)] = s0;
         if (keep1) vrow[popc64(m0) + popc64(m1 & below)] = s1;
-        if (J.bitmap) {
+        if (J.bitmap && J.g <= 1) {
             // bit c of the vector's bitmap: channel c kept (channels lane and lane + 64 of the ballots)
             if (lane == 0) {
                 uint64_t *brow = reinterpret_cast<uint64_t *>(J.idxs + (size_t)slot * (D / 8));
                 brow[0] = m0;
                 brow[1] = m1;
+            }
+        } else if (J.bitmap) {
+            // bit i: group i (channels g i ..) kept, read from its first channel's ballot bit
+            const int c = J.g * lane;
+            const bool kg = lane < D / J.g && (((c < 64 ? m0 >> c : m1 >> (c - 64)) & 1ull) != 0);
+            const uint64_t gb = ballot(kg);
+            if (lane == 0) {
+                uint8_t *brow = J.idxs + (size_t)slot * (D / 8 / J.g);
+                if (J.g == 2) *reinterpret_cast<uint64_t *>(brow) = gb;
+                else if (J.g == 4) *reinterpret_cast<uint32_t *>(brow) = (uint32_t)gb;
+                else *reinterpret_cast<uint16_t *>(brow) = (uint16_t)gb;
             }
         } else {
             uint8_t *irow = J.idxs + (size_t)slot * J.r;
@@ -419,7 +487,7 @@ __device__ __forceinline__ void store_kept(BlockJob<ST> &J, int slot, double v0,
 template <typename ST>
 __device__ __forceinline__ void store_token(BlockJob<ST> &J, int slot, double v0, double v1, int lane) {
     bool keep0 = false, keep1 = false;
-    if (J.packed) topr_keep(v0, v1, J.r, lane, keep0, keep1);
+    if (J.packed) topr_keep_g(v0, v1, J.r, J.g, lane, keep0, keep1);
     store_kept<ST>(J, slot, v0, v1, keep0, keep1, lane);
 }
 
@@ -431,7 +499,7 @@ __device__ __forceinline__ void block_finish(const BlockJob<ST> &J, int blk, int
     if (J.sa == 0 && J.se < BT) {
         if (J.packed) {
             for (int i = J.se * J.r + lane; i < BT * J.r; i += 64) J.vals[i] = (bits_t)0;
-            const int ib = J.bitmap ? D / 8 : J.r;  // position bytes per vector
+            const int ib = J.bitmap ? D / 8 / J.g : J.r;  // position bytes per vector
             for (int i = J.se * ib + lane; i < BT * ib; i += 64) J.idxs[i] = 0;
         } else {
             for (int i = J.se * D + lane; i < BT * D; i += 64) J.vals[i] = (bits_t)0;
@@ -628,7 +696,7 @@ __global__ __launch_bounds__(64 * BULK_WAVES) void k_compress_bulk(const Compres
             }
             bool keep0[BULK_NT], keep1[BULK_NT];
             if (J.packed) {
-                topr_keep_nt<BULK_NT>(a0, a1, nt, J.r, lane, keep0, keep1);
+                topr_keep_nt_g<BULK_NT>(a0, a1, nt, J.r, J.g, lane, keep0, keep1);
             } else {
 #pragma unroll
                 for (int t = 0; t < BULK_NT; ++t) keep0[t] = keep1[t] = false;
@@ -654,7 +722,8 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
     const int lane = lane_id();
     const int r = E.r;
     const bool bitmap = E.kind == MKV_SEG_BITMAP;
-    const size_t rec = (size_t)record_bytes(E.kind, r, ST::bytes);
+    const int gs = E.group;
+    const size_t rec = (size_t)record_bytes(E.kind, r, ST::bytes, gs);
     const char *base = static_cast<const char *>(E.data) + ((size_t)g * E.nbcap + blk) * rec;
     const bits_t *kv = reinterpret_cast<const bits_t *>(base);
     const uint8_t *ki = reinterpret_cast<const uint8_t *>(base + (size_t)2 * BT * r * ST::bytes);
@@ -663,7 +732,17 @@ __global__ __launch_bounds__(64) void k_block_meta(const MetaArgs A) {
     uint32_t mn0 = 0xFFFFFFFFu, mx0 = 0u, mn1 = 0xFFFFFFFFu, mx1 = 0u;
     for (int t = 0; t < nvalid; ++t) {
         bits_t v0, v1;
-        if (bitmap) {
+        if (bitmap && gs > 1) {
+            // channel c is kept with its group c / gs; its rank: gs per kept group before it, plus c % gs
+            const uint8_t *gp = ki + (size_t)t * (D / 8 / gs);
+            uint64_t gb = 0;
+            for (int q = 0; q < D / 8 / gs; ++q) gb |= (uint64_t)gp[q] << (8 * q);
+            const int i0 = lane / gs, i1 = (lane + 64) / gs;
+            const int r0 = gs * popc64(gb & ((1ull << i0) - 1ull)) + lane % gs;
+            const int r1 = gs * popc64(gb & ((i1 >= 64 ? 0ull : (1ull << i1)) - 1ull)) + (lane + 64) % gs;
+            v0 = ((gb >> i0) & 1ull) ? kv[t * r + r0] : (bits_t)0;
+            v1 = ((gb >> i1) & 1ull) ? kv[t * r + r1] : (bits_t)0;
+        } else if (bitmap) {
             // channel c is the rank(c)-th kept element of the token
             const uint64_t *bm = reinterpret_cast<const uint64_t *>(ki + (size_t)t * (D / 8));
             const uint64_t m0 = bm[0], m1 = bm[1];

@@ -1245,10 +1245,11 @@ struct PkGeom {
     uint32_t o_kv, o_vv, o_ki, o_vi;  // window offsets in the record
     uint32_t sv, si;                  // byte shifts of the value / index windows
     uint32_t o_bk, o_bv;              // bitmap records: the token's K and V bitmaps
+    int g;                            // bitmap records: channels per position bit
     uint32_t l_ki, l_vi;              // bitmap records: index windows in the wave's LDS index buffer
     int cnt;                          // elements of this lane's part
     int row;                          // t * 128: this token's tile row
-    __device__ __forceinline__ void init(int r) {
+    __device__ __forceinline__ void init(int r, int gsz) {
         const int lane = lane_id();
         const int t = lane >> 2, p = lane & 3;
         const int Q = (r + 3) >> 2;
@@ -1262,8 +1263,10 @@ struct PkGeom {
         o_vv = reg + o_kv;
         o_ki = 2 * reg + (e0 & ~3u);
         o_vi = o_ki + (uint32_t)BT * r;
-        o_bk = 2 * reg + (uint32_t)t * (D / 8);
-        o_bv = o_bk + (uint32_t)BT * (D / 8);
+        g = gsz;
+        const uint32_t vb_bytes = (uint32_t)(D / 8 / gsz);  // one vector's bitmap
+        o_bk = 2 * reg + (uint32_t)t * vb_bytes;
+        o_bv = o_bk + (uint32_t)BT * vb_bytes;
         l_ki = e0 & ~3u;
         l_vi = l_ki + (uint32_t)BT * r;
         row = t * D;
@@ -1275,8 +1278,12 @@ __device__ __forceinline__ void load_win(const char *rec, const PkGeom<ST, QM> &
     load_words(rec + gm.o_kv, W.kv);
     load_words(rec + gm.o_vv, W.vv);
     if constexpr (BM) {
-        W.bk = *reinterpret_cast<const uint4 *>(rec + gm.o_bk);
-        W.bv = *reinterpret_cast<const uint4 *>(rec + gm.o_bv);
+        // the 16-byte aligned window holding the token's bitmap (all of it for
+        // one bit per channel; 8, 4 or 2 bytes of it with element groups)
+        const W4 a = *reinterpret_cast<const W4 *>(rec + (gm.o_bk & ~15u));
+        const W4 b = *reinterpret_cast<const W4 *>(rec + (gm.o_bv & ~15u));
+        W.bk = make_uint4(a.x, a.y, a.z, a.w);
+        W.bv = make_uint4(b.x, b.y, b.z, b.w);
     } else {
         load_words(rec + gm.o_ki, W.ki);
         load_words(rec + gm.o_vi, W.vi);
@@ -1293,6 +1300,31 @@ __device__ __forceinline__ void bitmap_positions(const uint4 b, int p, uint8_t *
     int pos = (p > 0 ? c0 : 0) + (p > 1 ? c1 : 0) + (p > 2 ? c2 : 0);
     while (w) {
         dst[pos++] = (uint8_t)(32 * p + __builtin_ctz(w));
+        w &= w - 1u;
+    }
+}
+
+// Bitmap records with element groups of g channels (bit i: channels g i ..
+// g i + g - 1 kept): the token's group bits are the bytes at `off` (0..15) of
+// the 16-byte window w. Lane p of a token writes the channels of its groups
+// in channels 32 p .. 32 p + 31, g bytes per group as one aligned store (r is
+// a multiple of g, so every group's rank is), at rank g * (groups before it).
+__device__ __forceinline__ uint64_t group_bits(const uint4 w, uint32_t off, int g) {
+    const uint64_t lo = ((uint64_t)w.y << 32) | w.x, hi = ((uint64_t)w.w << 32) | w.z;
+    const uint64_t x = ((off & 8u) ? hi : lo) >> (8 * (off & 7u));
+    const int n = D / g;  // bits
+    return n >= 64 ? x : (x & ((1ull << n) - 1ull));
+}
+__device__ __forceinline__ void group_positions(uint64_t gb, int g, int p, uint8_t *dst) {
+    const int gw = 32 / g, i0 = p * gw;  // groups per lane, the lane's first group
+    uint32_t w = (uint32_t)((gb >> i0) & ((1ull << gw) - 1ull));
+    int pos = g * __popcll(gb & ((1ull << i0) - 1ull));
+    while (w) {
+        const uint32_t c = (uint32_t)(g * (i0 + __builtin_ctz(w)));
+        if (g == 2) *reinterpret_cast<uint16_t *>(dst + pos) = (uint16_t)(c | ((c + 1u) << 8));
+        else if (g == 4) *reinterpret_cast<uint32_t *>(dst + pos) = c * 0x01010101u + 0x03020100u;
+        else *reinterpret_cast<uint64_t *>(dst + pos) = (uint64_t)c * 0x0101010101010101ull + 0x0706050403020100ull;
+        pos += g;
         w &= w - 1u;
     }
 }
@@ -1410,8 +1442,13 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM, BM> &W, const PkGeom
         // the record's u8 indices, decoded from its bitmaps into the wave's
         // LDS buffer ([16][r] K then [16][r] V), then read as index windows
         const int t = lane >> 2, p = lane & 3;
-        bitmap_positions(W.bk, p, ib + t * r);
-        bitmap_positions(W.bv, p, ib + BT * r + t * r);
+        if (gm.g > 1) {
+            group_positions(group_bits(W.bk, gm.o_bk & 15u, gm.g), gm.g, p, ib + t * r);
+            group_positions(group_bits(W.bv, gm.o_bv & 15u, gm.g), gm.g, p, ib + BT * r + t * r);
+        } else {
+            bitmap_positions(W.bk, p, ib + t * r);
+            bitmap_positions(W.bv, p, ib + BT * r + t * r);
+        }
         wave_lds_sync();
         lds_words(ib + gm.l_ki, wki);
         lds_words(ib + gm.l_vi, wvi);
@@ -1490,11 +1527,11 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM, BM> &W, const PkGeom
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <typename ST, int G, int QM, bool BM>
-__device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_base, size_t rec, int r,
+__device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_base, size_t rec, int r, int gsz,
                                        int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L, PkState<G> &S,
                                        uint8_t *ib) {
     PkGeom<ST, QM> gm;
-    gm.init(r);
+    gm.init(r, gsz);
     constexpr int WN = PkWin<ST, QM, BM>::LOADS;
     PkWin<ST, QM, BM> B0, B1;
     // a load past the end of the list repeats its last record, so every step
@@ -1518,14 +1555,14 @@ __device__ __forceinline__ void pk_run(const int2 *list, int n, const char *seg_
 // index buffer for them)
 template <typename ST, int G, int QA, int QB, bool BM>
 __device__ __forceinline__ void run_records(const int2 *list, int n, const char *seg_base, size_t rec, int r,
-                                            int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L,
+                                            int gsz, int filled, const float (*qsh)[2 * D], PkLds<ST, G> &L,
                                             PkState<G> &S, uint8_t *ib) {
-    if (((r + 3) >> 2) <= QA) pk_run<ST, G, QA, BM>(list, n, seg_base, rec, r, filled, qsh, L, S, ib);
-    else pk_run<ST, G, QB, BM>(list, n, seg_base, rec, r, filled, qsh, L, S, ib);
+    if (((r + 3) >> 2) <= QA) pk_run<ST, G, QA, BM>(list, n, seg_base, rec, r, gsz, filled, qsh, L, S, ib);
+    else pk_run<ST, G, QB, BM>(list, n, seg_base, rec, r, gsz, filled, qsh, L, S, ib);
 }
 
-__device__ __forceinline__ int64_t packed_weight(int kind, int r, int sb, int G) {
-    const int64_t rec = record_bytes(kind, r, sb);
+__device__ __forceinline__ int64_t packed_weight(int kind, int r, int gsz, int sb, int G) {
+    const int64_t rec = record_bytes(kind, r, sb, gsz);
     return (G > 1 ? rec * 4 / 5 : rec) + 256;
 }
 
@@ -1704,7 +1741,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
     for (int si = 0; si < A.nseg; ++si) {
         const DSeg &Sg = seg_of(A, bl, si);
         if (packed_kind(Sg.kind) && Sg.slot == A.cur_slot)
-            W += (int64_t)G * Sg.k * packed_weight(Sg.kind, Sg.r, sb, G);
+            W += (int64_t)G * Sg.k * packed_weight(Sg.kind, Sg.r, Sg.group, sb, G);
     }
     const int64_t lo = W * s / A.S_p, hi = W * (s + 1) / A.S_p;
     int64_t Wb = 0;
@@ -1714,7 +1751,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
         if (!packed_kind(Sg.kind)) continue;
         const int myj = pj++;
         if (Sg.slot != A.cur_slot) continue;
-        const int64_t w = packed_weight(Sg.kind, Sg.r, sb, G);
+        const int64_t w = packed_weight(Sg.kind, Sg.r, Sg.group, sb, G);
         const int64_t items = (int64_t)G * Sg.k;
         int64_t i0 = lo - Wb, i1 = hi - Wb;
         i0 = i0 <= 0 ? 0 : (i0 + w - 1) / w;
@@ -1724,7 +1761,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
         Wb += items * w;
         if (i0 >= i1) continue;
         const int r = Sg.r;
-        const size_t rec = (size_t)record_bytes(Sg.kind, r, sb);
+        const size_t rec = (size_t)record_bytes(Sg.kind, r, sb, Sg.group);
         const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
         const int kc = A.kcap[myj];
         const int32_t *sel = A.sel + A.sl_off[myj] + ((size_t)b * A.hq + g * G) * kc;
@@ -1748,7 +1785,7 @@ __device__ __forceinline__ void attend_packed_split(const DecodeArgs &A, int bl,
             if (keep) list[popc64(km & lanes_below(lane))] = make_int2(blk, hm);
             const int n = popc64(km);
             wave_lds_sync();
-            if (n > 0) run_records<ST, G, QA, QB, BM>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S, ib);
+            if (n > 0) run_records<ST, G, QA, QB, BM>(list, n, seg_base, rec, r, Sg.group, Sg.filled, qsh, L, S, ib);
             wave_lds_sync();
         }
     }
@@ -1846,7 +1883,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
         const DSeg &Sg = seg_of(A, bl, A.pseg[min(j, npk - 1)]);
         nbj[j] = (j < npk && Sg.slot == A.cur_slot) ? Sg.nb : 0;
         rj[j] = Sg.r;
-        wj[j] = (uint32_t)(record_bytes(Sg.kind, Sg.r, sb) + UNION_RECORD_FIXED);
+        wj[j] = (uint32_t)(record_bytes(Sg.kind, Sg.r, sb, Sg.group) + UNION_RECORD_FIXED);
     }
     uint32_t w[UNION_MAX_SEGS][16];
 #pragma unroll
@@ -1926,7 +1963,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
         if (v0 >= v1) continue;
         const DSeg &Sg = seg_of(A, bl, A.pseg[j]);
         const int r = rj[j];
-        const size_t rec = (size_t)record_bytes(Sg.kind, r, sb);
+        const size_t rec = (size_t)record_bytes(Sg.kind, r, sb, Sg.group);
         const char *seg_base = static_cast<const char *>(Sg.data) + (size_t)g * Sg.nbcap * rec;
         for (int base = v0; base < v1; base += 64) {
             // (the host bounds the workgroup's entries by UNION_CAP; the clamp
@@ -1938,7 +1975,7 @@ __device__ __forceinline__ void attend_packed_union(const DecodeArgs &A, int bl,
                 list[lane] = make_int2((int)(e & 0xFFFFu), (int)(e >> 16));
             }
             wave_lds_sync();
-            run_records<ST, G, QA, QB, BM>(list, n, seg_base, rec, r, Sg.filled, qsh, L, S, ib);
+            run_records<ST, G, QA, QB, BM>(list, n, seg_base, rec, r, Sg.group, Sg.filled, qsh, L, S, ib);
             wave_lds_sync();
         }
     }

@@ -118,7 +118,7 @@ mkv_status check_cache(const mkv_cache *c) {
             if (s.kind != MKV_SEG_DENSE && !packed_kind(s.kind)) return MKV_ERR_ARG;
             if (s.t_begin != t || s.t_cap < 1 || !s.data) return MKV_ERR_ARG;
             if (s.kind != s0.kind || s.r != s0.r || s.keep_ppm != s0.keep_ppm || s.k_abs != s0.k_abs ||
-                s.key_ch != s0.key_ch)
+                s.key_ch != s0.key_ch || s.group != s0.group)
                 return MKV_ERR_ARG;
             if (packed_kind(s.kind)) {
                 // one position format per cache (u8 indices or bitmaps)
@@ -127,7 +127,9 @@ mkv_status check_cache(const mkv_cache *c) {
                 if (s.kind == MKV_SEG_BITMAP && c->head_dim != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
                 if (s.r < 1 || s.r > c->head_dim || !s.meta || s.k_abs < 0) return MKV_ERR_ARG;
                 if (s.key_ch < 0 || s.key_ch > c->head_dim || s.key_ch % 8) return MKV_ERR_ARG;
-                if (s.reserved != 0) return MKV_ERR_ARG;
+                if (s.group != 0 && s.group != 1 && s.group != 2 && s.group != 4 && s.group != 8)
+                    return MKV_ERR_ARG;
+                if (s.r % group_size(s.group)) return MKV_ERR_ARG;
                 if (s.k_abs == 0 && (s.keep_ppm < 1 || s.keep_ppm > 1000000)) return MKV_ERR_ARG;
                 if (ceil_div(s.t_cap, BT) > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
             }
@@ -291,8 +293,9 @@ mkv_status append_enqueue(mkv_cache *c, const void *k_new, const void *v_new, co
             E.e = (int32_t)e;
             E.row0 = (int32_t)(sg.t_begin + a - p0);
             E.b = b;
-            E.r = (int16_t)sg.r;
+            E.r = (uint8_t)sg.r;
             E.kind = (int8_t)sg.kind;
+            E.group = (uint8_t)group_size(sg.group);
             E.kch = (uint8_t)key_channels(sg.key_ch);
             E.blk0 = (int32_t)(a / BT);
             E.nblk = (int32_t)((e - 1) / BT - a / BT + 1);
@@ -354,7 +357,7 @@ void plan_splits(DecodeArgs &A, const mkv_cache *c, int slot, int G, int sb, int
             const DSeg &D_ = A.seg[i * c->n_segments + j];
             if (D_.slot != slot) continue;
             if (packed_kind(D_.kind)) {
-                const int64_t rec = record_bytes(D_.kind, D_.r, sb);
+                const int64_t rec = record_bytes(D_.kind, D_.r, sb, D_.group);
                 W += (int64_t)G * D_.k * ((G > 1 ? rec * 4 / 5 : rec) + 256);
                 max_nb = std::max(max_nb, D_.nb);
             } else {
@@ -387,7 +390,7 @@ void plan_splits(DecodeArgs &A, const mkv_cache *c, int slot, int G, int sb, int
                 const DSeg &D_ = A.seg[i * c->n_segments + j];
                 if (!packed_kind(D_.kind) || D_.slot != slot) continue;
                 u += std::min<int64_t>((int64_t)G * D_.k, D_.nb);
-                const int64_t w = record_bytes(D_.kind, D_.r, sb) + UNION_RECORD_FIXED;
+                const int64_t w = record_bytes(D_.kind, D_.r, sb, D_.group) + UNION_RECORD_FIXED;
                 wmin = std::min(wmin, w);
                 wmax = std::max(wmax, w);
             }
@@ -453,7 +456,8 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                 D_.data = sg.data;
                 D_.meta = sg.meta;
                 D_.rot = sg.rot;
-                D_.kind = (int16_t)sg.kind;
+                D_.kind = (int8_t)sg.kind;
+                D_.group = (int8_t)group_size(sg.group);
                 // a segment index with a slot of its own keeps that slot in
                 // every request; requests whose segment has no own rotation
                 // there use the cache's, through the slot's launch
@@ -536,7 +540,7 @@ const char *mkv_status_str(mkv_status s) {
 }
 
 size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int32_t n_kv_heads, int64_t t_cap,
-                         int32_t key_ch, size_t *meta_bytes_out) {
+                         int32_t key_ch, int32_t group, size_t *meta_bytes_out) {
     if (meta_bytes_out) *meta_bytes_out = 0;
     if ((dtype != MKV_F32 && dtype != MKV_BF16) || d < 1 || n_kv_heads < 1 || t_cap < 1) return 0;
     const size_t s = elem_bytes(dtype);
@@ -544,11 +548,12 @@ size_t mkv_segment_bytes(int32_t dtype, int32_t kind, int32_t r, int32_t d, int3
     if (kind == MKV_SEG_DENSE) return (size_t)n_kv_heads * nb * 2 * BT * d * s;
     if (!packed_kind(kind) || r < 1 || r > d || (kind == MKV_SEG_BITMAP && d != D)) return 0;
     if (key_ch < 0 || key_ch > d || key_ch % 8) return 0;
+    if ((group != 0 && group != 1 && group != 2 && group != 4 && group != 8) || r % group_size(group)) return 0;
     if (meta_bytes_out) {
         const size_t ntile = ceil_div((int64_t)nb, META_TILE);
         *meta_bytes_out = (size_t)n_kv_heads * ntile * META_TILE * 2 * (key_ch > 0 ? key_ch : d) * s;
     }
-    return (size_t)n_kv_heads * nb * record_bytes(kind, r, s) + MKV_PACKED_TAIL_BYTES;
+    return (size_t)n_kv_heads * nb * record_bytes(kind, r, s, group) + MKV_PACKED_TAIL_BYTES;
 }
 
 mkv_status mkv_compress_append(mkv_cache *c, const void *k_new, const void *v_new, const int32_t *n_new,
@@ -583,6 +588,7 @@ mkv_status mkv_block_meta(const mkv_cache *c, int32_t seg, void *stream) {
             E.nbcap = (int32_t)ceil_div(sg.t_cap, BT);
             E.kind = sg.kind;
             E.kch = key_channels(sg.key_ch);
+            E.group = group_size(sg.group);
             max_nb = std::max(max_nb, E.nb);
         }
         A.n_ent = n;

@@ -21,9 +21,15 @@ constexpr int META_TILE = 64;   // blocks per meta tile
 __host__ __device__ constexpr bool packed_kind(int kind) { return kind == MKV_SEG_PACKED || kind == MKV_SEG_BITMAP; }
 // channels covered by a packed segment's block keys (0 means all)
 __host__ __device__ constexpr int key_channels(int key_ch) { return key_ch > 0 ? key_ch : D; }
+// channels per kept group (0 means single channels)
+__host__ __device__ constexpr int group_size(int group) { return group > 1 ? group : 1; }
+// position bytes of one vector: u8 indices, or a bitmap of one bit per group
+__host__ __device__ constexpr int pos_bytes(int kind, int r, int g) {
+    return kind == MKV_SEG_BITMAP ? D / 8 / group_size(g) : r;
+}
 // bytes of one packed block record (values, then u8 indices or bitmaps)
-__host__ __device__ constexpr int64_t record_bytes(int kind, int r, int sb) {
-    return (int64_t)BT * r * 2 * sb + (kind == MKV_SEG_BITMAP ? (int64_t)2 * BT * (D / 8) : (int64_t)2 * BT * r);
+__host__ __device__ constexpr int64_t record_bytes(int kind, int r, int sb, int g = 1) {
+    return (int64_t)BT * r * 2 * sb + (int64_t)2 * BT * pos_bytes(kind, r, g);
 }
 constexpr int MAX_SPLITS = 256; // attention splits per (request, KV head)
 // Partials per (request, query head): one per attend workgroup of 4 splits.
@@ -51,9 +57,10 @@ struct CompressEntry {
     int32_t blk0;     // first block touched
     int32_t nblk;     // blocks touched
     int32_t nbcap;    // block capacity of the segment
-    int16_t r;        // kept elements (packed)
+    uint8_t r;        // kept elements (packed)
     int8_t kind;      // MKV_SEG_*
     uint8_t kch;      // channels of the block keys (packed)
+    uint8_t group;    // channels per kept group (1: single channels)
 };  // 56 bytes
 
 struct CompressArgs {
@@ -78,7 +85,8 @@ struct MetaEntry {
     const void *data;
     void *meta;
     int32_t filled, nb, r, b, nbcap, kind;
-    int32_t kch, pad;  // channels of the block keys
+    int32_t kch;       // channels of the block keys
+    int32_t group;     // channels per kept group
 };  // 48 bytes
 
 struct MetaArgs {
@@ -91,7 +99,8 @@ struct DSeg {
     const void *data;
     const void *meta;
     const float *rot; // the segment's own rotations [n_kv][2][D][D], or nullptr (the cache's)
-    int16_t kind;
+    int8_t kind;
+    int8_t group;     // channels per kept group (1: single channels)
     int16_t slot;     // rotation slot: 0 the cache's rotation, else that of the segment index
     int16_t r;
     int16_t kch;      // channels of the block keys (packed)

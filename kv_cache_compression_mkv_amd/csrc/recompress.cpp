@@ -5,8 +5,11 @@
 // the segment itself, with the arithmetic of the GPU append:
 //   x'_c = sum_j R[c][j] x_j   binary64, exact products (binary32 x bfloat16
 //                               or binary32 x binary32 fit in 53 bits), j ascending
-//   the r largest |x'_c| kept (ties to the lower channel), stored in ascending
-//   channel order, each rounded once to nearest even to the storage type;
+//   the r largest |x'_c| kept (ties to the lower channel) -- or, with element
+//   groups of g adjacent channels, the r / g groups of largest energy
+//   sum_m x'^2 (binary64, each square and sum rounded, m ascending; ties to the
+//   lower group) -- stored in ascending channel order, each rounded once to
+//   nearest even to the storage type;
 //   per-block min/max keys of the stored sparse keys (0 at dropped channels)
 //   in IEEE totalOrder.
 // The result is written in the documented device layouts (include/mkv.h), so
@@ -77,12 +80,14 @@ uint32_t order_key(uint32_t v, int s) {
 
 extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_host, int32_t dtype, int32_t d,
                                              int32_t n_kv_heads, int64_t n_tokens, int64_t t_cap, int32_t kind,
-                                             int32_t r, int32_t key_ch, void *data_out, void *meta_out,
-                                             float *rot_out) {
+                                             int32_t r, int32_t key_ch, int32_t group, void *data_out,
+                                             void *meta_out, float *rot_out) {
     if (!k_host || !v_host || !data_out || !meta_out || !rot_out || n_kv_heads < 1 || t_cap < 1 || n_tokens < 1 ||
         n_tokens > t_cap || r < 1 || r > d || (kind != MKV_SEG_PACKED && kind != MKV_SEG_BITMAP) || key_ch < 0 ||
-        key_ch > d || key_ch % 8)
+        key_ch > d || key_ch % 8 || (group != 0 && group != 1 && group != 2 && group != 4 && group != 8))
         return MKV_ERR_ARG;
+    const int gs = group > 1 ? group : 1;  // channels per kept group
+    if (r % gs) return MKV_ERR_ARG;
     if (d != MKV_HEAD_DIM) return MKV_ERR_UNSUPPORTED;
     if (dtype != MKV_F32 && dtype != MKV_BF16) return MKV_ERR_UNSUPPORTED;
     if ((t_cap + BT - 1) / BT > MKV_MAX_PACKED_BLOCKS) return MKV_ERR_UNSUPPORTED;
@@ -91,7 +96,7 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
     const bool bitmap = kind == MKV_SEG_BITMAP;
     // record: K values, V values, then K and V positions (u8 indices [16][r]
     // each, or 16-byte bitmaps [16] each)
-    const int64_t pos_bytes = bitmap ? (int64_t)BT * (d / 8) : (int64_t)BT * r;
+    const int64_t pos_bytes = bitmap ? (int64_t)BT * (d / 8 / gs) : (int64_t)BT * r;
     const int64_t rec = (int64_t)BT * r * 2 * s + 2 * pos_bytes;
     const int64_t ntile = (nbcap + 63) / 64;
     const int kch = key_ch > 0 ? key_ch : d;  // channels of the block keys
@@ -116,7 +121,7 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
     // records: one (KV head, block) per iteration
 #pragma omp parallel
     {
-        std::vector<double> xr(d);
+        std::vector<double> xr(d), energy(d);
         std::vector<int> order(d), kept(r);
 #pragma omp for schedule(dynamic, 16) collapse(2)
         for (int g = 0; g < n_kv_heads; ++g)
@@ -139,16 +144,36 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
                             for (int j = 0; j < d; ++j) a += (double)R[(size_t)c * d + j] * raw_value(x, dtype, row + j);
                             xr[c] = a;
                         }
-                        for (int c = 0; c < d; ++c) order[c] = c;
-                        std::partial_sort(order.begin(), order.begin() + r, order.end(), [&](int a, int b) {
-                            const double ma = xr[a] < 0 ? -xr[a] : xr[a], mb = xr[b] < 0 ? -xr[b] : xr[b];
-                            return ma > mb || (ma == mb && a < b);
-                        });
-                        std::copy(order.begin(), order.begin() + r, kept.begin());
+                        if (gs == 1) {
+                            for (int c = 0; c < d; ++c) order[c] = c;
+                            std::partial_sort(order.begin(), order.begin() + r, order.end(), [&](int a, int b) {
+                                const double ma = xr[a] < 0 ? -xr[a] : xr[a], mb = xr[b] < 0 ? -xr[b] : xr[b];
+                                return ma > mb || (ma == mb && a < b);
+                            });
+                            std::copy(order.begin(), order.begin() + r, kept.begin());
+                        } else {
+                            const int ng = d / gs;
+                            for (int i = 0; i < ng; ++i) {
+                                double e = 0.0;
+                                for (int m = 0; m < gs; ++m) {
+                                    const double v = xr[gs * i + m];
+                                    const double sq = v * v;  // ISO C++ mode: no contraction
+                                    e += sq;
+                                }
+                                energy[i] = e;
+                                order[i] = i;
+                            }
+                            std::partial_sort(order.begin(), order.begin() + r / gs, order.begin() + ng,
+                                              [&](int a, int b) {
+                                                  return energy[a] > energy[b] || (energy[a] == energy[b] && a < b);
+                                              });
+                            for (int k = 0; k < r / gs; ++k)
+                                for (int m = 0; m < gs; ++m) kept[k * gs + m] = gs * order[k] + m;
+                        }
                         std::sort(kept.begin(), kept.end());
                         char *vals = blk + (size_t)kv * BT * r * s + (size_t)slot * r * s;
                         uint8_t *pos = reinterpret_cast<uint8_t *>(blk + (size_t)2 * BT * r * s + kv * pos_bytes +
-                                                                   (size_t)slot * (bitmap ? d / 8 : r));
+                                                                   (size_t)slot * (bitmap ? d / 8 / gs : r));
                         uint32_t stored[MKV_HEAD_DIM] = {0};
                         for (int m = 0; m < r; ++m) {
                             const int c = kept[m];
@@ -159,8 +184,11 @@ extern "C" mkv_status mkv_recompress_segment(const void *k_host, const void *v_h
                             } else {
                                 memcpy(vals + (size_t)m * 4, &bits, 4);
                             }
-                            if (bitmap) pos[c / 8] |= (uint8_t)(1u << (c % 8));
-                            else pos[m] = (uint8_t)c;
+                            if (bitmap) {
+                                if (c % gs == 0) pos[c / gs / 8] |= (uint8_t)(1u << ((c / gs) % 8));
+                            } else {
+                                pos[m] = (uint8_t)c;
+                            }
                             stored[c] = bits;
                         }
                         if (kv == 0)

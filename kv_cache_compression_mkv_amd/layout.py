@@ -32,25 +32,29 @@ def unpack_packed(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str):
                 kidx=ki, vidx=vi)
 
 
-def record_bytes(kind: int, r: int, dtype: str, d: int = 128) -> int:
-    """Bytes of one packed block record (kind 1: u8 indices, kind 2: bitmaps)."""
+def record_bytes(kind: int, r: int, dtype: str, d: int = 128, group: int = 0) -> int:
+    """Bytes of one packed block record (kind 1: u8 indices, kind 2: bitmaps of
+    one bit per channel, or per group of `group` channels)."""
     s = 2 if dtype == "bf16" else 4
-    return BT * r * 2 * s + (2 * BT * (d // 8) if kind == 2 else 2 * BT * r)
+    return BT * r * 2 * s + (2 * BT * (d // 8 // max(group, 1)) if kind == 2 else 2 * BT * r)
 
 
-def unpack_bitmap(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, d: int = 128):
-    """Bitmap records -> the fields of unpack_packed (indices are the set bits in
-    ascending order, 0-padded after a vector's last set bit) plus the bitmaps
-    as booleans [hkv][nbcap][16][d] (kbm, vbm)."""
+def unpack_bitmap(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, d: int = 128, group: int = 0):
+    """Bitmap records -> the fields of unpack_packed (indices are the kept
+    channels in ascending order, 0-padded after a vector's last one) plus the
+    kept channels as booleans [hkv][nbcap][16][d] (kbm, vbm; with element
+    groups, every channel of a set group bit)."""
     s = 2 if dtype == "bf16" else 4
-    rec = record_bytes(2, r, dtype, d)
+    g = max(group, 1)
+    rec = record_bytes(2, r, dtype, d, group)
     a = np.ascontiguousarray(data, np.uint8)[:hkv * nbcap * rec].reshape(hkv, nbcap, rec)
     kb, kv = _vals(np.ascontiguousarray(a[:, :, :BT * r * s]).reshape(-1), dtype)
     vb, vv = _vals(np.ascontiguousarray(a[:, :, BT * r * s:2 * BT * r * s]).reshape(-1), dtype)
-    nbm = BT * (d // 8)
+    nbm = BT * (d // 8 // g)
     def bits(x):
-        return np.unpackbits(np.ascontiguousarray(x).reshape(hkv, nbcap, BT, d // 8), axis=-1,
-                             bitorder="little").astype(bool)
+        gb = np.unpackbits(np.ascontiguousarray(x).reshape(hkv, nbcap, BT, d // 8 // g), axis=-1,
+                           bitorder="little").astype(bool)
+        return np.repeat(gb, g, axis=-1)
     kbm = bits(a[:, :, 2 * BT * r * s:2 * BT * r * s + nbm])
     vbm = bits(a[:, :, 2 * BT * r * s + nbm:2 * BT * r * s + 2 * nbm])
     def idx(bm):
@@ -65,10 +69,11 @@ def unpack_bitmap(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, d:
                 kidx=idx(kbm), vidx=idx(vbm), kbm=kbm, vbm=vbm)
 
 
-def unpack_records(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, kind: int, d: int = 128):
+def unpack_records(data: np.ndarray, hkv: int, nbcap: int, r: int, dtype: str, kind: int, d: int = 128,
+                   group: int = 0):
     """unpack_packed or unpack_bitmap by segment kind."""
     if kind == 2:
-        return unpack_bitmap(data, hkv, nbcap, r, dtype, d)
+        return unpack_bitmap(data, hkv, nbcap, r, dtype, d, group)
     return unpack_packed(data, hkv, nbcap, r, dtype)
 
 

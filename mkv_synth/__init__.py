@@ -192,6 +192,11 @@ def seg(kind, t_begin, t_cap, r=0, keep_ppm=0, k_abs=0, key_ch=0):
                 keep_ppm=int(keep_ppm), k_abs=int(k_abs), key_ch=int(key_ch))
 
 
+def with_groups(segs, group: int):
+    """The same segment table with every packed segment keeping whole groups of `group` channels."""
+    return [[dict(s, group=int(group)) if is_packed(s["kind"]) else dict(s) for s in row] for row in segs]
+
+
 def with_key_channels(segs, key_ch: int):
     """The same segment table with every packed segment's block keys over key_ch channels."""
     return [[dict(s, key_ch=int(key_ch)) if is_packed(s["kind"]) else dict(s) for s in row] for row in segs]

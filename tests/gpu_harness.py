@@ -136,8 +136,9 @@ def compare_compress(cache, w, comp, b, g, length):
                 assert np.all(bits[0, nb - 1, :, filled % 16:] == 0)
             continue
         r = s["r"]
-        rec = layout.record_bytes(s["kind"], r, dt, d)
-        P = layout.unpack_records(_head_bytes(cache.data[b][j], g, nbcap * rec), 1, nbcap, r, dt, s["kind"], d)
+        gs = s.get("group", 0)
+        rec = layout.record_bytes(s["kind"], r, dt, d, gs)
+        P = layout.unpack_records(_head_bytes(cache.data[b][j], g, nbcap * rec), 1, nbcap, r, dt, s["kind"], d, gs)
         for hat, idx, gbits, gidx, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
                                             (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
             ei = idx[tb:tb + filled, :r].astype(np.int64)
@@ -236,12 +237,12 @@ def compare_packed_blocks(cache, w, comp, b, g, j, blocks, length):
     s = w["segs"][b][j]
     r, tb = s["r"], s["t_begin"]
     nbcap = -(-s["t_cap"] // 16)
-    rec = layout.record_bytes(s["kind"], r, dt, d)
+    rec = layout.record_bytes(s["kind"], r, dt, d, s.get("group", 0))
     filled = min(max(length - tb, 0), s["t_cap"])
     data = cache.data[b][j]
     for l in blocks:
         off = (g * nbcap + l) * rec
-        P = layout.unpack_records(data[off:off + rec].cpu().numpy(), 1, 1, r, dt, s["kind"], d)
+        P = layout.unpack_records(data[off:off + rec].cpu().numpy(), 1, 1, r, dt, s["kind"], d, s.get("group", 0))
         nv = min(16, filled - 16 * l)
         for hat, idx, gb, gi, name in ((comp["Khat"], comp["Kidx"], P["kbits"], P["kidx"], "K"),
                                        (comp["Vhat"], comp["Vidx"], P["vbits"], P["vidx"], "V")):
@@ -283,7 +284,7 @@ class Snapshot:
         out = set()
         if synth.is_packed(s["kind"]):
             from kv_cache_compression_mkv_amd import layout
-            per = layout.record_bytes(s["kind"], s["r"], dt, d)
+            per = layout.record_bytes(s["kind"], s["r"], dt, d, s.get("group", 0))
         else:
             per = 2 * 16 * d * sb
         for off in self._diff(cache.data[b][j], self.data[b][j]):

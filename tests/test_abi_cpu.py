@@ -69,6 +69,15 @@ def test_segment_bytes(L):
     data, meta = L.mkv_segment_bytes(L.MKV_F32, L.MKV_SEG_BITMAP, 16, 128, 2, 100, 24)
     assert meta == 2 * 1 * 64 * 2 * 24 * 4
     assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_DENSE, 0, 128, 8, 100, 12)[0] > 0  # ignored for dense
+    # element groups: bitmaps of one bit per group; u8 records unchanged; g must divide r
+    for g, bm_bytes in ((1, 16), (2, 8), (4, 4), (8, 2)):
+        data, _ = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_BITMAP, 40, 128, 8, 63456, 0, g)
+        assert data == 8 * 3966 * (2 * 16 * 40 * 2 + 2 * 16 * bm_bytes) + L.MKV_PACKED_TAIL_BYTES
+        data, _ = L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_PACKED, 40, 128, 8, 63456, 0, g)
+        assert data == 8 * 3966 * 16 * 40 * 2 * 3 + L.MKV_PACKED_TAIL_BYTES
+    for g in (3, 16, -2):
+        assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_BITMAP, 40, 128, 8, 100, 0, g)[0] == 0
+    assert L.mkv_segment_bytes(L.MKV_BF16, L.MKV_SEG_BITMAP, 38, 128, 8, 100, 0, 4)[0] == 0  # 4 does not divide 38
 
 
 class FakeCache:
@@ -85,6 +94,7 @@ class FakeCache:
                 e.kind, e.r, e.keep_ppm, e.k_abs = s["kind"], s["r"], s["keep_ppm"], s["k_abs"]
                 e.t_begin, e.t_cap = s["t_begin"], s["t_cap"]
                 e.key_ch = s.get("key_ch", 0)
+                e.group = s.get("group", 0)
                 e.data = 0x10000 * (1 + b * n + j)
                 e.meta = 0x90000000 + 0x10000 * (b * n + j) if s["kind"] in (1, 2) else None
         self.c = L.mkv_cache(batch, hq, hkv, d, L.MKV_BF16 if dtype is None else dtype, n,
@@ -165,7 +175,18 @@ def test_key_channel_descriptors(L):
     f.arr[1 * len(base) + 1].key_ch = 64
     assert L.mkv_decode_workspace_bytes(f.c) == 0
     f.arr[1 * len(base) + 1].key_ch = 32
-    f.arr[1].reserved = 1
+    assert L.mkv_decode_workspace_bytes(f.c) > 0
+
+
+def test_group_descriptors(L):
+    """group: 0, 1, 2, 4 or 8, dividing r, the same in every request."""
+    base = _segs_cfg2()  # r = 38
+    for g, ok in ((0, True), (1, True), (2, True), (4, False), (3, False), (16, False)):
+        segs = synth.with_groups([base], g)[0]
+        assert (L.mkv_decode_workspace_bytes(FakeCache(L, segs, lengths=[32768]).c) > 0) == ok, g
+    f = FakeCache(L, synth.with_groups([base], 2)[0], batch=2, lengths=[32768, 32768])
+    assert L.mkv_decode_workspace_bytes(f.c) > 0
+    f.arr[1 * len(base) + 1].group = 0
     assert L.mkv_decode_workspace_bytes(f.c) == 0
 
 

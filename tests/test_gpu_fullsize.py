@@ -62,7 +62,7 @@ def check_index_properties(c, w):
                 continue
             r, nbcap = s["r"], -(-s["t_cap"] // 16)
             if s["kind"] == synth.BITMAP:
-                rec = layout.record_bytes(s["kind"], r, w["dtype"], w["d"])
+                rec = layout.record_bytes(s["kind"], r, w["dtype"], w["d"], s.get("group", 0))
                 for g in range(w["n_kv_heads"]):
                     raw = c.data[b][j][g * nbcap * rec:(g + 1) * nbcap * rec].view(nbcap, rec)
                     bm = raw[:, 2 * 16 * r * sb:].cpu().numpy().reshape(nbcap, 2, 16, w["d"] // 8)

@@ -21,11 +21,12 @@ def _bits(v, dtype):
     return (f.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else f.view(np.uint32)
 
 
-@pytest.mark.parametrize("dtype,r,n,cap,kind,key_ch", [("bf16", 26, 500, 520, 1, 0), ("bf16", 38, 1024, 1024, 1, 0),
-                                                       ("f32", 32, 333, 400, 1, 0), ("bf16", 38, 500, 520, 2, 0),
-                                                       ("f32", 17, 333, 400, 2, 0), ("bf16", 38, 500, 520, 1, 32),
-                                                       ("f32", 20, 333, 400, 2, 96)])
-def test_recompress_matches_oracle(L, dtype, r, n, cap, kind, key_ch):
+@pytest.mark.parametrize("dtype,r,n,cap,kind,key_ch,group", [
+    ("bf16", 26, 500, 520, 1, 0, 0), ("bf16", 38, 1024, 1024, 1, 0, 0), ("f32", 32, 333, 400, 1, 0, 0),
+    ("bf16", 38, 500, 520, 2, 0, 0), ("f32", 17, 333, 400, 2, 0, 0), ("bf16", 38, 500, 520, 1, 32, 0),
+    ("f32", 20, 333, 400, 2, 96, 0), ("bf16", 40, 500, 520, 2, 0, 4), ("bf16", 38, 333, 400, 1, 0, 2),
+    ("f32", 48, 300, 320, 2, 64, 8)])
+def test_recompress_matches_oracle(L, dtype, r, n, cap, kind, key_ch, group):
     from kv_cache_compression_mkv_amd import layout
     hkv, d = 2, 128
     code = L.MKV_BF16 if dtype == "bf16" else L.MKV_F32
@@ -35,14 +36,14 @@ def test_recompress_matches_oracle(L, dtype, r, n, cap, kind, key_ch):
     for g in range(hkv):
         synth.gen_kv_into(7, 0, g, 0, 1000, 1000 + n, dtype, K[g], d)
         synth.gen_kv_into(7, 0, g, 1, 1000, 1000 + n, dtype, V[g], d)
-    nbytes, mbytes = L.mkv_segment_bytes(code, kind, r, d, hkv, cap, key_ch)
+    nbytes, mbytes = L.mkv_segment_bytes(code, kind, r, d, hkv, cap, key_ch, group)
     data = np.full(nbytes, 0xAB, np.uint8)
     meta = np.full(mbytes, 0xCD, np.uint8)
     rot = np.empty((hkv, 2, d, d), np.float32)
     L.mkv_recompress_segment(K.ctypes.data, V.ctypes.data, code, d, hkv, n, cap, kind, r, data.ctypes.data,
-                             meta.ctypes.data, rot.ctypes.data, key_ch)
+                             meta.ctypes.data, rot.ctypes.data, key_ch, group)
     nbcap, nb = -(-cap // 16), -(-n // 16)
-    P = layout.unpack_records(data, hkv, nbcap, r, dtype, kind, d)
+    P = layout.unpack_records(data, hkv, nbcap, r, dtype, kind, d, group)
     if kind == L.MKV_SEG_BITMAP:  # exactly r positions per stored vector, none in empty slots
         for bm in (P["kbm"], P["vbm"]):
             cnt = bm.sum(axis=-1).reshape(hkv, -1)
@@ -51,7 +52,7 @@ def test_recompress_matches_oracle(L, dtype, r, n, cap, kind, key_ch):
     _, mbits = layout.unpack_meta(meta, hkv, nbcap, dtype, d, key_ch)
     to64 = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if dtype == "bf16" else \
         (lambda a: a.astype(np.float64))
-    segs = [synth.seg(1, 0, cap, r, 100000, 0)]
+    segs = [dict(synth.seg(1, 0, cap, r, 100000, 0), group=group)]
     for g in range(hkv):
         Kr, Vr = to64(K[g]), to64(V[g])
         # the segment's rotation is the one the library computes from its vectors
@@ -69,7 +70,7 @@ def test_recompress_matches_oracle(L, dtype, r, n, cap, kind, key_ch):
         assert np.array_equal(mbits[g, :nb], _bits(comp["meta"][0][:, :, :kch], dtype))
         assert np.all(mbits[g, nb:] == 0)
     # the tail bytes after the last record are not written
-    assert np.all(data[hkv * nbcap * layout.record_bytes(kind, r, dtype, d):] == 0xAB)
+    assert np.all(data[hkv * nbcap * layout.record_bytes(kind, r, dtype, d, group):] == 0xAB)
 
 
 def test_recompress_rejects_bad_arguments(L):

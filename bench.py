@@ -113,9 +113,10 @@ def union_summary(w, lengths, sel):
     return out
 
 
-def counter_traffic(kernel_key: str):
+def counter_traffic(kernel_key: str, workload_key: dict):
     """HBM bytes per dispatch from the committed counter summary, or None when it
-    is missing or was taken on other kernel sources."""
+    is missing, was taken on other kernel sources or on another workload
+    (workload_key: config, scale, record layout, key channels, element group)."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
@@ -126,7 +127,7 @@ def counter_traffic(kernel_key: str):
     for name in sorted(os.listdir(src)):
         with open(os.path.join(src, name), "rb") as f:
             h.update(f.read())
-    if c.get("source_sha256") != h.hexdigest():
+    if c.get("source_sha256") != h.hexdigest() or c.get("workload") != workload_key:
         return None
     k = c.get("kernels", {}).get(kernel_key)
     if not k:
@@ -387,7 +388,8 @@ def main():
     dom = max(("attend", "score"), key=lambda k: stage_ms.get(k, 0.0))
     dom_ms = stage_ms[dom]
     achieved = cand[dom] / (dom_ms * 1e-3) / 1e9
-    traffic = counter_traffic(dom)
+    traffic = counter_traffic(dom, {"config": args.config, "scale": args.scale, "layout": args.layout,
+                                    "key_ch": args.key_ch, "group": max(args.group, 1)})
     dense_equiv = bm.dense_kv_bytes(int(np.sum(lens_now)), d, sb) * hkv
     dec_ms = sum(stage_ms.get(k, 0.0) for k in ("q_rotate", "score", "select", "attend", "merge"))
     if not stage_ms.get("q_rotate"):

@@ -1309,24 +1309,36 @@ __device__ __forceinline__ void bitmap_positions(const uint4 b, int p, uint8_t *
 // the 16-byte window w. Lane p of a token writes the channels of its groups
 // in channels 32 p .. 32 p + 31, g bytes per group as one aligned store (r is
 // a multiple of g, so every group's rank is), at rank g * (groups before it).
-__device__ __forceinline__ uint64_t group_bits(const uint4 w, uint32_t off, int g) {
+// (The group size is a template argument: with it known, the shifts, masks
+// and the store width fold away; a uniform switch picks the instance.)
+template <int GS>
+__device__ __forceinline__ uint64_t group_bits(const uint4 w, uint32_t off) {
     const uint64_t lo = ((uint64_t)w.y << 32) | w.x, hi = ((uint64_t)w.w << 32) | w.z;
     const uint64_t x = ((off & 8u) ? hi : lo) >> (8 * (off & 7u));
-    const int n = D / g;  // bits
-    return n >= 64 ? x : (x & ((1ull << n) - 1ull));
+    constexpr int n = D / GS;  // bits
+    if constexpr (n >= 64) return x;
+    else return x & ((1ull << n) - 1ull);
 }
-__device__ __forceinline__ void group_positions(uint64_t gb, int g, int p, uint8_t *dst) {
-    const int gw = 32 / g, i0 = p * gw;  // groups per lane, the lane's first group
+template <int GS>
+__device__ __forceinline__ void group_positions(uint64_t gb, int p, uint8_t *dst) {
+    constexpr int gw = 32 / GS;  // groups per lane
+    const int i0 = p * gw;       // the lane's first group
     uint32_t w = (uint32_t)((gb >> i0) & ((1ull << gw) - 1ull));
-    int pos = g * __popcll(gb & ((1ull << i0) - 1ull));
+    int pos = GS * __popcll(gb & ((1ull << i0) - 1ull));
     while (w) {
-        const uint32_t c = (uint32_t)(g * (i0 + __builtin_ctz(w)));
-        if (g == 2) *reinterpret_cast<uint16_t *>(dst + pos) = (uint16_t)(c | ((c + 1u) << 8));
-        else if (g == 4) *reinterpret_cast<uint32_t *>(dst + pos) = c * 0x01010101u + 0x03020100u;
+        const uint32_t c = (uint32_t)(GS * (i0 + __builtin_ctz(w)));
+        if constexpr (GS == 2) *reinterpret_cast<uint16_t *>(dst + pos) = (uint16_t)(c | ((c + 1u) << 8));
+        else if constexpr (GS == 4) *reinterpret_cast<uint32_t *>(dst + pos) = c * 0x01010101u + 0x03020100u;
         else *reinterpret_cast<uint64_t *>(dst + pos) = (uint64_t)c * 0x0101010101010101ull + 0x0706050403020100ull;
-        pos += g;
+        pos += GS;
         w &= w - 1u;
     }
+}
+template <int GS>
+__device__ __forceinline__ void group_positions_kv(const uint4 &bk, const uint4 &bv, uint32_t ok, uint32_t ov, int p,
+                                                   uint8_t *dk, uint8_t *dv) {
+    group_positions<GS>(group_bits<GS>(bk, ok), p, dk);
+    group_positions<GS>(group_bits<GS>(bv, ov), p, dv);
 }
 
 // N dwords from the wave's LDS index buffer (4-byte aligned)
@@ -1442,12 +1454,15 @@ __device__ __forceinline__ void pk_proc(const PkWin<ST, QM, BM> &W, const PkGeom
         // the record's u8 indices, decoded from its bitmaps into the wave's
         // LDS buffer ([16][r] K then [16][r] V), then read as index windows
         const int t = lane >> 2, p = lane & 3;
-        if (gm.g > 1) {
-            group_positions(group_bits(W.bk, gm.o_bk & 15u, gm.g), gm.g, p, ib + t * r);
-            group_positions(group_bits(W.bv, gm.o_bv & 15u, gm.g), gm.g, p, ib + BT * r + t * r);
-        } else {
-            bitmap_positions(W.bk, p, ib + t * r);
-            bitmap_positions(W.bv, p, ib + BT * r + t * r);
+        uint8_t *dk = ib + t * r, *dv = ib + BT * r + t * r;
+        const uint32_t ok = gm.o_bk & 15u, ov = gm.o_bv & 15u;
+        switch (gm.g) {
+        case 2: group_positions_kv<2>(W.bk, W.bv, ok, ov, p, dk, dv); break;
+        case 4: group_positions_kv<4>(W.bk, W.bv, ok, ov, p, dk, dv); break;
+        case 8: group_positions_kv<8>(W.bk, W.bv, ok, ov, p, dk, dv); break;
+        default:
+            bitmap_positions(W.bk, p, dk);
+            bitmap_positions(W.bv, p, dv);
         }
         wave_lds_sync();
         lds_words(ib + gm.l_ki, wki);

@@ -49,3 +49,21 @@ def test_noalloc_equals_workspace_decode():
         assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), name
         assert np.all(np.isfinite(out.cpu().numpy()))
         log("noalloc call %d (%s): outputs and selections equal the workspace call's" % (i, name))
+
+
+def test_noalloc_equals_workspace_decode_other_layouts():
+    """The same equality for bitmap records with element pairs and 64-channel
+    block keys, then the default layout again (the scratch array keeps the
+    previous call's contents)."""
+    from kv_cache_compression_mkv_amd import _lib as L
+    w = synth.workload(3, scale=16)
+    w["segs"] = synth.with_key_channels(synth.with_groups(synth.as_bitmap(w["segs"]), 2), 64)
+    c, _, _ = build(torch, w)
+    d, _, _ = build(torch, synth.workload(2, scale=8))
+    for i, (name, ww, cc) in enumerate((("bitmap pairs, 64-channel keys", w, c), ("default", synth.workload(2, scale=8), d))):
+        assert cc.workspace_bytes() <= L.MKV_SCRATCH_BYTES
+        q = torch.from_numpy(synth.gen_q(ww["cfg"], 60 + i, ww["batch"], ww["n_q_heads"], ww["dtype"])).cuda()
+        ref_out, ref_sel, out, sel = _both(cc, q)
+        assert torch.equal(sel, ref_sel), name
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), name
+        log("noalloc (%s): outputs and selections equal the workspace call's" % name)

@@ -32,17 +32,25 @@ def _workload(G, dtype, B=2):
                 segs=[segs] * B)
 
 
-@pytest.mark.parametrize("G,dtype", [(1, "bf16"), (2, "bf16"), (2, "f32"), (1, "f32")])
-def test_group_sizes_match_oracle(G, dtype):
+@pytest.mark.parametrize("G,dtype,layout", [(1, "bf16", "u8"), (2, "bf16", "u8"), (2, "f32", "u8"), (1, "f32", "u8"),
+                                            (1, "bf16", "bitmap"), (2, "bf16", "bitmap_pairs"),
+                                            (2, "f32", "bitmap")])
+def test_group_sizes_match_oracle(G, dtype, layout):
+    """Also with bitmap records (one bit per channel, or per pair of channels
+    with element pairs), whose decode runs its own kernel instances."""
     from kv_cache_compression_mkv_amd import _lib as L
     w = _workload(G, dtype)
+    if layout != "u8":
+        w["segs"] = synth.as_bitmap(w["segs"])
+    if layout == "bitmap_pairs":
+        w["segs"] = synth.with_groups(w["segs"], 2)
     T0 = [int(t) for t in w["lengths"]]
     steps = [1, 1, 24]
     K, V, _ = gen_raw(w, [t + sum(steps) for t in T0])
     R = rotations(L, w, K, V, T0)
     a, _, _ = build(torch, w, lengths=T0, raw=(K, V, T0), R=R)
     t, _, _ = build(torch, w, lengths=T0, raw=(K, V, T0), R=R)
-    log("groups G=%d %s lengths=%s" % (G, dtype, T0))
+    log("groups G=%d %s %s lengths=%s" % (G, dtype, layout, T0))
     B, hq = w["batch"], w["n_q_heads"]
     for i, nn in enumerate(steps):
         lens = a.lengths

@@ -125,8 +125,8 @@ def test_element_groups_128k_layout_scaled():
     log("element pairs on the 128K layout (1/32): records, keys, selections and outputs match the oracle")
 
 
-@pytest.mark.parametrize("bitmap", [True, False])
-def test_element_group_edge_cases(bitmap):
+@pytest.mark.parametrize("bitmap,dtype", [(True, "bf16"), (False, "bf16"), (True, "f32")])
+def test_element_group_edge_cases(bitmap, dtype):
     """One group per vector (r = g = 8), every group kept (r = d = 128, g = 4),
     and tokens whose rotated vectors are all zero (every group ties at energy
     0: the lowest groups are kept), through a bulk append, one-token appends
@@ -137,7 +137,7 @@ def test_element_group_edge_cases(bitmap):
             dict(synth.seg(P, 32 + 16 * 40, 16 * 30, 128, 200000, 0), group=4),
             dict(synth.seg(P, 32 + 16 * 70, 64, 16, 500000, 0), group=2)]
     B, T0 = 2, [32 + 16 * 70 + 3, 32 + 16 * 55 + 7]
-    w = dict(cfg=2, batch=B, n_q_heads=32, n_kv_heads=8, d=128, dtype="bf16", lengths=np.array(T0), segs=[segs] * B)
+    w = dict(cfg=2, batch=B, n_q_heads=32, n_kv_heads=8, d=128, dtype=dtype, lengths=np.array(T0), segs=[segs] * B)
     K, V, _ = gen_raw(w, [t + 3 for t in T0])
     R = rotations(L, w, K, V, T0)
     # zero vectors: a few whole tokens of every head, in every packed segment
@@ -149,7 +149,7 @@ def test_element_group_edge_cases(bitmap):
         lens = a.lengths
         kk = np.ascontiguousarray(np.stack([K[b, :, lens[b]:lens[b] + 1] for b in range(B)]))
         vv = np.ascontiguousarray(np.stack([V[b, :, lens[b]:lens[b] + 1] for b in range(B)]))
-        q = synth.gen_q(2, 950 + i, B, 32, "bf16")
+        q = synth.gen_q(2, 950 + i, B, 32, dtype)
         out, sel = a.append_decode(to_device(torch, kk), to_device(torch, vv), [1] * B, torch.from_numpy(q).cuda(),
                                    want_sel=True)
         torch.cuda.synchronize()
@@ -160,5 +160,5 @@ def test_element_group_edge_cases(bitmap):
                 comp, Rk, Rv = oracle_unit(w, (K, V, a.lengths), R, b, gg, length)
                 compare_compress(a, w, comp, b, gg, length)
                 check_decode_unit(w, comp, Rk, Rv, q[b, 4 * gg:4 * gg + 4].astype(np.float64),
-                                  out[b, 4 * gg:4 * gg + 4], sel[b, 4 * gg:4 * gg + 4], 5e-3, length, b, gg)
-    log("element-group edge cases (bitmap=%s): one group, all groups, zero vectors" % bitmap)
+                                  out[b, 4 * gg:4 * gg + 4], sel[b, 4 * gg:4 * gg + 4], TOL[dtype], length, b, gg)
+    log("element-group edge cases (bitmap=%s, %s): one group, all groups, zero vectors" % (bitmap, dtype))

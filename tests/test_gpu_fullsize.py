@@ -62,11 +62,12 @@ def check_index_properties(c, w):
                 continue
             r, nbcap = s["r"], -(-s["t_cap"] // 16)
             if s["kind"] == synth.BITMAP:
-                rec = layout.record_bytes(s["kind"], r, w["dtype"], w["d"], s.get("group", 0))
+                gs = max(s.get("group", 0), 1)  # channels per position bit
+                rec = layout.record_bytes(s["kind"], r, w["dtype"], w["d"], gs)
                 for g in range(w["n_kv_heads"]):
                     raw = c.data[b][j][g * nbcap * rec:(g + 1) * nbcap * rec].view(nbcap, rec)
-                    bm = raw[:, 2 * 16 * r * sb:].cpu().numpy().reshape(nbcap, 2, 16, w["d"] // 8)
-                    cnt = _POPC8[bm].sum(axis=-1, dtype=np.int32).transpose(0, 2, 1).reshape(nbcap * 16, 2)
+                    bm = raw[:, 2 * 16 * r * sb:].cpu().numpy().reshape(nbcap, 2, 16, w["d"] // 8 // gs)
+                    cnt = gs * _POPC8[bm].sum(axis=-1, dtype=np.int32).transpose(0, 2, 1).reshape(nbcap * 16, 2)
                     assert np.all(cnt[:filled] == r), "b=%d seg=%d g=%d: bitmap counts" % (b, j, g)
                     assert np.all(cnt[filled:] == 0), "b=%d seg=%d g=%d: bitmap padding" % (b, j, g)
                 continue
@@ -159,18 +160,23 @@ def _check_outputs(w, lengths, q, out, sel, comps):
     return ex
 
 
-def test_128k_batch4_benchmark_launch():
+@pytest.mark.parametrize("variant", ["u8", "bitmap_pairs_keych32"])
+def test_128k_batch4_benchmark_launch(variant):
     """128K context, batch 4, three segments plus the decode-time update segment,
     stepped exactly as the benchmark steps it: one mkv_append_decode call per
     step appending one token per request. A twin cache stepped with separate
     mkv_compress_append and mkv_decode_attn calls gives the same outputs,
     selections and stored bytes; three sampled units match the oracle at every
-    step (selection and outputs) and, at the end, every stored token."""
+    step (selection and outputs) and, at the end, every stored token. Also in
+    the paper's packed format: bitmap records with element pairs and block keys
+    over 32 channels (bench.py --layout bitmap --group 2 --key-ch 32)."""
     steps = 3
     w = synth.with_update_segment(synth.workload(3), cap=109)
+    if variant != "u8":
+        w["segs"] = synth.with_key_channels(synth.with_groups(synth.as_bitmap(w["segs"]), 2), 32)
     T0 = [int(t) for t in w["lengths"]]
     B = w["batch"]
-    log("128K batch-4 full: generating %d x %d rows" % (B * w["n_kv_heads"] * 2, T0[0] + steps))
+    log("128K batch-4 full (%s): generating %d x %d rows" % (variant, B * w["n_kv_heads"] * 2, T0[0] + steps))
     K, V, n = gen_raw(w, [t + steps for t in T0])
     from kv_cache_compression_mkv_amd import _lib as L
     R = rotations(L, w, K, V, T0)

@@ -3,8 +3,9 @@
  * MosaicKV ("MosaicKV: Serving Long-Context LLM with Dynamic Two-D KV Cache
  * Compression", arXiv 2607.00760) compresses a KV cache in two dimensions:
  * every key/value vector is rotated by its head's SVD-derived orthogonal
- * matrix and keeps only its own r largest elements, stored as packed
- * (channel index, value) pairs; at decode time each query head scores blocks
+ * matrix and keeps only its own r largest elements (or whole groups of
+ * adjacent channels), stored as packed (channel index, value) pairs or as
+ * values with a position bitmap; at decode time each query head scores blocks
  * of 16 tokens from per-block min/max keys, keeps the top-k blocks and runs
  * attention directly on the packed vectors, rotating the result back.
  *
@@ -13,7 +14,7 @@
  *       (Eq. 3-5), rotation (Eq. 6-8), per-vector selection (Eq. 9,
  *       Algorithm 1), block score / compressed attention / inverse rotation
  *       (Eq. 12-14), packed sparse attention section, Quest paragraph.
- *   [S] paperlayer.ai summary of the paper: sections 4.2, 4.3, 5.1-5.4, 6.3.
+ *   [S] paperlayer.ai summary of the paper: sections 4.2, 4.3, 5.1-5.5, 6.3.
  *
  * Conventions for every call:
  *   - Arguments are validated on the host before anything is enqueued. On an
@@ -27,7 +28,7 @@
  *     used from one stream at a time.
  *   - Inputs must be finite (NaN/Inf behaviour is unspecified).
  *   - The GPU path supports head_dim == 128, storage MKV_F32 or MKV_BF16, and
- *     1 to 4 query heads per KV head.
+ *     1, 2 or 4 query heads per KV head.
  */
 #ifndef MKV_H
 #define MKV_H

@@ -2121,10 +2121,38 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
         for (int u = 0; u < 16; ++u) rv[u] = Rv4[(size_t)(cc * 16 + u) * (D / 4) + j4];
     }
 
+    // Every load of the first slot is issued before any result is used: the
+    // partials' (m, l) (thread t takes partials t, t + 256, ...) and this
+    // thread's accumulator words, channels 4 quad .. 4 quad + 3 of partials
+    // grp, grp + 8, ... (grp, quad) = (t / 32, t % 32).
+    constexpr int NML = (MAX_SLOTS * MAX_PARTS + 255) / 256;
+    constexpr int NY = (MAX_PARTS + 7) / 8;
+    const int quad = t & 31, grp = t >> 5;
+    float mi[NML], li[NML];
+#pragma unroll
+    for (int u = 0; u < NML; ++u) {
+        const int i = t + 256 * u;
+        const bool ok = i < ns * MAX_PARTS && i % MAX_PARTS < A.nparts[i / MAX_PARTS];
+        mi[u] = ok ? pp[(size_t)i * PART] : -INFINITY;
+        li[u] = ok ? pp[(size_t)i * PART + 1] : 0.f;
+    }
+    float2 xa[NY], xb[NY];
+    {
+        const int np = A.nparts[0];
+#pragma unroll
+        for (int k = 0; k < NY; ++k) {
+            const int y = grp + 8 * k;
+            if (y < np) {
+                const float *src = pp + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
+                xa[k] = *reinterpret_cast<const float2 *>(src);
+                xb[k] = *reinterpret_cast<const float2 *>(src + 2);
+            }
+        }
+    }
     // partial weights: w_p = exp2(m_p - M), L = sum_p w_p l_p over every slot
     float m = -INFINITY;
-    for (int i = t; i < ns * MAX_PARTS; i += 256)
-        if (i % MAX_PARTS < A.nparts[i / MAX_PARTS]) m = fmaxf(m, pp[(size_t)i * PART]);
+#pragma unroll
+    for (int u = 0; u < NML; ++u) m = fmaxf(m, mi[u]);
     {
         float v = row_max16(m);
         v = fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
@@ -2133,14 +2161,17 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     float wl = 0.f;
-    for (int i = t; i < ns * MAX_PARTS; i += 256) {
-        float w = 0.f;
-        if (i % MAX_PARTS < A.nparts[i / MAX_PARTS]) {
-            const float mi = pp[(size_t)i * PART];
-            w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
-            wl = fmaf(w, pp[(size_t)i * PART + 1], wl);
+#pragma unroll
+    for (int u = 0; u < NML; ++u) {
+        const int i = t + 256 * u;
+        if (i < ns * MAX_PARTS) {
+            float w = 0.f;
+            if (i % MAX_PARTS < A.nparts[i / MAX_PARTS]) {
+                w = (mi[u] == -INFINITY) ? 0.f : fast_exp2(mi[u] - M);
+                wl = fmaf(w, li[u], wl);
+            }
+            wsc[i] = w;
         }
-        wsc[i] = w;
     }
     {
         const float v = wave_sum(wl);
@@ -2154,18 +2185,31 @@ __global__ __launch_bounds__(256) void k_merge(const DecodeArgs A) {
         const int np = A.nparts[slot];
         {
             // thread (grp, quad): channels 4 quad .. 4 quad + 3 over partials grp, grp + 8, ...
-            const int quad = t & 31, grp = t >> 5;
             float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot == 0) {
+#pragma unroll
+                for (int k = 0; k < NY; ++k) {
+                    const int y = grp + 8 * k;
+                    if (y < np) {
+                        const float wy = wsc[y];
+                        o.x = fmaf(wy, xa[k].x, o.x);
+                        o.y = fmaf(wy, xa[k].y, o.y);
+                        o.z = fmaf(wy, xb[k].x, o.z);
+                        o.w = fmaf(wy, xb[k].y, o.w);
+                    }
+                }
+            } else {
 #pragma unroll 8
-            for (int y = grp; y < np; y += 8) {
-                const float wy = wsc[slot * MAX_PARTS + y];
-                const float *src = ps + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
-                const float2 x0 = *reinterpret_cast<const float2 *>(src);
-                const float2 x1 = *reinterpret_cast<const float2 *>(src + 2);
-                o.x = fmaf(wy, x0.x, o.x);
-                o.y = fmaf(wy, x0.y, o.y);
-                o.z = fmaf(wy, x1.x, o.z);
-                o.w = fmaf(wy, x1.y, o.w);
+                for (int y = grp; y < np; y += 8) {
+                    const float wy = wsc[slot * MAX_PARTS + y];
+                    const float *src = ps + (size_t)y * PART + 2 + quad * 4;  // 8-byte aligned
+                    const float2 x0 = *reinterpret_cast<const float2 *>(src);
+                    const float2 x1 = *reinterpret_cast<const float2 *>(src + 2);
+                    o.x = fmaf(wy, x0.x, o.x);
+                    o.y = fmaf(wy, x0.y, o.y);
+                    o.z = fmaf(wy, x1.x, o.z);
+                    o.w = fmaf(wy, x1.y, o.w);
+                }
             }
             *reinterpret_cast<float4 *>(&part_o[grp][quad * 4]) = o;
         }

@@ -2258,6 +2258,7 @@ hipError_t select_launch(const DecodeArgs &a, hipStream_t s) {
     switch (a.sel_kpt) {
     case 0: break;  // every packed segment takes the sliced select
     case 4: e = select_launch_kpt<G, 4>(a, s); break;
+    case 8: e = select_launch_kpt<G, 8>(a, s); break;
     case 16: e = select_launch_kpt<G, 16>(a, s); break;
     default: return hipErrorInvalidValue;
     }

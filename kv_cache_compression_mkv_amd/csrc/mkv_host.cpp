@@ -483,10 +483,11 @@ mkv_status decode_enqueue(const mkv_cache *c, const float *q, float *out, int32_
                 }
             }
         }
-        // select: 4 keys per lane up to 1024 blocks, 16 up to BIG_SEL_MIN
-        // (at most 16 waves); larger segments take the sliced select
+        // select: the fewest keys per lane (4, 8 or 16) that 16 waves cover;
+        // more waves with fewer keys each shorten every phase of this
+        // latency-bound kernel. Larger segments take the sliced select.
         static_assert(BIG_SEL_MIN <= 16 * 64 * 16, "one select workgroup covers every unsliced segment");
-        const int kpt = max_nb <= 1024 ? 4 : 16;
+        const int kpt = max_nb <= 16 * 64 * 4 ? 4 : max_nb <= 16 * 64 * 8 ? 8 : 16;
         A.sel_kpt = unsliced ? kpt : 0;  // 0: no one-workgroup select launch
         A.sel_waves = (int32_t)std::max<int64_t>(1, ceil_div(max_nb, 64 * kpt));
 

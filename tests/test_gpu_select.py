@@ -69,11 +69,12 @@ def _set_block_values(c, w, comp, b, g, j, a):
     comp["meta_flat"][off:off + nb] = vals
 
 
-@pytest.mark.parametrize("nb", [3000, 20000])
+@pytest.mark.parametrize("nb", [3000, 6000, 12000, 20000])
 @pytest.mark.parametrize("case", ["ties", "outlier", "mixed_sign", "all_equal", "crowded"])
 def test_select_adversarial_scores(case, nb):
-    """nb = 3000 blocks: one workgroup per head; nb = 20000 (more than
-    16384): the sliced select over 4096-block slices."""
+    """nb = 3000, 6000 and 12000 blocks: one workgroup per head, with 4, 8
+    and 16 keys per lane; nb = 20000 (more than 16384): the sliced select over
+    4096-block slices."""
     hkv = 2 if nb <= 4096 else 1
     segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * nb, 38, 100000, 0),
             synth.seg(synth.DENSE, 32 + 16 * nb, 64)]

@@ -113,3 +113,28 @@ def test_select_adversarial_scores(case, nb):
                 "%s: g=%d h=%d selection differs" % (case, g, h)
         ex += check_decode_unit(w, comp, Rk, Rv, q[0, hs].astype(np.float64), out[0, hs], sel[0, hs], 5e-3, T, 0, g)
     log("adversarial select (%s, %d blocks): selections equal the oracle's" % (case, nb))
+
+
+@pytest.mark.parametrize("G,nb", [(1, 3000), (2, 6000), (1, 12000), (2, 12000)])
+def test_select_group_sizes_on_ties(G, nb):
+    """The one-workgroup select instances for 1 and 2 query heads per KV head
+    (4, 8 and 16 keys per lane at 3000, 6000 and 12000 blocks), on scores with
+    many exact ties at the k-th value: selections equal the oracle's."""
+    segs = [synth.seg(synth.DENSE, 0, 32), synth.seg(synth.PACKED, 32, 16 * nb, 38, 100000, 0),
+            synth.seg(synth.DENSE, 32 + 16 * nb, 64)]
+    T = 32 + 16 * nb + 40
+    w = dict(cfg=2, batch=1, n_q_heads=G, n_kv_heads=1, d=128, dtype="bf16", lengths=np.array([T]), segs=[segs])
+    c, raw, R = build(torch, w)
+    rng = np.random.default_rng(100 + G)
+    a = np.round(rng.uniform(1.0, 2.0, nb) * 8) / 8  # 9 distinct values
+    q = synth.gen_q(2, 12, 1, G, "bf16")
+    comp, Rk, Rv = oracle_unit(w, raw, R, 0, 0, T)
+    _set_block_values(c, w, comp, 0, 0, 1, a)
+    out, sel = c.decode(torch.from_numpy(q).cuda(), want_sel=True)
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    own = orc.decode_unit(comp, q[0].astype(np.float64), Rk, Rv)
+    for h in range(G):
+        assert sel[0, h, :own["sel"][0].shape[1]].tolist() == own["sel"][0][h].tolist(), "G=%d h=%d" % (G, h)
+    check_decode_unit(w, comp, Rk, Rv, q[0].astype(np.float64), out[0], sel[0], 5e-3, T, 0, 0)
+    log("select with G=%d on %d tied blocks: selections equal the oracle's" % (G, nb))
